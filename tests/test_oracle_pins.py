@@ -1,0 +1,486 @@
+"""Pins of the CPU oracle to things other than itself (no GPU needed).
+
+Each test ties one oracle function to a library routine, a closed form, an
+invariant, a brute force on tiny inputs, or a printed code table, so that a
+plausible slip in the oracle (a dropped term, a wrong sign or index, a
+transposed operand, a missed mask) fails at least one of them.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ----------------------------------------------------------------- helpers
+
+def mk(*, q_idx, w, k_idx, q_lens, ctx_lens, idx_dtype="f32", attn_dtype="f32", q=None, k_cache=None,
+       v_cache=None, gate=None, q_scale=None, k_scale=None, page_size=4, page_table=None, Hq=1,
+       d_qk=None, d_v=None, gate_per_channel=True):
+    """Inputs over an identity (or given) page table; rows of caches are physical rows."""
+    q_lens, ctx_lens = list(q_lens), list(ctx_lens)
+    B = len(q_lens)
+    q_start = np.zeros(B + 1, np.int32)
+    q_start[1:] = np.cumsum(q_lens)
+    if page_table is None:
+        npg = [(L + page_size - 1) // page_size for L in ctx_lens]
+        mp = max(npg)
+        page_table = np.zeros((B, mp), np.int32)
+        off = 0
+        for b, n in enumerate(npg):
+            page_table[b, :n] = np.arange(off, off + n)
+            off += n
+    T = int(q_start[-1])
+    H_I, d_I = q_idx.shape[1], q_idx.shape[2]
+    if q is None:
+        d_qk = d_qk or 4
+        d_v = d_v or 4
+        rows = k_idx.shape[0]
+        q = np.zeros((T, Hq, d_qk), np.float32)
+        k_cache = np.zeros((rows, d_qk), np.float32)
+        v_cache = np.zeros((rows, d_v), np.float32)
+        gate = np.zeros((T, Hq, d_v), np.float32)
+    return O.Inputs(q_start=q_start, ctx_len=np.array(ctx_lens, np.int32), page_table=page_table,
+                    page_size=page_size, idx_dtype=idx_dtype, attn_dtype=attn_dtype, q_idx=q_idx,
+                    q_scale=q_scale, w=w, k_idx=k_idx, k_scale=k_scale, q=q, k_cache=k_cache,
+                    v_cache=v_cache, gate=gate, H_I=H_I, d_I=d_I, Hq=q.shape[1], d_qk=q.shape[2],
+                    d_v=v_cache.shape[-1], row_stride=k_cache.shape[-1], gate_per_channel=gate_per_channel)
+
+
+def attn_inputs(rng, T, L, Hq, d, dv, page_size=8, mla=False, dtype="f32", q_gain=1.0, per_channel=True,
+                q_lens=None, ctx_lens=None):
+    q_lens = q_lens or [T]
+    ctx_lens = ctx_lens or [L]
+    Ttot = sum(q_lens)
+    rows = sum((c + page_size - 1) // page_size for c in ctx_lens) * page_size
+    q = (rng.standard_normal((Ttot, Hq, d)) * q_gain / math.sqrt(d)).astype(np.float32)
+    kc = (rng.standard_normal((rows, d)) / math.sqrt(d)).astype(np.float32)
+    # K and V caches share one row stride (d); V occupies the first dv elements of its row
+    vfull = kc if mla else (rng.standard_normal((rows, d)) / math.sqrt(dv)).astype(np.float32)
+    vc = vfull[:, :dv]
+    g = rng.standard_normal((Ttot, Hq, dv) if per_channel else (Ttot, Hq)).astype(np.float32)
+    qi = np.zeros((Ttot, 1, 4), np.float32)
+    ki = np.zeros((rows, 4), np.float32)
+    inp = mk(q_idx=qi, w=np.ones((Ttot, 1), np.float32), k_idx=ki, q_lens=q_lens, ctx_lens=ctx_lens,
+             q=q, k_cache=kc, v_cache=vfull, gate=g, page_size=page_size, gate_per_channel=per_channel)
+    inp.d_v = dv
+    return inp, q, kc, vc, g
+
+
+def sdpa_gated(q, k, v, pos, gate, scale, per_channel=True):
+    """torch SDPA (float64, CPU) over positions s <= pos[i], then * sigmoid(gate)."""
+    qt = torch.from_numpy(q.astype(np.float64)).transpose(0, 1)          # [H, T, d]
+    H = qt.shape[0]
+    kt = torch.from_numpy(k.astype(np.float64))[None].expand(H, -1, -1)
+    vt = torch.from_numpy(v.astype(np.float64))[None].expand(H, -1, -1)
+    L = kt.shape[1]
+    mask = torch.arange(L)[None, :] <= torch.from_numpy(np.asarray(pos))[:, None]
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None], scale=scale)
+    o = o.transpose(0, 1)                                                  # [T, H, dv]
+    g = torch.sigmoid(torch.from_numpy(gate.astype(np.float64)))
+    if not per_channel:
+        g = g[..., None]
+    return (o * g).numpy()
+
+
+# ------------------------------------------------------------ decoding pins
+
+def test_fp8_codes_match_ocp_table():
+    tab = O.fp8_table()
+    for line in open(os.path.join(GOLDEN, "e4m3fn_codes.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, val = line.split()
+        got = tab[int(code, 16)]
+        want = float(val)
+        if math.isnan(want):
+            assert math.isnan(got)
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), (code, got, want)
+
+
+def test_fp8_table_matches_torch_decoding():
+    tab = O.fp8_table()
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(tab))
+    assert np.array_equal(ref[~nan], tab[~nan])
+
+
+def test_bf16_decoding_matches_torch_all_codes():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([O.bf16_value(int(b)) for b in bits[::97]])
+    r = ref[::97]
+    nan = np.isnan(r)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(r[~nan], got[~nan])
+
+
+# -------------------------------------------------------------- indexer pins
+
+def test_indexer_identity_relu_is_matmul():
+    """H_I=1, w=1, positive entries: every dot is > 0, so ReLU is the identity
+    and the causal score block equals the numpy product q k^T."""
+    rng = np.random.default_rng(0)
+    T, D = 13, 8
+    q = rng.uniform(0.1, 1.0, (T, 1, D)).astype(np.float32)
+    k = rng.uniform(0.1, 1.0, (16, D)).astype(np.float32)   # 4 pages of 4
+    inp = mk(q_idx=q, w=np.ones((T, 1), np.float32), k_idx=k, q_lens=[T], ctx_lens=[T])
+    sc = O.indexer(inp)
+    ref = q[:, 0, :].astype(np.float64) @ k[:T].astype(np.float64).T
+    tri = np.tril(np.ones((T, T), bool))
+    assert np.allclose(sc[tri], ref[tri], rtol=1e-14, atol=0)
+    assert np.all(np.isnan(sc[~tri]))          # nothing written past the causal boundary
+
+
+def test_indexer_head_weights_reduce_to_weighted_query():
+    """All dots positive: sum_h w[i,h] (q_h . k) = (sum_h w[i,h] q_h) . k (numpy einsum + matmul).
+    T != H so a transposed w index cannot pass."""
+    rng = np.random.default_rng(1)
+    T, H, D = 7, 3, 5
+    q = rng.uniform(0.1, 1.0, (T, H, D)).astype(np.float32)
+    w = rng.uniform(0.0, 1.0, (T, H)).astype(np.float32)
+    k = rng.uniform(0.1, 1.0, (8, D)).astype(np.float32)
+    inp = mk(q_idx=q, w=w, k_idx=k, q_lens=[T], ctx_lens=[T])
+    sc = O.indexer(inp)
+    qbar = np.einsum("th,thd->td", w.astype(np.float64), q.astype(np.float64))
+    ref = qbar @ k[:T].astype(np.float64).T
+    tri = np.tril(np.ones((T, T), bool))
+    assert np.allclose(sc[tri], ref[tri], rtol=1e-13, atol=0)
+
+
+def test_indexer_relu_drops_negative_heads():
+    """Head 1 is the negation of head 0, so its dot is -(dot of head 0) < 0 and
+    contributes nothing: score = w0 * (q0 . k)."""
+    rng = np.random.default_rng(2)
+    T, D = 6, 4
+    u = rng.uniform(0.1, 1.0, (T, D)).astype(np.float32)
+    q = np.stack([u, -u], axis=1)
+    w = rng.uniform(0.5, 1.0, (T, 2)).astype(np.float32)
+    k = rng.uniform(0.1, 1.0, (8, D)).astype(np.float32)
+    inp = mk(q_idx=q, w=w, k_idx=k, q_lens=[T], ctx_lens=[T])
+    sc = O.indexer(inp)
+    ref = w[:, :1].astype(np.float64) * (u.astype(np.float64) @ k[:T].astype(np.float64).T)
+    tri = np.tril(np.ones((T, T), bool))
+    assert np.allclose(sc[tri], ref[tri], rtol=1e-13, atol=0)
+
+
+def test_indexer_weight_outside_relu():
+    """A negative weight multiplies the rectified dot (w * ReLU(x) <= 0), it is not
+    rectified itself (ReLU(w x) >= 0 would give 0 here)."""
+    T, D = 3, 2
+    q = np.ones((T, 1, D), np.float32)
+    k = np.ones((4, D), np.float32)
+    inp = mk(q_idx=q, w=-np.ones((T, 1), np.float32), k_idx=k, q_lens=[T], ctx_lens=[T])
+    sc = O.indexer(inp)
+    tri = np.tril(np.ones((T, T), bool))
+    assert np.all(sc[tri] == -2.0)
+
+
+def test_indexer_one_hot_by_inspection():
+    """One-hot query heads and keys: dot(q_h, k_s) = [a_h == b_s]; the score is the sum of
+    the weights of the heads whose one-hot position matches the key's."""
+    D, H = 4, 3
+    a = [0, 2, 2]               # head h points at dim a[h]
+    w = np.array([[1.0, 10.0, 100.0]], np.float32)
+    q = np.zeros((1, H, D), np.float32)
+    for h in range(H):
+        q[0, h, a[h]] = 1.0
+    k = np.zeros((4, D), np.float32)
+    for s, b in enumerate([2, 0, 3, 1]):
+        k[s, b] = 1.0
+    inp = mk(q_idx=q, w=w, k_idx=k, q_lens=[1], ctx_lens=[4])
+    sc = O.indexer(inp)[0]
+    assert list(sc) == [110.0, 1.0, 0.0, 0.0]
+
+
+def test_indexer_homogeneity_and_sign():
+    rng = np.random.default_rng(3)
+    T, H, D = 9, 4, 6
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    w = rng.uniform(0, 1, (T, H)).astype(np.float32)
+    k = rng.standard_normal((12, D)).astype(np.float32)
+    base = O.indexer(mk(q_idx=q, w=w, k_idx=k, q_lens=[T], ctx_lens=[T]))
+    tri = np.tril(np.ones((T, T), bool))
+    assert np.all(base[tri] >= 0.0)                     # w >= 0 gives nonnegative scores
+    w2 = O.indexer(mk(q_idx=q, w=w * 4, k_idx=k, q_lens=[T], ctx_lens=[T]))
+    q2 = O.indexer(mk(q_idx=q * 2, w=w, k_idx=k, q_lens=[T], ctx_lens=[T]))
+    assert np.allclose(w2[tri], 4 * base[tri], rtol=1e-12)
+    assert np.allclose(q2[tri], 2 * base[tri], rtol=1e-12)
+
+
+def test_indexer_fp8_scales_apply_to_the_dot():
+    """fp8 codes with per-token scales: with positive codes, H=1 and w=1 the score is
+    q_scale[i] * k_scale[s] * (decoded q . decoded k) (torch decoding + numpy matmul)."""
+    rng = np.random.default_rng(4)
+    T, D = 5, 16
+    qc = rng.integers(0x08, 0x50, (T, 1, D)).astype(np.uint8)   # positive normal codes
+    kc = rng.integers(0x08, 0x50, (8, D)).astype(np.uint8)
+    qs = rng.uniform(0.5, 2.0, T).astype(np.float32)
+    ks = rng.uniform(0.5, 2.0, 8).astype(np.float32)
+    inp = mk(q_idx=qc, w=np.ones((T, 1), np.float32), k_idx=kc, q_lens=[T], ctx_lens=[T], idx_dtype="fp8",
+             q_scale=qs, k_scale=ks)
+    sc = O.indexer(inp)
+    dec = lambda c: torch.from_numpy(c).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = (dec(qc)[:, 0, :] @ dec(kc[:T]).T) * qs[:, None].astype(np.float64) * ks[None, :T].astype(np.float64)
+    tri = np.tril(np.ones((T, T), bool))
+    assert np.allclose(sc[tri], ref[tri], rtol=1e-14)
+
+
+def test_indexer_paging_and_ragged_positions():
+    """Scores depend only on logical positions: the same logical keys behind a random page
+    table give the same rows.  Sequence b's last query sees all ctx_len[b] positions; a
+    prefill's first query sees one."""
+    rng = np.random.default_rng(5)
+    ps, D, H = 4, 3, 2
+    q_lens, ctx_lens = [3, 1, 5], [7, 10, 5]
+    T = sum(q_lens)
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    w = rng.uniform(0, 1, (T, H)).astype(np.float32)
+    logical = [rng.standard_normal((L, D)).astype(np.float32) for L in ctx_lens]
+    npg = [(L + ps - 1) // ps for L in ctx_lens]
+    total = sum(npg)
+
+    def lay(perm):
+        kc = np.zeros((total * ps, D), np.float32)
+        table = np.zeros((3, max(npg)), np.int32)
+        off = 0
+        for b, L in enumerate(ctx_lens):
+            pages = perm[off:off + npg[b]]
+            table[b, :npg[b]] = pages
+            for s in range(L):
+                kc[pages[s // ps] * ps + s % ps] = logical[b][s]
+            off += npg[b]
+        return mk(q_idx=q, w=w, k_idx=kc, q_lens=q_lens, ctx_lens=ctx_lens, page_size=ps, page_table=table)
+
+    a = O.indexer(lay(np.arange(total)))
+    b = O.indexer(lay(rng.permutation(total)))
+    assert np.array_equal(np.isnan(a), np.isnan(b))
+    assert np.array_equal(a[~np.isnan(a)], b[~np.isnan(b)])
+    n = O.row_lengths(lay(np.arange(total)))
+    q_start = np.concatenate([[0], np.cumsum(q_lens)])
+    for bi in range(3):
+        assert n[q_start[bi + 1] - 1] == ctx_lens[bi]
+    assert n[q_start[2]] == 1                         # fresh prefill sequence: first query sees itself
+    assert np.all(np.diff(n[q_start[0]:q_start[1]]) == 1)
+
+
+def test_indexer_row_subset_equals_full_rows():
+    rng = np.random.default_rng(6)
+    T, H, D = 11, 2, 4
+    q = rng.standard_normal((T, H, D)).astype(np.float32)
+    w = rng.uniform(0, 1, (T, H)).astype(np.float32)
+    k = rng.standard_normal((12, D)).astype(np.float32)
+    inp = mk(q_idx=q, w=w, k_idx=k, q_lens=[T], ctx_lens=[T])
+    full = O.indexer(inp)
+    rows = [10, 3, 0]
+    sub = O.indexer(inp, rows)
+    assert np.array_equal(np.nan_to_num(sub, nan=-7), np.nan_to_num(full[rows], nan=-7))
+
+
+# ----------------------------------------------------------------- Top-K pins
+
+def lexsort_topk(row, n, K):
+    s = row[:n]
+    order = np.lexsort((np.arange(n), -s))      # primary: score desc, secondary: position asc
+    sel = np.sort(order[:min(K, n)])
+    return np.concatenate([sel, -np.ones(K - sel.size, np.int64)])
+
+
+@pytest.mark.parametrize("alphabet", [None, 5, 2])
+def test_topk_matches_lexsort(alphabet):
+    rng = np.random.default_rng(7)
+    R, L, K = 40, 64, 9
+    if alphabet is None:
+        sc = rng.standard_normal((R, L))
+    else:
+        sc = rng.integers(0, alphabet, (R, L)).astype(np.float64) * 0.25 - 0.5
+    n = rng.integers(1, L + 1, R)
+    got = O.topk(sc, n, K)
+    for r in range(R):
+        assert np.array_equal(got[r], lexsort_topk(sc[r], n[r], K)), r
+
+
+def test_topk_invariants_and_ties():
+    rng = np.random.default_rng(8)
+    R, L, K = 25, 200, 31
+    sc = np.round(rng.standard_normal((R, L)), 1)          # heavy ties
+    n = rng.integers(1, L + 1, R)
+    idx = O.topk(sc, n, K)
+    for r in range(R):
+        v = idx[r][idx[r] >= 0]
+        assert v.size == min(K, n[r])
+        assert np.all(idx[r][v.size:] == -1)
+        assert np.all(np.diff(v) > 0) and v.min() >= 0 and v.max() < n[r]
+        unsel = np.setdiff1d(np.arange(n[r]), v)
+        if unsel.size:
+            thr = sc[r][v].min()
+            assert sc[r][unsel].max() <= thr
+            ties_out = unsel[sc[r][unsel] == thr]
+            ties_in = v[sc[r][v] == thr]
+            if ties_out.size:
+                assert ties_in.max() < ties_out.min()      # lowest positions win ties
+
+
+def test_topk_short_rows_take_everything_and_needle():
+    sc = np.zeros((3, 50))
+    sc[1, 37] = 1e9
+    n = np.array([5, 50, 32])
+    idx = O.topk(sc, n, 32)
+    assert list(idx[0][:5]) == [0, 1, 2, 3, 4] and np.all(idx[0][5:] == -1)
+    assert 37 in idx[1]
+    assert list(idx[2]) == list(range(32))
+    # all-equal row: the K lowest positions
+    assert list(idx[1][idx[1] != 37]) == list(range(31))
+
+
+def test_topk_signed_zero_ties_by_position():
+    row = np.array([[0.0, -0.0, 0.0, -0.0, -1.0]])
+    idx = O.topk(row, np.array([5]), 2)
+    assert list(idx[0]) == [0, 1]
+
+
+# ------------------------------------------------------------- attention pins
+
+def test_sparse_attention_with_all_positions_equals_sdpa_and_dense():
+    """K >= n: the sparse path over every causal position equals torch SDPA (float64, causal
+    mask) times sigmoid(gate), and the separately written dense control oracle."""
+    rng = np.random.default_rng(9)
+    T, Hq, d, dv = 10, 3, 8, 6
+    inp, q, kc, vc, g = attn_inputs(rng, T, T, Hq, d, dv, page_size=4)
+    K = 16
+    idx = np.full((T, K), -1, np.int32)
+    for i in range(T):
+        idx[i, :i + 1] = np.arange(i + 1)
+    out = O.sparse_attn(inp, idx)
+    dense = O.dense_attn(inp)
+    ref = sdpa_gated(q, kc[:T], vc[:T], np.arange(T), g, 1 / math.sqrt(d))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-15)
+    assert np.allclose(dense, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_mla_latent_row_serves_k_and_v():
+    rng = np.random.default_rng(10)
+    T, Hq, d, dv = 6, 2, 12, 8
+    inp, q, kc, vc, g = attn_inputs(rng, T, T, Hq, d, dv, page_size=4, mla=True)
+    idx = np.tile(np.arange(T, dtype=np.int32), (T, 1))
+    for i in range(T):
+        idx[i, i + 1:] = -1
+    out = O.sparse_attn(inp, idx)
+    ref = sdpa_gated(q, kc[:T], kc[:T, :dv], np.arange(T), g, 1 / math.sqrt(d))
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_single_index_gives_gated_value_row():
+    rng = np.random.default_rng(11)
+    inp, q, kc, vc, g = attn_inputs(rng, 4, 8, 2, 8, 8, page_size=4, ctx_lens=[8], q_lens=[4])
+    idx = np.array([[3], [0], [6], [7]], np.int32)
+    out, lse = O.sparse_attn(inp, idx, with_lse=True)
+    sig = torch.sigmoid(torch.from_numpy(g.astype(np.float64))).numpy()
+    for i in range(4):
+        s = idx[i, 0]
+        assert np.allclose(out[i], vc[s].astype(np.float64)[None, :] * sig[i], rtol=1e-15, atol=0)
+        z = (q[i].astype(np.float64) @ kc[s].astype(np.float64)) / math.sqrt(8)
+        assert np.allclose(lse[i], z, rtol=1e-14)
+
+
+def test_zero_query_is_mean_of_selected_rows_and_padding_is_ignored():
+    rng = np.random.default_rng(12)
+    inp, q, kc, vc, g = attn_inputs(rng, 2, 16, 2, 8, 4, page_size=4, ctx_lens=[16], q_lens=[2])
+    inp.q[:] = 0.0
+    idx = np.array([[1, 5, 9, -1, -1], [0, 14, -1, 2, -1]], np.int32)
+    out, lse = O.sparse_attn(inp, idx, with_lse=True)
+    sig = torch.sigmoid(torch.from_numpy(g.astype(np.float64))).numpy()
+    for i in range(2):
+        s = idx[i][idx[i] >= 0]
+        assert np.allclose(out[i], vc[s].astype(np.float64).mean(0)[None] * sig[i], rtol=1e-14)
+        assert np.allclose(lse[i], math.log(s.size), rtol=1e-14)
+
+
+def test_index_order_does_not_matter():
+    rng = np.random.default_rng(13)
+    inp, *_ = attn_inputs(rng, 3, 40, 2, 8, 8, page_size=8, ctx_lens=[40], q_lens=[3], q_gain=6.0)
+    idx = np.stack([rng.choice(38 + i, 12, replace=False) for i in range(3)]).astype(np.int32)
+    a = O.sparse_attn(inp, idx)
+    b = O.sparse_attn(inp, idx[:, ::-1].copy())
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-16)
+
+
+def test_gate_limits():
+    """G = 100: sigmoid rounds to 1 in double, so y is the ungated output; G = 0 halves it."""
+    rng = np.random.default_rng(14)
+    inp, q, kc, vc, g = attn_inputs(rng, 3, 12, 2, 8, 8, page_size=4, ctx_lens=[12], q_lens=[3])
+    idx = np.array([[0, 3, 9], [1, 2, 10], [4, 5, 11]], np.int32)
+    inp.gate[:] = 100.0
+    ungated = O.sparse_attn(inp, idx)
+    ref = np.zeros_like(ungated)
+    for i in range(3):
+        ref[i] = sdpa_gated(q[i:i + 1], kc[idx[i]], vc[idx[i]], [len(idx[i]) - 1],
+                            np.full((1, 2, 8), 100.0, np.float32), 1 / math.sqrt(8))[0]
+    assert np.allclose(ungated, ref, rtol=1e-13)
+    inp.gate[:] = 0.0
+    half = O.sparse_attn(inp, idx)
+    assert np.array_equal(half, ungated * 0.5)
+
+
+def test_per_head_gate_is_broadcast_per_channel_gate():
+    rng = np.random.default_rng(15)
+    a, q, kc, vc, gh = attn_inputs(rng, 3, 9, 2, 8, 8, page_size=4, ctx_lens=[9], q_lens=[3], per_channel=False)
+    idx = np.array([[0, 1, 6], [2, 3, 7], [4, 5, 8]], np.int32)
+    out_h = O.sparse_attn(a, idx)
+    a.gate = np.ascontiguousarray(np.repeat(gh[:, :, None], 8, axis=2))
+    a.gate_per_channel = True
+    out_c = O.sparse_attn(a, idx)
+    assert np.array_equal(out_h, out_c)
+
+
+def test_sharp_softmax_matches_sdpa():
+    """Large logits (q x 40): exercises the max subtraction."""
+    rng = np.random.default_rng(16)
+    T = 8
+    inp, q, kc, vc, g = attn_inputs(rng, T, T, 2, 16, 8, page_size=4, q_gain=40.0)
+    idx = np.full((T, T), -1, np.int32)
+    for i in range(T):
+        idx[i, :i + 1] = np.arange(i + 1)
+    out = O.sparse_attn(inp, idx)
+    ref = sdpa_gated(q, kc[:T], vc[:T], np.arange(T), g, 1 / math.sqrt(16))
+    assert np.allclose(out, ref, rtol=1e-11, atol=1e-15)
+
+
+# -------------------------------------------------------------- end to end
+
+def test_pipeline_with_k_at_least_context_is_dense_gated_attention():
+    """Tiny causal prefill with K = T: selection keeps every causal position, so the pipeline
+    equals dense causal gated attention (torch SDPA)."""
+    import indexer_top_sparse_relu_amd.workloads as W
+    spec = W.tiny_prefill_fp32().replace(q_lens=(64,), ctx_lens=(64,), K=64)
+    wl = W.generate(spec, "cpu")
+    inp = O.Inputs.from_workload(wl)
+    sc, idx, out = O.pipeline(inp, spec.K)
+    n = O.row_lengths(inp)
+    for i in range(spec.T):
+        assert np.array_equal(idx[i][:n[i]], np.arange(n[i])) and np.all(idx[i][n[i]:] == -1)
+    kc = inp.k_cache.reshape(-1, spec.d_qk)
+    vc = inp.v_cache.reshape(-1, spec.d_v)
+    ref = sdpa_gated(inp.q, kc[:spec.T], vc[:spec.T], np.arange(spec.T), inp.gate, spec.softmax_scale)
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_small_k_pipeline_selects_planted_needle():
+    """A key row planted equal to a query's indexer heads scores highest and is selected."""
+    import indexer_top_sparse_relu_amd.workloads as W
+    spec = W.tiny_prefill_fp32().replace(q_lens=(48,), ctx_lens=(48,), K=8)
+    wl = W.generate(spec, "cpu")
+    inp = O.Inputs.from_workload(wl)
+    i, s = 40, 3
+    inp.k_idx.reshape(-1, spec.d_I)[s] = 10.0 * inp.q_idx[i].sum(0)
+    sc, idx, _ = O.pipeline(inp, spec.K, rows=[i])
+    assert s in idx[0]
