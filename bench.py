@@ -1,0 +1,223 @@
+"""Benchmark: query tokens/s of indexer + Top-K + gated sparse attention on one MI355X.
+
+Workload (default): chunked prefill with an MLA-like latent cache — 4096 new
+query tokens on a 131072-token cached context (ctx 135168), fp8 e4m3 indexer
+(64 heads x 128) with per-token scales, 128 query heads over 576-dim latent
+rows (V = first 512 dims), bf16 attention, K = 2048, paged cache (64-token
+pages, random page table).  One step = the three C-ABI calls over the whole
+batch; inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  Per-stage durations come from HIP events recorded on
+the stream the kernels run on; the dominant stage's roofline uses algorithmic
+work only (flops of the contraction, or bytes the method must move).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+# MI355X published peaks
+PEAK = {"hbm_GBs": 8000.0, "fp8_TFLOPs": 5000.0, "bf16_TFLOPs": 2500.0, "fp32_TFLOPs": 157.3}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "indexer": "indexer_top_sparse_relu_amd/csrc/indexer.hip",
+    "topk": "indexer_top_sparse_relu_amd/csrc/topk.hip",
+    "attn": "indexer_top_sparse_relu_amd/csrc/attn.hip",
+}
+
+
+def source_hash(stage: str) -> str:
+    h = hashlib.sha256()
+    for rel in (KERNEL_SOURCES[stage], "indexer_top_sparse_relu_amd/csrc/sa_device.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def causal_lengths(spec):
+    """n = pos + 1 of every query token (new tokens are the last positions of each sequence)."""
+    out = []
+    for nq, L in zip(spec.q_lens, spec.ctx_lens):
+        out.extend(L - nq + j + 1 for j in range(nq))
+    return out
+
+
+def algorithmic_work(spec, n_valid):
+    """Per-step algorithmic work of each stage: flops of the contractions, and the bytes the
+    method must move (inputs read once, outputs written once)."""
+    pairs = int(sum(causal_lengths(spec)))
+    esz = {"fp8": 1, "bf16": 2, "f32": 4}
+    ie, ae = esz[spec.idx_dtype], esz[spec.attn_dtype]
+    scale_b = 4 if spec.idx_dtype == "fp8" else 0
+    keys = int(sum(spec.ctx_lens))
+    kv_row = spec.d_qk * ae + (0 if spec.mla else spec.d_v * ae)
+    gate_elems = spec.Hq * (spec.d_v if spec.gate_per_channel else 1)
+    return {
+        "indexer": {"flops": 2.0 * spec.H_I * spec.d_I * pairs,
+                    "bytes": spec.T * (spec.H_I * spec.d_I * ie + scale_b + spec.H_I * 4)
+                    + keys * (spec.d_I * ie + scale_b) + pairs * 4},
+        "topk": {"bytes": pairs * 4 + spec.T * spec.K * 4},
+        "attn": {"flops": 2.0 * spec.Hq * n_valid * (spec.d_qk + spec.d_v),
+                 "bytes": n_valid * kv_row + spec.T * (spec.Hq * spec.d_qk + gate_elems + spec.Hq * spec.d_v) * ae
+                 + spec.T * spec.K * 4},
+    }
+
+
+def to_np(t):
+    import numpy as np
+    import torch
+
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def cpu_baseline(wl, sample_tokens: int):
+    """The oracle (as it stands) on the last `sample_tokens` query tokens of the workload."""
+    import numpy as np
+
+    from oracle import oracle as O
+
+    s = wl.spec
+    S = min(sample_tokens, s.T)
+    sl = slice(s.T - S, s.T)
+    same = wl.v_cache.data_ptr() == wl.k_cache.data_ptr()
+    kc = to_np(wl.k_cache)
+    inp = O.Inputs(q_start=np.array([0, S], np.int32), ctx_len=np.array(s.ctx_lens[-1:], np.int32),
+                   page_table=to_np(wl.page_table[-1:]), page_size=s.page_size, idx_dtype=s.idx_dtype,
+                   attn_dtype=s.attn_dtype, q_idx=to_np(wl.q_idx[sl]),
+                   q_scale=to_np(wl.q_scale[sl]) if wl.q_scale is not None else None, w=to_np(wl.w[sl]),
+                   k_idx=to_np(wl.k_idx), k_scale=to_np(wl.k_scale) if wl.k_scale is not None else None,
+                   q=to_np(wl.q[sl]), k_cache=kc, v_cache=kc if same else to_np(wl.v_cache), gate=to_np(wl.gate[sl]),
+                   H_I=s.H_I, d_I=s.d_I, Hq=s.Hq, d_qk=s.d_qk, d_v=s.d_v, row_stride=wl.kv_row_stride,
+                   gate_per_channel=s.gate_per_channel)
+    threads = O.set_threads(0)
+    t0 = time.perf_counter()
+    O.pipeline(inp, s.K, scale=s.softmax_scale)
+    dt = time.perf_counter() - t0
+    return {"value": S / dt, "unit": "query_tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"last {S} of {s.T} query tokens (positions {s.ctx_lens[-1] - S}..{s.ctx_lens[-1] - 1}), "
+                      f"full indexer + Top-K + gated attention in fp64, {dt:.1f} s"}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="chunked_prefill_mla_128k")
+    ap.add_argument("--cpu-sample", type=int, default=48, help="query tokens the oracle baseline runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from indexer_top_sparse_relu_amd import binding as B
+    from indexer_top_sparse_relu_amd import workloads as W
+
+    spec = W.CONFIGS[args.workload]()
+    wl = W.generate(spec, "cuda")
+    pl = B.Pipeline(wl)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        pl.run(stream)
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        pl.indexer(stream)
+        e[1].record(stream)
+        pl.topk(stream)
+        e[2].record(stream)
+        pl.attn(stream, with_lse=False)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    stage_ms = {
+        "indexer": sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps,
+        "topk": sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps,
+        "attn": sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps,
+    }
+    step_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
+    wall_ms = wall * 1e3 / args.steps
+    n_valid = int((pl.indices >= 0).sum().item())
+    assert torch.isfinite(pl.out.float()).all().item(), "non-finite output"
+
+    work = algorithmic_work(spec, n_valid)
+    dom = max(stage_ms, key=stage_ms.get)
+    rl = {}
+    for st, ms in stage_ms.items():
+        w = work[st]
+        if st == "indexer":
+            peak = PEAK["fp8_TFLOPs"] if spec.idx_dtype == "fp8" else PEAK["bf16_TFLOPs"] if spec.idx_dtype == "bf16" \
+                else PEAK["fp32_TFLOPs"]
+            ach = w["flops"] / (ms * 1e-3) / 1e12
+            rl[st] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
+        elif st == "attn":
+            peak = PEAK["bf16_TFLOPs"] if spec.attn_dtype == "bf16" else PEAK["fp32_TFLOPs"]
+            ach = w["flops"] / (ms * 1e-3) / 1e12
+            rl[st] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
+        else:
+            ach = w["bytes"] / (ms * 1e-3) / 1e9
+            rl[st] = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"], "unit": "GB/s",
+                      "frac": ach / PEAK["hbm_GBs"]}
+        rl[st]["ms"] = ms
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(args.workload, {}).get(dom)
+        if ent and ent.get("source_hash") == source_hash(dom):
+            traffic = ent["bytes_per_launch"]
+    roof = {k: v for k, v in rl[dom].items() if k != "ms"}
+    roof["kernel"] = dom
+    roof["traffic"] = traffic
+
+    tokens = spec.T
+    line = {
+        "metric": "query tokens/s (indexer+TopK+sparse attn) at 128K ctx, K=2048; % HBM/MFMA peak",
+        "value": tokens / (step_ms * 1e-3),
+        "unit": "query_tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": f"{spec.idx_dtype}+{spec.attn_dtype}",
+        "data": "synthetic",
+        "config": {"workload": spec.name, "new_tokens": spec.T, "ctx": spec.max_ctx, "K": spec.K,
+                   "indexer": f"{spec.H_I}x{spec.d_I} {spec.idx_dtype}", "q_heads": spec.Hq,
+                   "d_qk": spec.d_qk, "d_v": spec.d_v, "kv": "latent (V = first d_v of K row)" if spec.mla else "MQA",
+                   "page_size": spec.page_size, "gate": "per-channel" if spec.gate_per_channel else "per-head"},
+        "roofline": roof,
+        "stages": rl,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

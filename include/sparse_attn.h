@@ -1,0 +1,183 @@
+/*
+ * sparse_attn.h — C ABI of the MI355X (gfx950) gated sparse attention hot path.
+ *
+ * The path, per query token: a lightweight multi-head indexer scores every
+ * causal history position, a per-token Top-K keeps K positions, and exact
+ * softmax attention over only those K KV rows (shared by all query heads) is
+ * scaled by a sigmoid output gate.
+ *
+ * Pages cited (by title):
+ *   [HAT] "Hybrid Attention Architectures: Engineering Trade-offs from Linear
+ *          Attention to Gated Sparse Attention"
+ *   [F2S] "From Full Attention to Sparsity: The Evolution of Hybrid Attention
+ *          Architectures in Large Language Models"
+ *   [SAD] "Sparse Attention and Hybrid Attention Architecture Design in Large
+ *          Language Models"
+ *   [SEL] "Hybrid Attention Architecture Evolution in LLMs: From Full
+ *          Attention to Sparse Selection"
+ *
+ * Conventions shared by every call
+ *   - Pointers are DEVICE pointers unless marked (host).  Tensors are dense
+ *     row-major; base pointers are 16-byte aligned.
+ *   - Every call is asynchronous on `stream` (a hipStream_t); the library
+ *     never allocates, frees or synchronises and keeps no global state, so it
+ *     is reentrant.  The caller owns every buffer, including workspaces sized
+ *     by the *_workspace_size queries.
+ *   - Argument errors are detected on the host before any launch and return
+ *     SA_EINVAL (bad value / NULL / shape) or SA_EUNSUPPORTED (a valid request
+ *     this build has no kernel for); nothing is launched then.  A failed
+ *     launch returns SA_ELAUNCH.  Device-side data (page ids, index values,
+ *     lengths inside q_start / ctx_len) is trusted and not range-checked.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *sa_stream_t; /* a hipStream_t; NULL is the default stream */
+
+typedef enum {
+    SA_F32 = 0,
+    SA_BF16 = 1,
+    SA_FP8_E4M3 = 2 /* OCP e4m3fn: bias 7, max 448, NaN = S.1111.111, no infinity */
+} sa_dtype;
+
+typedef enum {
+    SA_OK = 0,
+    SA_EINVAL = -1,
+    SA_EUNSUPPORTED = -2,
+    SA_EWORKSPACE = -3,
+    SA_ELAUNCH = -4
+} sa_status;
+
+/*
+ * Ragged batch over a paged cache.  [HAT §5 item 4] asks for varying lengths
+ * within a batch; [F2S "Engineering Considerations" item 1] for variable-length
+ * Top-K and paged cache management.  Prefill passes an identity page table.
+ *
+ * Query token j of sequence b (global token q_start[b] + j) sits at position
+ *     pos = ctx_len[b] - (q_start[b+1] - q_start[b]) + j,
+ * i.e. the new tokens are the last positions of the cache, already appended.
+ * Its causal candidates are the n = pos + 1 positions 0..pos (self-inclusive).
+ * Logical position s of sequence b lives at physical cache row
+ *     page_table[b * max_pages + s / page_size] * page_size + s % page_size.
+ * Decode is the case of one new token per sequence.
+ */
+typedef struct {
+    int32_t num_seqs;          /* (host) B >= 1 */
+    int32_t total_q;           /* (host) T = q_start[B] >= 1 */
+    int32_t max_q;             /* (host) max_b (q_start[b+1] - q_start[b]) */
+    int32_t max_ctx;           /* (host) max_b ctx_len[b]; sizes grids and bounds score rows */
+    int32_t page_size;         /* (host) tokens per page: power of two, 16..4096 */
+    int32_t max_pages;         /* (host) row stride of page_table, >= ceil(max_ctx / page_size) */
+    const int32_t *q_start;    /* [B+1] nondecreasing prefix offsets, q_start[0] = 0 */
+    const int32_t *ctx_len;    /* [B] cache length after the new tokens; >= the sequence's new tokens */
+    const int32_t *page_table; /* [B, max_pages] physical page ids */
+} sa_batch;
+
+/*
+ * a1 — indexer scores.  [HAT §3.1, §3.3]: a lightweight relevance score of
+ * each query against every history position, before selection.
+ * [F2S "Fine-Grained Sparse Attention: Indexer Plus Top-K"]: few heads, low
+ * dims, content only (no positional encoding), scores of shape [n, n].
+ * The form is the DSA-style reading (the pages print no formula):
+ *     scores[i, s] = sum_h w[i,h] * max(0, q_idx[i,h,:] . k_idx[s,:])
+ * for s in [0, n_i); one k_idx row per position is shared by all heads.
+ * fp8: the dot of the decoded e4m3fn codes is multiplied by
+ * q_scale[i] * k_scale[s]; both scales must be >= 0.
+ *
+ *   q_idx      [T, n_heads, head_dim] in dtype
+ *   q_scale    [T] fp32 (fp8 only, else NULL)
+ *   weights    [T, n_heads] fp32
+ *   k_idx_cache   [num_pages, page_size, head_dim] in dtype
+ *   k_scale_cache [num_pages, page_size] fp32 (fp8 only, else NULL)
+ *   scores     [T, ld_scores] fp32; row i gets entries [0, n_i) and nothing
+ *              else is written.  ld_scores >= max_ctx and a multiple of 4.
+ * Supported (dtype, n_heads, head_dim): f32 with head_dim 32; bf16 with
+ * head_dim 64; fp8 with head_dim 128; n_heads in {4, 8, 16, 32, 64}.
+ * Scores are finite for finite inputs.
+ */
+sa_status sparse_indexer_scores(const sa_batch *batch, sa_dtype dtype,
+                                const void *q_idx, int32_t n_heads, int32_t head_dim,
+                                const float *q_scale, const float *weights,
+                                const void *k_idx_cache, const float *k_scale_cache,
+                                float *scores, int64_t ld_scores, sa_stream_t stream);
+
+/*
+ * a2 — per-token Top-K.  [HAT §3.1]: keep the K highest-scoring positions;
+ * [F2S "Fine-Grained Sparse Attention: Indexer Plus Top-K"]: indices of
+ * shape [n, K]; [HAT §5 item 4]: fewer candidates than K are padded.
+ * [EVO: "Evolution of Hybrid Attention in Open-Source LLMs..." §5 item 3]
+ * warns against approximate Top-K: this one is exact.
+ *
+ * Row i (token i) selects from scores[i, 0..n_i): if n_i <= k all n_i
+ * positions, else the k positions with the largest scores, ties broken
+ * toward the lower position (+0 and -0 compare equal).  indices[i, :] holds
+ * the min(k, n_i) selected positions in ascending order, then -1.
+ * Scores must be finite.  1 <= k <= 4096.
+ *   workspace: >= sparse_topk_workspace_size(batch, k) bytes (may be 0 bytes;
+ *   then workspace may be NULL), 256-byte aligned.  Results are deterministic.
+ */
+size_t sparse_topk_workspace_size(const sa_batch *batch, int32_t k);
+sa_status sparse_topk(const sa_batch *batch, const float *scores, int64_t ld_scores,
+                      int32_t k, int32_t *indices, void *workspace, size_t workspace_bytes,
+                      sa_stream_t stream);
+
+/*
+ * a3-a5 — gather, exact sparse attention, sigmoid output gate.
+ * [HAT §3.3]: exact attention over kv_history[idx], then the gate scales it.
+ * [F2S "Fine-Grained Sparse Attention: Indexer Plus Top-K", pseudocode]:
+ * attention(q, gather(k, idx), gather(v, idx)) and g = sigmoid(...).
+ * [SEL §3.2]: standard attention over the selected set.
+ * [SAD §4 "Output gating"]: per-channel or per-head scaling of the output.
+ * [SAD §2]: query heads share one KV head; a latent row may serve as K and V.
+ *
+ * For token i, head h, over the valid entries s_j of indices[i, :] (values
+ * < 0 are padding and are skipped):
+ *     z_j = softmax_scale * q[i,h,:] . K[s_j, 0:d_qk]
+ *     o   = sum_j softmax(z)_j * V[s_j, 0:d_v]
+ *     out[i,h,c] = o[c] * sigmoid(G),  G = gate_logits[i,h,c] (per channel)
+ *                                      or gate_logits[i,h]   (per head)
+ *     lse[i,h]   = max_j z_j + log(sum_j exp(z_j - max_j z_j))
+ * A row with no valid entry gives out = 0 and lse = -inf.
+ *
+ *   q            [T, n_q_heads, d_qk] in dtype (SA_F32 or SA_BF16)
+ *   k_cache      [num_pages, page_size, kv_row_stride]: K row = first d_qk elements
+ *   v_cache      [num_pages, page_size, kv_row_stride]: V row = first d_v elements;
+ *                may equal k_cache (latent layout, d_v <= d_qk)
+ *   indices      [T, k] int32 positions (as produced by sparse_topk)
+ *   gate_logits  [T, n_q_heads, d_v] if gate_per_channel else [T, n_q_heads], in dtype
+ *   out          [T, n_q_heads, d_v] in dtype (bf16 rounded to nearest even)
+ *   lse          [T, n_q_heads] fp32, or NULL
+ * Supported: SA_F32 with d_qk = d_v in {32, 64, 128}; SA_BF16 with
+ * (d_qk, d_v) in {(128, 128), (576, 512)}; n_q_heads a multiple of 16 (bf16)
+ * or any (f32); 1 <= k <= 65536.
+ */
+size_t sparse_gated_attn_workspace_size(const sa_batch *batch, int32_t n_q_heads, int32_t d_v, int32_t k);
+sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype,
+                                const void *q, int32_t n_q_heads, int32_t d_qk,
+                                const void *k_cache, const void *v_cache, int32_t d_v,
+                                int64_t kv_row_stride,
+                                const int32_t *indices, int32_t k,
+                                const void *gate_logits, int32_t gate_per_channel,
+                                float softmax_scale, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes, sa_stream_t stream);
+
+/* Static description of a status code; never NULL. */
+const char *sa_status_string(sa_status s);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int32_t sa_abi_version(void);
+
+#define SA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -5,15 +5,12 @@ The compute runs in hand-written HIP kernels behind the C ABI declared in
 Importing the package does not load the shared library; the first call does,
 and fails loudly if it has not been built.
 """
+import importlib
 
 __all__ = ["binding", "workloads"]
 
 
 def __getattr__(name):
-    if name == "binding":
-        from . import binding
-        return binding
-    if name == "workloads":
-        from . import workloads
-        return workloads
+    if name in __all__:
+        return importlib.import_module(f"{__name__}.{name}")
     raise AttributeError(name)

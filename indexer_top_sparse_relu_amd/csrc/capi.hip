@@ -1,0 +1,167 @@
+// extern "C" entry points of libsparse_attn.so: argument validation on the
+// host, then kernel launches on the caller's stream.  No allocation, no
+// synchronisation, no global state.  The operations and their citations are
+// documented in sparse_attn.h.
+#include "sparse_attn.h"
+
+#include "launch.h"
+#include "sa_device.h"
+
+namespace {
+
+bool aligned16(const void *p) { return (((uintptr_t)p) & 15u) == 0; }
+
+int log2_exact(int x)
+{
+    if (x <= 0 || (x & (x - 1)))
+        return -1;
+    int s = 0;
+    while ((1 << s) < x)
+        ++s;
+    return s;
+}
+
+sa_status make_batch(const sa_batch *in, sa::Batch *out)
+{
+    if (!in || in->num_seqs < 1 || in->total_q < 1 || in->max_q < 1 || in->max_ctx < 1 || in->max_pages < 1)
+        return SA_EINVAL;
+    if (!in->q_start || !in->ctx_len || !in->page_table)
+        return SA_EINVAL;
+    const int shift = log2_exact(in->page_size);
+    if (shift < 4 || shift > 12)
+        return SA_EINVAL;
+    if ((int64_t)in->max_pages * in->page_size < in->max_ctx)
+        return SA_EINVAL;
+    if (in->max_q > in->total_q)
+        return SA_EINVAL;
+    out->num_seqs = in->num_seqs;
+    out->total_q = in->total_q;
+    out->max_q = in->max_q;
+    out->max_ctx = in->max_ctx;
+    out->page_shift = shift;
+    out->max_pages = in->max_pages;
+    out->q_start = in->q_start;
+    out->ctx_len = in->ctx_len;
+    out->page_table = in->page_table;
+    return SA_OK;
+}
+
+sa_status launched(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ELAUNCH; }
+
+} // namespace
+
+extern "C" {
+
+sa_status sparse_indexer_scores(const sa_batch *batch, sa_dtype dtype, const void *q_idx, int32_t n_heads,
+                                int32_t head_dim, const float *q_scale, const float *weights,
+                                const void *k_idx_cache, const float *k_scale_cache, float *scores,
+                                int64_t ld_scores, sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (dtype != SA_F32 && dtype != SA_BF16 && dtype != SA_FP8_E4M3)
+        return SA_EINVAL;
+    if (!q_idx || !weights || !k_idx_cache || !scores || n_heads < 1 || head_dim < 1)
+        return SA_EINVAL;
+    if (dtype == SA_FP8_E4M3 && (!q_scale || !k_scale_cache))
+        return SA_EINVAL;
+    if (ld_scores < bt.max_ctx || (ld_scores & 3))
+        return SA_EINVAL;
+    if (!aligned16(q_idx) || !aligned16(k_idx_cache) || !aligned16(scores))
+        return SA_EINVAL;
+    if (!sa::indexer_supported((int)dtype, n_heads, head_dim))
+        return SA_EUNSUPPORTED;
+    return launched(sa::launch_indexer((int)dtype, n_heads, head_dim, bt, q_idx, q_scale, weights, k_idx_cache,
+                                       k_scale_cache, scores, ld_scores, (hipStream_t)stream));
+}
+
+size_t sparse_topk_workspace_size(const sa_batch *batch, int32_t k)
+{
+    sa::Batch bt;
+    if (make_batch(batch, &bt) != SA_OK || k < 1)
+        return 0;
+    return sa::topk_plan(bt.total_q, bt.max_ctx, k).ws_bytes;
+}
+
+sa_status sparse_topk(const sa_batch *batch, const float *scores, int64_t ld_scores, int32_t k, int32_t *indices,
+                      void *workspace, size_t workspace_bytes, sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (!scores || !indices || k < 1)
+        return SA_EINVAL;
+    if (k > 4096)
+        return SA_EUNSUPPORTED;
+    if (ld_scores < bt.max_ctx || (ld_scores & 3) || !aligned16(scores))
+        return SA_EINVAL;
+    const sa::TopkPlan plan = sa::topk_plan(bt.total_q, bt.max_ctx, k);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+        return SA_EWORKSPACE;
+    if (plan.chunked && bt.total_q > 65535)
+        return SA_EUNSUPPORTED;
+    return launched(sa::launch_topk(bt, plan, scores, ld_scores, k, indices, workspace, (hipStream_t)stream));
+}
+
+size_t sparse_gated_attn_workspace_size(const sa_batch *batch, int32_t n_q_heads, int32_t d_v, int32_t k)
+{
+    sa::Batch bt;
+    if (make_batch(batch, &bt) != SA_OK || n_q_heads < 1 || d_v < 1 || k < 1)
+        return 0;
+    return sa::attn_plan(bt.total_q, n_q_heads, d_v, k).ws_bytes;
+}
+
+sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
+                                int32_t d_qk, const void *k_cache, const void *v_cache, int32_t d_v,
+                                int64_t kv_row_stride, const int32_t *indices, int32_t k, const void *gate_logits,
+                                int32_t gate_per_channel, float softmax_scale, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes, sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (dtype != SA_F32 && dtype != SA_BF16)
+        return SA_EINVAL;
+    if (!q || !k_cache || !v_cache || !indices || !gate_logits || !out)
+        return SA_EINVAL;
+    if (n_q_heads < 1 || d_qk < 1 || d_v < 1 || k < 1 || k > 65536)
+        return SA_EINVAL;
+    if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
+        return SA_EINVAL;
+    if (kv_row_stride < d_qk || kv_row_stride < d_v)
+        return SA_EINVAL;
+    const int esz = dtype == SA_BF16 ? 2 : 4;
+    if ((kv_row_stride * esz) % 16 || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(out) || !aligned16(gate_logits))
+        return SA_EINVAL;
+    if (k_cache == v_cache && d_v > d_qk)
+        return SA_EINVAL;
+    if (!sa::attn_supported((int)dtype, n_q_heads, d_qk, d_v))
+        return SA_EUNSUPPORTED;
+    const sa::AttnPlan plan = sa::attn_plan(bt.total_q, n_q_heads, d_v, k);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+        return SA_EWORKSPACE;
+    return launched(sa::launch_attn((int)dtype, bt, plan, q, n_q_heads, d_qk, k_cache, v_cache, d_v, kv_row_stride,
+                                    indices, k, gate_logits, gate_per_channel ? 1 : 0, softmax_scale, out, lse,
+                                    workspace, (hipStream_t)stream));
+}
+
+const char *sa_status_string(sa_status s)
+{
+    switch (s) {
+    case SA_OK: return "ok";
+    case SA_EINVAL: return "invalid argument";
+    case SA_EUNSUPPORTED: return "unsupported shape or dtype";
+    case SA_EWORKSPACE: return "workspace missing, too small or misaligned";
+    case SA_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int32_t sa_abi_version(void) { return SA_ABI_VERSION; }
+
+} // extern "C"

@@ -1,0 +1,41 @@
+// Internal launchers shared by the kernel sources and the C-ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sa {
+
+struct Batch;
+
+// a1
+int indexer_supported(int dtype, int H, int D);
+hipError_t launch_indexer(int dtype, int H, int D, const Batch &bt, const void *q_idx, const float *q_scale,
+                          const float *w, const void *k_idx, const float *k_scale, float *scores, int64_t ld,
+                          hipStream_t st);
+
+// a2
+struct TopkPlan {
+    int chunked;      // 1: per-chunk selection followed by a merge pass
+    int chunk;        // chunk length (positions) when chunked
+    int n_chunks;     // chunks per row when chunked
+    size_t ws_bytes;  // workspace the plan needs
+};
+TopkPlan topk_plan(int total_q, int max_ctx, int k);
+hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *scores, int64_t ld, int k,
+                       int32_t *indices, void *ws, hipStream_t st);
+
+// a3-a5
+struct AttnPlan {
+    int n_split;      // workgroups per (token, head group) along the index list
+    size_t ws_bytes;
+};
+AttnPlan attn_plan(int total_q, int Hq, int d_v, int k);
+int attn_supported(int dtype, int Hq, int d_qk, int d_v);
+hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &plan, const void *q, int Hq, int d_qk,
+                       const void *k_cache, const void *v_cache, int d_v, int64_t row_stride,
+                       const int32_t *indices, int k, const void *gate, int per_channel, float scale,
+                       void *out, float *lse, void *ws, hipStream_t st);
+
+} // namespace sa

@@ -1,0 +1,149 @@
+// Device-side helpers shared by the HIP kernels of the gated sparse attention
+// path (gfx950 / CDNA4, wave64).  Host code never includes this file.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// Ragged batch over a paged cache, passed to kernels by value.  Query token j
+// of sequence b sits at pos = ctx_len[b] - nq_b + j; position s of sequence b
+// lives at physical row page_table[b*max_pages + s/page_size]*page_size +
+// s%page_size (page_size is a power of two).
+struct Batch {
+    int32_t num_seqs;
+    int32_t total_q;
+    int32_t max_q;
+    int32_t max_ctx;
+    int32_t page_shift;
+    int32_t max_pages;
+    const int32_t *q_start;
+    const int32_t *ctx_len;
+    const int32_t *page_table;
+};
+
+// Largest b with q_start[b] <= tok: the sequence that owns token tok (empty
+// sequences have q_start[b] == q_start[b+1] and are skipped by construction).
+__device__ __forceinline__ int seq_of_token(const Batch &bt, int tok)
+{
+    int lo = 0, hi = bt.num_seqs - 1;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if (bt.q_start[mid] <= tok)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// Position of token tok, given its sequence b.
+__device__ __forceinline__ int pos_of_token(const Batch &bt, int b, int tok)
+{
+    int q0 = bt.q_start[b];
+    int nq = bt.q_start[b + 1] - q0;
+    return bt.ctx_len[b] - nq + (tok - q0);
+}
+
+__device__ __forceinline__ int64_t phys_row(const Batch &bt, int b, int s)
+{
+    int page = bt.page_table[(int64_t)b * bt.max_pages + (s >> bt.page_shift)];
+    return ((int64_t)page << bt.page_shift) + (s & ((1 << bt.page_shift) - 1));
+}
+
+// ---------------------------------------------------------------- MFMA tiles
+// 32x32 output tile layout (all 32x32 MFMAs used here): lane l holds column
+// l % 32; register i holds row 8*(i/4) + 4*(l/32) + i%4.
+__device__ __forceinline__ int mfma32_row(int i, int lane)
+{
+    return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+// 16x16 output tile layout: lane l holds column l % 16; register i holds row
+// 4*(l/16) + i.
+__device__ __forceinline__ int mfma16_row(int i, int lane)
+{
+    return 4 * (lane >> 4) + i;
+}
+
+// A/B operands: lane l supplies row (A) or column (B) l % 32 (32x32) or
+// l % 16 (16x16), and a contiguous run of the contraction index selected by
+// l / 32 (resp. l / 16).  A and B use the same run for the same lane group,
+// so the product contracts matching elements whatever order the hardware
+// walks inside a run.
+
+__device__ __forceinline__ f32x16 mma32_f32(float a, float b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mma32_bf16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// fp8 (OCP e4m3fn) x fp8, 32x32x64, unit block scales (E8M0 127 = 2^0).
+__device__ __forceinline__ f32x16 mma32_fp8(i32x8 a, i32x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ f32x4 mma16_bf16(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------- conversions
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b)
+{
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float sigmoidf_(float x)
+{
+    return 1.0f / (1.0f + __expf(-x));
+}
+
+// ------------------------------------------------------------ wave helpers
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int m)
+{
+    return __shfl_xor(v, m, kWave);
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v = fmaxf(v, shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        v += shfl_xor(v, m);
+    return v;
+}
+
+} // namespace sa

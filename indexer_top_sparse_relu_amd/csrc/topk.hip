@@ -1,0 +1,525 @@
+// a2 — exact per-token Top-K (gfx950).
+//
+// Pages (by title):
+//   [HAT] "Hybrid Attention Architectures: Engineering Trade-offs from Linear
+//          Attention to Gated Sparse Attention", §3.1 (keep the K highest-
+//          scoring positions) and §5 item 4 (rows shorter than K are padded).
+//   [F2S] "From Full Attention to Sparsity: The Evolution of Hybrid Attention
+//          Architectures in Large Language Models", "Fine-Grained Sparse
+//          Attention: Indexer Plus Top-K" (indices of shape [n, K]) and
+//          "Engineering Considerations" item 1 (variable-length Top-K).
+//   [EVO] "Evolution of Hybrid Attention in Open-Source LLMs: From Linear to
+//          Gated Sparse Attention", §5 item 3: approximate Top-K breaks
+//          train/inference consistency, so selection here is exact.
+// Order: (score descending, position ascending); +0 and -0 compare equal.
+//
+// One workgroup (512 threads) selects from one segment of slots:
+//   1. a strided sample (<= 4096 slots) gives a key window [lo, hi];
+//   2. a pass over the segment counts slots above the window (registers) and
+//      histograms the window into 4096 LDS bins; the bin holding the K-th key
+//      narrows the window (a refinement pass repeats this when that bin is
+//      still large, at most three times for 32-bit keys);
+//   3. an order-preserving pass writes the slots above the window (sure
+//      winners) and keeps the window's slots in LDS, both in slot order;
+//   4. LDS histograms narrow the kept slots down to the exact K-th key; ties
+//      at that key go to the lowest slots;
+//   5. the two ascending runs are merged by co-rank and written.
+// Keys are the order-preserving uint32 image of the fp32 score.
+//
+// Rows up to a few hundred thousand slots take one workgroup each.  When there
+// are too few rows to fill the GPU, each row is cut into chunks selected in
+// parallel (stage 1: top-K per chunk, with scores), and a second pass selects
+// from the concatenated per-chunk winners (stage 2).  The global top-K is a
+// subset of the union of per-chunk top-Ks under the same total order, and the
+// chunk lists are concatenated in position order, so slot order is position
+// order in both stages.
+#include "sa_device.h"
+#include "launch.h"
+
+namespace sa {
+
+constexpr int kTkThreads = 512;
+constexpr int kTkWaves = kTkThreads / 64;
+constexpr int kBins = 4096;
+constexpr int kCap = 2048;      // LDS slots for the window's candidates
+constexpr int kSample = 4096;
+constexpr int kMaxK = 4096;
+
+__device__ __forceinline__ uint32_t fkey(float v)
+{
+    uint32_t u = __float_as_uint(v);
+    u = (u == 0x80000000u) ? 0u : u;                  // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float kval(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+__device__ __forceinline__ int bitlen(uint32_t x) { return x ? 32 - __clz((int)x) : 0; }
+
+struct TkSmem {
+    uint32_t *hist;     // [kBins]
+    uint32_t *ckey;     // [kCap]
+    int32_t *cidx;      // [kCap]
+    uint32_t *okey;     // [K]
+    int32_t *oidx;      // [K]
+    uint32_t *misc;     // [64]
+};
+
+// Exclusive block scan of v (512 threads); *total gets the block sum.
+__device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *misc, uint32_t &total)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= d)
+            x += y;
+    }
+    if (lane == 63)
+        misc[wv] = x;
+    __syncthreads();
+    uint32_t off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+        uint32_t s = misc[w];
+        off += (w < wv) ? s : 0u;
+        tot += s;
+    }
+    total = tot;
+    __syncthreads();
+    return off + x - v;
+}
+
+__device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *misc)
+{
+    uint32_t t;
+    block_scan(v, misc, t);
+    return t;
+}
+
+__device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, uint32_t *misc)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, m, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, m, 64));
+    }
+    if (lane == 0) {
+        misc[16 + wv] = mn;
+        misc[24 + wv] = mx;
+    }
+    __syncthreads();
+    mn = 0xFFFFFFFFu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+        mn = min(mn, misc[16 + w]);
+        mx = max(mx, misc[24 + w]);
+    }
+    __syncthreads();
+}
+
+// Bin b with sum(hist[b+1..]) < need <= sum(hist[b..]); *gt = sum(hist[b+1..]).
+// Requires 1 <= need <= sum(hist).  Each thread owns 8 consecutive bins.
+__device__ __forceinline__ void find_bin(const TkSmem &sm, uint32_t need, int &b_out, uint32_t &gt_out)
+{
+    const int t = threadIdx.x;
+    uint32_t h[8], local = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        h[j] = sm.hist[t * 8 + j];
+        local += h[j];
+    }
+    uint32_t total;
+    const uint32_t excl = block_scan(local, sm.misc, total);
+    const uint32_t above = total - excl - local;      // bins owned by higher threads
+    if (need > above && need <= above + local) {
+        uint32_t acc = above;
+#pragma unroll
+        for (int j = 7; j >= 0; --j) {
+            if (acc + h[j] >= need) {
+                sm.misc[40] = (uint32_t)(t * 8 + j);
+                sm.misc[41] = acc;
+                break;
+            }
+            acc += h[j];
+        }
+    }
+    __syncthreads();
+    b_out = (int)sm.misc[40];
+    gt_out = sm.misc[41];
+    __syncthreads();
+}
+
+// One selection problem: n slots with values `vals`; positions are idx0 + j,
+// or idxs[j] when idxs != nullptr (then slots with idxs[j] < 0 are empty).
+// Writes K entries to gidx (and their scores to gval when non-null): the
+// selected positions in ascending order, then -1 (score 0).
+template <bool EXPLICIT>
+__device__ void select_topk(const float *__restrict__ vals, const int32_t *__restrict__ idxs, int n, int idx0,
+                            int K, int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
+{
+    const int tid = threadIdx.x;
+    auto pos_of = [&](int j) -> int32_t { return EXPLICIT ? idxs[j] : idx0 + j; };
+    auto valid = [&](int j) -> bool { return j < n && (!EXPLICIT || idxs[j] >= 0); };
+
+    // ---- number of non-empty slots
+    int nvalid = n;
+    if (EXPLICIT) {
+        uint32_t c = 0;
+        for (int j = tid; j < n; j += kTkThreads)
+            c += idxs[j] >= 0;
+        nvalid = (int)block_sum(c, sm.misc);
+    }
+
+    if (nvalid <= K) {
+        // everything is selected: slot order is ascending position order
+        uint32_t base = 0;
+        for (int j0 = 0; j0 < n; j0 += kTkThreads) {
+            const int j = j0 + tid;
+            const bool v = valid(j);
+            uint32_t tot;
+            const uint32_t p = base + block_scan(v ? 1u : 0u, sm.misc, tot);
+            if (v) {
+                gidx[p] = pos_of(j);
+                if (gval)
+                    gval[p] = vals[j];
+            }
+            base += tot;
+        }
+        for (int p = nvalid + tid; p < K; p += kTkThreads) {
+            gidx[p] = -1;
+            if (gval)
+                gval[p] = 0.0f;
+        }
+        return;
+    }
+
+    // ---- 1. sample -> initial window
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    {
+        const int S = n < kSample ? n : kSample;
+        for (int k = tid; k < S; k += kTkThreads) {
+            const int j = (int)(((int64_t)k * n) / S);
+            if (valid(j)) {
+                const uint32_t key = fkey(vals[j]);
+                lo = min(lo, key);
+                hi = max(hi, key);
+            }
+        }
+        block_minmax(lo, hi, sm.misc);
+        if (lo > hi) {
+            lo = 0u;
+            hi = 0xFFFFFFFFu;
+        }
+    }
+
+    // ---- 2. histogram passes over the segment until the K-th key's bin is small
+    uint32_t above = 0, cnt = 0;
+    for (int iter = 0; iter < 12; ++iter) {
+        const int sh = max(0, bitlen(hi - lo) - 12);
+        for (int b = tid; b < kBins; b += kTkThreads)
+            sm.hist[b] = 0u;
+        __syncthreads();
+        uint32_t ab = 0;
+        const bool aligned = ((((uintptr_t)vals) & 15u) == 0);
+        for (int j0 = tid * 4; j0 < n; j0 += kTkThreads * 4) {
+            float v4[4];
+            if (aligned && j0 + 3 < n) {
+                const float4 f = *(const float4 *)(vals + j0);
+                v4[0] = f.x; v4[1] = f.y; v4[2] = f.z; v4[3] = f.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v4[e] = (j0 + e < n) ? vals[j0 + e] : 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (!valid(j0 + e))
+                    continue;
+                const uint32_t key = fkey(v4[e]);
+                if (key > hi)
+                    ++ab;
+                else if (key >= lo)
+                    atomicAdd(&sm.hist[(key - lo) >> sh], 1u);
+            }
+        }
+        above = block_sum(ab, sm.misc);          // also orders the histogram writes
+        if (above >= (uint32_t)K) {              // the K-th key lies above the window
+            lo = hi + 1u;
+            hi = 0xFFFFFFFFu;
+            continue;
+        }
+        const uint32_t need = (uint32_t)K - above;
+        uint32_t wtot = 0;
+        for (int b = tid; b < kBins; b += kTkThreads)
+            wtot += sm.hist[b];
+        wtot = block_sum(wtot, sm.misc);
+        if (wtot < need) {                       // it lies below the window (lo > 0 here)
+            hi = lo - 1u;
+            lo = 0u;
+            continue;
+        }
+        int bsel;
+        uint32_t gt;
+        find_bin(sm, need, bsel, gt);
+        cnt = sm.hist[bsel];
+        const uint64_t nlo = (uint64_t)lo + ((uint64_t)bsel << sh);
+        const uint64_t nhi = min((uint64_t)hi, nlo + ((1ull << sh) - 1ull));
+        lo = (uint32_t)nlo;
+        hi = (uint32_t)nhi;
+        above += gt;
+        __syncthreads();
+        if (cnt <= (uint32_t)kCap || lo == hi)
+            break;
+    }
+    const uint32_t need = (uint32_t)K - above;   // 1 <= need <= cnt
+    const bool single = (lo == hi);
+
+    // ---- 3. order-preserving pass: winners to okey/oidx[0, above); window slots kept
+    {
+        const bool aligned = ((((uintptr_t)vals) & 15u) == 0);
+        uint32_t bw = 0, bc = 0;
+        for (int j00 = 0; j00 < n; j00 += kTkThreads * 4) {
+            const int j0 = j00 + tid * 4;
+            float v4[4];
+            if (aligned && j0 + 3 < n) {
+                const float4 f = *(const float4 *)(vals + j0);
+                v4[0] = f.x; v4[1] = f.y; v4[2] = f.z; v4[3] = f.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v4[e] = (j0 + e < n) ? vals[j0 + e] : 0.0f;
+            }
+            uint32_t kk[4];
+            bool w4[4], c4[4];
+            uint32_t nw = 0, nc = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool v = valid(j0 + e);
+                kk[e] = fkey(v4[e]);
+                w4[e] = v && kk[e] > hi;
+                c4[e] = v && kk[e] >= lo && kk[e] <= hi;
+                nw += w4[e];
+                nc += c4[e];
+            }
+            uint32_t tot;
+            const uint32_t ex = block_scan(nw | (nc << 16), sm.misc, tot);
+            uint32_t pw = bw + (ex & 0xFFFFu), pc = bc + (ex >> 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (w4[e] && pw < (uint32_t)K) {
+                    sm.okey[pw] = kk[e];
+                    sm.oidx[pw] = pos_of(j0 + e);
+                    ++pw;
+                }
+                if (c4[e]) {
+                    if (single) {
+                        if (pc < need) {
+                            sm.okey[above + pc] = kk[e];
+                            sm.oidx[above + pc] = pos_of(j0 + e);
+                        }
+                    } else if (pc < (uint32_t)kCap) {
+                        sm.ckey[pc] = kk[e];
+                        sm.cidx[pc] = pos_of(j0 + e);
+                    }
+                    ++pc;
+                }
+            }
+            bw += tot & 0xFFFFu;
+            bc += tot >> 16;
+        }
+        __syncthreads();
+    }
+
+    // ---- 4. resolve the window inside LDS
+    if (!single) {
+        const int C = (int)min(cnt, (uint32_t)kCap);
+        uint32_t wl = lo, wh = hi, needw = need;
+        bool all_in = false;
+        // each pass narrows a window of width W to at most W / 4096 (or stops): <= 3 passes
+        for (int pass = 0; pass < 4 && wl != wh && !all_in; ++pass) {
+            const int sh = max(0, bitlen(wh - wl) - 12);
+            for (int b = tid; b < kBins; b += kTkThreads)
+                sm.hist[b] = 0u;
+            __syncthreads();
+            for (int c = tid; c < C; c += kTkThreads) {
+                const uint32_t key = sm.ckey[c];
+                if (key >= wl && key <= wh)
+                    atomicAdd(&sm.hist[(key - wl) >> sh], 1u);
+            }
+            __syncthreads();
+            int bsel;
+            uint32_t gt;
+            find_bin(sm, needw, bsel, gt);
+            const uint32_t hb = sm.hist[bsel];
+            needw -= gt;
+            const uint64_t nlo = (uint64_t)wl + ((uint64_t)bsel << sh);
+            wh = (uint32_t)min((uint64_t)wh, nlo + ((1ull << sh) - 1ull));
+            wl = (uint32_t)nlo;
+            all_in = (hb == needw);
+            __syncthreads();
+        }
+        // ordered selection: keys above the window, then the first needw keys inside it
+        uint32_t bsel_ = 0, bwin = 0;
+        for (int c0 = 0; c0 < C; c0 += kTkThreads) {
+            const int c = c0 + tid;
+            const uint32_t key = c < C ? sm.ckey[c] : 0u;
+            const bool inw = c < C && key >= wl && key <= wh;
+            const bool abv = c < C && key > wh;
+            uint32_t tot;
+            const uint32_t ex = block_scan((inw ? 1u : 0u) | ((abv ? 1u : 0u) << 16), sm.misc, tot);
+            const uint32_t rank_w = bwin + (ex & 0xFFFFu);
+            const bool sel = abv || (inw && (all_in || rank_w < needw));
+            uint32_t tot2;
+            const uint32_t ps = bsel_ + block_scan(sel ? 1u : 0u, sm.misc, tot2);
+            if (sel && above + ps < (uint32_t)K) {
+                sm.okey[above + ps] = key;
+                sm.oidx[above + ps] = sm.cidx[c];
+            }
+            bwin += tot & 0xFFFFu;
+            bsel_ += tot2;
+        }
+        __syncthreads();
+    }
+
+    // ---- 5. merge the two ascending runs [0, above) and [above, K)
+    {
+        const int A = (int)above, Bn = K - (int)above;
+        const int32_t *ra = sm.oidx, *rb = sm.oidx + A;
+        for (int i = tid; i < K; i += kTkThreads) {
+            const bool inA = i < A;
+            const int32_t x = sm.oidx[i];
+            const int32_t *other = inA ? rb : ra;
+            int lo2 = 0, hi2 = inA ? Bn : A;         // count of `other` elements < x
+            while (lo2 < hi2) {
+                const int mid = (lo2 + hi2) >> 1;
+                if (other[mid] < x)
+                    lo2 = mid + 1;
+                else
+                    hi2 = mid;
+            }
+            const int p = (inA ? i : i - A) + lo2;
+            gidx[p] = x;
+            if (gval)
+                gval[p] = kval(sm.okey[i]);
+        }
+    }
+}
+
+__device__ __forceinline__ TkSmem tk_smem(int K)
+{
+    extern __shared__ __align__(16) uint32_t tk_lds[];
+    TkSmem sm;
+    sm.hist = tk_lds;
+    sm.ckey = sm.hist + kBins;
+    sm.cidx = (int32_t *)(sm.ckey + kCap);
+    sm.okey = (uint32_t *)(sm.cidx + kCap);
+    sm.oidx = (int32_t *)(sm.okey + ((K + 3) & ~3));
+    sm.misc = (uint32_t *)(sm.oidx + ((K + 3) & ~3));
+    return sm;
+}
+
+static size_t tk_smem_bytes(int K)
+{
+    return (size_t)(kBins + 2 * kCap + 2 * ((K + 3) & ~3) + 64) * 4;
+}
+
+// One workgroup per token row.
+__global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(Batch bt, const float *__restrict__ scores,
+                                                               int64_t ld, int K, int32_t *__restrict__ out)
+{
+    const int row = blockIdx.x;
+    const int b = seq_of_token(bt, row);
+    const int n = pos_of_token(bt, b, row) + 1;
+    select_topk<false>(scores + (int64_t)row * ld, nullptr, n, 0, K, out + (int64_t)row * K, nullptr, tk_smem(K));
+}
+
+// Stage 1: blockIdx.x = chunk, blockIdx.y = row; per-chunk top-K with scores.
+__global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(Batch bt, const float *__restrict__ scores,
+                                                                int64_t ld, int K, int chunk, int64_t cand_ld,
+                                                                int32_t *__restrict__ cidx, float *__restrict__ cval)
+{
+    const int c = blockIdx.x, row = blockIdx.y;
+    const int b = seq_of_token(bt, row);
+    const int n = pos_of_token(bt, b, row) + 1;
+    const int j0 = c * chunk;
+    const int len = max(0, min(chunk, n - j0));
+    const int64_t o = (int64_t)row * cand_ld + (int64_t)c * K;
+    select_topk<false>(scores + (int64_t)row * ld + j0, nullptr, len, j0, K, cidx + o, cval + o, tk_smem(K));
+}
+
+// Stage 2: one workgroup per row over the concatenated chunk winners.
+__global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(int K, int n_cand, int64_t cand_ld,
+                                                                const int32_t *__restrict__ cidx,
+                                                                const float *__restrict__ cval,
+                                                                int32_t *__restrict__ out)
+{
+    const int row = blockIdx.x;
+    const int64_t o = (int64_t)row * cand_ld;
+    select_topk<true>(cval + o, cidx + o, n_cand, 0, K, out + (int64_t)row * K, nullptr, tk_smem(K));
+}
+
+TopkPlan topk_plan(int total_q, int max_ctx, int k)
+{
+    TopkPlan p{0, 0, 1, 0};
+    // Few rows cannot fill 256 CUs: cut long rows into chunks (>= 4 * k each).
+    if (total_q < 256 && max_ctx > 16384) {
+        const int want_chunks = (512 + total_q - 1) / total_q;
+        int chunk = (max_ctx + want_chunks - 1) / want_chunks;
+        chunk = max(chunk, max(4 * k, 8192));
+        chunk = (chunk + 1023) / 1024 * 1024;
+        const int n_chunks = (max_ctx + chunk - 1) / chunk;
+        if (n_chunks > 1) {
+            p.chunked = 1;
+            p.chunk = chunk;
+            p.n_chunks = n_chunks;
+            const int64_t cand_ld = ((int64_t)n_chunks * k + 63) / 64 * 64;
+            p.ws_bytes = (size_t)total_q * (size_t)cand_ld * 8u;
+        }
+    }
+    return p;
+}
+
+hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *scores, int64_t ld, int k,
+                       int32_t *indices, void *ws, hipStream_t st)
+{
+    if (k < 1 || k > kMaxK)
+        return hipErrorInvalidValue;
+    const size_t smem = tk_smem_bytes(k);
+    if (smem > 65536) {
+        // above the default dynamic-LDS limit: raise it for the kernels this plan launches
+        if (hipFuncSetAttribute((const void *)topk_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem) != hipSuccess ||
+            hipFuncSetAttribute((const void *)topk_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem) != hipSuccess ||
+            hipFuncSetAttribute((const void *)topk_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem) != hipSuccess)
+            return hipErrorInvalidValue;
+    }
+    if (!plan.chunked) {
+        hipLaunchKernelGGL(topk_rows_kernel, dim3(bt.total_q), dim3(kTkThreads), smem, st, bt, scores, ld, k,
+                           indices);
+        return hipGetLastError();
+    }
+    const int64_t cand_ld = ((int64_t)plan.n_chunks * k + 63) / 64 * 64;
+    int32_t *cidx = (int32_t *)ws;
+    float *cval = (float *)((char *)ws + (size_t)bt.total_q * (size_t)cand_ld * 4u);
+    if (bt.total_q > 65535)
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL(topk_chunk_kernel, dim3(plan.n_chunks, bt.total_q), dim3(kTkThreads), smem, st, bt, scores,
+                       ld, k, plan.chunk, cand_ld, cidx, cval);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(bt.total_q), dim3(kTkThreads), smem, st, k,
+                       (int)(plan.n_chunks * k), cand_ld, cidx, cval, indices);
+    return hipGetLastError();
+}
+
+} // namespace sa

@@ -1,0 +1,218 @@
+"""Comparison rules and host marshalling shared by the GPU parity tests.
+
+Scores: |x - r| <= rtol * max(|r|, 0.01 * max_row |r|) on every entry of a
+token's row, rtol 1e-5 (fp32) or 2e-2 (bf16/fp8).  Attention outputs: the
+relative error of each (token, head) output vector in the 2-norm is at most
+1e-5 (fp32) or 2e-2 (bf16), and bf16 outputs also meet the entrywise rule.
+Top-K: bit-exact against the oracle's brute force on the GPU's own fp32
+scores; against the oracle's double scores, the set must match wherever the
+K-th/(K+1)-th gap exceeds 1e-3 relative, else every selected score must be at
+least s_K - 1e-3 |s_K|.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import oracle as O
+
+RTOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------ rules
+
+def close(x, r, rtol, floor=0.01):
+    """Boolean mask of the tolerance rule along the last axis."""
+    x = np.asarray(x, np.float64)
+    r = np.asarray(r, np.float64)
+    rowmax = np.max(np.abs(r), axis=-1, keepdims=True)
+    den = np.maximum(np.abs(r), floor * rowmax)
+    return np.abs(x - r) <= rtol * den + 1e-300
+
+
+def check_scores(gpu, ref, n, rtol, what="scores"):
+    """gpu [R, >=max n] fp32, ref [R, >=max n] double; compare entries [0, n_r) of each row."""
+    bad = 0
+    worst = 0.0
+    for r in range(len(n)):
+        x, y = gpu[r, :n[r]], ref[r, :n[r]]
+        ok = close(x, y, rtol)
+        if not ok.all():
+            bad += int((~ok).sum())
+        rowmax = np.abs(y).max()
+        worst = max(worst, float((np.abs(x - y) / np.maximum(np.abs(y), 0.01 * rowmax)).max()))
+    assert bad == 0, f"{what}: {bad} entries outside rtol {rtol} (worst rel {worst:.3g})"
+    return worst
+
+
+def check_idx_invariants(idx, n, K):
+    idx = np.asarray(idx)
+    for r in range(idx.shape[0]):
+        v = idx[r]
+        c = min(K, int(n[r]))
+        assert np.all(v[:c] >= 0) and np.all(v[c:] == -1), f"row {r}: padding layout"
+        s = v[:c]
+        assert np.all(np.diff(s) > 0), f"row {r}: not ascending/unique"
+        assert s.size == 0 or (s[0] >= 0 and s[-1] < n[r]), f"row {r}: out of causal range"
+
+
+def check_topk_exact(gpu_idx, gpu_scores, n, K):
+    """Bit-exact Top-K of the GPU's own fp32 scores (oracle brute force on the same values)."""
+    ref = O.topk(np.asarray(gpu_scores, np.float64), np.asarray(n, np.int64), K)
+    diff = np.nonzero((ref != np.asarray(gpu_idx)).any(axis=1))[0]
+    assert diff.size == 0, f"Top-K differs from brute force on rows {diff[:10].tolist()}"
+
+
+def check_selection(gpu_idx, ref_scores, n, K, tol=1e-3):
+    """The spec rule against the oracle's double scores; returns mean recall@K."""
+    recalls = []
+    for r in range(len(n)):
+        nr = int(n[r])
+        sel = np.asarray(gpu_idx[r][:min(K, nr)])
+        if nr <= K:
+            assert np.array_equal(sel, np.arange(nr))
+            recalls.append(1.0)
+            continue
+        row = ref_scores[r, :nr]
+        order = np.lexsort((np.arange(nr), -row))
+        sK, sK1 = row[order[K - 1]], row[order[K]]
+        ref_set = np.sort(order[:K])
+        recalls.append(np.intersect1d(sel, ref_set).size / K)
+        if sK - sK1 > tol * abs(sK):
+            assert np.array_equal(sel, ref_set), f"row {r}: selection differs with a clear gap"
+        else:
+            assert np.all(row[sel] >= sK - tol * abs(sK)), f"row {r}: selected score below threshold"
+    return float(np.mean(recalls))
+
+
+def check_attn(gpu_out, ref_out, rtol, what="attention"):
+    """Relative error of every (token, head) output vector in the 2-norm <= rtol; bf16
+    outputs (rtol >= 1e-3) must also meet the elementwise rule."""
+    x = np.asarray(gpu_out, np.float64)
+    r = np.asarray(ref_out, np.float64)
+    num = np.linalg.norm(x - r, axis=-1)
+    den = np.linalg.norm(r, axis=-1)
+    rel = num / np.maximum(den, 1e-300)
+    bad = rel > rtol
+    assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} vectors above rtol {rtol} (worst {rel.max():.3g})"
+    if rtol >= 1e-3:
+        ok = close(x, r, rtol)
+        assert ok.all(), f"{what}: {(~ok).sum()} of {ok.size} elements outside rtol {rtol}"
+    return float(rel.max())
+
+
+# --------------------------------------------------------- host marshalling
+
+def to_np(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def token_geometry(spec):
+    """(sequence, position, n) of every token, from the layout convention."""
+    seq, pos = [], []
+    for b, (nq, L) in enumerate(zip(spec.q_lens, spec.ctx_lens)):
+        for j in range(nq):
+            seq.append(b)
+            pos.append(L - nq + j)
+    pos = np.array(pos, np.int64)
+    return np.array(seq, np.int64), pos, pos + 1
+
+
+def logical_rows(wl, b: int, n: int) -> torch.Tensor:
+    """Physical cache rows of positions 0..n-1 of sequence b (device tensor)."""
+    ps = wl.spec.page_size
+    s = torch.arange(n, device=wl.page_table.device)
+    return wl.page_table[b, s // ps].long() * ps + s % ps
+
+
+def indexer_inputs(wl, toks):
+    """Oracle inputs holding only what the indexer needs for the listed tokens: one
+    sequence per token with that token as its last query, its logical key rows packed
+    behind an identity page table.  Row r of the result is token toks[r]."""
+    spec = wl.spec
+    seq, pos, n = token_geometry(spec)
+    ps = spec.page_size
+    kr, ksr, ctx = [], [], []
+    for t in toks:
+        rows = logical_rows(wl, int(seq[t]), int(n[t]))
+        pad = (-int(n[t])) % ps
+        rows = torch.cat([rows, rows[:1].expand(pad)]) if pad else rows
+        kr.append(wl.k_idx.view(-1, spec.d_I)[rows])
+        if wl.k_scale is not None:
+            ksr.append(wl.k_scale.view(-1)[rows])
+        ctx.append(int(n[t]))
+    toks_t = torch.as_tensor(np.asarray(toks), device=wl.q_idx.device)
+    npg = [(c + ps - 1) // ps for c in ctx]
+    table = np.zeros((len(toks), max(npg)), np.int32)
+    off = 0
+    for r, m in enumerate(npg):
+        table[r, :m] = np.arange(off, off + m)
+        off += m
+    B = len(toks)
+    z = np.zeros((B, 1, 16), np.float32)
+    return O.Inputs(q_start=np.arange(B + 1, dtype=np.int32), ctx_len=np.array(ctx, np.int32), page_table=table,
+                    page_size=ps, idx_dtype=spec.idx_dtype, attn_dtype="f32", q_idx=to_np(wl.q_idx[toks_t]),
+                    q_scale=to_np(wl.q_scale[toks_t]) if wl.q_scale is not None else None,
+                    w=to_np(wl.w[toks_t]), k_idx=to_np(torch.cat(kr)),
+                    k_scale=to_np(torch.cat(ksr)) if ksr else None, q=z, k_cache=np.zeros((off * ps, 16), np.float32),
+                    v_cache=np.zeros((off * ps, 16), np.float32), gate=np.zeros((B, 1, 16), np.float32),
+                    H_I=spec.H_I, d_I=spec.d_I, Hq=1, d_qk=16, d_v=16, row_stride=16, gate_per_channel=True)
+
+
+def attn_inputs(wl, toks, idx_rows):
+    """Oracle inputs for attention of the listed tokens over their GPU index rows: the
+    selected cache rows are packed per token (in index order) and the indices rewritten
+    to those packed positions; padding (-1) stays padding."""
+    spec = wl.spec
+    seq, pos, n = token_geometry(spec)
+    K = idx_rows.shape[1]
+    ps = spec.page_size
+    width = (K + ps - 1) // ps * ps
+    kc_rows, new_idx = [], np.full((len(toks), K), -1, np.int32)
+    rs = wl.kv_row_stride
+    kflat = wl.k_cache.view(-1, rs)
+    vflat = wl.v_cache.view(-1, rs)
+    same = wl.v_cache.data_ptr() == wl.k_cache.data_ptr()
+    vk_rows = []
+    for r, t in enumerate(toks):
+        sel = idx_rows[r]
+        valid = sel[sel >= 0]
+        rows = logical_rows(wl, int(seq[t]), int(n[t]))[torch.as_tensor(valid, device=wl.page_table.device).long()]
+        pad = width - rows.numel()
+        rows = torch.cat([rows, rows.new_zeros(pad)])
+        kc_rows.append(kflat[rows])
+        vk_rows.append(vflat[rows])
+        new_idx[r, :valid.size] = np.arange(valid.size)
+    toks_t = torch.as_tensor(np.asarray(toks), device=wl.q.device)
+    B = len(toks)
+    table = np.arange(B * (width // ps), dtype=np.int32).reshape(B, width // ps)
+    kc = to_np(torch.cat(kc_rows))
+    vc = kc if same else to_np(torch.cat(vk_rows))
+    inp = O.Inputs(q_start=np.arange(B + 1, dtype=np.int32), ctx_len=np.full(B, width, np.int32), page_table=table,
+                   page_size=ps, idx_dtype="f32", attn_dtype=spec.attn_dtype,
+                   q_idx=np.zeros((B, 1, 16), np.float32), q_scale=None, w=np.zeros((B, 1), np.float32),
+                   k_idx=np.zeros((B * width, 16), np.float32), k_scale=None, q=to_np(wl.q[toks_t]), k_cache=kc,
+                   v_cache=vc, gate=to_np(wl.gate[toks_t]), H_I=1, d_I=16, Hq=spec.Hq, d_qk=spec.d_qk,
+                   d_v=spec.d_v, row_stride=rs, gate_per_channel=spec.gate_per_channel)
+    return inp, new_idx
+
+
+def sample_tokens(T, k, seed=0, edge=4):
+    """First/last `edge` tokens plus random ones, sorted, unique."""
+    rng = np.random.default_rng(seed)
+    base = set(range(min(edge, T))) | set(range(max(0, T - edge), T))
+    rest = [t for t in range(T) if t not in base]
+    extra = rng.choice(rest, size=min(len(rest), max(0, k - len(base))), replace=False) if rest else []
+    return sorted(base | set(int(x) for x in extra))

@@ -1,0 +1,133 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad
+arguments on the host before any launch (no GPU needed: no call here reaches a
+kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from indexer_top_sparse_relu_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from indexer_top_sparse_relu_amd import build
+        build.build()
+    return binding
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sa_status|size_t|const char \*|int32_t)\s*\*?\s*(\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("sparse_indexer_scores", "sparse_topk", "sparse_topk_workspace_size", "sparse_gated_attn_fwd",
+              "sparse_gated_attn_workspace_size", "sa_status_string", "sa_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    L = B.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+    assert set(B.EXPORTS) == set(declared_functions())
+    assert L.sa_abi_version() == 1
+
+
+def test_status_strings(B):
+    for st in (0, -1, -2, -3, -4, 7):
+        s = B.status_string(st)
+        assert isinstance(s, str) and s
+
+
+FAKE = 1 << 20   # an aligned non-null address: validation rejects before anything dereferences it
+
+
+def batch(B, **kw):
+    f = dict(num_seqs=1, total_q=4, max_q=4, max_ctx=100, page_size=64, max_pages=2,
+             q_start=FAKE, ctx_len=FAKE, page_table=FAKE)
+    f.update(kw)
+    return B.SaBatch(f["num_seqs"], f["total_q"], f["max_q"], f["max_ctx"], f["page_size"], f["max_pages"],
+                     f["q_start"], f["ctx_len"], f["page_table"])
+
+
+def idx_call(B, bt, dtype=1, H=16, D=64, q=FAKE, qs=None, w=FAKE, k=FAKE, ks=None, sc=FAKE, ld=128):
+    return B.lib().sparse_indexer_scores(ctypes.byref(bt), dtype, q, H, D, qs, w, k, ks, sc, ld, None)
+
+
+def test_indexer_argument_errors(B):
+    ok = batch(B)
+    assert B.lib().sparse_indexer_scores(None, 1, FAKE, 16, 64, None, FAKE, FAKE, None, FAKE, 128, None) == B.SA_EINVAL
+    assert idx_call(B, batch(B, page_size=48)) == B.SA_EINVAL          # not a power of two
+    assert idx_call(B, batch(B, page_size=8)) == B.SA_EINVAL           # below 16
+    assert idx_call(B, batch(B, max_pages=1)) == B.SA_EINVAL           # table too short for max_ctx
+    assert idx_call(B, batch(B, total_q=0)) == B.SA_EINVAL
+    assert idx_call(B, batch(B, q_start=None)) == B.SA_EINVAL
+    assert idx_call(B, ok, ld=64) == B.SA_EINVAL                       # ld < max_ctx
+    assert idx_call(B, ok, ld=130) == B.SA_EINVAL                      # ld not a multiple of 4
+    assert idx_call(B, ok, q=None) == B.SA_EINVAL
+    assert idx_call(B, ok, q=FAKE + 4) == B.SA_EINVAL                  # misaligned
+    assert idx_call(B, ok, dtype=2) == B.SA_EINVAL                     # fp8 without scales
+    assert idx_call(B, ok, dtype=5) == B.SA_EINVAL
+    assert idx_call(B, ok, H=12) == B.SA_EUNSUPPORTED
+    assert idx_call(B, ok, D=48) == B.SA_EUNSUPPORTED
+    assert idx_call(B, ok, dtype=2, D=64, qs=FAKE, ks=FAKE) == B.SA_EUNSUPPORTED
+
+
+def test_topk_argument_errors_and_workspace(B):
+    L = B.lib()
+    ok = batch(B)
+    call = lambda bt, k=32, ld=128, ws=None, wsb=0, sc=FAKE, out=FAKE: L.sparse_topk(
+        ctypes.byref(bt), sc, ld, k, out, ws, wsb, None)
+    assert call(ok, k=0) == B.SA_EINVAL
+    assert call(ok, k=5000) == B.SA_EUNSUPPORTED
+    assert call(ok, sc=None) == B.SA_EINVAL
+    assert call(ok, out=None) == B.SA_EINVAL
+    assert call(ok, ld=96) == B.SA_EINVAL
+    # few rows over a long context need a workspace (chunked selection)
+    long = batch(B, num_seqs=16, total_q=16, max_q=1, max_ctx=1 << 20, max_pages=(1 << 20) // 64)
+    need = L.sparse_topk_workspace_size(ctypes.byref(long), 2048)
+    assert need > 0
+    assert call(long, k=2048, ld=1 << 20) == B.SA_EWORKSPACE
+    assert call(long, k=2048, ld=1 << 20, ws=FAKE, wsb=need - 1) == B.SA_EWORKSPACE
+    # many rows: no workspace
+    assert L.sparse_topk_workspace_size(ctypes.byref(batch(B, total_q=4096, max_q=4096, max_ctx=8192,
+                                                           max_pages=128)), 2048) == 0
+
+
+def test_attention_argument_errors(B):
+    L = B.lib()
+    ok = batch(B)
+
+    def call(bt=ok, dtype=1, H=32, dqk=128, kc=FAKE, vc=FAKE + (1 << 16), dv=128, rs=128, idx=FAKE, k=32,
+             gate=FAKE, scale=0.1, out=FAKE, ws=None, wsb=0):
+        return L.sparse_gated_attn_fwd(ctypes.byref(bt), dtype, FAKE, H, dqk, kc, vc, dv, rs, idx, k, gate, 1,
+                                       ctypes.c_float(scale), out, None, ws, wsb, None)
+
+    assert call(dtype=2) == B.SA_EINVAL
+    assert call(k=0) == B.SA_EINVAL
+    assert call(idx=None) == B.SA_EINVAL
+    assert call(gate=None) == B.SA_EINVAL
+    assert call(rs=100) == B.SA_EINVAL                     # row stride below d_qk
+    assert call(rs=132) == B.SA_EINVAL                     # row not 16-byte aligned
+    assert call(scale=float("nan")) == B.SA_EINVAL
+    assert call(H=24) == B.SA_EUNSUPPORTED                 # bf16 needs heads in multiples of 16
+    assert call(dqk=96, dv=96, rs=96) == B.SA_EUNSUPPORTED
+    assert call(kc=FAKE, vc=FAKE, dqk=512, dv=576, rs=576) == B.SA_EINVAL   # aliased V wider than K
+    dec = batch(B, num_seqs=16, total_q=16, max_q=1)
+    need = L.sparse_gated_attn_workspace_size(ctypes.byref(dec), 128, 512, 2048)
+    assert need > 0
+    assert call(bt=dec, H=128, dqk=576, dv=512, rs=576, kc=FAKE, vc=FAKE, k=2048) == B.SA_EWORKSPACE
+
+
+def test_binding_fails_loudly_without_library(B, monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        B.lib()

@@ -1,0 +1,235 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small workloads are compared element by element on every row; the full-size
+workloads (the shapes the benchmark times) on sampled rows that the oracle
+computes one by one, plus properties that hold at any size.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests import parity as P
+from indexer_top_sparse_relu_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from indexer_top_sparse_relu_amd import binding as B  # noqa: E402
+
+DEV = "cuda"
+
+
+def run(wl, stages=("indexer", "topk", "attn"), canary=True):
+    pl = B.Pipeline(wl)
+    if canary:
+        pl.scores.fill_(float("nan"))
+        pl.indices.fill_(-7)
+        pl.out.fill_(float("nan"))
+    for st in stages:
+        P.say(f"  [{wl.spec.name}] launch {st}")
+        getattr(pl, st)()
+        torch.cuda.synchronize()
+    return pl
+
+
+def full_check(spec, tag, attn_rows=None):
+    """Every row: scores, Top-K exactness, selection rule, invariants, attention, lse."""
+    P.say(f"[{tag}] {spec.name} T={spec.T} B={spec.B} K={spec.K} max_ctx={spec.max_ctx}")
+    wl = W.generate(spec, DEV)
+    pl = run(wl)
+    inp = O.Inputs.from_workload(wl)
+    seq, pos, n = P.token_geometry(spec)
+    sc_gpu = pl.scores.cpu().numpy()
+    sc_ref = O.indexer(inp, ld=pl.ld)
+    w1 = P.check_scores(sc_gpu, sc_ref, n, P.RTOL[spec.idx_dtype])
+    # nothing written beyond each row's causal length
+    for r in range(spec.T):
+        assert np.all(np.isnan(sc_gpu[r, n[r]:])), f"row {r} written past n"
+    idx = pl.indices.cpu().numpy()
+    P.check_idx_invariants(idx, n, spec.K)
+    P.check_topk_exact(idx, sc_gpu, n, spec.K)
+    rec = P.check_selection(idx, sc_ref, n, spec.K)
+    rows = np.arange(spec.T) if attn_rows is None else np.asarray(attn_rows)
+    ref_out, ref_lse = O.sparse_attn(inp, idx[rows], rows, spec.softmax_scale, with_lse=True)
+    out = pl.out.float().cpu().numpy()[rows]
+    w2 = P.check_attn(out, ref_out, P.RTOL[spec.attn_dtype])
+    lse = pl.lse.cpu().numpy()[rows]
+    assert P.close(lse, ref_lse, P.RTOL[spec.attn_dtype]).all()
+    P.say(f"[{tag}] ok: worst score rel {w1:.2e}, worst attn rel {w2:.2e}, recall {rec:.4f}")
+    return wl, pl
+
+
+# ------------------------------------------------------------------ tiny fp32
+
+def test_tiny_prefill_fp32():
+    full_check(W.tiny_prefill_fp32(), "tiny")
+
+
+def test_tiny_prefill_fp32_sharp_softmax_and_per_head_gate():
+    spec = W.tiny_prefill_fp32().replace(q_gain=4.0 * 8.0, gate_per_channel=False, seed=11)
+    full_check(spec, "tiny-sharp")
+
+
+def test_k_covering_context_equals_dense_control():
+    """K >= every row's length: the path must equal dense causal gated attention."""
+    spec = W.tiny_prefill_fp32().replace(K=256, seed=12)
+    wl = W.generate(spec, DEV)
+    pl = run(wl)
+    inp = O.Inputs.from_workload(wl)
+    dense = O.dense_attn(inp, scale=spec.softmax_scale)
+    P.check_attn(pl.out.cpu().numpy(), dense, P.RTOL["f32"], "dense control")
+
+
+# ------------------------------------------------------------ prefill bf16
+
+def test_prefill_bf16_ragged():
+    spec = W.prefill_bf16(T=1000).replace(K=256)       # ragged against every tile size
+    full_check(spec, "prefill-ragged")
+
+
+def test_prefill_bf16_multi_sequence_per_head_gate():
+    """Packed prefill of three sequences with cached prefixes (multi-turn concatenation)."""
+    spec = W.prefill_bf16().replace(q_lens=(300, 17, 450), ctx_lens=(700, 17, 1200), K=128,
+                                    gate_per_channel=False, paged_random=True, seed=21)
+    full_check(spec, "prefill-multi")
+
+
+def test_prefill_bf16_full_size_sampled():
+    spec = W.prefill_bf16()
+    P.say(f"[prefill-full] {spec.name} T={spec.T}")
+    wl = W.generate(spec, DEV)
+    pl = run(wl, canary=False)
+    seq, pos, n = P.token_geometry(spec)
+    idx = pl.indices.cpu().numpy()
+    sc_gpu = pl.scores.cpu().numpy()
+    P.check_idx_invariants(idx, n, spec.K)
+    rows = P.sample_tokens(spec.T, 256, seed=1, edge=64)
+    P.check_topk_exact(idx[rows], sc_gpu[rows], n[rows], spec.K)
+    srows = P.sample_tokens(spec.T, 24, seed=2)
+    inp = P.indexer_inputs(wl, srows)
+    ref = O.indexer(inp, ld=pl.ld)
+    P.check_scores(sc_gpu[srows], ref, n[srows], P.RTOL["bf16"])
+    P.check_selection(idx[srows], ref, n[srows], spec.K)
+    arows = P.sample_tokens(spec.T, 16, seed=3)
+    ainp, aidx = P.attn_inputs(wl, arows, idx[arows])
+    ref_out = O.sparse_attn(ainp, aidx, None, spec.softmax_scale)
+    P.check_attn(pl.out.float().cpu().numpy()[arows], ref_out, P.RTOL["bf16"])
+
+
+# ------------------------------------------------------------- decode bf16
+
+def test_decode_bf16_full_size():
+    full_check(W.decode_bf16(), "decode")
+
+
+def test_decode_bf16_short_contexts():
+    """Decode rows shorter than K (all positions taken, -1 padded) next to long ones."""
+    spec = W.decode_bf16(B=8, lo=100, hi=5000).replace(K=1024, seed=31)
+    full_check(spec, "decode-short")
+
+
+# -------------------------------------------------------- MLA + fp8 indexer
+
+def test_chunked_prefill_mla_reduced():
+    spec = W.chunked_prefill_mla(cached=3000, T=333)
+    full_check(spec, "mla-prefill-reduced", attn_rows=P.sample_tokens(333, 48, seed=4))
+
+
+def test_chunked_prefill_mla_full_size_sampled():
+    spec = W.chunked_prefill_mla()
+    P.say(f"[mla-prefill-full] T={spec.T} ctx={spec.max_ctx}")
+    wl = W.generate(spec, DEV)
+    pl = run(wl, canary=False)
+    seq, pos, n = P.token_geometry(spec)
+    idx = pl.indices.cpu().numpy()
+    P.check_idx_invariants(idx, n, spec.K)
+    rows = P.sample_tokens(spec.T, 96, seed=5, edge=16)
+    sc_rows = pl.scores[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    P.check_topk_exact(idx[rows], sc_rows, n[rows], spec.K)
+    srows = P.sample_tokens(spec.T, 6, seed=6, edge=1)
+    inp = P.indexer_inputs(wl, srows)
+    ref = O.indexer(inp, ld=pl.ld)
+    sc = pl.scores[torch.as_tensor(srows, device=DEV)].cpu().numpy()
+    P.check_scores(sc, ref, n[srows], P.RTOL["fp8"])
+    rec = P.check_selection(idx[srows], ref, n[srows], spec.K)
+    arows = P.sample_tokens(spec.T, 8, seed=7, edge=1)
+    ainp, aidx = P.attn_inputs(wl, arows, idx[arows])
+    ref_out = O.sparse_attn(ainp, aidx, None, spec.softmax_scale)
+    P.check_attn(pl.out.float().cpu().numpy()[arows], ref_out, P.RTOL["bf16"])
+    P.say(f"[mla-prefill-full] recall {rec:.4f}")
+
+
+def test_long_decode_mla_reduced_with_ties():
+    spec = W.long_decode_mla(lo=5000, hi=40000)
+    full_check(spec, "long-decode-reduced")
+
+
+def test_ties_straddling_the_boundary():
+    """Copies of the oracle's K-th ranked key row planted at 4 positions below and 4 above
+    it: exact score ties across the selection boundary; lowest positions must win."""
+    spec = W.long_decode_mla(B=4, lo=6000, hi=9000, short_at=1).replace(dup_frac=0.0, seed=41)
+    wl = W.generate(spec, DEV)
+    seq, pos, n = P.token_geometry(spec)
+    inp = O.Inputs.from_workload(wl)
+    ref = O.indexer(inp)
+    kflat = wl.k_idx.view(-1, spec.d_I).view(torch.uint8)
+    ksf = wl.k_scale.view(-1)
+    for t in range(spec.T):
+        if n[t] <= spec.K + 8:
+            continue
+        order = np.lexsort((np.arange(n[t]), -ref[t, :n[t]]))
+        s_k = int(order[spec.K - 1])
+        rows = P.logical_rows(wl, int(seq[t]), int(n[t]))
+        for d in (-4, -3, -2, -1, 1, 2, 3, 4):
+            s2 = min(max(s_k + d, 0), int(n[t]) - 1)
+            kflat[rows[s2]] = kflat[rows[s_k]]
+            ksf[rows[s2]] = ksf[rows[s_k]]
+    pl = run(wl)
+    inp = O.Inputs.from_workload(wl)
+    ref = O.indexer(inp, ld=pl.ld)
+    sc = pl.scores.cpu().numpy()
+    idx = pl.indices.cpu().numpy()
+    P.check_scores(sc, ref, n, P.RTOL["fp8"])
+    P.check_topk_exact(idx, sc, n, spec.K)
+    P.check_selection(idx, ref, n, spec.K)
+
+
+def test_long_decode_mla_full_size_sampled():
+    spec = W.long_decode_mla()
+    P.say(f"[long-decode-full] B={spec.B} max_ctx={spec.max_ctx}")
+    wl = W.generate(spec, DEV)
+    pl = run(wl, canary=False)
+    seq, pos, n = P.token_geometry(spec)
+    idx = pl.indices.cpu().numpy()
+    sc = pl.scores.cpu().numpy()
+    P.check_idx_invariants(idx, n, spec.K)
+    P.check_topk_exact(idx, sc, n, spec.K)
+    short = int(np.argmin(n))
+    longs = [int(t) for t in np.argsort(n) if n[t] > spec.K]
+    srows = sorted({short, longs[0]})
+    inp = P.indexer_inputs(wl, srows)
+    ref = O.indexer(inp, ld=pl.ld)
+    P.check_scores(sc[srows], ref, n[srows], P.RTOL["fp8"])
+    P.check_selection(idx[srows], ref, n[srows], spec.K)
+    arows = list(range(spec.T))
+    ainp, aidx = P.attn_inputs(wl, arows, idx)
+    ref_out = O.sparse_attn(ainp, aidx, None, spec.softmax_scale)
+    P.check_attn(pl.out.float().cpu().numpy(), ref_out, P.RTOL["bf16"])
+
+
+# --------------------------------------------------------------- properties
+
+def test_runs_are_bitwise_deterministic():
+    spec = W.decode_bf16(B=16).replace(seed=51)
+    wl = W.generate(spec, DEV)
+    a = run(wl)
+    b = run(wl)
+    assert torch.equal(a.indices, b.indices)
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    n = P.token_geometry(spec)[2]
+    sa, sb = a.scores.cpu().numpy(), b.scores.cpu().numpy()
+    for r in range(spec.T):
+        assert np.array_equal(sa[r, :n[r]], sb[r, :n[r]])
