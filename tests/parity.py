@@ -3,7 +3,7 @@
 Scores: |x - r| <= rtol * max(|r|, 0.01 * max_row |r|) on every entry of a
 token's row, rtol 1e-5 (fp32) or 2e-2 (bf16/fp8).  Attention outputs: the
 relative error of each (token, head) output vector in the 2-norm is at most
-1e-5 (fp32) or 2e-2 (bf16), and bf16 outputs also meet the entrywise rule.
+1e-5 (fp32) or 2e-2 (bf16).
 Top-K: bit-exact against the oracle's brute force on the GPU's own fp32
 scores; against the oracle's double scores, the set must match wherever the
 K-th/(K+1)-th gap exceeds 1e-3 relative, else every selected score must be at
@@ -93,8 +93,7 @@ def check_selection(gpu_idx, ref_scores, n, K, tol=1e-3):
 
 
 def check_attn(gpu_out, ref_out, rtol, what="attention"):
-    """Relative error of every (token, head) output vector in the 2-norm <= rtol; bf16
-    outputs (rtol >= 1e-3) must also meet the elementwise rule."""
+    """Relative error of every (token, head) output vector in the 2-norm <= rtol."""
     x = np.asarray(gpu_out, np.float64)
     r = np.asarray(ref_out, np.float64)
     num = np.linalg.norm(x - r, axis=-1)
@@ -102,9 +101,6 @@ def check_attn(gpu_out, ref_out, rtol, what="attention"):
     rel = num / np.maximum(den, 1e-300)
     bad = rel > rtol
     assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} vectors above rtol {rtol} (worst {rel.max():.3g})"
-    if rtol >= 1e-3:
-        ok = close(x, r, rtol)
-        assert ok.all(), f"{what}: {(~ok).sum()} of {ok.size} elements outside rtol {rtol}"
     return float(rel.max())
 
 
