@@ -9,6 +9,8 @@
  * Pages cited (by title):
  *   [HAT] "Hybrid Attention Architectures: Engineering Trade-offs from Linear
  *          Attention to Gated Sparse Attention"
+ *   [EVO] "Evolution of Hybrid Attention in Open-Source LLMs: From Linear to
+ *          Gated Sparse Attention"
  *   [F2S] "From Full Attention to Sparsity: The Evolution of Hybrid Attention
  *          Architectures in Large Language Models"
  *   [SAD] "Sparse Attention and Hybrid Attention Architecture Design in Large
@@ -112,8 +114,7 @@ sa_status sparse_indexer_scores(const sa_batch *batch, sa_dtype dtype,
  * a2 — per-token Top-K.  [HAT §3.1]: keep the K highest-scoring positions;
  * [F2S "Fine-Grained Sparse Attention: Indexer Plus Top-K"]: indices of
  * shape [n, K]; [HAT §5 item 4]: fewer candidates than K are padded.
- * [EVO: "Evolution of Hybrid Attention in Open-Source LLMs..." §5 item 3]
- * warns against approximate Top-K: this one is exact.
+ * [EVO] §5 item 3 warns against approximate Top-K: this one is exact.
  *
  * Row i (token i) selects from scores[i, 0..n_i): if n_i <= k all n_i
  * positions, else the k positions with the largest scores, ties broken
@@ -155,8 +156,9 @@ sa_status sparse_topk(const sa_batch *batch, const float *scores, int64_t ld_sco
  *   out          [T, n_q_heads, d_v] in dtype (bf16 rounded to nearest even)
  *   lse          [T, n_q_heads] fp32, or NULL
  * Supported: SA_F32 with d_qk = d_v in {32, 64, 128}; SA_BF16 with
- * (d_qk, d_v) in {(128, 128), (576, 512)}; n_q_heads a multiple of 16 (bf16)
- * or any (f32); 1 <= k <= 65536.
+ * (d_qk, d_v) = (128, 128), separate or shared caches, or (576, 512) with
+ * v_cache == k_cache (latent layout); n_q_heads a multiple of 16 (bf16) or
+ * any (f32); 1 <= k <= 65536.
  */
 size_t sparse_gated_attn_workspace_size(const sa_batch *batch, int32_t n_q_heads, int32_t d_v, int32_t k);
 sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype,

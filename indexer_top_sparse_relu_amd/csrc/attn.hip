@@ -17,25 +17,48 @@
 //          hold K and V) and §4 "Output gating" (per-channel or per-head).
 //
 // bf16 kernel.  A workgroup owns one token, a group of 16*NW query heads (16
-// per wave) and a contiguous range of that token's index list.  Per 32-key
-// tile it gathers the selected K rows through the page table into LDS
-// (row-major) and V rows into LDS transposed (dim-major, keys in pairs per
-// dword), then on 16x16x32 bf16 MFMA computes S^T = K Q^T (keys x heads, so a
-// lane owns one head's column and the softmax is mostly in-lane), the online
-// softmax in fp32, and O^T += V^T P^T.  The K-tile operand order inside a lane
-// (keys 4g..4g+3 of the first 16, then of the second 16) is matched by the V^T
-// operand, so P feeds the second MFMA straight from registers.  The epilogue
-// divides by the softmax sum, multiplies by sigmoid(gate) and rounds to bf16;
-// with a split index list it writes (O, max, sum) partials that a combine
-// kernel merges by log-sum-exp.
+// per wave) and a contiguous range of that token's index list.  At start it
+// resolves every slot of its range to a physical cache row (page table) in
+// LDS.  The selected rows are then gathered 64 at a time straight from global
+// memory into LDS (global_load_lds, no registers), double-buffered so the next
+// tile's gather runs under the current tile's math.  The tile is stored in
+// blocks of 8 rows x 8 sixteen-byte chunks (1 KB, exactly one wave-wide load),
+// with the chunks of each row XOR-swizzled by the row index, which spreads both
+// operand reads over the LDS banks.  Per 32-key half tile, on 16x16x32 bf16
+// MFMA: S^T = K Q^T (keys x heads: a lane owns one head's column, so the
+// softmax is mostly in-lane), the online softmax in fp32, and O^T += V^T P^T
+// with the V^T operand read by the LDS transpose load (ds_read_b64_tr_b16)
+// directly from the row-major tile, so no transposed copy of V is made (for
+// the latent layout V is the first d_v elements of the same rows).  The key
+// order inside a lane's P registers (keys 4g..4g+3, then 16+4g..16+4g+3) is
+// the order the transpose load delivers V in.  The epilogue divides by the
+// softmax sum, multiplies by sigmoid(gate) and rounds to bf16; with a split
+// index list it writes (O, max, sum) partials that a combine kernel merges by
+// log-sum-exp.
 #include "sa_device.h"
 #include "launch.h"
 
 namespace sa {
 
-constexpr int kTK = 32;                 // keys per tile
+constexpr int kTK = 64;                 // keys per LDS tile
+constexpr int kMaxSplit = 2048;         // index slots one workgroup resolves up front
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+
+// Swizzle of tile row r: logical chunk c of the row sits at chunk position
+// (c & ~7) | ((c & 7) ^ f(r)) of its 8-chunk block, f(r) = (r & 6) | (r >> 3 & 1).
+// LDS serves 128-bit reads 16 lanes at a time and 64-bit (transpose) reads 32
+// lanes at a time over 64 four-byte banks; a row's 16-byte chunk at position p
+// falls in bank group ((r & 1) * 8 + p) mod 16.  K-operand reads (16 rows, one
+// logical chunk) then see a bijection of (r >> 1) & 7 per row parity, and the
+// transpose reads (8 rows, one chunk pair each) see distinct pairs per parity:
+// both are conflict-free.
+__device__ __forceinline__ int swzf(int r) { return (r & 6) | ((r >> 3) & 1); }
 
 template <int DQK, int DV, bool MLA, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
@@ -47,14 +70,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     constexpr int NT = NW * 64;
     constexpr int NKQ = DQK / 32;           // MFMA steps over d_qk
     constexpr int NMO = DV / 16;            // 16-dim tiles of O
-    constexpr int KROW = DQK + 8;           // padded K row in LDS (bf16)
-    constexpr int VROW = kTK + 4;           // padded V^T row in LDS (bf16)
     constexpr int KCH = DQK / 8;            // 16-byte chunks per K row
     constexpr int VCH = DV / 8;             // 16-byte chunks per V row
-    static_assert(DQK % 32 == 0 && DV % 16 == 0, "dims");
-    __shared__ __align__(16) uint16_t lk[kTK * KROW];
-    __shared__ __align__(16) uint16_t lv[DV * VROW];
-    __shared__ int64_t lrow[kTK];           // physical rows of the tile (-1: empty slot)
+    constexpr int KCHUNKS = kTK * KCH, VCHUNKS = MLA ? 0 : kTK * VCH;
+    constexpr int KCB = KCH / 8, VCB = VCH / 8;     // 8-chunk blocks per row
+    constexpr int VROWB = MLA ? KCB : VCB;          // blocks per row of the buffer V is read from
+    static_assert(DQK % 64 == 0 && DV % 16 == 0 && KCH % 8 == 0 && VCH % 8 == 0, "dims");
+    static_assert(kTK % (8 * NW) == 0, "whole 8-row groups per wave");
+    __shared__ __align__(16) uint8_t lk0[KCHUNKS * 16];
+    __shared__ __align__(16) uint8_t lk1[KCHUNKS * 16];
+    __shared__ __align__(16) uint8_t lv0[(MLA ? 16 : VCHUNKS * 16)];
+    __shared__ __align__(16) uint8_t lv1[(MLA ? 16 : VCHUNKS * 16)];
+    __shared__ int32_t prow[kMaxSplit];     // physical row of each slot; -1 - row0 when empty
 
     const int tok = blockIdx.x;
     const int hg = blockIdx.y;               // head group
@@ -65,7 +92,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     const int b = seq_of_token(bt, tok);
     const int j0 = sp * split_len;
     const int j1 = min(K, j0 + split_len);
-    const int32_t *irow = idx + (int64_t)tok * K;
+    const int nslots = max(0, j1 - j0);
+    const int32_t *irow = idx + (int64_t)tok * K + j0;
+
+    // ---- resolve slots to physical rows; empty slots point at position 0 (a real row)
+    {
+        const int row0 = (int)phys_row(bt, b, 0);
+        for (int j = tid; j < nslots; j += NT) {
+            const int s = irow[j];
+            prow[j] = s >= 0 ? (int)phys_row(bt, b, s) : -1 - row0;
+        }
+    }
 
     // Q^T operand: head h, dims 32*ks + 8*g .. +7
     bf16x8 qop[NKQ];
@@ -80,111 +117,154 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     for (int mt = 0; mt < NMO; ++mt)
         o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
+    __syncthreads();
 
-    // gather tasks: (key pair, 16-byte chunk); K chunks first, then separate V chunks
-    constexpr int KT = (kTK / 2) * KCH;
-    constexpr int VT = MLA ? 0 : (kTK / 2) * VCH;
-    constexpr int TASKS = (KT + VT + NT - 1) / NT;
-
-    for (int t0 = j0; t0 < j1; t0 += kTK) {
-        if (tid < kTK) {
-            const int j = t0 + tid;
-            const int s = j < j1 ? irow[j] : -1;
-            lrow[tid] = s >= 0 ? phys_row(bt, b, s) : -1;
+    const int ntiles = (nslots + kTK - 1) / kTK;
+    // Direct loads of one tile: block (rg, cb) holds rows 8rg..8rg+7, logical chunks
+    // 8cb..8cb+7; lane i of the wave that loads it fetches row 8rg + i/8, chunk
+    // position i%8 (logical chunk (i%8) ^ f(row)).  Wave wv owns row groups wv,
+    // wv+NW, ... so it resolves one physical row per group.
+    constexpr int RG = kTK / 8;
+    auto issue = [&](int t, lds_u8 *dk, lds_u8 *dv) {
+#pragma unroll
+        for (int rg = wv; rg < RG; rg += NW) {
+            const int r = 8 * rg + (lane >> 3);
+            const int slot = t * kTK + r;
+            int pr = prow[slot < nslots ? slot : 0];
+            pr = pr >= 0 ? pr : -1 - pr;
+            const int cpos = (lane & 7) ^ swzf(r);
+            const uint16_t *ksrc = kc + (int64_t)pr * rs + cpos * 8;
+#pragma unroll
+            for (int cb = 0; cb < KCB; ++cb)
+                __builtin_amdgcn_global_load_lds(ksrc + cb * 64, (lds_void *)(dk + (rg * KCB + cb) * 1024), 16, 0, 0);
+            if (!MLA) {
+                const uint16_t *vsrc = vc + (int64_t)pr * rs + cpos * 8;
+#pragma unroll
+                for (int cb = 0; cb < VCB; ++cb)
+                    __builtin_amdgcn_global_load_lds(vsrc + cb * 64, (lds_void *)(dv + (rg * VCB + cb) * 1024), 16, 0, 0);
+            }
         }
+    };
+    lds_u8 *const LK0 = (lds_u8 *)lk0, *const LK1 = (lds_u8 *)lk1;
+    lds_u8 *const LV0 = (lds_u8 *)lv0, *const LV1 = (lds_u8 *)lv1;
+    if (ntiles > 0)
+        issue(0, LK0, LV0);
+
+    for (int t = 0; t < ntiles; ++t) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        // ---- gather the tile into LDS
+        const bool odd = t & 1;
+        // which of the tile's 64 slots hold a selected position (one bit per slot)
+        const int myslot = t * kTK + lane;
+        const uint64_t vmask = __ballot(myslot < nslots && prow[myslot < nslots ? myslot : 0] >= 0);
+        lds_u8 *tk = odd ? LK1 : LK0;
+        lds_u8 *tv = MLA ? tk : (odd ? LV1 : LV0);
+        if (t + 1 < ntiles) {
+            if (odd)
+                issue(t + 1, LK0, LV0);
+            else
+                issue(t + 1, LK1, LV1);
+        }
+#pragma unroll 1
+        for (int kh = 0; kh < 2; ++kh) {
+            const int rb = 32 * kh;                       // first row of this half tile
+            // ---- S^T = K Q^T for keys rb..rb+15 and rb+16..rb+31.  Logical chunk
+            // 4ks+g of row r: block ks/2, position 4(ks&1)+g xor f(r).  Operands
+            // stream through a ring of QD steps so each MFMA waits only for its own.
+            f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
+            {
+                constexpr int QD = 2;
+                const int r0 = rb + n, r1 = rb + 16 + n;
+                lds_u8 *k0 = tk + (r0 >> 3) * KCB * 1024 + (r0 & 7) * 128;
+                lds_u8 *k1 = tk + (r1 >> 3) * KCB * 1024 + (r1 & 7) * 128;
+                lds_u8 *k0e = k0 + 16 * (g ^ swzf(r0)), *k0o = k0 + 16 * ((4 + g) ^ swzf(r0));
+                lds_u8 *k1e = k1 + 16 * (g ^ swzf(r1)), *k1o = k1 + 16 * ((4 + g) ^ swzf(r1));
+                auto lda = [&](lds_u8 *e, lds_u8 *o_, int ks) {
+                    return *(lds_bf16x8 *)(((ks & 1) ? o_ : e) + 1024 * (ks >> 1));
+                };
+                bf16x8 ra[QD], rb_[QD];
 #pragma unroll
-        for (int u = 0; u < TASKS; ++u) {
-            const int e = tid + u * NT;
-            if (e < KT + VT) {
-                const bool isk = e < KT;
-                const int e2 = isk ? e : e - KT;
-                const int nch = isk ? KCH : VCH;
-                const int kp = e2 / nch, ch = e2 % nch;
-                const int64_t r0 = lrow[2 * kp], r1 = lrow[2 * kp + 1];
-                const uint16_t *base = isk ? kc : vc;
-                i32x4 x0 = i32x4{0, 0, 0, 0}, x1 = i32x4{0, 0, 0, 0};
-                if (r0 >= 0)
-                    x0 = *(const i32x4 *)(base + r0 * rs + ch * 8);
-                if (r1 >= 0)
-                    x1 = *(const i32x4 *)(base + r1 * rs + ch * 8);
-                if (isk) {
-                    *(i32x4 *)(&lk[(2 * kp) * KROW + ch * 8]) = x0;
-                    *(i32x4 *)(&lk[(2 * kp + 1) * KROW + ch * 8]) = x1;
+                for (int d = 0; d < QD; ++d) {
+                    ra[d] = lda(k0e, k0o, d);
+                    rb_[d] = lda(k1e, k1o, d);
                 }
-                if ((MLA && isk && ch < VCH) || !isk) {
-                    // V^T: dword (V[2kp][d], V[2kp+1][d]) at lv[d][2kp]
 #pragma unroll
-                    for (int q2 = 0; q2 < 4; ++q2) {
-                        const uint32_t a = (uint32_t)x0[q2], c = (uint32_t)x1[q2];
-                        const int d = ch * 8 + 2 * q2;
-                        *(uint32_t *)(&lv[d * VROW + 2 * kp]) = (a & 0xFFFFu) | (c << 16);
-                        *(uint32_t *)(&lv[(d + 1) * VROW + 2 * kp]) = (a >> 16) | (c & 0xFFFF0000u);
+                for (int ks = 0; ks < NKQ; ++ks) {
+                    s0 = mma16_bf16(ra[ks % QD], qop[ks], s0);
+                    s1 = mma16_bf16(rb_[ks % QD], qop[ks], s1);
+                    if (ks + QD < NKQ) {
+                        ra[ks % QD] = lda(k0e, k0o, ks + QD);
+                        rb_[ks % QD] = lda(k1e, k1o, ks + QD);
                     }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
             }
-        }
-        __syncthreads();
-
-        // ---- S^T = K Q^T for keys 0-15 and 16-31 of the tile
-        f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-        {
-            const uint16_t *k0 = &lk[n * KROW + 8 * g];
-            const uint16_t *k1 = &lk[(16 + n) * KROW + 8 * g];
+            // ---- V^T operand ring: the transpose load gives lane (dim i, group g) the
+            // dims of keys rb+4g..+3 (first load) and rb+16+4g..+3 (second load).
+            // Logical chunk 2mt+hh of row r: block mt/4, position (2(mt&3)+hh) xor f(r).
+            constexpr int PD = 3;
+            const int jj = lane & 15;
+            const int ra_ = rb + 4 * g + (jj >> 2), rc_ = ra_ + 16;
+            const int cc = jj & 3, hh = cc >> 1;
+            const int fa = swzf(ra_), fc = swzf(rc_);
+            lds_u8 *va = tv + (ra_ >> 3) * VROWB * 1024 + (ra_ & 7) * 128 + (cc & 1) * 8;
+            lds_u8 *vc2 = tv + (rc_ >> 3) * VROWB * 1024 + (rc_ & 7) * 128 + (cc & 1) * 8;
+            auto ldv = [&](lds_u8 *v, int f, int mt) {
+                return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4 *)(v + 1024 * (mt >> 2) + 16 * ((2 * (mt & 3) + hh) ^ f)));
+            };
+            bf16x4 la[PD], lc[PD];
 #pragma unroll
-            for (int ks = 0; ks < NKQ; ++ks) {
-                s0 = mma16_bf16(*(const bf16x8 *)(k0 + 32 * ks), qop[ks], s0);
-                s1 = mma16_bf16(*(const bf16x8 *)(k1 + 32 * ks), qop[ks], s1);
+            for (int d = 0; d < PD; ++d) {
+                la[d] = ldv(va, fa, d);
+                lc[d] = ldv(vc2, fc, d);
             }
-        }
-        // lane holds keys 4g+i (s0) and 16+4g+i (s1) of head h
-        float z[8];
+            // ---- online softmax (log2 domain).  The running max is raised lazily:
+            // only when some head of the wave grows by more than 2^8 are O and the
+            // sum rescaled; otherwise probabilities use the stale max (<= 2^8).
+            float z[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            z[i] = lrow[4 * g + i] >= 0 ? s0[i] * scale_log2 : -INFINITY;
-            z[4 + i] = lrow[16 + 4 * g + i] >= 0 ? s1[i] * scale_log2 : -INFINITY;
-        }
-        float mt_ = z[0];
+            for (int i = 0; i < 4; ++i) {
+                z[i] = ((vmask >> (rb + 4 * g + i)) & 1) ? s0[i] * scale_log2 : -INFINITY;
+                z[4 + i] = ((vmask >> (rb + 16 + 4 * g + i)) & 1) ? s1[i] * scale_log2 : -INFINITY;
+            }
+            float mt_ = fmaxf(fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])), fmaxf(fmaxf(z[4], z[5]), fmaxf(z[6], z[7])));
+            mt_ = fmaxf(mt_, shfl_xor(mt_, 16));
+            mt_ = fmaxf(mt_, shfl_xor(mt_, 32));
+            if (__any(mt_ > m_run + 8.0f)) {
+                const float m_new = fmaxf(m_run, mt_);
+                const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
 #pragma unroll
-        for (int i = 1; i < 8; ++i)
-            mt_ = fmaxf(mt_, z[i]);
-        mt_ = fmaxf(mt_, shfl_xor(mt_, 16));
-        mt_ = fmaxf(mt_, shfl_xor(mt_, 32));
-        const float m_new = fmaxf(m_run, mt_);
-        const float base = m_new == -INFINITY ? 0.0f : m_new;
-        const float alpha = exp2f(m_run - base);          // 0 when m_run = -inf
-        float p[8], psum = 0.0f;
+                for (int mt = 0; mt < NMO; ++mt)
+                    o[mt] *= alpha;
+                m_run = m_new;
+            }
+            const float base = m_run == -INFINITY ? 0.0f : m_run;
+            bf16x8 pop;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            p[i] = exp2f(z[i] - base);
-            psum += p[i];
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        bf16x8 pop;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            pop[i] = (__bf16)p[i];
-        // ---- O^T = alpha O^T + V^T P^T
-        {
-            const uint16_t *vp = &lv[n * VROW + 4 * g];
+            for (int i = 0; i < 8; ++i) {
+                const float pi = __builtin_amdgcn_exp2f(z[i] - base);
+                l_run += pi;
+                pop[i] = (__bf16)pi;
+            }
+            // ---- O^T += V^T P^T
 #pragma unroll
             for (int mt = 0; mt < NMO; ++mt) {
-                const uint16_t *vr = vp + (16 * mt) * VROW;
-                const bf16x4 lo4 = *(const bf16x4 *)(vr);
-                const bf16x4 hi4 = *(const bf16x4 *)(vr + 16);
                 bf16x8 vop;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    vop[i] = lo4[i];
-                    vop[4 + i] = hi4[i];
+                    vop[i] = la[mt % PD][i];
+                    vop[4 + i] = lc[mt % PD][i];
                 }
-                o[mt] *= alpha;
                 o[mt] = mma16_bf16(vop, pop, o[mt]);
+                if (mt + PD < NMO) {
+                    la[mt % PD] = ldv(va, fa, mt + PD);
+                    lc[mt % PD] = ldv(vc2, fc, mt + PD);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        __syncthreads();
     }
 
     // ---- epilogue
@@ -205,7 +285,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t gw = i < 2 ? gv.x : gv.y;
-                const float gi = per_channel ? sigmoidf_(bf16_bits_to_f32((uint16_t)(gw >> (16 * (i & 1))))) : gh;
+                const float gl = bf16_bits_to_f32((uint16_t)(gw >> (16 * (i & 1))));
+                const float gi = per_channel ? __builtin_amdgcn_rcpf(1.0f + __expf(-gl)) : gh;
                 r[i] = f32_to_bf16_bits(o[mt][i] * inv * gi);
             }
             *(uint2 *)(op + 16 * mt) = uint2{(uint32_t)r[0] | ((uint32_t)r[1] << 16),
@@ -366,19 +447,30 @@ int attn_supported(int dtype, int Hq, int d_qk, int d_v)
     return 0;
 }
 
+int attn_supported_layout(int dtype, int d_qk, int d_v, int aliased)
+{
+    // two double-buffered 576-wide tiles do not fit the 160 KB LDS: latent layout only
+    if (dtype == 1 && d_qk == 576 && d_v == 512)
+        return aliased;
+    return 1;
+    return 0;
+}
+
 AttnPlan attn_plan(int total_q, int Hq, int d_v, int k)
 {
     AttnPlan p{1, 0};
     const int groups = Hq % 16 == 0 ? (Hq / 16) / bf16_waves(Hq) : Hq;
     const int64_t wgs = (int64_t)total_q * groups;
+    int ns = 1;
     if (wgs < 512) {
-        int ns = (int)((512 + wgs - 1) / wgs);
+        ns = (int)((512 + wgs - 1) / wgs);
         ns = min(ns, max(1, k / 128));
         ns = min(ns, 16);
-        if (ns > 1) {
-            p.n_split = ns;
-            p.ws_bytes = (size_t)total_q * ns * Hq * (d_v + 4) * sizeof(float);
-        }
+    }
+    ns = max(ns, (k + kMaxSplit - 1) / kMaxSplit);     // a workgroup resolves at most kMaxSplit slots
+    if (ns > 1) {
+        p.n_split = ns;
+        p.ws_bytes = (size_t)total_q * ns * Hq * (d_v + 4) * sizeof(float);
     }
     return p;
 }
@@ -426,9 +518,6 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const voi
         else if (d_qk == 576 && d_v == 512 && mla)
             e = launch_bf16<576, 512, true>(bt, pl, q, Hq, k_cache, v_cache, row_stride, indices, k, gate,
                                             per_channel, sl2, out, lse, part, split_len, st);
-        else if (d_qk == 576 && d_v == 512)
-            e = launch_bf16<576, 512, false>(bt, pl, q, Hq, k_cache, v_cache, row_stride, indices, k, gate,
-                                             per_channel, sl2, out, lse, part, split_len, st);
     } else if (dtype == 0) {
         const dim3 grid(bt.total_q, Hq, pl.n_split);
 #define SA_LAUNCH_F32(D)                                                                                         \

@@ -140,7 +140,8 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const voi
         return SA_EINVAL;
     if (k_cache == v_cache && d_v > d_qk)
         return SA_EINVAL;
-    if (!sa::attn_supported((int)dtype, n_q_heads, d_qk, d_v))
+    if (!sa::attn_supported((int)dtype, n_q_heads, d_qk, d_v) ||
+        !sa::attn_supported_layout((int)dtype, d_qk, d_v, k_cache == v_cache))
         return SA_EUNSUPPORTED;
     const sa::AttnPlan plan = sa::attn_plan(bt.total_q, n_q_heads, d_v, k);
     if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))

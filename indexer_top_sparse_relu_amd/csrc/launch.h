@@ -33,6 +33,7 @@ struct AttnPlan {
 };
 AttnPlan attn_plan(int total_q, int Hq, int d_v, int k);
 int attn_supported(int dtype, int Hq, int d_qk, int d_v);
+int attn_supported_layout(int dtype, int d_qk, int d_v, int aliased);
 hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &plan, const void *q, int Hq, int d_qk,
                        const void *k_cache, const void *v_cache, int d_v, int64_t row_stride,
                        const int32_t *indices, int k, const void *gate, int per_channel, float scale,
