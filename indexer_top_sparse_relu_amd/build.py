@@ -17,6 +17,11 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
 SOURCES = ["capi.hip", "indexer.hip", "topk.hip", "attn.hip"]
+# per-source code generation options: the indexer keeps MFMA accumulators in
+# arch VGPRs, where its VALU epilogue reads them without v_accvgpr_read copies,
+# and assumes finite values (scores are defined for finite inputs), so max(x, 0)
+# needs no NaN-quieting instruction in front of it
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -26,11 +31,12 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-u
 
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
-    warn = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l and l.strip())
+    warn = "\n".join(l for l in r.stderr.splitlines()
+                     if "packed-fp32-ops" not in l and "--hip-link" not in l and l.strip())
     if warn:
         sys.stderr.write(warn + "\n")
     return obj

@@ -15,7 +15,12 @@
 // pairs and whose columns are key positions.  A lane of a 32x32 output holds
 // 16 rows of one column, so the head reduction is mostly in-lane: ReLU and the
 // w-FMA per element, then one cross-half add.  Positive scales factor out of
-// the ReLU, so fp8 scales are applied once per (token, key).
+// the ReLU, so fp8 scales are applied once per (token, key).  The fp8 path runs
+// the epilogue on packed fp16 pairs (convert, ReLU, dot2 with fp32
+// accumulation: 1.5 VALU instructions per element instead of 2): the MFMA's
+// own block scales shrink every dot by 2^-10 so it always fits fp16, and the
+// factor is given back once per score.  Each term then carries a relative
+// rounding of at most 2^-10 (dot) and 2^-11 (weight) before the fp32 sum.
 //
 // Two kernels:
 //   indexer_tile_kernel — prefill: a workgroup owns TQ tokens of one sequence
@@ -49,7 +54,13 @@ template <> struct IdxT<2> {
     static constexpr int ELEM = 1, KS = 64, LB = 32;
     typedef i32x8 Op;
     static __device__ __forceinline__ Op load(const uint8_t *p) { return *(const i32x8 *)p; }
-    static __device__ __forceinline__ f32x16 mma(Op a, Op b, f32x16 c) { return mma32_fp8(a, b, c); }
+    static __device__ __forceinline__ f32x16 mma(Op a, Op b, f32x16 c) { return mma32_fp8_s10(a, b, c); }
+};
+// fp8 MFMAs return dots scaled by 2^-10 (UNSCALE gives it back per score);
+// with at least 8 heads the fp8 epilogue runs on packed fp16 pairs.
+template <int DT> struct IdxEpi {
+    static constexpr bool F16 = DT == 2;
+    static constexpr float UNSCALE = DT == 2 ? 1024.0f : 1.0f;
 };
 
 // Rows per wave = 32*MT; tokens per wave = 32*MT/H.
@@ -63,7 +74,7 @@ constexpr int kIdxTileKeys = 64;
 
 // ------------------------------------------------------------------ prefill
 template <int DT, int H, int D>
-__global__ __launch_bounds__(256) void indexer_tile_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void indexer_tile_kernel(
     Batch bt, const uint8_t *__restrict__ q_idx, const float *__restrict__ q_scale,
     const float *__restrict__ w, const uint8_t *__restrict__ k_idx, const float *__restrict__ k_scale,
     float *__restrict__ scores, int64_t ld, int key_chunk, int n_chunks, int n_tiles_max)
@@ -78,6 +89,11 @@ __global__ __launch_bounds__(256) void indexer_tile_kernel(
     static_assert(RB % 32 == 0, "row bytes");
     __shared__ __align__(16) uint8_t lds_k[2][kIdxTileKeys * RBP];
     __shared__ float lds_ks[2][kIdxTileKeys];
+    // fp8 with >= 16 heads: the linear part of the ReLU runs on the MFMA (see below)
+    constexpr bool LIN = (DT == 2) && (H >= 16) && (MT % 2 == 0) && (D == 128);
+    constexpr int LTS = 128 + 16;                // padded term row (bank spread, as RBP)
+    __shared__ __align__(16) uint8_t lterm[LIN ? kIdxWaves * 32 * LTS : 16];
+    __shared__ int lscl[LIN ? kIdxWaves * 32 : 1];
 
     // ---- workgroup -> (token tile, key chunk): chunk c always runs on XCD c % 8
     const int bid = blockIdx.x;
@@ -113,8 +129,10 @@ __global__ __launch_bounds__(256) void indexer_tile_kernel(
     const int half = lane >> 5, col = lane & 31;
 
     // ---- A operands (this wave's tokens x heads) and weights, kept in registers
+    constexpr bool F16E = IdxEpi<DT>::F16 && H >= 8 && !LIN;
     typename X::Op a[MT][NKS];
-    float wr[MT][16];
+    float wr[MT][F16E ? 1 : 16];
+    f16x2 wp[MT][F16E ? 8 : 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int R = mt * 32 + col;              // operand row of this lane
@@ -130,14 +148,22 @@ __global__ __launch_bounds__(256) void indexer_tile_kernel(
         for (int i = 0; i < 16; ++i) {
             const int Ro = mt * 32 + mfma32_row(i, lane);
             const int to = wv * TPW + Ro / H;
-            wr[mt][i] = to < ntok ? w[(int64_t)(tok0 + to) * H + Ro % H] : 0.0f;
+            const float wv_ = to < ntok ? w[(int64_t)(tok0 + to) * H + Ro % H] : 0.0f;
+            if constexpr (F16E) {
+                if (i & 1)
+                    wp[mt][i >> 1][1] = (_Float16)wv_;
+                else
+                    wp[mt][i >> 1][0] = (_Float16)wv_;
+            } else {
+                wr[mt][i] = wv_;
+            }
         }
     }
     float qs[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int tl = wv * TPW + t;
-        qs[t] = (FP8 && tl < ntok) ? q_scale[tok0 + tl] : 1.0f;
+        qs[t] = ((FP8 && tl < ntok) ? q_scale[tok0 + tl] : 1.0f) * IdxEpi<DT>::UNSCALE;
     }
 
     // ---- key tile staging: thread -> (key, 32-byte part)
@@ -184,6 +210,233 @@ __global__ __launch_bounds__(256) void indexer_tile_kernel(
     gload(kb0);
     lstore(0);
     __syncthreads();
+
+    if constexpr (LIN) {
+        // w * ReLU(x) = (w x + w |x|) / 2.  The w |x| sum is one FMA per element
+        // (|x| is a free source modifier); the linear sum over heads,
+        // sum_h w_h (q_h . k) = (sum_h w_h q_h) . k, runs on the MFMA as extra A
+        // rows: the weighted query qbar is split into 8 fp8 terms, term t scaled
+        // by 2^e_t, and each row's 2^e_t is applied by the MFMA's per-row block
+        // scale.  Eight terms carry qbar to full fp32 precision.
+        // Row layout of the 32-row term tile: token tt's term t sits at row
+        // 8*(2*(tt/2) + t/4) + 4*(tt%2) + t%4, so in the 32x32 output the terms of
+        // token tt land in the lanes of half tt%2 (registers 0-7 for tt < 2,
+        // 8-15 for tt >= 2): the lanes that write that token's scores.
+        uint8_t *myterm = lterm + wv * 32 * LTS;
+        int *myscl = lscl + wv * 32;
+        for (int e = lane; e < 32 * LTS / 16; e += 64)
+            ((i32x4 *)myterm)[e] = i32x4{0, 0, 0, 0};
+        if (lane < 32)
+            myscl[lane] = 127;
+        for (int tt = 0; tt < TPW; ++tt) {
+            const int tl = wv * TPW + tt;
+            if (tl >= ntok)
+                break;
+            const int tok = tok0 + tl;
+            float r0 = 0.0f, r1 = 0.0f;             // qbar at dims 2*lane, 2*lane+1
+            const uint8_t *qp = q_idx + (int64_t)tok * H * 128 + 2 * lane;
+            for (int h = 0; h < H; ++h) {
+                const float wh = w[(int64_t)tok * H + h];
+                const int pr = *(const uint16_t *)(qp + h * 128);
+                r0 = fmaf(wh, __builtin_amdgcn_cvt_f32_fp8(pr, 0), r0);
+                r1 = fmaf(wh, __builtin_amdgcn_cvt_f32_fp8(pr, 1), r1);
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const float mx = wave_max(fmaxf(fabsf(r0), fabsf(r1)));
+                const int ex = (int)((__float_as_uint(mx) >> 23) & 0xFF) - 127;   // floor(log2 mx)
+                const int e = ex - 7;                                             // mx * 2^-e < 256
+                if (mx > 0.0f && ex > -100) {
+                    const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r0, -e), ldexpf(r1, -e), 0, false);
+                    r0 -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), e);
+                    r1 -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 1), e);
+                    const int row = 8 * (2 * (tt >> 1) + (t >> 2)) + 4 * (tt & 1) + (t & 3);
+                    *(uint16_t *)(myterm + row * LTS + 2 * lane) = (uint16_t)pk;
+                    if (lane == 0)
+                        myscl[row] = e + 122;                  // with B's 2^-5: 2^(e - 10)
+                }
+            }
+        }
+        __syncthreads();
+        const int sal = myscl[col];
+        const uint8_t *arow = myterm + col * LTS + half * X::LB;
+
+        constexpr int MH = MT / 2, TH = TPW / 2;
+        auto epi = [&](const f32x16 (&c)[MH], int gh, int s, float ks_s, float L) {
+            float acc[TH];
+#pragma unroll
+            for (int t = 0; t < TH; ++t)
+                acc[t] = 0.0f;
+#pragma unroll
+            for (int m = 0; m < MH; ++m) {
+                const int mt = gh * MH + m;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int t = (mt * 32 + 8 * (i >> 2)) / H - gh * TH;
+                    acc[t] = fmaf(wr[mt][i], fabsf(c[m][i]), acc[t]);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TH; ++t)
+                acc[t] += shfl_xor(acc[t], 32);
+            // writer of token gh*TH + t is the half t%2 (TH == 2) or half gh (TH == 1)
+            const int tw = TH == 1 ? 0 : half;
+            const float a = (TH > 1 && half) ? acc[TH - 1] : acc[0];
+            const float qv = (TH > 1 && half) ? qs[gh * TH + TH - 1] : qs[gh * TH];
+            const int tl = wv * TPW + gh * TH + tw;
+            if ((TH > 1 || half == gh) && tl < ntok && s <= pos0 + tl && s < kb1)
+                scores[(int64_t)(tok0 + tl) * ld + s] = 0.5f * (a + L) * qv * ks_s;
+        };
+        f32x16 c0[MH], c1[MH];
+        int s_prev = 0;
+        float ks_prev = 0.0f, L_prev = 0.0f;
+        for (int it = 0; it < ntiles; ++it) {
+            const int buf = it & 1;
+            const int t0 = kb0 + it * kIdxTileKeys;
+            if (it + 1 < ntiles)
+                gload(t0 + kIdxTileKeys);
+#pragma unroll
+            for (int nt = 0; nt < kIdxTileKeys / 32; ++nt) {
+                const uint8_t *brow = &lds_k[buf][(nt * 32 + col) * RBP + half * X::LB];
+                typename X::Op bop[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    bop[ks] = X::load(brow + ks * X::KS * X::ELEM);
+                const int s = t0 + nt * 32 + col;
+                const float ks_s = lds_ks[buf][nt * 32 + col];
+                // linear term first, reduced to one value per lane right away
+                float La = 0.0f, Lb = 0.0f;
+                {
+                    f32x16 cl = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        cl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            *(const i32x8 *)(arow + ks * X::KS), bop[ks], cl, 0, 0, 0, sal, 0, 122);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        La += cl[i];
+                        if (TPW == 4)
+                            Lb += cl[8 + i];
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < MH; ++m) {
+                    c0[m] = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        c0[m] = X::mma(a[m][ks], bop[ks], c0[m]);
+                }
+                if (it > 0 || nt > 0)
+                    epi(c1, 1, s_prev, ks_prev, L_prev);
+#pragma unroll
+                for (int m = 0; m < MH; ++m) {
+                    c1[m] = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        c1[m] = X::mma(a[MH + m][ks], bop[ks], c1[m]);
+                }
+                epi(c0, 0, s, ks_s, La);
+                s_prev = s;
+                ks_prev = ks_s;
+                L_prev = TPW == 4 ? Lb : La;
+            }
+            if (it + 1 < ntiles)
+                lstore(buf ^ 1);
+            __syncthreads();
+        }
+        if (ntiles > 0)
+            epi(c1, 1, s_prev, ks_prev, L_prev);
+        return;
+    }
+
+    if constexpr (H >= 8 && MT % 2 == 0) {
+        // Ping-pong over the two halves of the wave's M-tiles (G0 = first MT/2,
+        // G1 = the rest; each holds whole tokens): the MFMAs of one half run
+        // while the VALU epilogue of the other half (of this or the previous
+        // 32-key N-tile) runs, with no extra accumulator registers.
+        constexpr int MH = MT / 2, TH = TPW / 2;
+        auto epi = [&](const f32x16 (&c)[MH], int gh, int s, float ks_s) {
+            float acc[TH];
+#pragma unroll
+            for (int t = 0; t < TH; ++t)
+                acc[t] = 0.0f;
+#pragma unroll
+            for (int m = 0; m < MH; ++m) {
+                const int mt = gh * MH + m;
+                if constexpr (F16E) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int t = (mt * 32 + 8 * (j >> 1)) / H - gh * TH;
+                        acc[t] = relu_dot2(c[m][2 * j], c[m][2 * j + 1], wp[mt][j], acc[t]);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int t = (mt * 32 + 8 * (i >> 2)) / H - gh * TH;
+                        acc[t] = fmaf(wr[mt][i], fmaxf(c[m][i], 0.0f), acc[t]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TH; ++t)
+                acc[t] += shfl_xor(acc[t], 32);
+            // one token per half: lanes of half 0 write it; two: half h writes token h
+#pragma unroll
+            for (int t0w = 0; t0w < TH; t0w += 2) {
+                const int t1 = t0w + 1 < TH ? t0w + 1 : t0w;
+                const int tw = t0w + (TH > 1 ? half : 0);
+                const float v = (TH > 1 && half) ? acc[t1] * qs[gh * TH + t1] : acc[t0w] * qs[gh * TH + t0w];
+                const int tl = wv * TPW + gh * TH + tw;
+                if ((TH > 1 || half == 0) && tw < TH && tl < ntok && s <= pos0 + tl && s < kb1)
+                    scores[(int64_t)(tok0 + tl) * ld + s] = v * ks_s;
+            }
+        };
+        f32x16 c0[MH], c1[MH];
+        int s_prev = 0;
+        float ks_prev = 0.0f;
+        for (int it = 0; it < ntiles; ++it) {
+            const int buf = it & 1;
+            const int t0 = kb0 + it * kIdxTileKeys;
+            if (it + 1 < ntiles)
+                gload(t0 + kIdxTileKeys);
+#pragma unroll
+            for (int nt = 0; nt < kIdxTileKeys / 32; ++nt) {
+                const uint8_t *brow = &lds_k[buf][(nt * 32 + col) * RBP + half * X::LB];
+                typename X::Op bop[NKS];
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    bop[ks] = X::load(brow + ks * X::KS * X::ELEM);
+                const int s = t0 + nt * 32 + col;
+                const float ks_s = FP8 ? lds_ks[buf][nt * 32 + col] : 1.0f;
+#pragma unroll
+                for (int m = 0; m < MH; ++m) {
+                    c0[m] = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        c0[m] = X::mma(a[m][ks], bop[ks], c0[m]);
+                }
+                if (it > 0 || nt > 0)
+                    epi(c1, 1, s_prev, ks_prev);
+#pragma unroll
+                for (int m = 0; m < MH; ++m) {
+                    c1[m] = f32x16{};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks)
+                        c1[m] = X::mma(a[MH + m][ks], bop[ks], c1[m]);
+                }
+                epi(c0, 0, s, ks_s);
+                s_prev = s;
+                ks_prev = ks_s;
+            }
+            if (it + 1 < ntiles)
+                lstore(buf ^ 1);
+            __syncthreads();
+        }
+        if (ntiles > 0)
+            epi(c1, 1, s_prev, ks_prev);
+        return;
+    }
+
     for (int it = 0; it < ntiles; ++it) {
         const int buf = it & 1;
         const int t0 = kb0 + it * kIdxTileKeys;
@@ -212,11 +465,19 @@ __global__ __launch_bounds__(256) void indexer_tile_kernel(
                 for (int t = 0; t < TPW; ++t)
                     acc[t] = 0.0f;
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
+                for (int mt = 0; mt < MT; ++mt) {
+                    if constexpr (F16E) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        acc[(mt * 32 + 8 * (i >> 2)) / H] =
-                            fmaf(wr[mt][i], fmaxf(c[mt][i], 0.0f), acc[(mt * 32 + 8 * (i >> 2)) / H]);
+                        for (int j = 0; j < 8; ++j)
+                            acc[(mt * 32 + 8 * (j >> 1)) / H] = relu_dot2(
+                                c[mt][2 * j], c[mt][2 * j + 1], wp[mt][j], acc[(mt * 32 + 8 * (j >> 1)) / H]);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            acc[(mt * 32 + 8 * (i >> 2)) / H] =
+                                fmaf(wr[mt][i], fmaxf(c[mt][i], 0.0f), acc[(mt * 32 + 8 * (i >> 2)) / H]);
+                    }
+                }
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
                     acc[t] += shfl_xor(acc[t], 32);
@@ -280,8 +541,10 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int half = lane >> 5, col = lane & 31;
 
+    constexpr bool F16E = IdxEpi<DT>::F16 && H >= 8;
     typename X::Op a[MT][NKS];
-    float wr[MT][16];
+    float wr[MT][F16E ? 1 : 16];
+    f16x2 wp[MT][F16E ? 8 : 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int h = mt * 32 + col;
@@ -295,10 +558,18 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int ho = mt * 32 + mfma32_row(i, lane);
-            wr[mt][i] = ho < H ? w[(int64_t)tok * H + ho] : 0.0f;
+            const float wv_ = ho < H ? w[(int64_t)tok * H + ho] : 0.0f;
+            if constexpr (F16E) {
+                if (i & 1)
+                    wp[mt][i >> 1][1] = (_Float16)wv_;
+                else
+                    wp[mt][i >> 1][0] = (_Float16)wv_;
+            } else {
+                wr[mt][i] = wv_;
+            }
         }
     }
-    const float qs = FP8 ? q_scale[tok] : 1.0f;
+    const float qs = (FP8 ? q_scale[tok] : 1.0f) * IdxEpi<DT>::UNSCALE;
 
     const int ntiles = (kb1 - kb0 + 31) / 32;
     // two operand slots, software-pipelined; the loop is unrolled by two so
@@ -332,11 +603,19 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
         }
         float acc = 0.0f;
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (F16E) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (mt * 32 + 8 * (i >> 2) < H)
-                    acc = fmaf(wr[mt][i], fmaxf(c[mt][i], 0.0f), acc);
+                for (int j = 0; j < 8; ++j)
+                    if (mt * 32 + 8 * (j >> 1) < H)
+                        acc = relu_dot2(c[mt][2 * j], c[mt][2 * j + 1], wp[mt][j], acc);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (mt * 32 + 8 * (i >> 2) < H)
+                        acc = fmaf(wr[mt][i], fmaxf(c[mt][i], 0.0f), acc);
+            }
+        }
         acc += shfl_xor(acc, 32);
         const int s = kb0 + t * 32 + col;
         if (half == 0 && s < kb1)

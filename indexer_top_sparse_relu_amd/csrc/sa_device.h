@@ -14,6 +14,7 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -99,6 +100,14 @@ __device__ __forceinline__ f32x16 mma32_fp8(i32x8 a, i32x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// Same, with both block scales 2^-5 (E8M0 122): the product comes out scaled by
+// 2^-10, which keeps any fp8 dot of length <= 128 (|dot| <= 128 * 448^2) inside
+// the fp16 range for a packed-fp16 epilogue.
+__device__ __forceinline__ f32x16 mma32_fp8_s10(i32x8 a, i32x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 122, 0, 122);
+}
+
 __device__ __forceinline__ f32x4 mma16_bf16(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -121,6 +130,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
 __device__ __forceinline__ float sigmoidf_(float x)
 {
     return 1.0f / (1.0f + __expf(-x));
+}
+
+// ReLU of two fp32 values rounded (toward zero) to a packed fp16 pair, then
+// acc + w.x with the fp16 products summed in fp32 (v_dot2_f32_f16).
+__device__ __forceinline__ float relu_dot2(float x0, float x1, f16x2 w, float acc)
+{
+    f16x2 x = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(x0, x1));
+    x = __builtin_elementwise_max(x, f16x2{(_Float16)0.0f, (_Float16)0.0f});
+    return __builtin_amdgcn_fdot2(x, w, acc, false);
 }
 
 // ------------------------------------------------------------ wave helpers
