@@ -125,14 +125,14 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     // position i%8 (logical chunk (i%8) ^ f(row)).  Wave wv owns row groups wv,
     // wv+NW, ... so it resolves one physical row per group.
     constexpr int RG = kTK / 8;
-    auto issue = [&](int t, lds_u8 *dk, lds_u8 *dv) {
+    auto issue = [&](int t, lds_u8 *dk, lds_u8 *dv, int ln) {
 #pragma unroll
         for (int rg = wv; rg < RG; rg += NW) {
-            const int r = 8 * rg + (lane >> 3);
+            const int r = 8 * rg + (ln >> 3);
             const int slot = t * kTK + r;
             int pr = prow[slot < nslots ? slot : 0];
             pr = pr >= 0 ? pr : -1 - pr;
-            const int cpos = (lane & 7) ^ swzf(r);
+            const int cpos = (ln & 7) ^ swzf(r);
             const uint16_t *ksrc = kc + (int64_t)pr * rs + cpos * 8;
 #pragma unroll
             for (int cb = 0; cb < KCB; ++cb)
@@ -148,26 +148,29 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     lds_u8 *const LK0 = (lds_u8 *)lk0, *const LK1 = (lds_u8 *)lk1;
     lds_u8 *const LV0 = (lds_u8 *)lv0, *const LV1 = (lds_u8 *)lv1;
     if (ntiles > 0)
-        issue(0, LK0, LV0);
+        issue(0, LK0, LV0, lane);
 
     for (int t = 0; t < ntiles; ++t) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         const bool odd = t & 1;
+        const int ln = opaque(lane);
         // which of the tile's 64 slots hold a selected position (one bit per slot)
-        const int myslot = t * kTK + lane;
+        const int myslot = t * kTK + ln;
         const uint64_t vmask = __ballot(myslot < nslots && prow[myslot < nslots ? myslot : 0] >= 0);
         lds_u8 *tk = odd ? LK1 : LK0;
         lds_u8 *tv = MLA ? tk : (odd ? LV1 : LV0);
         if (t + 1 < ntiles) {
             if (odd)
-                issue(t + 1, LK0, LV0);
+                issue(t + 1, LK0, LV0, ln);
             else
-                issue(t + 1, LK1, LV1);
+                issue(t + 1, LK1, LV1, ln);
         }
 #pragma unroll 1
         for (int kh = 0; kh < 2; ++kh) {
             const int rb = 32 * kh;                       // first row of this half tile
+            const int lk = opaque(lane);
+            const int g = lk >> 4, n = lk & 15;
             // ---- S^T = K Q^T for keys rb..rb+15 and rb+16..rb+31.  Logical chunk
             // 4ks+g of row r: block ks/2, position 4(ks&1)+g xor f(r).  Operands
             // stream through a ring of QD steps so each MFMA waits only for its own.
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
             // dims of keys rb+4g..+3 (first load) and rb+16+4g..+3 (second load).
             // Logical chunk 2mt+hh of row r: block mt/4, position (2(mt&3)+hh) xor f(r).
             constexpr int PD = 3;
-            const int jj = lane & 15;
+            const int jj = lk & 15;
             const int ra_ = rb + 4 * g + (jj >> 2), rc_ = ra_ + 16;
             const int cc = jj & 3, hh = cc >> 1;
             const int fa = swzf(ra_), fc = swzf(rc_);

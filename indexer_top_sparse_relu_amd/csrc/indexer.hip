@@ -71,6 +71,34 @@ template <int H> struct IdxShape {
 
 constexpr int kIdxWaves = 4;
 constexpr int kIdxTileKeys = 64;
+constexpr int kIdxMaxChunk = 8192;     // keys per prefill workgroup, at most
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) float lds_f32;
+
+// Direct global->LDS loads (global_load_lds): lane i's 16 (resp. 4) bytes land
+// at lds + 16*i (resp. 4*i); lds is wave-uniform and goes through M0, which is
+// saved and restored.  Written as asm so the compiler does not track them:
+// its LDS-DMA tracking would put a full vmcnt wait in front of every LDS read
+// of the ring.  Completion is awaited explicitly with s_waitcnt vmcnt, and
+// loads unknown to the compiler can only make its own waits stricter.
+__device__ __forceinline__ void dma_b128(const void *src, const lds_u8 *lds)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)lds;
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(src), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void *src, const lds_u8 *lds)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)lds;
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(src), "s"(base) : "memory");
+}
 
 // ------------------------------------------------------------------ prefill
 template <int DT, int H, int D>
@@ -87,10 +115,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     constexpr int NKS = D / X::KS;               // MFMA steps along d
     constexpr bool FP8 = DT == 2;
     static_assert(RB % 32 == 0, "row bytes");
-    __shared__ __align__(16) uint8_t lds_k[2][kIdxTileKeys * RBP];
-    __shared__ float lds_ks[2][kIdxTileKeys];
     // fp8 with >= 16 heads: the linear part of the ReLU runs on the MFMA (see below)
     constexpr bool LIN = (DT == 2) && (H >= 16) && (MT % 2 == 0) && (D == 128);
+    __shared__ __align__(16) uint8_t lds_k[2][LIN ? 16 : kIdxTileKeys * RBP];
+    __shared__ float lds_ks[2][LIN ? 1 : kIdxTileKeys];
+    __shared__ __align__(16) uint8_t lkr0[LIN ? kIdxTileKeys * 128 : 16];
+    __shared__ __align__(16) uint8_t lkr1[LIN ? kIdxTileKeys * 128 : 16];
+    __shared__ __align__(16) uint8_t lkr2[LIN ? kIdxTileKeys * 128 : 16];
+    __shared__ float lksr[LIN ? 3 * kIdxWaves * kIdxTileKeys : 1];
+    __shared__ int lpt[LIN ? kIdxMaxChunk / 16 + 2 : 1];
     constexpr int LTS = 128 + 16;                // padded term row (bank spread, as RBP)
     __shared__ __align__(16) uint8_t lterm[LIN ? kIdxWaves * 32 * LTS : 16];
     __shared__ int lscl[LIN ? kIdxWaves * 32 : 1];
@@ -125,7 +158,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     if (kb0 >= kb1)
         return;
 
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
     const int half = lane >> 5, col = lane & 31;
 
     // ---- A operands (this wave's tokens x heads) and weights, kept in registers
@@ -207,9 +241,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     };
 
     const int ntiles = (kb1 - kb0 + kIdxTileKeys - 1) / kIdxTileKeys;
-    gload(kb0);
-    lstore(0);
-    __syncthreads();
+    if constexpr (!LIN) {
+        gload(kb0);
+        lstore(0);
+        __syncthreads();
+    }
 
     if constexpr (LIN) {
         // w * ReLU(x) = (w x + w |x|) / 2.  The w |x| sum is one FMA per element
@@ -228,6 +264,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             ((i32x4 *)myterm)[e] = i32x4{0, 0, 0, 0};
         if (lane < 32)
             myscl[lane] = 127;
+        // physical page of every page the chunk touches
+        const int pshift = bt.page_shift, pmask = (1 << pshift) - 1;
+        const int pg0 = kb0 >> pshift;
+        const int npg = ((kb1 - 1) >> pshift) - pg0 + 1;
+        for (int i = tid; i < npg; i += 256)
+            lpt[i] = bt.page_table[(int64_t)b * bt.max_pages + pg0 + i];
         for (int tt = 0; tt < TPW; ++tt) {
             const int tl = wv * TPW + tt;
             if (tl >= ntok)
@@ -261,6 +303,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         const int sal = myscl[col];
         const uint8_t *arow = myterm + col * LTS + half * X::LB;
 
+        // Key tiles: a ring of KST stages of 64 rows x 128 bytes, filled by direct
+        // global->LDS loads (no registers).  The 16-byte chunk c of row r sits at
+        // chunk position c ^ ((r >> 1) & 7): the B-operand reads (16 rows of one
+        // chunk per LDS phase) then hit 16 distinct bank groups.  Wave wv loads
+        // the 1 KB blocks wv and wv + 4 (8 rows each) and its own copy of the
+        // tile's 64 key scales.  Positions past the chunk are clamped to its last
+        // key, so every tile, also one past the end, is a full, in-bounds load.
+        constexpr int KST = 3;
+        auto stage = [&](int st) -> lds_u8 * {
+            return st == 0 ? (lds_u8 *)lkr0 : st == 1 ? (lds_u8 *)lkr1 : (lds_u8 *)lkr2;
+        };
+        lds_f32 *const LKS = (lds_f32 *)lksr;
+        auto krow = [&](int s) -> int64_t {
+            s = min(s, kb1 - 1);
+            return ((int64_t)lpt[(s >> pshift) - pg0] << pshift) + (s & pmask);
+        };
+        auto issue = [&](int tt, int ln) {
+            const int st = tt % KST;
+            const int t0 = kb0 + tt * kIdxTileKeys;
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int blk = u * kIdxWaves + wv;
+                const int r = blk * 8 + (ln >> 3);
+                const int c = (ln & 7) ^ ((r >> 1) & 7);
+                dma_b128(k_idx + krow(t0 + r) * 128 + c * 16, stage(st) + blk * 1024);
+            }
+            dma_b32(k_scale + krow(t0 + ln), (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * 64));
+        };
+
+        // Scores go out through a buffer resource spanning this wave's token rows:
+        // a masked lane gets an offset past the end, which the hardware drops, so
+        // every store instruction issues and the memory-op count per tile is fixed.
+        const int wt0 = min(wv * TPW, ntok - 1);
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            scores + (int64_t)(tok0 + wt0) * ld, 0, (int)(TPW * ld * 4), 0x00020000);
+
         constexpr int MH = MT / 2, TH = TPW / 2;
         auto epi = [&](const f32x16 (&c)[MH], int gh, int s, float ks_s, float L) {
             float acc[TH];
@@ -284,26 +362,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             const float a = (TH > 1 && half) ? acc[TH - 1] : acc[0];
             const float qv = (TH > 1 && half) ? qs[gh * TH + TH - 1] : qs[gh * TH];
             const int tl = wv * TPW + gh * TH + tw;
-            if ((TH > 1 || half == gh) && tl < ntok && s <= pos0 + tl && s < kb1)
-                scores[(int64_t)(tok0 + tl) * ld + s] = 0.5f * (a + L) * qv * ks_s;
+            const bool ok = (TH > 1 || half == gh) && tl < ntok && s <= pos0 + tl && s < kb1;
+            const uint32_t off = ok ? (uint32_t)(((int64_t)(tl - wt0) * ld + s) * 4) : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(0.5f * (a + L) * qv * ks_s), srs, off, 0, 0);
         };
         f32x16 c0[MH], c1[MH];
         int s_prev = 0;
         float ks_prev = 0.0f, L_prev = 0.0f;
+        issue(0, lane);
+        issue(1, lane);
         for (int it = 0; it < ntiles; ++it) {
-            const int buf = it & 1;
+            // Tile it was issued two iterations back (3 ops per wave); since then
+            // each iteration issued 3 loads and 4 stores (3 in the first), which
+            // may stay in flight.
+            if (it == 0)
+                asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+            else if (it == 1)
+                asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+            else if (it == 2)
+                asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+            __syncthreads();
+            const int ln = opaque(lane);
+            issue(it + 2, ln);
+            const int st = it % KST;
             const int t0 = kb0 + it * kIdxTileKeys;
-            if (it + 1 < ntiles)
-                gload(t0 + kIdxTileKeys);
 #pragma unroll
             for (int nt = 0; nt < kIdxTileKeys / 32; ++nt) {
-                const uint8_t *brow = &lds_k[buf][(nt * 32 + col) * RBP + half * X::LB];
+                const int r = nt * 32 + (ln & 31);
+                const lds_u8 *brow = stage(st) + r * 128;
+                const int f = (r >> 1) & 7, hf = ln >> 5;
                 typename X::Op bop[NKS];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    bop[ks] = X::load(brow + ks * X::KS * X::ELEM);
-                const int s = t0 + nt * 32 + col;
-                const float ks_s = lds_ks[buf][nt * 32 + col];
+                for (int ks = 0; ks < NKS; ++ks) {
+                    const int c = 2 * hf + 4 * ks;
+                    const i32x4 lo = *(const __attribute__((address_space(3))) i32x4 *)(brow + 16 * (c ^ f));
+                    const i32x4 hi = *(const __attribute__((address_space(3))) i32x4 *)(brow + 16 * ((c + 1) ^ f));
+                    bop[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                }
+                const int s = t0 + r;
+                const float ks_s = LKS[(st * kIdxWaves + wv) * 64 + r];
                 // linear term first, reduced to one value per lane right away
                 float La = 0.0f, Lb = 0.0f;
                 {
@@ -340,12 +439,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                 ks_prev = ks_s;
                 L_prev = TPW == 4 ? Lb : La;
             }
-            if (it + 1 < ntiles)
-                lstore(buf ^ 1);
-            __syncthreads();
         }
         if (ntiles > 0)
             epi(c1, 1, s_prev, ks_prev, L_prev);
+        // the ring's last two tiles were loaded past the end: drain them before
+        // the workgroup's LDS is released
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         return;
     }
 
@@ -649,6 +748,8 @@ static hipError_t launch_indexer_t(const Batch &bt, const void *q_idx, const flo
         int key_chunk = (bt.max_ctx + n_chunks - 1) / n_chunks;
         key_chunk = (key_chunk + kIdxTileKeys - 1) / kIdxTileKeys * kIdxTileKeys;
         n_chunks = (bt.max_ctx + key_chunk - 1) / key_chunk;
+        if (key_chunk > kIdxMaxChunk || ld * 4 * IdxShape<H>::TPW >= (1LL << 31))
+            return hipErrorInvalidValue;
         const int n_tiles_max = (bt.total_q + TQ - 1) / TQ + bt.num_seqs - 1;
         const int cpx_max = (n_chunks + 7) / 8;
         const int64_t grid = 8LL * cpx_max * n_tiles_max;

@@ -141,6 +141,17 @@ __device__ __forceinline__ float relu_dot2(float x0, float x1, f16x2 w, float ac
     return __builtin_amdgcn_fdot2(x, w, acc, false);
 }
 
+// A copy of v that the compiler cannot see through.  Lane-derived addresses
+// computed from it inside a loop body are recomputed there (a few VALU ops)
+// instead of being hoisted and kept live across the loop, where register
+// pressure would spill them: a scratch reload waits on vmcnt, which also
+// counts the loop's in-flight prefetches.
+__device__ __forceinline__ int opaque(int v)
+{
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
 // ------------------------------------------------------------ wave helpers
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m)
