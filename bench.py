@@ -14,7 +14,6 @@ work only (flops of the contraction, or bytes the method must move).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -27,19 +26,20 @@ if ROOT not in sys.path:
 # MI355X published peaks
 PEAK = {"hbm_GBs": 8000.0, "fp8_TFLOPs": 5000.0, "bf16_TFLOPs": 2500.0, "fp32_TFLOPs": 157.3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {
-    "indexer": "indexer_top_sparse_relu_amd/csrc/indexer.hip",
-    "topk": "indexer_top_sparse_relu_amd/csrc/topk.hip",
-    "attn": "indexer_top_sparse_relu_amd/csrc/attn.hip",
-}
+COPY_ELEMS = 1 << 28          # calibration copy: 2^28 fp32 = 1 GiB read + 1 GiB written
 
 
-def source_hash(stage: str) -> str:
-    h = hashlib.sha256()
-    for rel in (KERNEL_SOURCES[stage], "indexer_top_sparse_relu_amd/csrc/sa_device.h"):
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def calibration_copy():
+    """A plain streaming kernel of known traffic for scaling HBM counters: y = -x over
+    COPY_ELEMS fp32 (reads and writes 4 * COPY_ELEMS bytes), run three times."""
+    import torch
+
+    x = torch.ones(COPY_ELEMS, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    del x, y
 
 
 def causal_lengths(spec):
@@ -119,6 +119,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="chunked_prefill_mla_128k")
     ap.add_argument("--cpu-sample", type=int, default=48, help="query tokens the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a copy kernel of known size (for HBM counter calibration)")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this path has no multi-GPU mode (run with --gpus 1)", file=sys.stderr)
@@ -129,6 +131,10 @@ def main(argv=None):
     from indexer_top_sparse_relu_amd import binding as B
     from indexer_top_sparse_relu_amd import workloads as W
 
+    from indexer_top_sparse_relu_amd.profiling import source_hash
+
+    if args.calibrate_copy:
+        calibration_copy()
     spec = W.CONFIGS[args.workload]()
     wl = W.generate(spec, "cuda")
     pl = B.Pipeline(wl)
@@ -184,7 +190,7 @@ def main(argv=None):
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        ent = tr.get(args.workload, {}).get(dom)
+        ent = tr.get(spec.name, {}).get(dom)
         if ent and ent.get("source_hash") == source_hash(dom):
             traffic = ent["bytes_per_launch"]
     roof = {k: v for k, v in rl[dom].items() if k != "ms"}
