@@ -26,6 +26,11 @@
 //   5. the two ascending runs are merged by co-rank and written.
 // Keys are the order-preserving uint32 image of the fp32 score.
 //
+// Long rows first try a single-pass variant (select_topk_fast): a contiguous-
+// run sample fixes a conservative threshold and one order-preserving pass
+// keeps every slot at or above it in LDS, where the steps 4-5 finish; when the
+// kept count misses [K, kCap] the general steps 1-5 run instead.
+//
 // Rows up to a few hundred thousand slots take one workgroup each.  When there
 // are too few rows to fill the GPU, each row is cut into chunks selected in
 // parallel (stage 1: top-K per chunk, with scores), and a second pass selects
@@ -41,7 +46,7 @@ namespace sa {
 constexpr int kTkThreads = 512;
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kBins = 4096;
-constexpr int kCap = 2048;      // LDS slots for the window's candidates
+constexpr int kCap = 4096;      // LDS slots for the window's candidates
 constexpr int kSample = 4096;
 constexpr int kMaxK = 4096;
 
@@ -154,6 +159,89 @@ __device__ __forceinline__ void find_bin(const TkSmem &sm, uint32_t need, int &b
     b_out = (int)sm.misc[40];
     gt_out = sm.misc[41];
     __syncthreads();
+}
+
+// Steps 4-5 of a selection: the window's slots (ckey/cidx[0, C), in slot order)
+// hold the remaining `need` winners; the sure winners are okey/oidx[0, above),
+// in slot order.  Resolves the exact K-th key inside LDS (ties to the lowest
+// slots), then merges the two ascending runs into gidx (and gval).
+__device__ void finish_select(uint32_t lo, uint32_t hi, uint32_t cnt, uint32_t above, uint32_t need, bool single,
+                              int K, int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
+{
+    const int tid = threadIdx.x;
+    // ---- 4. resolve the window inside LDS
+    if (!single) {
+        const int C = (int)min(cnt, (uint32_t)kCap);
+        uint32_t wl = lo, wh = hi, needw = need;
+        bool all_in = false;
+        // each pass narrows a window of width W to at most W / 4096 (or stops): <= 3 passes
+        for (int pass = 0; pass < 4 && wl != wh && !all_in; ++pass) {
+            const int sh = max(0, bitlen(wh - wl) - 12);
+            for (int b = tid; b < kBins; b += kTkThreads)
+                sm.hist[b] = 0u;
+            __syncthreads();
+            for (int c = tid; c < C; c += kTkThreads) {
+                const uint32_t key = sm.ckey[c];
+                if (key >= wl && key <= wh)
+                    atomicAdd(&sm.hist[(key - wl) >> sh], 1u);
+            }
+            __syncthreads();
+            int bsel;
+            uint32_t gt;
+            find_bin(sm, needw, bsel, gt);
+            const uint32_t hb = sm.hist[bsel];
+            needw -= gt;
+            const uint64_t nlo = (uint64_t)wl + ((uint64_t)bsel << sh);
+            wh = (uint32_t)min((uint64_t)wh, nlo + ((1ull << sh) - 1ull));
+            wl = (uint32_t)nlo;
+            all_in = (hb == needw);
+            __syncthreads();
+        }
+        // ordered selection: keys above the window, then the first needw keys inside it
+        uint32_t bsel_ = 0, bwin = 0;
+        for (int c0 = 0; c0 < C; c0 += kTkThreads) {
+            const int c = c0 + tid;
+            const uint32_t key = c < C ? sm.ckey[c] : 0u;
+            const bool inw = c < C && key >= wl && key <= wh;
+            const bool abv = c < C && key > wh;
+            uint32_t tot;
+            const uint32_t ex = block_scan((inw ? 1u : 0u) | ((abv ? 1u : 0u) << 16), sm.misc, tot);
+            const uint32_t rank_w = bwin + (ex & 0xFFFFu);
+            const bool sel = abv || (inw && (all_in || rank_w < needw));
+            uint32_t tot2;
+            const uint32_t ps = bsel_ + block_scan(sel ? 1u : 0u, sm.misc, tot2);
+            if (sel && above + ps < (uint32_t)K) {
+                sm.okey[above + ps] = key;
+                sm.oidx[above + ps] = sm.cidx[c];
+            }
+            bwin += tot & 0xFFFFu;
+            bsel_ += tot2;
+        }
+        __syncthreads();
+    }
+
+    // ---- 5. merge the two ascending runs [0, above) and [above, K)
+    {
+        const int A = (int)above, Bn = K - (int)above;
+        const int32_t *ra = sm.oidx, *rb = sm.oidx + A;
+        for (int i = tid; i < K; i += kTkThreads) {
+            const bool inA = i < A;
+            const int32_t x = sm.oidx[i];
+            const int32_t *other = inA ? rb : ra;
+            int lo2 = 0, hi2 = inA ? Bn : A;         // count of `other` elements < x
+            while (lo2 < hi2) {
+                const int mid = (lo2 + hi2) >> 1;
+                if (other[mid] < x)
+                    lo2 = mid + 1;
+                else
+                    hi2 = mid;
+            }
+            const int p = (inA ? i : i - A) + lo2;
+            gidx[p] = x;
+            if (gval)
+                gval[p] = kval(sm.okey[i]);
+        }
+    }
 }
 
 // One selection problem: n slots with values `vals`; positions are idx0 + j,
@@ -337,79 +425,126 @@ __device__ void select_topk(const float *__restrict__ vals, const int32_t *__res
         __syncthreads();
     }
 
-    // ---- 4. resolve the window inside LDS
-    if (!single) {
-        const int C = (int)min(cnt, (uint32_t)kCap);
-        uint32_t wl = lo, wh = hi, needw = need;
-        bool all_in = false;
-        // each pass narrows a window of width W to at most W / 4096 (or stops): <= 3 passes
-        for (int pass = 0; pass < 4 && wl != wh && !all_in; ++pass) {
-            const int sh = max(0, bitlen(wh - wl) - 12);
-            for (int b = tid; b < kBins; b += kTkThreads)
-                sm.hist[b] = 0u;
-            __syncthreads();
-            for (int c = tid; c < C; c += kTkThreads) {
-                const uint32_t key = sm.ckey[c];
-                if (key >= wl && key <= wh)
-                    atomicAdd(&sm.hist[(key - wl) >> sh], 1u);
-            }
-            __syncthreads();
-            int bsel;
-            uint32_t gt;
-            find_bin(sm, needw, bsel, gt);
-            const uint32_t hb = sm.hist[bsel];
-            needw -= gt;
-            const uint64_t nlo = (uint64_t)wl + ((uint64_t)bsel << sh);
-            wh = (uint32_t)min((uint64_t)wh, nlo + ((1ull << sh) - 1ull));
-            wl = (uint32_t)nlo;
-            all_in = (hb == needw);
-            __syncthreads();
-        }
-        // ordered selection: keys above the window, then the first needw keys inside it
-        uint32_t bsel_ = 0, bwin = 0;
-        for (int c0 = 0; c0 < C; c0 += kTkThreads) {
-            const int c = c0 + tid;
-            const uint32_t key = c < C ? sm.ckey[c] : 0u;
-            const bool inw = c < C && key >= wl && key <= wh;
-            const bool abv = c < C && key > wh;
-            uint32_t tot;
-            const uint32_t ex = block_scan((inw ? 1u : 0u) | ((abv ? 1u : 0u) << 16), sm.misc, tot);
-            const uint32_t rank_w = bwin + (ex & 0xFFFFu);
-            const bool sel = abv || (inw && (all_in || rank_w < needw));
-            uint32_t tot2;
-            const uint32_t ps = bsel_ + block_scan(sel ? 1u : 0u, sm.misc, tot2);
-            if (sel && above + ps < (uint32_t)K) {
-                sm.okey[above + ps] = key;
-                sm.oidx[above + ps] = sm.cidx[c];
-            }
-            bwin += tot & 0xFFFFu;
-            bsel_ += tot2;
+    finish_select(lo, hi, cnt, above, need, single, K, gidx, gval, sm);
+}
+
+// rank-th largest key (1 <= rank <= cnt) of keys[0, cnt) in LDS: a radix
+// select over three digit levels (12, 12 and 8 bits).
+__device__ uint32_t lds_select_rank(const uint32_t *keys, int cnt, uint32_t rank, const TkSmem &sm)
+{
+    const int tid = threadIdx.x;
+    uint32_t prefix = 0u, pmask = 0u, need = rank;
+#pragma unroll 1
+    for (int lv = 0; lv < 3; ++lv) {
+        const int sh = lv == 0 ? 20 : (lv == 1 ? 8 : 0);
+        const uint32_t dm = lv == 2 ? 0xFFu : 0xFFFu;
+        for (int b = tid; b < kBins; b += kTkThreads)
+            sm.hist[b] = 0u;
+        __syncthreads();
+        for (int c = tid; c < cnt; c += kTkThreads) {
+            const uint32_t k = keys[c];
+            if ((k & pmask) == prefix)
+                atomicAdd(&sm.hist[(k >> sh) & dm], 1u);
         }
         __syncthreads();
+        int b;
+        uint32_t gt;
+        find_bin(sm, need, b, gt);
+        need -= gt;
+        prefix |= (uint32_t)b << sh;
+        pmask |= dm << sh;
     }
+    return prefix;
+}
 
-    // ---- 5. merge the two ascending runs [0, above) and [above, K)
-    {
-        const int A = (int)above, Bn = K - (int)above;
-        const int32_t *ra = sm.oidx, *rb = sm.oidx + A;
-        for (int i = tid; i < K; i += kTkThreads) {
-            const bool inA = i < A;
-            const int32_t x = sm.oidx[i];
-            const int32_t *other = inA ? rb : ra;
-            int lo2 = 0, hi2 = inA ? Bn : A;         // count of `other` elements < x
-            while (lo2 < hi2) {
-                const int mid = (lo2 + hi2) >> 1;
-                if (other[mid] < x)
-                    lo2 = mid + 1;
-                else
-                    hi2 = mid;
-            }
-            const int p = (inA ? i : i - A) + lo2;
-            gidx[p] = x;
-            if (gval)
-                gval[p] = kval(sm.okey[i]);
-        }
+// Single-pass selection for long rows (slot j has position idx0 + j).  A
+// sample of 64 runs of 64 consecutive slots, spread evenly over the row, gives
+// a threshold: the sample key whose rank is the K-th key's expected rank in
+// the sample plus about three standard deviations, so that the row's slots at
+// or above it very likely number between K and kCap.  One order-preserving
+// pass keeps exactly those slots in LDS (slot order); the exact K-th key and
+// its ties are then resolved there.  Returns false, having written nothing,
+// when the kept count falls outside [K, kCap]; the caller then runs the
+// general selection, so the result never depends on the sample.
+__device__ bool select_topk_fast(const float *__restrict__ vals, int n, int idx0, int K,
+                                 int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (n < 2 * kSample)
+        return false;
+    const float rexp = (float)K * (float)kSample / (float)n;
+    const int rlow = (int)(rexp + 3.0f * sqrtf(rexp) + 4.0f) + 1;
+    if (rlow >= kSample)
+        return false;
+
+    // ---- 1. sample -> threshold
+    constexpr int RUNS = kSample / 64;
+    for (int r = wv; r < RUNS; r += kTkWaves) {
+        const int j = (int)(((int64_t)r * (n - 64)) / (RUNS - 1)) + lane;
+        sm.ckey[r * 64 + lane] = fkey(vals[j]);
     }
+    __syncthreads();
+    const uint32_t thr = lds_select_rank(sm.ckey, kSample, (uint32_t)rlow, sm);
+
+    // ---- 2. one pass: slots with key >= thr to ckey/cidx in slot order.  Each
+    // thread owns 16 consecutive slots per step; the next step's loads are in
+    // flight while this step's block scan waits at its barriers.
+    const bool aligned = ((((uintptr_t)vals) & 15u) == 0);
+    auto load16 = [&](int j0, float (&v)[16]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + 4 * u;
+            if (aligned && j + 3 < n) {
+                const float4 f = *(const float4 *)(vals + j);
+                v[4 * u] = f.x;
+                v[4 * u + 1] = f.y;
+                v[4 * u + 2] = f.z;
+                v[4 * u + 3] = f.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    v[4 * u + e] = (j + e < n) ? vals[j + e] : 0.0f;
+            }
+        }
+    };
+    constexpr int STEP = kTkThreads * 16;
+    float cur[16], nxt[16];
+    load16(tid * 16, cur);
+    uint32_t base = 0;
+    for (int j00 = 0; j00 < n; j00 += STEP) {
+        const int j0 = j00 + tid * 16;
+        uint32_t kk[16], m = 0u;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            kk[e] = fkey(cur[e]);
+            if (j0 + e < n && kk[e] >= thr)
+                m |= 1u << e;
+        }
+        if (j00 + STEP < n)
+            load16(j0 + STEP, nxt);
+        uint32_t tot;
+        uint32_t p = base + block_scan((uint32_t)__popc(m), sm.misc, tot);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            if ((m >> e) & 1u) {
+                if (p < (uint32_t)kCap) {
+                    sm.ckey[p] = kk[e];
+                    sm.cidx[p] = idx0 + j0 + e;
+                }
+                ++p;
+            }
+        }
+        base += tot;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            cur[e] = nxt[e];
+    }
+    __syncthreads();
+    if (base < (uint32_t)K || base > (uint32_t)kCap)
+        return false;
+    // ---- 3. exact K-th key among the kept slots (all K winners are among them)
+    finish_select(thr, 0xFFFFFFFFu, base, 0u, (uint32_t)K, false, K, gidx, gval, sm);
+    return true;
 }
 
 __device__ __forceinline__ TkSmem tk_smem(int K)
@@ -437,7 +572,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(Batch bt, const f
     const int row = blockIdx.x;
     const int b = seq_of_token(bt, row);
     const int n = pos_of_token(bt, b, row) + 1;
-    select_topk<false>(scores + (int64_t)row * ld, nullptr, n, 0, K, out + (int64_t)row * K, nullptr, tk_smem(K));
+    const TkSmem sm = tk_smem(K);
+    const float *vals = scores + (int64_t)row * ld;
+    int32_t *o = out + (int64_t)row * K;
+    if (!select_topk_fast(vals, n, 0, K, o, nullptr, sm))
+        select_topk<false>(vals, nullptr, n, 0, K, o, nullptr, sm);
 }
 
 // Stage 1: blockIdx.x = chunk, blockIdx.y = row; per-chunk top-K with scores.
@@ -451,7 +590,10 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(Batch bt, const 
     const int j0 = c * chunk;
     const int len = max(0, min(chunk, n - j0));
     const int64_t o = (int64_t)row * cand_ld + (int64_t)c * K;
-    select_topk<false>(scores + (int64_t)row * ld + j0, nullptr, len, j0, K, cidx + o, cval + o, tk_smem(K));
+    const TkSmem sm = tk_smem(K);
+    const float *vals = scores + (int64_t)row * ld + j0;
+    if (!select_topk_fast(vals, len, j0, K, cidx + o, cval + o, sm))
+        select_topk<false>(vals, nullptr, len, j0, K, cidx + o, cval + o, sm);
 }
 
 // Stage 2: one workgroup per row over the concatenated chunk winners.

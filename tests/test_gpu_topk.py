@@ -1,0 +1,121 @@
+"""GPU Top-K on crafted score rows, bit-exact against the oracle's brute force.
+
+The rows kernel and the chunked kernels try a single pass whose threshold comes
+from a sample of 64 runs of 64 consecutive slots; when the kept count misses
+[K, capacity] they fall back to the general selection.  These rows drive both
+branches: plain random rows, constant rows and coarse alphabets (massive
+ties), ramps, rows whose large values sit exactly on (or exactly off) the
+sampled runs, and signed zeros.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from indexer_top_sparse_relu_amd import binding as B  # noqa: E402
+
+DEV = "cuda"
+RUNS = 64
+
+
+def sampled_mask(n):
+    """Slots the single-pass sample reads: run r starts at r*(n-64)//63."""
+    m = np.zeros(n, bool)
+    for r in range(RUNS):
+        j = (r * (n - 64)) // (RUNS - 1)
+        m[j:j + 64] = True
+    return m
+
+
+def pattern_row(kind, n, rng):
+    if kind == "normal":
+        return rng.standard_normal(n).astype(np.float32)
+    if kind == "constant":
+        return np.full(n, 1.25, np.float32)
+    if kind == "alphabet":
+        return rng.choice(np.array([-1.0, 0.0, 0.5, 2.0, 3.0], np.float32), n)
+    if kind == "ramp":
+        return (1.0 + np.arange(n) * 1e-6).astype(np.float32)
+    if kind == "on_sample":
+        v = rng.uniform(0.0, 1.0, n).astype(np.float32)
+        m = sampled_mask(n)
+        v[m] = rng.uniform(10.0, 11.0, int(m.sum())).astype(np.float32)
+        return v
+    if kind == "off_sample":
+        v = rng.uniform(10.0, 11.0, n).astype(np.float32)
+        m = sampled_mask(n)
+        v[m] = rng.uniform(0.0, 1.0, int(m.sum())).astype(np.float32)
+        return v
+    if kind == "signed_zero":
+        v = rng.standard_normal(n).astype(np.float32)
+        z = rng.random(n) < 0.5
+        v[z] = np.where(rng.random(int(z.sum())) < 0.5, np.float32(0.0), np.float32(-0.0))
+        v[v > 0] *= -1.0                       # the top K are all zeros of either sign
+        return v
+    if kind == "rounded":
+        return np.round(rng.standard_normal(n), 2).astype(np.float32)
+    raise ValueError(kind)
+
+
+KINDS = ["normal", "constant", "alphabet", "ramp", "on_sample", "off_sample", "signed_zero", "rounded"]
+
+
+def run_rows(lengths, kinds, K, seed):
+    rng = np.random.default_rng(seed)
+    Bn = len(lengths)
+    n = np.asarray(lengths, np.int64)
+    ld = int((n.max() + 63) // 64 * 64)
+    sc = np.full((Bn, ld), np.nan, np.float32)
+    for r in range(Bn):
+        sc[r, :n[r]] = pattern_row(kinds[r % len(kinds)], int(n[r]), rng)
+    # one query token per sequence: row r has n[r] causal candidates
+    q_start = torch.arange(Bn + 1, dtype=torch.int32, device=DEV)
+    ctx = torch.as_tensor(n.astype(np.int32), device=DEV)
+    ps = 64
+    max_pages = (ld + ps - 1) // ps
+    pt = torch.zeros((Bn, max_pages), dtype=torch.int32, device=DEV)
+    bt = B.make_batch(q_start, ctx, pt, total_q=Bn, max_q=1, max_ctx=int(n.max()), page_size=ps)
+    scores = torch.as_tensor(sc, device=DEV)
+    idx = torch.full((Bn, K), -7, dtype=torch.int32, device=DEV)
+    wsb = B.sparse_topk_workspace_size(bt, K)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=DEV) if wsb else None
+    B.sparse_topk(bt, scores, K, idx, ws)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    ref = O.topk(sc.astype(np.float64), n, K)
+    for r in range(Bn):
+        assert np.array_equal(got[r], ref[r]), f"row {r} ({kinds[r % len(kinds)]}, n={n[r]}) differs"
+    P.check_idx_invariants(got, n, K)
+    return wsb
+
+
+def test_topk_rows_kernel_crafted_rows():
+    """256 rows (the per-row kernel), lengths 9K-40K, every pattern."""
+    rng = np.random.default_rng(7)
+    lengths = rng.integers(9000, 40000, 256).tolist()
+    P.say("[topk-rows] 256 rows, K=2048")
+    wsb = run_rows(lengths, KINDS, 2048, seed=8)
+    assert wsb == 0                       # 256 rows: no chunking
+
+
+def test_topk_chunked_crafted_rows():
+    """Few long rows (chunked selection, then merge), every pattern."""
+    lengths = [300000, 150001, 70000, 40960, 262144, 100000, 65537, 200000]
+    P.say("[topk-chunked] 8 rows up to 300K, K=2048")
+    wsb = run_rows(lengths, KINDS, 2048, seed=9)
+    assert wsb > 0
+
+
+def test_topk_small_k_and_large_k():
+    rng = np.random.default_rng(10)
+    lengths = rng.integers(8192, 30000, 256).tolist()
+    for K in (1, 64, 4096):
+        P.say(f"[topk-k] K={K}")
+        run_rows(lengths, KINDS, K, seed=11 + K)
