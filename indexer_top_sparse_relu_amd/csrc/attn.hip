@@ -45,8 +45,6 @@ constexpr int kMaxSplit = 2048;         // index slots one workgroup resolves up
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
@@ -309,6 +307,304 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     }
 }
 
+// Latent-layout kernel (d_qk = 576, d_v = 512, V = the first 512 dims of each
+// gathered row) on 32x32x16 bf16 MFMA: 4 waves x 32 query heads per
+// workgroup, one wave per SIMD.  Compared with 16 heads per wave on 16x16
+// tiles, every LDS operand read feeds twice the MACs, so the tile reads per
+// flop halve; Q^T stays in 144 VGPRs and the 16 O^T tiles (512 dims x 32
+// heads) accumulate in the AGPR half of the register file.
+// Per 32-key sub-tile: S^T = K Q^T (36 MFMAs; a lane holds one head's column
+// and 16 keys), the online softmax, then O^T += V^T P^T (2 x 16 MFMAs).  The
+// P^T operand is the lane's own S registers: in step j, lane half hq supplies
+// keys 16j + 4hq + {0..3} and 16j + 8 + 4hq + {0..3}, the order in which two
+// transpose loads of V deliver them.
+// Tile layout: 64 rows x 72 sixteen-byte chunks, blocks of 8 rows x 8 chunks;
+// chunk c of row r sits at block position (c & 7) ^ g(r), g(r) = 4*r[1] +
+// 2*r[3] + r[2].  On gfx950 a 128-bit LDS read is served in four phases of 16
+// lanes grouped by (lane bit 5, lane bit 3 ^ lane bit 4) and a transpose read
+// in two phases of 32 lanes (bit 5), over 64 four-byte banks; under that
+// (measured) rule g makes both the K reads (32 rows of one chunk per wave
+// half) and the V reads (4 rows x 4 chunks per phase) conflict-free.
+constexpr float kMlaHeadroom = 64.0f;   // log2 units a logit may exceed the softmax reference by
+
+__device__ __forceinline__ int swzg(int r) { return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1); }
+
+template <int DQK, int DV>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_mla_kernel(
+    Batch bt, const uint16_t *__restrict__ q, int Hq, const uint16_t *__restrict__ kc, int64_t rs,
+    const int32_t *__restrict__ idx, int K, const uint16_t *__restrict__ gate, int per_channel, float scale_log2,
+    uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ part, int n_split, int split_len)
+{
+    constexpr int NW = 4;
+    constexpr int NKQ = DQK / 16;           // MFMA k-steps over d_qk
+    constexpr int NDT = DV / 32;            // 32-dim tiles of O^T
+    constexpr int KCH = DQK / 8;            // 16-byte chunks per row
+    constexpr int KCB = KCH / 8;            // 8-chunk blocks per row
+    constexpr int KCHUNKS = kTK * KCH;
+    static_assert(DQK % 64 == 0 && DV % 32 == 0 && DV <= DQK, "dims");
+    __shared__ __align__(16) uint8_t lk0[KCHUNKS * 16];
+    __shared__ __align__(16) uint8_t lk1[KCHUNKS * 16];
+    __shared__ int32_t prow[kMaxSplit];
+
+    const int tok = blockIdx.x, hg = blockIdx.y, sp = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, hq = lane >> 5;
+    const int h = hg * (32 * NW) + wv * 32 + col;
+    const int b = seq_of_token(bt, tok);
+    const int j0 = sp * split_len;
+    const int j1 = min(K, j0 + split_len);
+    const int nslots = max(0, j1 - j0);
+    const int32_t *irow = idx + (int64_t)tok * K + j0;
+    {
+        const int row0 = (int)phys_row(bt, b, 0);
+        for (int j = tid; j < nslots; j += 64 * NW) {
+            const int s = irow[j];
+            prow[j] = s >= 0 ? (int)phys_row(bt, b, s) : -1 - row0;
+        }
+    }
+    // Q^T operand: head h, dims 16ks + 8hq .. +7
+    bf16x8 qop[NKQ];
+    {
+        const uint16_t *qp = q + ((int64_t)tok * Hq + h) * DQK + 8 * hq;
+#pragma unroll
+        for (int ks = 0; ks < NKQ; ++ks)
+            qop[ks] = *(const bf16x8 *)(qp + 16 * ks);
+    }
+    f32x16 o[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        o[dt] = f32x16{};
+    // Softmax reference (log2 units) of this lane's head: fixed at the maximum of
+    // its first valid keys and never moved, so O is never rescaled inside the
+    // loop.  Exponentials relative to it stay exact in fp32/bf16 while no logit
+    // exceeds it by more than kMlaHeadroom; m_true tracks the exact maximum, and
+    // if that bound is ever broken the token is run once more with m_true as
+    // the reference (all terms then <= 1).
+    float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
+    bool over = false;
+    __syncthreads();
+
+    const int ntiles = (nslots + kTK - 1) / kTK;
+    constexpr int RG = kTK / 8;
+    auto issue = [&](int t, lds_u8 *dk, int ln) {
+#pragma unroll
+        for (int rg = wv; rg < RG; rg += NW) {
+            const int r = 8 * rg + (ln >> 3);
+            const int slot = t * kTK + r;
+            int pr = prow[slot < nslots ? slot : 0];
+            pr = pr >= 0 ? pr : -1 - pr;
+            const int cpos = (ln & 7) ^ swzg(r);
+            const uint16_t *ksrc = kc + (int64_t)pr * rs + cpos * 8;
+#pragma unroll
+            for (int cb = 0; cb < KCB; ++cb)
+                dma_b128(ksrc + cb * 64, dk + (rg * KCB + cb) * 1024);
+        }
+    };
+    lds_u8 *const LK0 = (lds_u8 *)lk0, *const LK1 = (lds_u8 *)lk1;
+    // one pass over the index list into the accumulators oa; `fixed` keeps the
+    // reference m_ref as given (the second pass), else it is set by the first
+    // valid keys and the bound is checked
+    auto run = [&](f32x16 (&oa)[NDT], bool fixed) {
+    if (ntiles > 0)
+        issue(0, LK0, lane);
+
+    for (int t = 0; t < ntiles; ++t) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const bool odd = t & 1;
+        const int ln = opaque(lane);
+        const int myslot = t * kTK + ln;
+        const uint64_t vmask = __ballot(myslot < nslots && prow[myslot < nslots ? myslot : 0] >= 0);
+        lds_u8 *tk = odd ? LK1 : LK0;
+        if (t + 1 < ntiles) {
+            if (odd)
+                issue(t + 1, LK0, ln);
+            else
+                issue(t + 1, LK1, ln);
+        }
+#pragma unroll 1
+        for (int kh = 0; kh < 2; ++kh) {
+            const int lk = opaque(lane);
+            const int cl = lk & 31, hl = lk >> 5;
+            // ---- S^T = K Q^T: A = K row r = 32kh + cl, chunk c = 2ks + hl.  With
+            // (c & 7) ^ g(r) = 2(ks & 3) ^ (hl ^ g(r)) and c >> 3 = ks >> 2, every
+            // read is one of four lane bases plus a constant offset.
+            f32x16 s;
+            {
+                constexpr int QD = 3;
+                const int r = 32 * kh + cl;
+                lds_u8 *krow = tk + (r >> 3) * KCB * 1024 + (r & 7) * 128;
+                const int gh = hl ^ swzg(r);
+                lds_u8 *kb[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    kb[m] = krow + 16 * ((2 * m) ^ gh);
+                auto lda = [&](int ks) { return *(lds_bf16x8 *)(kb[ks & 3] + 1024 * (ks >> 2)); };
+                bf16x8 ka[QD];
+#pragma unroll
+                for (int d = 0; d < QD; ++d)
+                    ka[d] = lda(d);
+                // The S chain is written as asm so that its accumulator stays in
+                // VGPRs: the AGPR half of the register file holds exactly the 256 O
+                // accumulators.  Dependent MFMAs of one opcode chain back to back;
+                // the last one is followed by the wait states a VALU read of its
+                // result needs.
+                // NSC independent chains (k-steps ks = c mod NSC) keep the MFMA pipe
+                // busy with one wave per SIMD; summed at the end
+                constexpr int NSC = 2;
+                f32x16 sc[NSC];
+#pragma unroll
+                for (int ks = 0; ks < NKQ; ++ks) {
+                    const int c = ks % NSC;
+                    if (ks < NSC)
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                                     : "=&v"(sc[c]) : "v"(ka[ks % QD]), "v"(qop[ks]));
+                    else if (ks + NSC < NKQ)
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                                     : "+v"(sc[c]) : "v"(ka[ks % QD]), "v"(qop[ks]));
+                    else if (ks + 1 < NKQ)
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                                     : "+v"(sc[c]) : "v"(ka[ks % QD]), "v"(qop[ks]));
+                    else
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+                                     "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                                     : "+v"(sc[c]) : "v"(ka[ks % QD]), "v"(qop[ks]));
+                    if (ks + QD < NKQ)
+                        ka[ks % QD] = lda(ks + QD);
+                }
+                s = sc[0];
+#pragma unroll
+                for (int c = 1; c < NSC; ++c)
+                    s += sc[c];
+            }
+            // ---- V^T operand ring: group G = lane / 16, i = lane % 16 reads row
+            // r = 32kh + 16j + 8sec + 4hl + (i >> 2) (sec = second half of the
+            // k-run), dims 32dt + 16(G & 1) + 4(i & 3) .. +3, i.e. chunk
+            // c = 4dt + 2(G & 1) + (i & 3) / 2.  Here g(r) = 4 i[3] + 2 sec + hl,
+            // so (c & 7) ^ g(r) splits into bits that depend on (dt & 1, sec) and
+            // on the lane only: four lane bases plus constant offsets.
+            constexpr int PD = 3;
+            const int G = lk >> 4, i16 = lk & 15;
+            lds_u8 *vrow = tk + kh * 4 * KCB * 1024 + (4 * hl + (i16 >> 2)) * 128 + 8 * (i16 & 1) +
+                           16 * (((i16 & 3) >> 1) ^ hl);
+            lds_u8 *vb[2][2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int sc = 0; sc < 2; ++sc)
+                    vb[a][sc] = vrow + 64 * (a ^ ((i16 >> 3) & 1)) + 32 * ((G & 1) ^ sc);
+            auto ldv = [&](int dt, int j, int sec) {
+                return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                    (lds_bf16x4 *)(vb[dt & 1][sec] + (2 * j + sec) * KCB * 1024 + (dt >> 1) * 1024));
+            };
+            auto ldv8 = [&](int step) {          // step = 2*dt + j
+                const bf16x4 lo = ldv(step >> 1, step & 1, 0), hi = ldv(step >> 1, step & 1, 1);
+                return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            };
+            bf16x8 va[PD];
+#pragma unroll
+            for (int d = 0; d < PD; ++d)
+                va[d] = ldv8(d);
+            // ---- softmax terms relative to the head's fixed reference (log2 domain)
+            float z[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = 8 * (i >> 2) + 4 * hl + (i & 3);
+                z[i] = ((vmask >> (32 * kh + m)) & 1) ? s[i] * scale_log2 : -INFINITY;
+            }
+            float mt_ = z[0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i)
+                mt_ = fmaxf(mt_, z[i]);
+            mt_ = fmaxf(mt_, shfl_xor(mt_, 32));
+            if (!fixed) {
+                m_true = fmaxf(m_true, mt_);
+                if (m_ref == -INFINITY)
+                    m_ref = mt_;
+                over = over || (mt_ > m_ref + kMlaHeadroom);
+            }
+            const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+            bf16x8 pop[2];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float pi = __builtin_amdgcn_exp2f(z[i] - base);
+                l_run += pi;
+                pop[i >> 3][i & 7] = (__bf16)pi;
+            }
+            // ---- O^T += V^T P^T
+#pragma unroll
+            for (int st = 0; st < 2 * NDT; ++st) {
+                oa[st >> 1] = mma32_bf16(va[st % PD], pop[st & 1], oa[st >> 1]);
+                if (st + PD < 2 * NDT)
+                    va[st % PD] = ldv8(st + PD);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+
+    };
+
+    // ---- epilogue: lane holds head h, dims 32dt + 8g + 4hq + {0..3} of tile dt
+    auto store = [&](const f32x16 (&oa)[NDT]) {
+    float l_tot = l_run + shfl_xor(l_run, 32);
+    if (n_split == 1) {
+        const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+        float gh = 0.0f;
+        if (!per_channel)
+            gh = sigmoidf_(bf16_bits_to_f32(gate[(int64_t)tok * Hq + h]));
+        uint16_t *op = out + ((int64_t)tok * Hq + h) * DV + 4 * hq;
+        const uint16_t *gp = gate + ((int64_t)tok * Hq + h) * DV + 4 * hq;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int d0 = 32 * dt + 8 * g;
+                uint2 gv = per_channel ? *(const uint2 *)(gp + d0) : uint2{0u, 0u};
+                uint16_t r[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t gw = i < 2 ? gv.x : gv.y;
+                    const float gl = bf16_bits_to_f32((uint16_t)(gw >> (16 * (i & 1))));
+                    const float gi = per_channel ? __builtin_amdgcn_rcpf(1.0f + __expf(-gl)) : gh;
+                    r[i] = f32_to_bf16_bits(oa[dt][4 * g + i] * inv * gi);
+                }
+                *(uint2 *)(op + d0) = uint2{(uint32_t)r[0] | ((uint32_t)r[1] << 16),
+                                            (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+            }
+        if (lse && hq == 0)
+            lse[(int64_t)tok * Hq + h] = l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
+    } else {
+        float *pp = part + (((int64_t)tok * n_split + sp) * Hq + h) * (DV + 4) + 4 * hq;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *(f32x4 *)(pp + 32 * dt + 8 * g) =
+                    f32x4{oa[dt][4 * g], oa[dt][4 * g + 1], oa[dt][4 * g + 2], oa[dt][4 * g + 3]};
+        if (hq == 0) {
+            pp[DV] = m_ref;
+            pp[DV + 1] = l_tot;
+        }
+    }
+    };
+
+    run(o, false);
+    store(o);
+    if (__syncthreads_or(over)) {
+        // rare: some head's logits rose more than the headroom above its first
+        // keys; rerun with the exact maximum as the reference (every term <= 1)
+        f32x16 o2[NDT];
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            o2[dt] = f32x16{};
+        m_ref = m_true;
+        l_run = 0.0f;
+        run(o2, true);
+        store(o2);
+    }
+}
+
 // Merge split partials by log-sum-exp, then gate; one block per (token, head).
 __global__ __launch_bounds__(128) void attn_combine_kernel(int Hq, int DV, int n_split, const float *__restrict__ part,
                                                           const void *__restrict__ gate, int per_channel, int is_bf16,
@@ -517,7 +813,13 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const voi
         else if (d_qk == 128 && d_v == 128 && mla)
             e = launch_bf16<128, 128, true>(bt, pl, q, Hq, k_cache, v_cache, row_stride, indices, k, gate,
                                             per_channel, sl2, out, lse, part, split_len, st);
-        else if (d_qk == 576 && d_v == 512 && mla)
+        else if (d_qk == 576 && d_v == 512 && mla && Hq % 128 == 0) {
+            hipLaunchKernelGGL((attn_mla_kernel<576, 512>), dim3(bt.total_q, Hq / 128, pl.n_split), dim3(256), 0, st,
+                               bt, (const uint16_t *)q, Hq, (const uint16_t *)k_cache, row_stride, indices, k,
+                               (const uint16_t *)gate, per_channel, sl2, (uint16_t *)out, lse, part, pl.n_split,
+                               split_len);
+            e = hipGetLastError();
+        } else if (d_qk == 576 && d_v == 512 && mla)
             e = launch_bf16<576, 512, true>(bt, pl, q, Hq, k_cache, v_cache, row_stride, indices, k, gate,
                                             per_channel, sl2, out, lse, part, split_len, st);
     } else if (dtype == 0) {

@@ -73,32 +73,8 @@ constexpr int kIdxWaves = 4;
 constexpr int kIdxTileKeys = 64;
 constexpr int kIdxMaxChunk = 8192;     // keys per prefill workgroup, at most
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) float lds_f32;
 
-// Direct global->LDS loads (global_load_lds): lane i's 16 (resp. 4) bytes land
-// at lds + 16*i (resp. 4*i); lds is wave-uniform and goes through M0, which is
-// saved and restored.  Written as asm so the compiler does not track them:
-// its LDS-DMA tracking would put a full vmcnt wait in front of every LDS read
-// of the ring.  Completion is awaited explicitly with s_waitcnt vmcnt, and
-// loads unknown to the compiler can only make its own waits stricter.
-__device__ __forceinline__ void dma_b128(const void *src, const lds_u8 *lds)
-{
-    const uint32_t base = (uint32_t)(uintptr_t)lds;
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                 "global_load_lds_dwordx4 %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(src), "s"(base) : "memory");
-}
-__device__ __forceinline__ void dma_b32(const void *src, const lds_u8 *lds)
-{
-    const uint32_t base = (uint32_t)(uintptr_t)lds;
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-                 "global_load_lds_dword %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved) : "v"(src), "s"(base) : "memory");
-}
 
 // ------------------------------------------------------------------ prefill
 template <int DT, int H, int D>

@@ -152,6 +152,33 @@ __device__ __forceinline__ int opaque(int v)
     return v;
 }
 
+// ----------------------------------------------------------------- LDS DMA
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// Direct global->LDS loads (global_load_lds): lane i's 16 (resp. 4) bytes land
+// at lds + 16*i (resp. 4*i); lds is wave-uniform and goes through M0, which is
+// saved and restored.  Written as asm so the compiler does not track them:
+// its LDS-DMA tracking would put a full vmcnt wait in front of every LDS read
+// while a prefetch into another buffer is in flight.  Completion is awaited explicitly with s_waitcnt vmcnt, and
+// loads unknown to the compiler can only make its own waits stricter.
+__device__ __forceinline__ void dma_b128(const void *src, const lds_u8 *lds)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)lds;
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(src), "s"(base) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void *src, const lds_u8 *lds)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)lds;
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+                 "global_load_lds_dword %1, off\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(src), "s"(base) : "memory");
+}
+
 // ------------------------------------------------------------ wave helpers
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m)
