@@ -234,3 +234,58 @@ def test_runs_are_bitwise_deterministic():
     sa, sb = a.scores.cpu().numpy(), b.scores.cpu().numpy()
     for r in range(spec.T):
         assert np.array_equal(sa[r, :n[r]], sb[r, :n[r]])
+
+
+# ------------------------------------------------- softmax reference bound
+
+def _sharpen_to_last_selected(wl, pl, gain):
+    """Point each query head at the key row of its highest selected position, scaled so
+    that logit rises far (tens of nats) above those of the earlier keys."""
+    spec = wl.spec
+    idx = pl.indices.cpu().numpy()
+    seq, pos, n = P.token_geometry(spec)
+    kc = wl.k_cache.view(-1, wl.kv_row_stride)
+    for t in range(spec.T):
+        valid = idx[t][idx[t] >= 0]
+        s_last = int(valid.max())
+        row = P.logical_rows(wl, int(seq[t]), s_last + 1)[s_last]
+        kv = kc[row, :spec.d_qk].float()
+        q = kv / kv.norm() * gain
+        wl.q[t] = q.to(wl.q.dtype).unsqueeze(0).expand(spec.Hq, -1)
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode-split"])
+def test_latent_attention_logit_far_above_first_keys(mode):
+    """A logit ~70 nats above the first tile's: the latent kernel must rerun with the exact
+    maximum as its reference and still match the oracle."""
+    if mode == "prefill":
+        spec = W.chunked_prefill_mla(cached=3000, T=64).replace(seed=61)
+    else:
+        spec = W.long_decode_mla(B=4, lo=5000, hi=9000, short_at=1).replace(seed=62)
+    P.say(f"[rerun-{mode}] T={spec.T} max_ctx={spec.max_ctx}")
+    wl = W.generate(spec, DEV)
+    pl = run(wl, stages=("indexer", "topk"))
+    _sharpen_to_last_selected(wl, pl, gain=24.0 * 70.0)
+    # the data must break the kernel's bound: some logit (log2 units) exceeds the
+    # maximum over the first 32 selected keys by more than 64
+    idx_t = pl.indices.long()
+    seq, pos, n = P.token_geometry(spec)
+    jump = 0.0
+    for t in range(spec.T):
+        sel = idx_t[t][idx_t[t] >= 0]
+        rows = P.logical_rows(wl, int(seq[t]), int(n[t]))[sel]
+        k = wl.k_cache.view(-1, wl.kv_row_stride)[rows, :spec.d_qk].float()
+        z = (k @ wl.q[t, 0].float()) * spec.softmax_scale * 1.4426950408889634
+        jump = max(jump, float(z.max() - z[:32].max()))
+    assert jump > 64.0, jump
+    pl.attn()
+    torch.cuda.synchronize()
+    rows = list(range(spec.T))
+    idx = pl.indices.cpu().numpy()
+    ainp, aidx = P.attn_inputs(wl, rows, idx)
+    ref_out, ref_lse = O.sparse_attn(ainp, aidx, None, spec.softmax_scale, with_lse=True)
+    out = pl.out.float().cpu().numpy()
+    assert np.isfinite(out).all()
+    w = P.check_attn(out, ref_out, P.RTOL["bf16"])
+    assert P.close(pl.lse.cpu().numpy(), ref_lse, P.RTOL["bf16"]).all()
+    P.say(f"[rerun-{mode}] ok: worst attn rel {w:.2e}")
