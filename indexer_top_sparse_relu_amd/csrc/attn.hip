@@ -325,8 +325,6 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
 // in two phases of 32 lanes (bit 5), over 64 four-byte banks; under that
 // (measured) rule g makes both the K reads (32 rows of one chunk per wave
 // half) and the V reads (4 rows x 4 chunks per phase) conflict-free.
-constexpr float kMlaHeadroom = 64.0f;   // log2 units a logit may exceed the softmax reference by
-
 __device__ __forceinline__ int swzg(int r) { return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1); }
 
 template <int DQK, int DV>
@@ -340,10 +338,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int NDT = DV / 32;            // 32-dim tiles of O^T
     constexpr int KCH = DQK / 8;            // 16-byte chunks per row
     constexpr int KCB = KCH / 8;            // 8-chunk blocks per row
-    constexpr int KCHUNKS = kTK * KCH;
+    constexpr int TK = 32;                  // keys per tile (one 32x32 S^T tile)
+    constexpr int KCHUNKS = TK * KCH;
     static_assert(DQK % 64 == 0 && DV % 32 == 0 && DV <= DQK, "dims");
+    // a ring of four tiles: the gather of tile t+3 is issued while tile t is used
     __shared__ __align__(16) uint8_t lk0[KCHUNKS * 16];
     __shared__ __align__(16) uint8_t lk1[KCHUNKS * 16];
+    __shared__ __align__(16) uint8_t lk2[KCHUNKS * 16];
+    __shared__ __align__(16) uint8_t lk3[KCHUNKS * 16];
     __shared__ int32_t prow[kMaxSplit];
 
     const int tok = blockIdx.x, hg = blockIdx.y, sp = blockIdx.z;
@@ -377,21 +379,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         o[dt] = f32x16{};
     // Softmax reference (log2 units) of this lane's head: fixed at the maximum of
     // its first valid keys and never moved, so O is never rescaled inside the
-    // loop.  Exponentials relative to it stay exact in fp32/bf16 while no logit
-    // exceeds it by more than kMlaHeadroom; m_true tracks the exact maximum, and
-    // if that bound is ever broken the token is run once more with m_true as
-    // the reference (all terms then <= 1).
+    // loop and later keys need no maximum at all.  Terms relative to it are exact
+    // in fp32/bf16 while none exceeds 2^64; a sum above that (or a non-finite
+    // result) sends the workgroup through a rerun: one pass for the exact
+    // maximum, one with it as the reference (all terms then <= 1).
     float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
     bool over = false;
     __syncthreads();
 
-    const int ntiles = (nslots + kTK - 1) / kTK;
-    constexpr int RG = kTK / 8;
+    const int ntiles = (nslots + TK - 1) / TK;
+    constexpr int RG = TK / 8;
+    static_assert(RG == NW, "one 8-row group per wave");
+    // gather of tile t: wave wv loads row group wv (8 rows, KCB blocks of 1 KB):
+    // exactly KCB direct loads per wave per tile
     auto issue = [&](int t, lds_u8 *dk, int ln) {
-#pragma unroll
-        for (int rg = wv; rg < RG; rg += NW) {
+        {
+            const int rg = wv;
             const int r = 8 * rg + (ln >> 3);
-            const int slot = t * kTK + r;
+            const int slot = t * TK + r;
             int pr = prow[slot < nslots ? slot : 0];
             pr = pr >= 0 ? pr : -1 - pr;
             const int cpos = (ln & 7) ^ swzg(r);
@@ -401,30 +406,37 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 dma_b128(ksrc + cb * 64, dk + (rg * KCB + cb) * 1024);
         }
     };
-    lds_u8 *const LK0 = (lds_u8 *)lk0, *const LK1 = (lds_u8 *)lk1;
-    // one pass over the index list into the accumulators oa; `fixed` keeps the
-    // reference m_ref as given (the second pass), else it is set by the first
-    // valid keys and the bound is checked
-    auto run = [&](f32x16 (&oa)[NDT], bool fixed) {
-    if (ntiles > 0)
-        issue(0, LK0, lane);
+    auto buf = [&](int t) -> lds_u8 * {
+        const int i = t & 3;
+        return i == 0 ? (lds_u8 *)lk0 : i == 1 ? (lds_u8 *)lk1 : i == 2 ? (lds_u8 *)lk2 : (lds_u8 *)lk3;
+    };
+    // One pass over the index list.  mode 0: reference from the first valid
+    // keys, accumulate into oa; mode 1: exact maximum only (m_true), no P V;
+    // mode 2: reference m_ref as given, accumulate into oa.
+    auto run = [&](f32x16 (&oa)[NDT], const int mode) {
+#pragma unroll
+    for (int t = 0; t < 3; ++t)
+        if (t < ntiles)
+            issue(t, buf(t), lane);
 
     for (int t = 0; t < ntiles; ++t) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const bool odd = t & 1;
+        // Tile t's loads were followed by those of the (up to two) next tiles,
+        // KCB per wave each, and by no other memory operation of this loop.
+        if (t + 2 < ntiles)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * KCB) : "memory");
+        else if (t + 1 < ntiles)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KCB) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();            // tile t complete; the buffer of tile t-1 is free
         const int ln = opaque(lane);
-        const int myslot = t * kTK + ln;
+        const int myslot = t * TK + (ln & 31);
         const uint64_t vmask = __ballot(myslot < nslots && prow[myslot < nslots ? myslot : 0] >= 0);
-        lds_u8 *tk = odd ? LK1 : LK0;
-        if (t + 1 < ntiles) {
-            if (odd)
-                issue(t + 1, LK0, ln);
-            else
-                issue(t + 1, LK1, ln);
-        }
-#pragma unroll 1
-        for (int kh = 0; kh < 2; ++kh) {
+        lds_u8 *tk = buf(t);
+        if (t + 3 < ntiles)
+            issue(t + 3, buf(t + 3), ln);
+        {
+            constexpr int kh = 0;
             const int lk = opaque(lane);
             const int cl = lk & 31, hl = lk >> 5;
             // ---- S^T = K Q^T: A = K row r = 32kh + cl, chunk c = 2ks + hl.  With
@@ -478,67 +490,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 for (int c = 1; c < NSC; ++c)
                     s += sc[c];
             }
-            // ---- V^T operand ring: group G = lane / 16, i = lane % 16 reads row
-            // r = 32kh + 16j + 8sec + 4hl + (i >> 2) (sec = second half of the
-            // k-run), dims 32dt + 16(G & 1) + 4(i & 3) .. +3, i.e. chunk
-            // c = 4dt + 2(G & 1) + (i & 3) / 2.  Here g(r) = 4 i[3] + 2 sec + hl,
-            // so (c & 7) ^ g(r) splits into bits that depend on (dt & 1, sec) and
-            // on the lane only: four lane bases plus constant offsets.
-            constexpr int PD = 3;
-            const int G = lk >> 4, i16 = lk & 15;
-            lds_u8 *vrow = tk + kh * 4 * KCB * 1024 + (4 * hl + (i16 >> 2)) * 128 + 8 * (i16 & 1) +
-                           16 * (((i16 & 3) >> 1) ^ hl);
-            lds_u8 *vb[2][2];
-#pragma unroll
-            for (int a = 0; a < 2; ++a)
-#pragma unroll
-                for (int sc = 0; sc < 2; ++sc)
-                    vb[a][sc] = vrow + 64 * (a ^ ((i16 >> 3) & 1)) + 32 * ((G & 1) ^ sc);
-            auto ldv = [&](int dt, int j, int sec) {
-                return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                    (lds_bf16x4 *)(vb[dt & 1][sec] + (2 * j + sec) * KCB * 1024 + (dt >> 1) * 1024));
+            // ---- softmax terms against the head's reference (log2 units)
+            const bool full = (uint32_t)(vmask >> (32 * kh)) == 0xFFFFFFFFu;
+            auto valid = [&](int i) {
+                return full || ((vmask >> (32 * kh + 8 * (i >> 2) + 4 * hl + (i & 3))) & 1);
             };
-            auto ldv8 = [&](int step) {          // step = 2*dt + j
-                const bf16x4 lo = ldv(step >> 1, step & 1, 0), hi = ldv(step >> 1, step & 1, 1);
-                return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            };
-            bf16x8 va[PD];
+            if (mode == 1 || (mode == 0 && m_ref == -INFINITY)) {
+                float mx = -INFINITY;
 #pragma unroll
-            for (int d = 0; d < PD; ++d)
-                va[d] = ldv8(d);
-            // ---- softmax terms relative to the head's fixed reference (log2 domain)
-            float z[16];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int m = 8 * (i >> 2) + 4 * hl + (i & 3);
-                z[i] = ((vmask >> (32 * kh + m)) & 1) ? s[i] * scale_log2 : -INFINITY;
+                for (int i = 0; i < 16; ++i)
+                    if (valid(i))
+                        mx = fmaxf(mx, s[i] * scale_log2);
+                mx = fmaxf(mx, shfl_xor(mx, 32));
+                if (mode == 1)
+                    m_true = fmaxf(m_true, mx);
+                else
+                    m_ref = mx;
             }
-            float mt_ = z[0];
+            if (mode != 1) {
+                // ---- V^T operand ring: group G = lane / 16, i = lane % 16 reads row
+                // r = 32kh + 16j + 8sec + 4hl + (i >> 2) (sec = second half of the
+                // k-run), dims 32dt + 16(G & 1) + 4(i & 3) .. +3, i.e. chunk
+                // c = 4dt + 2(G & 1) + (i & 3) / 2.  Here g(r) = 4 i[3] + 2 sec + hl,
+                // so (c & 7) ^ g(r) splits into bits that depend on (dt & 1, sec) and
+                // on the lane only: four lane bases plus constant offsets.
+                constexpr int PD = 3;
+                const int G = lk >> 4, i16 = lk & 15;
+                lds_u8 *vrow = tk + kh * 4 * KCB * 1024 + (4 * hl + (i16 >> 2)) * 128 + 8 * (i16 & 1) +
+                               16 * (((i16 & 3) >> 1) ^ hl);
+                lds_u8 *vb[2][2];
 #pragma unroll
-            for (int i = 1; i < 16; ++i)
-                mt_ = fmaxf(mt_, z[i]);
-            mt_ = fmaxf(mt_, shfl_xor(mt_, 32));
-            if (!fixed) {
-                m_true = fmaxf(m_true, mt_);
-                if (m_ref == -INFINITY)
-                    m_ref = mt_;
-                over = over || (mt_ > m_ref + kMlaHeadroom);
-            }
-            const float base = m_ref == -INFINITY ? 0.0f : m_ref;
-            bf16x8 pop[2];
+                for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float pi = __builtin_amdgcn_exp2f(z[i] - base);
-                l_run += pi;
-                pop[i >> 3][i & 7] = (__bf16)pi;
-            }
-            // ---- O^T += V^T P^T
+                    for (int sc = 0; sc < 2; ++sc)
+                        vb[a][sc] = vrow + 64 * (a ^ ((i16 >> 3) & 1)) + 32 * ((G & 1) ^ sc);
+                auto ldv = [&](int dt, int j, int sec) {
+                    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4 *)(vb[dt & 1][sec] + (2 * j + sec) * KCB * 1024 + (dt >> 1) * 1024));
+                };
+                auto ldv8 = [&](int step) {          // step = 2*dt + j
+                    const bf16x4 lo = ldv(step >> 1, step & 1, 0), hi = ldv(step >> 1, step & 1, 1);
+                    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                };
+                bf16x8 va[PD];
 #pragma unroll
-            for (int st = 0; st < 2 * NDT; ++st) {
-                oa[st >> 1] = mma32_bf16(va[st % PD], pop[st & 1], oa[st >> 1]);
-                if (st + PD < 2 * NDT)
-                    va[st % PD] = ldv8(st + PD);
-                __builtin_amdgcn_sched_barrier(0);
+                for (int d = 0; d < PD; ++d)
+                    va[d] = ldv8(d);
+                const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+                bf16x8 pop[2];
+                if (full) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float pi = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -base));
+                        l_run += pi;
+                        pop[i >> 3][i & 7] = (__bf16)pi;
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const float pi = valid(i) ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -base)) : 0.0f;
+                        l_run += pi;
+                        pop[i >> 3][i & 7] = (__bf16)pi;
+                    }
+                }
+                // ---- O^T += V^T P^T
+#pragma unroll
+                for (int st = 0; st < 2 * NDT; ++st) {
+                    oa[st >> 1] = mma32_bf16(va[st % PD], pop[st & 1], oa[st >> 1]);
+                    if (st + PD < 2 * NDT)
+                        va[st % PD] = ldv8(st + PD);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
         }
     }
@@ -548,6 +570,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ---- epilogue: lane holds head h, dims 32dt + 8g + 4hq + {0..3} of tile dt
     auto store = [&](const f32x16 (&oa)[NDT]) {
     float l_tot = l_run + shfl_xor(l_run, 32);
+    float probe = 0.0f;                 // turns NaN if any result is not finite
     if (n_split == 1) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         float gh = 0.0f;
@@ -567,7 +590,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     const uint32_t gw = i < 2 ? gv.x : gv.y;
                     const float gl = bf16_bits_to_f32((uint16_t)(gw >> (16 * (i & 1))));
                     const float gi = per_channel ? __builtin_amdgcn_rcpf(1.0f + __expf(-gl)) : gh;
-                    r[i] = f32_to_bf16_bits(oa[dt][4 * g + i] * inv * gi);
+                    const float y = oa[dt][4 * g + i] * inv * gi;
+                    probe = fmaf(y, 0.0f, probe);
+                    r[i] = f32_to_bf16_bits(y);
                 }
                 *(uint2 *)(op + d0) = uint2{(uint32_t)r[0] | ((uint32_t)r[1] << 16),
                                             (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
@@ -579,28 +604,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
-                *(f32x4 *)(pp + 32 * dt + 8 * g) =
-                    f32x4{oa[dt][4 * g], oa[dt][4 * g + 1], oa[dt][4 * g + 2], oa[dt][4 * g + 3]};
+            for (int g = 0; g < 4; ++g) {
+                const f32x4 v4 = f32x4{oa[dt][4 * g], oa[dt][4 * g + 1], oa[dt][4 * g + 2], oa[dt][4 * g + 3]};
+                probe = fmaf(v4[0] + v4[1] + v4[2] + v4[3], 0.0f, probe);
+                *(f32x4 *)(pp + 32 * dt + 8 * g) = v4;
+            }
         if (hq == 0) {
             pp[DV] = m_ref;
             pp[DV + 1] = l_tot;
         }
     }
+    return !(l_tot <= 0x1p64f) || probe != 0.0f;
     };
 
-    run(o, false);
-    store(o);
+    run(o, 0);
+    over = store(o);
     if (__syncthreads_or(over)) {
-        // rare: some head's logits rose more than the headroom above its first
-        // keys; rerun with the exact maximum as the reference (every term <= 1)
+        // rare: some head's terms outgrew 2^64 relative to its first keys; find
+        // the exact maximum, then rerun with it as the reference (terms <= 1)
         f32x16 o2[NDT];
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
             o2[dt] = f32x16{};
+        run(o2, 1);
+        __syncthreads();
         m_ref = m_true;
         l_run = 0.0f;
-        run(o2, true);
+        run(o2, 2);
         store(o2);
     }
 }

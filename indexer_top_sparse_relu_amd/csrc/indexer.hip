@@ -298,14 +298,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         auto issue = [&](int tt, int ln) {
             const int st = tt % KST;
             const int t0 = kb0 + tt * kIdxTileKeys;
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const int blk = u * kIdxWaves + wv;
-                const int r = blk * 8 + (ln >> 3);
-                const int c = (ln & 7) ^ ((r >> 1) & 7);
-                dma_b128(k_idx + krow(t0 + r) * 128 + c * 16, stage(st) + blk * 1024);
-            }
-            dma_b32(k_scale + krow(t0 + ln), (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * 64));
+            // all three physical rows first (one LDS round trip), then the loads
+            const int r0 = wv * 8 + (ln >> 3), r1 = (kIdxWaves + wv) * 8 + (ln >> 3);
+            const int64_t p0 = krow(t0 + r0), p1 = krow(t0 + r1), p2 = krow(t0 + ln);
+            dma_b128(k_idx + p0 * 128 + ((ln & 7) ^ ((r0 >> 1) & 7)) * 16, stage(st) + wv * 1024);
+            dma_b128(k_idx + p1 * 128 + ((ln & 7) ^ ((r1 >> 1) & 7)) * 16, stage(st) + (kIdxWaves + wv) * 1024);
+            dma_b32(k_scale + p2, (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * 64));
         };
 
         // Scores go out through a buffer resource spanning this wave's token rows:
