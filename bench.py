@@ -117,7 +117,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="chunked_prefill_mla_128k")
-    ap.add_argument("--cpu-sample", type=int, default=48, help="query tokens the oracle baseline runs")
+    ap.add_argument("--cpu-sample", type=int, default=192, help="query tokens the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a copy kernel of known size (for HBM counter calibration)")

@@ -67,15 +67,25 @@ def _one(pattern: str) -> str:
 
 
 def kernel_stats(dirpath: str):
+    """Per path kernel: calls, average, min and max from the stats table, plus the median
+    duration from the kernel trace (the average includes the cold first launches)."""
     rows = list(csv.DictReader(open(_one(os.path.join(dirpath, "**", "*kernel_stats.csv")))))
+    durs = {}
+    trace = glob.glob(os.path.join(dirpath, "**", "*kernel_trace.csv"), recursive=True)
+    if trace:
+        for r in csv.DictReader(open(sorted(trace)[0])):
+            if stage_of(r["Kernel_Name"]) is not None:
+                durs.setdefault(r["Kernel_Name"], []).append(
+                    (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6)
     out = []
     for r in rows:
         name = r["Name"]
         if stage_of(name) is None:
             continue
+        d = durs.get(name)
         out.append({"kernel": short_name(name), "calls": int(r["Calls"]),
-                    "avg_ms": float(r["AverageNs"]) / 1e6, "min_ms": float(r["MinNs"]) / 1e6,
-                    "max_ms": float(r["MaxNs"]) / 1e6})
+                    "avg_ms": float(r["AverageNs"]) / 1e6, "median_ms": statistics.median(d) if d else None,
+                    "min_ms": float(r["MinNs"]) / 1e6, "max_ms": float(r["MaxNs"]) / 1e6})
     return out
 
 
@@ -124,9 +134,11 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int):
 def _stats_md(workload, command, stats):
     lines = [f"# Kernel stats — {workload}", "", "Command (repository root, one MI355X):", "", "```",
              "export TMPDIR=/tmp", command, "```", "",
-             "| kernel | calls | avg ms | min ms | max ms |", "|---|---|---|---|---|"]
+             "| kernel | calls | avg ms | median ms | min ms | max ms |", "|---|---|---|---|---|---|"]
     for s in sorted(stats, key=lambda s: -s["avg_ms"]):
-        lines.append(f"| `{s['kernel']}` | {s['calls']} | {s['avg_ms']:.3f} | {s['min_ms']:.3f} | {s['max_ms']:.3f} |")
+        med = "—" if s["median_ms"] is None else f"{s['median_ms']:.3f}"
+        lines.append(f"| `{s['kernel']}` | {s['calls']} | {s['avg_ms']:.3f} | {med} | {s['min_ms']:.3f} | "
+                     f"{s['max_ms']:.3f} |")
     return "\n".join(lines) + "\n"
 
 
