@@ -365,14 +365,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             prow[j] = s >= 0 ? (int)phys_row(bt, b, s) : -1 - row0;
         }
     }
-    // Q^T operand: head h, dims 16ks + 8hq .. +7
-    bf16x8 qop[NKQ];
-    {
-        const uint16_t *qp = q + ((int64_t)tok * Hq + h) * DQK + 8 * hq;
-#pragma unroll
-        for (int ks = 0; ks < NKQ; ++ks)
-            qop[ks] = *(const bf16x8 *)(qp + 16 * ks);
-    }
     f32x16 o[NDT];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
@@ -414,6 +406,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // keys, accumulate into oa; mode 1: exact maximum only (m_true), no P V;
     // mode 2: reference m_ref as given, accumulate into oa.
     auto run = [&](f32x16 (&oa)[NDT], const int mode) {
+    // Q^T operand: head h, dims 16ks + 8hq .. +7.  Loaded per pass, so that
+    // nothing of it is live in the epilogue (the rare rerun loads it again).
+    bf16x8 qop[NKQ];
+    {
+        const uint16_t *qp = q + ((int64_t)tok * Hq + h) * DQK + 8 * hq;
+#pragma unroll
+        for (int ks = 0; ks < NKQ; ++ks)
+            qop[ks] = *(const bf16x8 *)(qp + 16 * ks);
+    }
 #pragma unroll
     for (int t = 0; t < 3; ++t)
         if (t < ntiles)
