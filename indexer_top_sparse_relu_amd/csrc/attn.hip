@@ -419,6 +419,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     for (int t = 0; t < 3; ++t)
         if (t < ntiles)
             issue(t, buf(t), lane);
+    // One wait the compiler can see for the Q loads (and the first tiles).  Its
+    // own tracking does not count the asm tile loads, and without this it would
+    // keep the Q loads pending into the loop and wait on them before every MFMA
+    // of the S chain, which in hardware also drains the tile loads in flight.
+    __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0), expcnt and lgkmcnt unconstrained
 
     for (int t = 0; t < ntiles; ++t) {
         // Tile t's loads were followed by those of the (up to two) next tiles,
