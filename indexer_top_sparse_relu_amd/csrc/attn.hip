@@ -47,6 +47,10 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 // Swizzle of tile row r: logical chunk c of the row sits at chunk position
 // (c & ~7) | ((c & 7) ^ f(r)) of its 8-chunk block, f(r) = r & 7.  A K-operand
@@ -342,10 +346,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int KCHUNKS = TK * KCH;
     static_assert(DQK % 64 == 0 && DV % 32 == 0 && DV <= DQK, "dims");
     // a ring of four tiles: the gather of tile t+3 is issued while tile t is used
-    __shared__ __align__(16) uint8_t lk0[KCHUNKS * 16];
-    __shared__ __align__(16) uint8_t lk1[KCHUNKS * 16];
-    __shared__ __align__(16) uint8_t lk2[KCHUNKS * 16];
-    __shared__ __align__(16) uint8_t lk3[KCHUNKS * 16];
+    // (one array: after the last tile it also stages the gated output rows)
+    __shared__ __align__(16) uint8_t lkr[4 * KCHUNKS * 16];
     __shared__ int32_t prow[kMaxSplit];
 
     const int tok = blockIdx.x, hg = blockIdx.y, sp = blockIdx.z;
@@ -375,7 +377,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // in fp32/bf16 while none exceeds 2^64; a sum above that (or a non-finite
     // result) sends the workgroup through a rerun: one pass for the exact
     // maximum, one with it as the reference (all terms then <= 1).
-    float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
+    // l_run sums the terms of keys 0..15 of each tile, l_run2 those of keys
+    // 16..31 (two independent add chains)
+    float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f, l_run2 = 0.0f;
     bool over = false;
     __syncthreads();
 
@@ -383,24 +387,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int RG = TK / 8;
     static_assert(RG == NW, "one 8-row group per wave");
     // gather of tile t: wave wv loads row group wv (8 rows, KCB blocks of 1 KB):
-    // exactly KCB direct loads per wave per tile
+    // exactly KCB direct loads per wave per tile; src_of gives this lane's
+    // source (block 0) and the wave's LDS destination is dk + wv * KCB * 1024
+    auto src_of = [&](int t, int ln) -> const uint16_t * {
+        const int r = 8 * wv + (ln >> 3);
+        const int slot = t * TK + r;
+        int pr = prow[slot < nslots ? slot : 0];
+        pr = pr >= 0 ? pr : -1 - pr;
+        const int cpos = (ln & 7) ^ swzg(r);
+        return kc + (int64_t)pr * rs + cpos * 8;
+    };
+    // slot-validity entry of key (ln & 31) of tile t (-1 past the list)
+    auto vm_val = [&](int t, int ln) {
+        const int sl = t * TK + (ln & 31);
+        const int v = prow[sl < nslots ? sl : 0];
+        return sl < nslots ? v : -1;
+    };
     auto issue = [&](int t, lds_u8 *dk, int ln) {
-        {
-            const int rg = wv;
-            const int r = 8 * rg + (ln >> 3);
-            const int slot = t * TK + r;
-            int pr = prow[slot < nslots ? slot : 0];
-            pr = pr >= 0 ? pr : -1 - pr;
-            const int cpos = (ln & 7) ^ swzg(r);
-            const uint16_t *ksrc = kc + (int64_t)pr * rs + cpos * 8;
+        const uint16_t *ksrc = src_of(t, ln);
 #pragma unroll
-            for (int cb = 0; cb < KCB; ++cb)
-                dma_b128(ksrc + cb * 64, dk + (rg * KCB + cb) * 1024);
-        }
+        for (int cb = 0; cb < KCB; ++cb)
+            dma_b128(ksrc + cb * 64, dk + (wv * KCB + cb) * 1024);
     };
     auto buf = [&](int t) -> lds_u8 * {
-        const int i = t & 3;
-        return i == 0 ? (lds_u8 *)lk0 : i == 1 ? (lds_u8 *)lk1 : i == 2 ? (lds_u8 *)lk2 : (lds_u8 *)lk3;
+        return (lds_u8 *)lkr + (t & 3) * (KCHUNKS * 16);
     };
     // One pass over the index list.  mode 0: reference from the first valid
     // keys, accumulate into oa; mode 1: exact maximum only (m_true), no P V;
@@ -408,6 +418,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto run = [&](f32x16 (&oa)[NDT], const int mode) {
     // Q^T operand: head h, dims 16ks + 8hq .. +7.  Loaded per pass, so that
     // nothing of it is live in the epilogue (the rare rerun loads it again).
+    bool have_ref = false;      // mode 0: the reference has been set from some valid key
     bf16x8 qop[NKQ];
     {
         const uint16_t *qp = q + ((int64_t)tok * Hq + h) * DQK + 8 * hq;
@@ -425,6 +436,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // of the S chain, which in hardware also drains the tile loads in flight.
     __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0), expcnt and lgkmcnt unconstrained
 
+    // The next tile's key mask entry and the source of the loads of tile t+4
+    // are read from LDS inside the S chain of tile t, where the MFMAs cover the
+    // read latency, and used one iteration later.
+    int vm_cur = vm_val(0, lane);
+    const uint16_t *src_cur = src_of(3, lane);
     for (int t = 0; t < ntiles; ++t) {
         // Tile t's loads were followed by those of the (up to two) next tiles,
         // KCB per wave each, and by no other memory operation of this loop.
@@ -436,11 +452,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();            // tile t complete; the buffer of tile t-1 is free
         const int ln = opaque(lane);
-        const int myslot = t * TK + (ln & 31);
-        const uint64_t vmask = __ballot(myslot < nslots && prow[myslot < nslots ? myslot : 0] >= 0);
+        const uint64_t vmask = __ballot(vm_cur >= 0);
         lds_u8 *tk = buf(t);
-        if (t + 3 < ntiles)
-            issue(t + 3, buf(t + 3), ln);
+        // Tile t+3's loads are spread over the S chain (one per 4 MFMAs): issued
+        // together, the four waves' loads back up the memory pipeline and each
+        // wave stalls at issue with its MFMAs idle.
+        const bool nxt = t + 3 < ntiles;
+        const uint16_t *nsrc = src_cur;
+        lds_u8 *ndk = buf(t + 3) + wv * KCB * 1024;
+        static_assert(4 * (KCB - 1) < NKQ, "one tile load per 4 S-chain MFMAs");
         {
             constexpr int kh = 0;
             const int lk = opaque(lane);
@@ -450,7 +470,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             // read is one of four lane bases plus a constant offset.
             f32x16 s;
             {
-                constexpr int QD = 3;
+                constexpr int QD = 6;
                 const int r = 32 * kh + cl;
                 lds_u8 *krow = tk + (r >> 3) * KCB * 1024 + (r & 7) * 128;
                 const int gh = hl ^ swzg(r);
@@ -470,7 +490,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 // result needs.
                 // NSC independent chains (k-steps ks = c mod NSC) keep the MFMA pipe
                 // busy with one wave per SIMD; summed at the end
-                constexpr int NSC = 2;
+                constexpr int NSC = 1;
                 f32x16 sc[NSC];
 #pragma unroll
                 for (int ks = 0; ks < NKQ; ++ks) {
@@ -490,6 +510,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                      : "+v"(sc[c]) : "v"(ka[ks % QD]), "v"(qop[ks]));
                     if (ks + QD < NKQ)
                         ka[ks % QD] = lda(ks + QD);
+                    if (ks % 4 == 0 && ks / 4 < KCB && nxt)
+                        dma_b128(nsrc + (ks / 4) * 64, ndk + (ks / 4) * 1024);
+                    if (ks == NKQ - 12)
+                        vm_cur = vm_val(t + 1, ln);
+                    if (ks == NKQ - 8)
+                        src_cur = src_of(t + 4, ln);
                 }
                 s = sc[0];
 #pragma unroll
@@ -501,17 +527,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             auto valid = [&](int i) {
                 return full || ((vmask >> (32 * kh + 8 * (i >> 2) + 4 * hl + (i & 3))) & 1);
             };
-            if (mode == 1 || (mode == 0 && m_ref == -INFINITY)) {
+            // (have_ref and the key mask are wave-uniform: every head of the wave
+            // sees the same keys, so this is a scalar branch taken once in mode 0)
+            if (mode == 1 || (mode == 0 && !have_ref)) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (valid(i))
-                        mx = fmaxf(mx, s[i] * scale_log2);
+                    mx = fmaxf(mx, valid(i) ? s[i] * scale_log2 : -INFINITY);
                 mx = fmaxf(mx, shfl_xor(mx, 32));
-                if (mode == 1)
+                if (mode == 1) {
                     m_true = fmaxf(m_true, mx);
-                else
+                } else {
                     m_ref = mx;
+                    have_ref = (uint32_t)(vmask >> (32 * kh)) != 0u;
+                }
             }
             if (mode != 1) {
                 // ---- V^T operand ring: group G = lane / 16, i = lane % 16 reads row
@@ -520,7 +549,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 // c = 4dt + 2(G & 1) + (i & 3) / 2.  Here g(r) = 4 i[3] + 2 sec + hl,
                 // so (c & 7) ^ g(r) splits into bits that depend on (dt & 1, sec) and
                 // on the lane only: four lane bases plus constant offsets.
-                constexpr int PD = 3;
+                constexpr int PD = 5;
                 const int G = lk >> 4, i16 = lk & 15;
                 lds_u8 *vrow = tk + kh * 4 * KCB * 1024 + (4 * hl + (i16 >> 2)) * 128 + 8 * (i16 & 1) +
                                16 * (((i16 & 3) >> 1) ^ hl);
@@ -534,6 +563,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                         (lds_bf16x4 *)(vb[dt & 1][sec] + (2 * j + sec) * KCB * 1024 + (dt >> 1) * 1024));
                 };
+                // PV step u covers dim tile u % NDT and k-half u / NDT (dim tile
+                // fastest, so consecutive MFMAs never share an accumulator)
+                auto vstep = [](int u) { return 2 * (u % NDT) + u / NDT; };
                 auto ldv8 = [&](int step) {          // step = 2*dt + j
                     const bf16x4 lo = ldv(step >> 1, step & 1, 0), hi = ldv(step >> 1, step & 1, 1);
                     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -541,30 +573,45 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 bf16x8 va[PD];
 #pragma unroll
                 for (int d = 0; d < PD; ++d)
-                    va[d] = ldv8(d);
+                    va[d] = ldv8(vstep(d));
                 const float base = m_ref == -INFINITY ? 0.0f : m_ref;
                 bf16x8 pop[2];
-                if (full) {
+                auto pterm = [&](int i) {
+                    const float pi = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -base));
+                    l_run += pi;
+                    pop[i >> 3][i & 7] = (__bf16)pi;
+                };
+                // ---- O^T += V^T P^T.  The first NDT steps use keys 0..15 only
+                // (pop[0]); the terms of keys 16..31 are computed between those
+                // MFMAs, where VALU work hides behind the matrix pipe, as a
+                // three-stage pipeline (step u: fma of key 16+u, exp of key 15+u,
+                // sum and bf16 of key 14+u), so that no VALU op in a step waits
+                // on another and the next MFMA issues on time.  Keys outside the
+                // list get a logit of -inf (a term of exactly 0) up front, so every
+                // tile runs the same straight-line code.
+                static_assert(NDT >= 10, "keys 16..31 are ready before their first PV step");
+                if (!full) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float pi = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -base));
-                        l_run += pi;
-                        pop[i >> 3][i & 7] = (__bf16)pi;
-                    }
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        const float pi = valid(i) ? __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -base)) : 0.0f;
-                        l_run += pi;
-                        pop[i >> 3][i & 7] = (__bf16)pi;
-                    }
+                    for (int i = 0; i < 16; ++i)
+                        s[i] = valid(i) ? s[i] : -INFINITY;
                 }
-                // ---- O^T += V^T P^T
 #pragma unroll
-                for (int st = 0; st < 2 * NDT; ++st) {
-                    oa[st >> 1] = mma32_bf16(va[st % PD], pop[st & 1], oa[st >> 1]);
-                    if (st + PD < 2 * NDT)
-                        va[st % PD] = ldv8(st + PD);
+                for (int i = 0; i < 8; ++i)
+                    pterm(i);
+                float arg[8], ex[8];
+#pragma unroll
+                for (int u = 0; u < 2 * NDT; ++u) {
+                    oa[u % NDT] = mma32_bf16(va[u % PD], pop[u / NDT], oa[u % NDT]);
+                    if (u + PD < 2 * NDT)
+                        va[u % PD] = ldv8(vstep(u + PD));
+                    if (u < 8)
+                        arg[u] = fmaf(s[8 + u], scale_log2, -base);
+                    if (u >= 1 && u < 9)
+                        ex[u - 1] = __builtin_amdgcn_exp2f(arg[u - 1]);
+                    if (u >= 2 && u < 10) {
+                        l_run2 += ex[u - 2];
+                        pop[1][u - 2] = (__bf16)ex[u - 2];
+                    }
                     __builtin_amdgcn_sched_barrier(0);
                 }
             }
@@ -575,34 +622,73 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- epilogue: lane holds head h, dims 32dt + 8g + 4hq + {0..3} of tile dt
     auto store = [&](const f32x16 (&oa)[NDT]) {
-    float l_tot = l_run + shfl_xor(l_run, 32);
+    const float l_lane = l_run + l_run2;
+    float l_tot = l_lane + shfl_xor(l_lane, 32);
     float probe = 0.0f;                 // turns NaN if any result is not finite
     if (n_split == 1) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
         float gh = 0.0f;
         if (!per_channel)
             gh = sigmoidf_(bf16_bits_to_f32(gate[(int64_t)tok * Hq + h]));
-        uint16_t *op = out + ((int64_t)tok * Hq + h) * DV + 4 * hq;
-        const uint16_t *gp = gate + ((int64_t)tok * Hq + h) * DV + 4 * hq;
+        // The wave's 32 output rows (heads wv*32 .. +31, DV bf16 each) are
+        // staged in LDS, row j at stg + j*ROWB: the gate rows arrive there by
+        // direct loads (contiguous in memory), each lane forms y = o/l * gate
+        // for its 4 x 4 x NDT elements in place, and whole rows leave with
+        // 16-byte stores.  Straight from the O^T layout every access would be
+        // 8 bytes per lane, 64 rows apart.
+        constexpr int ROWB = 2 * DV + 16;
+        static_assert(4 * 32 * ROWB <= 4 * KCHUNKS * 16 && DV * 2 == 64 * 16, "output staging");
+        lds_u8 *stg = (lds_u8 *)lkr + wv * 32 * ROWB;
+        const int64_t row0 = (int64_t)tok * Hq + hg * (32 * NW) + wv * 32;
+        __syncthreads();                        // every wave is done with the tile ring
+        if (per_channel) {
+            const uint16_t *gsrc = gate + row0 * DV + 8 * lane;
+#pragma unroll 8
+            for (int j = 0; j < 32; ++j)
+                dma_b128(gsrc + j * DV, stg + j * ROWB);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): the gate rows are in LDS
+        lds_u8 *mine = stg + col * ROWB + 8 * hq;
+        auto put4 = [&](int dt, int g, const float (&gi)[4]) {
+            uint16_t r[4];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int d0 = 32 * dt + 8 * g;
-                uint2 gv = per_channel ? *(const uint2 *)(gp + d0) : uint2{0u, 0u};
-                uint16_t r[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t gw = i < 2 ? gv.x : gv.y;
-                    const float gl = bf16_bits_to_f32((uint16_t)(gw >> (16 * (i & 1))));
-                    const float gi = per_channel ? __builtin_amdgcn_rcpf(1.0f + __expf(-gl)) : gh;
-                    const float y = oa[dt][4 * g + i] * inv * gi;
-                    probe = fmaf(y, 0.0f, probe);
-                    r[i] = f32_to_bf16_bits(y);
-                }
-                *(uint2 *)(op + d0) = uint2{(uint32_t)r[0] | ((uint32_t)r[1] << 16),
-                                            (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+            for (int i = 0; i < 4; ++i) {
+                // (inv * gate first: with o * inv shared by both gate forms the
+                // compiler would compute all of them up front)
+                const float y = oa[dt][4 * g + i] * (inv * gi[i]);
+                probe = fmaf(y, 0.0f, probe);
+                r[i] = f32_to_bf16_bits(y);
             }
+            *(lds_u32x2 *)(mine + 2 * (32 * dt + 8 * g)) =
+                u32x2{(uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+        };
+        if (per_channel) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const u32x2 w = *(const lds_u32x2 *)(mine + 2 * (32 * dt + 8 * g));
+                    float gi[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float x = bf16_bits_to_f32((uint16_t)((i < 2 ? w.x : w.y) >> (16 * (i & 1))));
+                        gi[i] = __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+                    }
+                    put4(dt, g, gi);
+                }
+        } else {
+            const float gi[4] = {gh, gh, gh, gh};
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    put4(dt, g, gi);
+        }
+        __builtin_amdgcn_wave_barrier();
+        uint16_t *orow = out + row0 * DV + 8 * lane;
+#pragma unroll 8
+        for (int j = 0; j < 32; ++j)
+            *(u32x4 *)(orow + j * DV) = *(const lds_u32x4 *)(stg + j * ROWB + 16 * lane);
         if (lse && hq == 0)
             lse[(int64_t)tok * Hq + h] = l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
     } else {
@@ -636,6 +722,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __syncthreads();
         m_ref = m_true;
         l_run = 0.0f;
+        l_run2 = 0.0f;
         run(o2, 2);
         store(o2);
     }
