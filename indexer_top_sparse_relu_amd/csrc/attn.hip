@@ -360,8 +360,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int j1 = min(K, j0 + split_len);
     const int nslots = max(0, j1 - j0);
     const int32_t *irow = idx + (int64_t)tok * K + j0;
+    const int row0 = (int)phys_row(bt, b, 0);      // a valid row of this sequence
     {
-        const int row0 = (int)phys_row(bt, b, 0);
         for (int j = tid; j < nslots; j += 64 * NW) {
             const int s = irow[j];
             prow[j] = s >= 0 ? (int)phys_row(bt, b, s) : -1 - row0;
@@ -392,7 +392,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto src_of = [&](int t, int ln) -> const uint16_t * {
         const int r = 8 * wv + (ln >> 3);
         const int slot = t * TK + r;
-        int pr = prow[slot < nslots ? slot : 0];
+        const int raw = prow[slot < nslots ? slot : 0];
+        int pr = slot < nslots ? raw : row0;      // (prow is unset when the list is empty)
         pr = pr >= 0 ? pr : -1 - pr;
         const int cpos = (ln & 7) ^ swzg(r);
         return kc + (int64_t)pr * rs + cpos * 8;
@@ -426,10 +427,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int ks = 0; ks < NKQ; ++ks)
             qop[ks] = *(const bf16x8 *)(qp + 16 * ks);
     }
+    // Every pass issues exactly KCB loads per wave for each of the tiles
+    // 0 .. ntiles+2: past the end of the list src_of falls back to a valid row
+    // of the sequence and the data lands in a ring buffer nobody reads.  The
+    // waits below are then one constant, and no load sits behind a branch.
 #pragma unroll
     for (int t = 0; t < 3; ++t)
-        if (t < ntiles)
-            issue(t, buf(t), lane);
+        issue(t, buf(t), lane);
     // One wait the compiler can see for the Q loads (and the first tiles).  Its
     // own tracking does not count the asm tile loads, and without this it would
     // keep the Q loads pending into the loop and wait on them before every MFMA
@@ -442,14 +446,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int vm_cur = vm_val(0, lane);
     const uint16_t *src_cur = src_of(3, lane);
     for (int t = 0; t < ntiles; ++t) {
-        // Tile t's loads were followed by those of the (up to two) next tiles,
-        // KCB per wave each, and by no other memory operation of this loop.
-        if (t + 2 < ntiles)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * KCB) : "memory");
-        else if (t + 1 < ntiles)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(KCB) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // Tile t's loads were followed by those of tiles t+1 and t+2, KCB per
+        // wave each, and by no other memory operation of this loop.
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * KCB) : "memory");
         __syncthreads();            // tile t complete; the buffer of tile t-1 is free
         const int ln = opaque(lane);
         const uint64_t vmask = __ballot(vm_cur >= 0);
@@ -457,7 +456,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // Tile t+3's loads are spread over the S chain (one per 4 MFMAs): issued
         // together, the four waves' loads back up the memory pipeline and each
         // wave stalls at issue with its MFMAs idle.
-        const bool nxt = t + 3 < ntiles;
         const uint16_t *nsrc = src_cur;
         lds_u8 *ndk = buf(t + 3) + wv * KCB * 1024;
         static_assert(4 * (KCB - 1) < NKQ, "one tile load per 4 S-chain MFMAs");
@@ -510,7 +508,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                      : "+v"(sc[c]) : "v"(ka[ks % QD]), "v"(qop[ks]));
                     if (ks + QD < NKQ)
                         ka[ks % QD] = lda(ks + QD);
-                    if (ks % 4 == 0 && ks / 4 < KCB && nxt)
+                    if (ks % 4 == 0 && ks / 4 < KCB)
                         dma_b128(nsrc + (ks / 4) * 64, ndk + (ks / 4) * 1024);
                     if (ks == NKQ - 12)
                         vm_cur = vm_val(t + 1, ln);
@@ -617,7 +615,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
         }
     }
-
+    // the loads past the end of the list land before the ring is reused
+    __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0)
     };
 
     // ---- epilogue: lane holds head h, dims 32dt + 8g + 4hq + {0..3} of tile dt
@@ -713,18 +712,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     over = store(o);
     if (__syncthreads_or(over)) {
         // rare: some head's terms outgrew 2^64 relative to its first keys; find
-        // the exact maximum, then rerun with it as the reference (terms <= 1)
-        f32x16 o2[NDT];
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            o2[dt] = f32x16{};
-        run(o2, 1);
+        // the exact maximum, then rerun with it as the reference (terms <= 1).
+        // The max-only pass does not touch o; o is cleared only after it, so no
+        // second accumulator array is ever live.
+        run(o, 1);
         __syncthreads();
         m_ref = m_true;
         l_run = 0.0f;
         l_run2 = 0.0f;
-        run(o2, 2);
-        store(o2);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            o[dt] = f32x16{};
+        run(o, 2);
+        store(o);
     }
 }
 
