@@ -649,17 +649,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): the gate rows are in LDS
         lds_u8 *mine = stg + col * ROWB + 8 * hq;
         auto put4 = [&](int dt, int g, const float (&gi)[4]) {
-            uint16_t r[4];
+            float y[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // (inv * gate first: with o * inv shared by both gate forms the
                 // compiler would compute all of them up front)
-                const float y = oa[dt][4 * g + i] * (inv * gi[i]);
-                probe = fmaf(y, 0.0f, probe);
-                r[i] = f32_to_bf16_bits(y);
+                y[i] = oa[dt][4 * g + i] * (inv * gi[i]);
+                probe = fmaf(y[i], 0.0f, probe);
             }
+            // bf16 round-to-nearest-even, two values per convert instruction
+            const bf16x2 lo = {(__bf16)y[0], (__bf16)y[1]}, hi = {(__bf16)y[2], (__bf16)y[3]};
             *(lds_u32x2 *)(mine + 2 * (32 * dt + 8 * g)) =
-                u32x2{(uint32_t)r[0] | ((uint32_t)r[1] << 16), (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
+                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
         };
         if (per_channel) {
 #pragma unroll
