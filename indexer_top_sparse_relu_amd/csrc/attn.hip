@@ -532,7 +532,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     mx = fmaxf(mx, valid(i) ? s[i] * scale_log2 : -INFINITY);
-                mx = fmaxf(mx, shfl_xor(mx, 32));
+                mx = max_halves(mx);
                 if (mode == 1) {
                     m_true = fmaxf(m_true, mx);
                 } else {
@@ -622,7 +622,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // ---- epilogue: lane holds head h, dims 32dt + 8g + 4hq + {0..3} of tile dt
     auto store = [&](const f32x16 (&oa)[NDT]) {
     const float l_lane = l_run + l_run2;
-    float l_tot = l_lane + shfl_xor(l_lane, 32);
+    float l_tot = sum_halves(l_lane);
     float probe = 0.0f;                 // turns NaN if any result is not finite
     if (n_split == 1) {
         const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;

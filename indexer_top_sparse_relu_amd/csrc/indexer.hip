@@ -291,16 +291,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             return st == 0 ? (lds_u8 *)lkr0 : st == 1 ? (lds_u8 *)lkr1 : (lds_u8 *)lkr2;
         };
         lds_f32 *const LKS = (lds_f32 *)lksr;
-        auto krow = [&](int s) -> int64_t {
-            s = min(s, kb1 - 1);
-            return ((int64_t)lpt[(s >> pshift) - pg0] << pshift) + (s & pmask);
-        };
-        auto issue = [&](int tt, int ln) {
-            const int st = tt % KST;
+        // The lane's three key positions of tile tt (two rows of the key tile
+        // and one key scale) and their physical pages.  The pages are read from
+        // LDS one tile ahead of the loads, inside the previous tile's MFMA work,
+        // so the issue itself waits on nothing.
+        struct Pg { int a, b, c; };
+        auto kpos = [&](int tt, int ln, int which) {
             const int t0 = kb0 + tt * kIdxTileKeys;
-            // all three physical rows first (one LDS round trip), then the loads
+            const int r = which == 0 ? wv * 8 + (ln >> 3) : which == 1 ? (kIdxWaves + wv) * 8 + (ln >> 3) : ln;
+            return min(t0 + r, kb1 - 1);
+        };
+        auto pages = [&](int tt, int ln) {
+            return Pg{lpt[(kpos(tt, ln, 0) >> pshift) - pg0], lpt[(kpos(tt, ln, 1) >> pshift) - pg0],
+                      lpt[(kpos(tt, ln, 2) >> pshift) - pg0]};
+        };
+        auto issue = [&](int tt, int ln, const Pg &pg) {
+            const int st = tt % KST;
             const int r0 = wv * 8 + (ln >> 3), r1 = (kIdxWaves + wv) * 8 + (ln >> 3);
-            const int64_t p0 = krow(t0 + r0), p1 = krow(t0 + r1), p2 = krow(t0 + ln);
+            const int64_t p0 = ((int64_t)pg.a << pshift) + (kpos(tt, ln, 0) & pmask);
+            const int64_t p1 = ((int64_t)pg.b << pshift) + (kpos(tt, ln, 1) & pmask);
+            const int64_t p2 = ((int64_t)pg.c << pshift) + (kpos(tt, ln, 2) & pmask);
             dma_b128(k_idx + p0 * 128 + ((ln & 7) ^ ((r0 >> 1) & 7)) * 16, stage(st) + wv * 1024);
             dma_b128(k_idx + p1 * 128 + ((ln & 7) ^ ((r1 >> 1) & 7)) * 16, stage(st) + (kIdxWaves + wv) * 1024);
             dma_b32(k_scale + p2, (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * 64));
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             }
 #pragma unroll
             for (int t = 0; t < TH; ++t)
-                acc[t] += shfl_xor(acc[t], 32);
+                acc[t] = sum_halves(acc[t]);
             // writer of token gh*TH + t is the half t%2 (TH == 2) or half gh (TH == 1)
             const int tw = TH == 1 ? 0 : half;
             const float a = (TH > 1 && half) ? acc[TH - 1] : acc[0];
@@ -343,8 +353,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         f32x16 c0[MH], c1[MH];
         int s_prev = 0;
         float ks_prev = 0.0f, L_prev = 0.0f;
-        issue(0, lane);
-        issue(1, lane);
+        issue(0, lane, pages(0, lane));
+        issue(1, lane, pages(1, lane));
+        Pg pg_next = pages(2, lane);
         for (int it = 0; it < ntiles; ++it) {
             // Tile it was issued two iterations back (3 ops per wave); since then
             // each iteration issued 3 loads and 4 stores (3 in the first), which
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                 asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
             __syncthreads();
             const int ln = opaque(lane);
-            issue(it + 2, ln);
+            issue(it + 2, ln, pg_next);
             const int st = it % KST;
             const int t0 = kb0 + it * kIdxTileKeys;
 #pragma unroll
@@ -409,6 +420,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                         c1[m] = X::mma(a[MH + m][ks], bop[ks], c1[m]);
                 }
                 epi(c0, 0, s, ks_s, La);
+                if (nt == 0)
+                    pg_next = pages(it + 3, ln);
                 s_prev = s;
                 ks_prev = ks_s;
                 L_prev = TPW == 4 ? Lb : La;
@@ -452,7 +465,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             }
 #pragma unroll
             for (int t = 0; t < TH; ++t)
-                acc[t] += shfl_xor(acc[t], 32);
+                acc[t] = sum_halves(acc[t]);
             // one token per half: lanes of half 0 write it; two: half h writes token h
 #pragma unroll
             for (int t0w = 0; t0w < TH; t0w += 2) {
@@ -553,7 +566,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                 }
 #pragma unroll
                 for (int t = 0; t < TPW; ++t)
-                    acc[t] += shfl_xor(acc[t], 32);
+                    acc[t] = sum_halves(acc[t]);
                 // lanes of half 0 write even wave-tokens, half 1 odd ones
 #pragma unroll
                 for (int t0w = 0; t0w < TPW; t0w += 2) {
@@ -689,7 +702,7 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
                         acc = fmaf(wr[mt][i], fmaxf(c[mt][i], 0.0f), acc);
             }
         }
-        acc += shfl_xor(acc, 32);
+        acc = sum_halves(acc);
         const int s = kb0 + t * 32 + col;
         if (half == 0 && s < kb1)
             scores[(int64_t)tok * ld + s] = acc * qs * ksv;

@@ -187,12 +187,38 @@ __device__ __forceinline__ T shfl_xor(T v, int m)
     return __shfl_xor(v, m, kWave);
 }
 
+// x[l] + x[l ^ 32] and max(x[l], x[l ^ 32]) in every lane of a wave64, in the
+// VALU: v_permlane32_swap exchanges the upper half of one register with the
+// lower half of another, so two copies of x end up holding (lower, lower) and
+// (upper, upper).  (A lane shuffle goes through the LDS crossbar and makes the
+// wave wait for every LDS access in flight.)
+__device__ __forceinline__ float sum_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float max_halves(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Maximum over the 64 lanes, all in the VALU: DPP within each row of 16
+// lanes (pair swaps, then rotations by 4 and 8), v_permlane16_swap across the
+// rows of each half, v_permlane32_swap across the halves.
 __device__ __forceinline__ float wave_max(float v)
 {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v = fmaxf(v, shfl_xor(v, m));
-    return v;
+#define SA_DPP_MAX(ctrl) \
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false)))
+    SA_DPP_MAX(0xB1);                  // quad_perm [1,0,3,2]
+    SA_DPP_MAX(0x4E);                  // quad_perm [2,3,0,1]
+    SA_DPP_MAX(0x124);                 // row_ror:4
+    SA_DPP_MAX(0x128);                 // row_ror:8
+#undef SA_DPP_MAX
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_halves(v);
 }
 
 __device__ __forceinline__ float wave_sum(float v)
