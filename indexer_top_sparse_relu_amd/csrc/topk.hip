@@ -466,11 +466,11 @@ __device__ uint32_t lds_select_rank(const uint32_t *keys, int cnt, uint32_t rank
 // its ties are then resolved there.  Returns false, having written nothing,
 // when the kept count falls outside [K, kCap]; the caller then runs the
 // general selection, so the result never depends on the sample.
-__device__ bool select_topk_fast(const float *__restrict__ vals, int n, int idx0, int K,
+__device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad4, int idx0, int K,
                                  int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (n < 2 * kSample)
+    if (n < 2 * kSample || !pad4 || (((uintptr_t)vals) & 15u) != 0)
         return false;
     const float rexp = (float)K * (float)kSample / (float)n;
     const int rlow = (int)(rexp + 3.0f * sqrtf(rexp) + 4.0f) + 1;
@@ -486,62 +486,117 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, int idx0
     __syncthreads();
     const uint32_t thr = lds_select_rank(sm.ckey, kSample, (uint32_t)rlow, sm);
 
-    // ---- 2. one pass: slots with key >= thr to ckey/cidx in slot order.  Each
-    // thread owns 16 consecutive slots per step; the next step's loads are in
-    // flight while this step's block scan waits at its barriers.
-    const bool aligned = ((((uintptr_t)vals) & 15u) == 0);
-    auto load16 = [&](int j0, float (&v)[16]) {
+    // ---- 2. one pass, streamed per wave: wave w scans its own contiguous chunk
+    // of the segment in slot order and appends the slots with key >= thr to its
+    // own LDS region (RC slots); the regions, concatenated in wave order, hold
+    // the kept slots in slot order.  The pass has no barrier: each wave keeps
+    // TD steps of loads in flight, and its compaction is a lane prefix count
+    // from ballots (no LDS traffic).  A region that overflows sends the
+    // segment to the general path.
+    constexpr int WST = 1024;                   // slots per wave step: 4 runs of 64 lanes x 4
+    constexpr int RC = kCap / kTkWaves;         // region slots per wave
+    constexpr int TD = 3;                       // wave steps in flight
+    static_assert(RC == kTkThreads, "concatenation: thread t moves slot t of every region");
+    const int wchunk = (n + kTkWaves * WST - 1) / (kTkWaves * WST) * WST;
+    const int c0 = min(n, wv * wchunk), c1 = min(n, c0 + wchunk);
+    // every wave runs the same number of steps, a multiple of TD, so that the
+    // loop has one path and the compiler's waits count TD steps in flight
+    const int nsteps = (wchunk / WST + TD - 1) / TD * TD;
+    // step s of this lane: slots c0 + s*WST + 256u + 4*lane + q, u, q = 0..3,
+    // read as 16-byte loads without branches (so the compiler's waits can count
+    // the loads in flight).  jmax is the group holding the chunk's last slot; a
+    // group past it rereads it (a line already fetched) and its slots are
+    // masked out below.  Reading that whole group needs the segment to be
+    // readable up to a multiple of 4 slots (the caller's pad4 guarantee).
+    const int jmax = ((c1 > c0 ? c1 : n) - 1) & ~3;
+    auto load = [&](int s, float (&v)[16]) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int j = j0 + 4 * u;
-            if (aligned && j + 3 < n) {
-                const float4 f = *(const float4 *)(vals + j);
-                v[4 * u] = f.x;
-                v[4 * u + 1] = f.y;
-                v[4 * u + 2] = f.z;
-                v[4 * u + 3] = f.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    v[4 * u + e] = (j + e < n) ? vals[j + e] : 0.0f;
-            }
+            const int j = min(c0 + s * WST + 256 * u + 4 * lane, jmax);
+            const float4 f = *(const float4 *)(vals + j);
+            v[4 * u] = f.x;
+            v[4 * u + 1] = f.y;
+            v[4 * u + 2] = f.z;
+            v[4 * u + 3] = f.w;
         }
     };
-    constexpr int STEP = kTkThreads * 16;
-    float cur[16], nxt[16];
-    load16(tid * 16, cur);
-    uint32_t base = 0;
-    for (int j00 = 0; j00 < n; j00 += STEP) {
-        const int j0 = j00 + tid * 16;
-        uint32_t kk[16], m = 0u;
+    uint32_t *rkey = sm.ckey + wv * RC;
+    int32_t *ridx = sm.cidx + wv * RC;
+    uint32_t wcount = 0;                        // kept slots of this wave so far
+    auto keep = [&](int s, const float (&v)[16]) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            kk[e] = fkey(cur[e]);
-            if (j0 + e < n && kk[e] >= thr)
-                m |= 1u << e;
-        }
-        if (j00 + STEP < n)
-            load16(j0 + STEP, nxt);
-        uint32_t tot;
-        uint32_t p = base + block_scan((uint32_t)__popc(m), sm.misc, tot);
+        for (int u = 0; u < 4; ++u) {
+            const int j = c0 + s * WST + 256 * u + 4 * lane;
+            uint32_t kk[4], m = 0u;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            if ((m >> e) & 1u) {
-                if (p < (uint32_t)kCap) {
-                    sm.ckey[p] = kk[e];
-                    sm.cidx[p] = idx0 + j0 + e;
-                }
-                ++p;
+            for (int q = 0; q < 4; ++q) {
+                kk[q] = fkey(v[4 * u + q]);
+                if (j + q < c1 && kk[q] >= thr)
+                    m |= 1u << q;
             }
-        }
-        base += tot;
+            // exclusive prefix over lanes of the per-lane counts (0..4), bit-sliced
+            const int c = __popc(m);
+            const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
+            if ((b0 | b1 | b2) == 0)
+                continue;
+            auto below = [](uint64_t b) {
+                return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+            };
+            uint32_t p = wcount + below(b0) + 2u * below(b1) + 4u * below(b2);
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            cur[e] = nxt[e];
+            for (int q = 0; q < 4; ++q)
+                if ((m >> q) & 1u) {
+                    if (p < (uint32_t)RC) {
+                        rkey[p] = kk[q];
+                        ridx[p] = idx0 + j + q;
+                    }
+                    ++p;
+                }
+            wcount += (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
+        }
+    };
+    float buf[TD][16];
+#pragma unroll
+    for (int d = 0; d < TD; ++d)
+        load(d, buf[d]);
+    for (int s0 = 0; s0 < nsteps; s0 += TD) {
+#pragma unroll
+        for (int d = 0; d < TD; ++d) {
+            keep(s0 + d, buf[d]);
+            load(s0 + d + TD, buf[d]);
+        }
     }
+    if (lane == 0)
+        sm.misc[wv] = wcount;
     __syncthreads();
-    if (base < (uint32_t)K || base > (uint32_t)kCap)
+    uint32_t cnt[kTkWaves], pfx[kTkWaves], base = 0;
+    bool ovf = false;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+        cnt[w] = sm.misc[w];
+        pfx[w] = base;
+        base += cnt[w];
+        ovf |= cnt[w] > (uint32_t)RC;
+    }
+    if (ovf || base < (uint32_t)K || base > (uint32_t)kCap)
         return false;
+    // concatenate the regions in wave order (all reads, then all writes)
+    uint32_t rk[kTkWaves];
+    int32_t ri[kTkWaves];
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w)
+        if ((uint32_t)tid < cnt[w]) {
+            rk[w] = sm.ckey[w * RC + tid];
+            ri[w] = sm.cidx[w * RC + tid];
+        }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w)
+        if ((uint32_t)tid < cnt[w]) {
+            sm.ckey[pfx[w] + tid] = rk[w];
+            sm.cidx[pfx[w] + tid] = ri[w];
+        }
+    __syncthreads();
     // ---- 3. exact K-th key among the kept slots (all K winners are among them)
     finish_select(thr, 0xFFFFFFFFu, base, 0u, (uint32_t)K, false, K, gidx, gval, sm);
     return true;
@@ -575,7 +630,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(Batch bt, const f
     const TkSmem sm = tk_smem(K);
     const float *vals = scores + (int64_t)row * ld;
     int32_t *o = out + (int64_t)row * K;
-    if (!select_topk_fast(vals, n, 0, K, o, nullptr, sm))
+    // rows start 16-byte aligned and can be read up to a multiple of 4 slots
+    // when the row stride is a multiple of 4 floats
+    if (!select_topk_fast(vals, n, (ld & 3) == 0, 0, K, o, nullptr, sm))
         select_topk<false>(vals, nullptr, n, 0, K, o, nullptr, sm);
 }
 
@@ -592,7 +649,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(Batch bt, const 
     const int64_t o = (int64_t)row * cand_ld + (int64_t)c * K;
     const TkSmem sm = tk_smem(K);
     const float *vals = scores + (int64_t)row * ld + j0;
-    if (!select_topk_fast(vals, len, j0, K, cidx + o, cval + o, sm))
+    if (!select_topk_fast(vals, len, (ld & 3) == 0, j0, K, cidx + o, cval + o, sm))
         select_topk<false>(vals, nullptr, len, j0, K, cidx + o, cval + o, sm);
 }
 
