@@ -73,17 +73,28 @@ struct TkSmem {
     uint32_t *misc;     // [64]
 };
 
+// Inclusive scan over the 64 lanes of a wave in the VALU (DPP): shifts by 1,
+// 2, 4, 8 within each row of 16 lanes (lanes with no source add 0), then the
+// last lane of row 0 (resp. 1) is broadcast into rows 1 and 3 (resp. 2 and 3).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x)
+{
+#define SA_DPP_ADD(ctrl, rmask, bctl) \
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, ctrl, rmask, 0xF, bctl)
+    SA_DPP_ADD(0x111, 0xF, true);      // row_shr:1
+    SA_DPP_ADD(0x112, 0xF, true);      // row_shr:2
+    SA_DPP_ADD(0x114, 0xF, true);      // row_shr:4
+    SA_DPP_ADD(0x118, 0xF, true);      // row_shr:8
+    SA_DPP_ADD(0x142, 0xA, false);     // row_bcast:15 into rows 1, 3
+    SA_DPP_ADD(0x143, 0xC, false);     // row_bcast:31 into rows 2, 3
+#undef SA_DPP_ADD
+    return x;
+}
+
 // Exclusive block scan of v (512 threads); *total gets the block sum.
 __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t *misc, uint32_t &total)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t y = __shfl_up(x, d, 64);
-        if (lane >= d)
-            x += y;
-    }
+    const uint32_t x = wave_incl_scan(v);
     if (lane == 63)
         misc[wv] = x;
     __syncthreads();
@@ -479,9 +490,17 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
 
     // ---- 1. sample -> threshold
     constexpr int RUNS = kSample / 64;
-    for (int r = wv; r < RUNS; r += kTkWaves) {
-        const int j = (int)(((int64_t)r * (n - 64)) / (RUNS - 1)) + lane;
-        sm.ckey[r * 64 + lane] = fkey(vals[j]);
+    {
+        // all of the wave's runs in flight at once
+        float sv[RUNS / kTkWaves];
+#pragma unroll
+        for (int i = 0; i < RUNS / kTkWaves; ++i) {
+            const int r = wv + kTkWaves * i;
+            sv[i] = vals[(int)(((int64_t)r * (n - 64)) / (RUNS - 1)) + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < RUNS / kTkWaves; ++i)
+            sm.ckey[(wv + kTkWaves * i) * 64 + lane] = fkey(sv[i]);
     }
     __syncthreads();
     const uint32_t thr = lds_select_rank(sm.ckey, kSample, (uint32_t)rlow, sm);
