@@ -28,8 +28,9 @@
 //
 // Long rows first try a single-pass variant (select_topk_fast): a contiguous-
 // run sample fixes a conservative threshold and one order-preserving pass
-// keeps every slot at or above it in LDS, where the steps 4-5 finish; when the
-// kept count misses [K, kCap] the general steps 1-5 run instead.
+// keeps every slot at or above it in LDS, where step 4 finishes; when the
+// kept count misses [K, kCap] the general steps 1-5 run instead (for the rows
+// kernel: in a second launch, over the rows the first one marked).
 //
 // Rows up to a few hundred thousand slots take one workgroup each.  When there
 // are too few rows to fill the GPU, each row is cut into chunks selected in
@@ -38,6 +39,8 @@
 // subset of the union of per-chunk top-Ks under the same total order, and the
 // chunk lists are concatenated in position order, so slot order is position
 // order in both stages.
+#include <type_traits>
+
 #include "sa_device.h"
 #include "launch.h"
 
@@ -48,6 +51,7 @@ constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kBins = 4096;
 constexpr int kCap = 4096;      // LDS slots for the window's candidates
 constexpr int kSample = 4096;
+constexpr int kSampleBig = 8192;   // single-pass sample on long segments
 constexpr int kMaxK = 4096;
 
 __device__ __forceinline__ uint32_t fkey(float v)
@@ -176,8 +180,11 @@ __device__ __forceinline__ void find_bin(const TkSmem &sm, uint32_t need, int &b
 // hold the remaining `need` winners; the sure winners are okey/oidx[0, above),
 // in slot order.  Resolves the exact K-th key inside LDS (ties to the lowest
 // slots), then merges the two ascending runs into gidx (and gval).
+// direct (only with above == 0): the K selected slots go straight to gidx/gval
+// in slot order, without the okey/oidx staging.
 __device__ void finish_select(uint32_t lo, uint32_t hi, uint32_t cnt, uint32_t above, uint32_t need, bool single,
-                              int K, int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
+                              int K, int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm,
+                              bool direct = false)
 {
     const int tid = threadIdx.x;
     // ---- 4. resolve the window inside LDS
@@ -222,13 +229,21 @@ __device__ void finish_select(uint32_t lo, uint32_t hi, uint32_t cnt, uint32_t a
             uint32_t tot2;
             const uint32_t ps = bsel_ + block_scan(sel ? 1u : 0u, sm.misc, tot2);
             if (sel && above + ps < (uint32_t)K) {
-                sm.okey[above + ps] = key;
-                sm.oidx[above + ps] = sm.cidx[c];
+                if (direct) {
+                    gidx[ps] = sm.cidx[c];
+                    if (gval)
+                        gval[ps] = kval(key);
+                } else {
+                    sm.okey[above + ps] = key;
+                    sm.oidx[above + ps] = sm.cidx[c];
+                }
             }
             bwin += tot & 0xFFFFu;
             bsel_ += tot2;
         }
         __syncthreads();
+        if (direct)
+            return;
     }
 
     // ---- 5. merge the two ascending runs [0, above) and [above, K)
@@ -469,28 +484,35 @@ __device__ uint32_t lds_select_rank(const uint32_t *keys, int cnt, uint32_t rank
 }
 
 // Single-pass selection for long rows (slot j has position idx0 + j).  A
-// sample of 64 runs of 64 consecutive slots, spread evenly over the row, gives
-// a threshold: the sample key whose rank is the K-th key's expected rank in
-// the sample plus about three standard deviations, so that the row's slots at
-// or above it very likely number between K and kCap.  One order-preserving
-// pass keeps exactly those slots in LDS (slot order); the exact K-th key and
-// its ties are then resolved there.  Returns false, having written nothing,
-// when the kept count falls outside [K, kCap]; the caller then runs the
-// general selection, so the result never depends on the sample.
+// sample of 64 (128 on long rows) runs of 64 consecutive slots, spread evenly
+// over the row, gives a threshold: the sample key whose rank is the K-th key's
+// expected rank in the sample plus about four standard deviations, so that the
+// row's slots at or above it very likely number between K and kCap.  One
+// order-preserving pass keeps exactly those slots in LDS (slot order); the
+// exact K-th key and its ties are then resolved there and the K winners
+// written out.  Returns false, having written nothing, when the kept count
+// falls outside [K, kCap] (or a wave's share overflows its LDS region); the
+// caller then runs the general selection, so the result never depends on the
+// sample.
 __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad4, int idx0, int K,
                                  int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if (n < 2 * kSample || !pad4 || (((uintptr_t)vals) & 15u) != 0)
         return false;
-    const float rexp = (float)K * (float)kSample / (float)n;
-    const int rlow = (int)(rexp + 3.0f * sqrtf(rexp) + 4.0f) + 1;
-    if (rlow >= kSample)
+    // the sample: 64 runs, or 128 on segments of at least 16 runs per wave
+    // step (the K-th key's expected rank in it then doubles, so the same
+    // relative margin keeps fewer slots)
+    const bool big = n >= 4 * kSampleBig;
+    const int S = big ? kSampleBig : kSample;
+    const float rexp = (float)K * (float)S / (float)n;
+    const int rlow = (int)(rexp + 4.0f * sqrtf(rexp) + 4.0f) + 1;
+    if (rlow >= S)
         return false;
 
-    // ---- 1. sample -> threshold
-    constexpr int RUNS = kSample / 64;
-    {
+    // ---- 1. sample -> threshold (the sample sits in the pair area)
+    auto sample = [&](auto runs_c) {
+        constexpr int RUNS = decltype(runs_c)::value;
         // all of the wave's runs in flight at once
         float sv[RUNS / kTkWaves];
 #pragma unroll
@@ -501,9 +523,14 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
 #pragma unroll
         for (int i = 0; i < RUNS / kTkWaves; ++i)
             sm.ckey[(wv + kTkWaves * i) * 64 + lane] = fkey(sv[i]);
-    }
+    };
+    static_assert(kSampleBig <= 2 * kCap, "the sample fits in ckey and cidx");
+    if (big)
+        sample(std::integral_constant<int, kSampleBig / 64>{});
+    else
+        sample(std::integral_constant<int, kSample / 64>{});
     __syncthreads();
-    const uint32_t thr = lds_select_rank(sm.ckey, kSample, (uint32_t)rlow, sm);
+    const uint32_t thr = lds_select_rank(sm.ckey, S, (uint32_t)rlow, sm);
 
     // ---- 2. one pass, streamed per wave: wave w scans its own contiguous chunk
     // of the segment in slot order and appends the slots with key >= thr to its
@@ -513,9 +540,10 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
     // from ballots (no LDS traffic).  A region that overflows sends the
     // segment to the general path.
     constexpr int WST = 1024;                   // slots per wave step: 4 runs of 64 lanes x 4
-    constexpr int RC = kCap / kTkWaves;         // region slots per wave
+    constexpr int PC = kCap + kBins / 2;        // (key, index) pairs in ckey, cidx, hist
+    constexpr int RC = PC / kTkWaves;           // region pairs per wave
     constexpr int TD = 3;                       // wave steps in flight
-    static_assert(RC == kTkThreads, "concatenation: thread t moves slot t of every region");
+    static_assert(PC % kTkThreads == 0, "concatenation: every thread moves PC / kTkThreads pairs");
     const int wchunk = (n + kTkWaves * WST - 1) / (kTkWaves * WST) * WST;
     const int c0 = min(n, wv * wchunk), c1 = min(n, c0 + wchunk);
     // every wave runs the same number of steps, a multiple of TD, so that the
@@ -539,8 +567,8 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
             v[4 * u + 3] = f.w;
         }
     };
-    uint32_t *rkey = sm.ckey + wv * RC;
-    int32_t *ridx = sm.cidx + wv * RC;
+    u32x2 *const pairs = (u32x2 *)sm.ckey;     // the pair area (ckey, cidx, hist)
+    u32x2 *rgn = pairs + wv * RC;
     uint32_t wcount = 0;                        // kept slots of this wave so far
     auto keep = [&](int s, const float (&v)[16]) {
 #pragma unroll
@@ -565,10 +593,8 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 if ((m >> q) & 1u) {
-                    if (p < (uint32_t)RC) {
-                        rkey[p] = kk[q];
-                        ridx[p] = idx0 + j + q;
-                    }
+                    if (p < (uint32_t)RC)
+                        rgn[p] = u32x2{kk[q], (uint32_t)(idx0 + j + q)};
                     ++p;
                 }
             wcount += (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
@@ -599,36 +625,46 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
     }
     if (ovf || base < (uint32_t)K || base > (uint32_t)kCap)
         return false;
-    // concatenate the regions in wave order (all reads, then all writes)
-    uint32_t rk[kTkWaves];
-    int32_t ri[kTkWaves];
+    // concatenate the regions in wave order into ckey/cidx[0, base) (all reads,
+    // then all writes: the pair area overlaps its destination)
+    constexpr int PT = PC / kTkThreads;
+    u32x2 pv[PT];
+    int dst[PT];
 #pragma unroll
-    for (int w = 0; w < kTkWaves; ++w)
-        if ((uint32_t)tid < cnt[w]) {
-            rk[w] = sm.ckey[w * RC + tid];
-            ri[w] = sm.cidx[w * RC + tid];
-        }
+    for (int i = 0; i < PT; ++i) {
+        const int g = tid + kTkThreads * i, w = g / RC, o = g - w * RC;
+        dst[i] = -1;
+#pragma unroll
+        for (int x = 0; x < kTkWaves; ++x)
+            if (x == w && (uint32_t)o < cnt[x])
+                dst[i] = (int)pfx[x] + o;
+        if (dst[i] >= 0)
+            pv[i] = pairs[g];
+    }
     __syncthreads();
 #pragma unroll
-    for (int w = 0; w < kTkWaves; ++w)
-        if ((uint32_t)tid < cnt[w]) {
-            sm.ckey[pfx[w] + tid] = rk[w];
-            sm.cidx[pfx[w] + tid] = ri[w];
+    for (int i = 0; i < PT; ++i)
+        if (dst[i] >= 0) {
+            sm.ckey[dst[i]] = pv[i].x;
+            sm.cidx[dst[i]] = (int32_t)pv[i].y;
         }
     __syncthreads();
     // ---- 3. exact K-th key among the kept slots (all K winners are among them)
-    finish_select(thr, 0xFFFFFFFFu, base, 0u, (uint32_t)K, false, K, gidx, gval, sm);
+    finish_select(thr, 0xFFFFFFFFu, base, 0u, (uint32_t)K, false, K, gidx, gval, sm, true);
     return true;
 }
 
+// Both layouts start with ckey, cidx, hist back to back: during its pass the
+// single-pass selection uses those 2*kCap + kBins words as one area of
+// (key, index) pairs.
 __device__ __forceinline__ TkSmem tk_smem(int K)
 {
     extern __shared__ __align__(16) uint32_t tk_lds[];
     TkSmem sm;
-    sm.hist = tk_lds;
-    sm.ckey = sm.hist + kBins;
+    sm.ckey = tk_lds;
     sm.cidx = (int32_t *)(sm.ckey + kCap);
-    sm.okey = (uint32_t *)(sm.cidx + kCap);
+    sm.hist = (uint32_t *)(sm.cidx + kCap);
+    sm.okey = sm.hist + kBins;
     sm.oidx = (int32_t *)(sm.okey + ((K + 3) & ~3));
     sm.misc = (uint32_t *)(sm.oidx + ((K + 3) & ~3));
     return sm;
@@ -639,20 +675,55 @@ static size_t tk_smem_bytes(int K)
     return (size_t)(kBins + 2 * kCap + 2 * ((K + 3) & ~3) + 64) * 4;
 }
 
-// One workgroup per token row.
-__global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(Batch bt, const float *__restrict__ scores,
-                                                               int64_t ld, int K, int32_t *__restrict__ out)
+// The single pass alone needs no output staging (its selection is written
+// straight out): 48.25 KB, three workgroups per CU instead of two.
+__device__ __forceinline__ TkSmem tk_smem_fast()
+{
+    extern __shared__ __align__(16) uint32_t tk_lds[];
+    TkSmem sm;
+    sm.ckey = tk_lds;
+    sm.cidx = (int32_t *)(sm.ckey + kCap);
+    sm.hist = (uint32_t *)(sm.cidx + kCap);
+    sm.misc = sm.hist + kBins;
+    sm.okey = nullptr;
+    sm.oidx = nullptr;
+    return sm;
+}
+
+constexpr size_t kTkSmemFast = (size_t)(kBins + 2 * kCap + 64) * 4;
+constexpr int32_t kTkPending = INT32_MIN;   // first output slot of a row left to the general path
+
+// One workgroup per token row, in two launches: the single pass first (small
+// LDS, more workgroups per CU); a row it cannot finish gets kTkPending in its
+// first output slot and is selected by the general path in the second launch,
+// whose workgroups return at once for every other row.
+__global__ __launch_bounds__(kTkThreads) void topk_rows_fast_kernel(Batch bt, const float *__restrict__ scores,
+                                                                    int64_t ld, int K, int32_t *__restrict__ out)
 {
     const int row = blockIdx.x;
     const int b = seq_of_token(bt, row);
     const int n = pos_of_token(bt, b, row) + 1;
-    const TkSmem sm = tk_smem(K);
+    const TkSmem sm = tk_smem_fast();
     const float *vals = scores + (int64_t)row * ld;
     int32_t *o = out + (int64_t)row * K;
     // rows start 16-byte aligned and can be read up to a multiple of 4 slots
     // when the row stride is a multiple of 4 floats
-    if (!select_topk_fast(vals, n, (ld & 3) == 0, 0, K, o, nullptr, sm))
-        select_topk<false>(vals, nullptr, n, 0, K, o, nullptr, sm);
+    if (!select_topk_fast(vals, n, (ld & 3) == 0, 0, K, o, nullptr, sm) && threadIdx.x == 0)
+        o[0] = kTkPending;
+}
+
+__global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(Batch bt, const float *__restrict__ scores,
+                                                               int64_t ld, int K, int32_t *__restrict__ out)
+{
+    const int row = blockIdx.x;
+    int32_t *o = out + (int64_t)row * K;
+    if (o[0] != kTkPending)     // (read by every thread before any is written)
+        return;
+    const int b = seq_of_token(bt, row);
+    const int n = pos_of_token(bt, b, row) + 1;
+    const TkSmem sm = tk_smem(K);
+    const float *vals = scores + (int64_t)row * ld;
+    select_topk<false>(vals, nullptr, n, 0, K, o, nullptr, sm);
 }
 
 // Stage 1: blockIdx.x = chunk, blockIdx.y = row; per-chunk top-K with scores.
@@ -721,6 +792,8 @@ hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *score
             return hipErrorInvalidValue;
     }
     if (!plan.chunked) {
+        hipLaunchKernelGGL(topk_rows_fast_kernel, dim3(bt.total_q), dim3(kTkThreads), kTkSmemFast, st, bt, scores,
+                           ld, k, indices);
         hipLaunchKernelGGL(topk_rows_kernel, dim3(bt.total_q), dim3(kTkThreads), smem, st, bt, scores, ld, k,
                            indices);
         return hipGetLastError();
