@@ -121,14 +121,32 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t v, uint32_t *misc)
     return t;
 }
 
+// Minimum and maximum over the 64 lanes of a wave, in the VALU (DPP within
+// rows of 16, then v_permlane16_swap and v_permlane32_swap across rows).
+__device__ __forceinline__ void wave_minmax(uint32_t &mn, uint32_t &mx)
+{
+#define SA_DPP_MM(ctrl)                                                                                   \
+    mn = min(mn, (uint32_t)__builtin_amdgcn_update_dpp((int)0xFFFFFFFF, (int)mn, ctrl, 0xF, 0xF, false));  \
+    mx = max(mx, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mx, ctrl, 0xF, 0xF, false))
+    SA_DPP_MM(0xB1);                   // quad_perm [1,0,3,2]
+    SA_DPP_MM(0x4E);                   // quad_perm [2,3,0,1]
+    SA_DPP_MM(0x124);                  // row_ror:4
+    SA_DPP_MM(0x128);                  // row_ror:8
+#undef SA_DPP_MM
+    auto a = __builtin_amdgcn_permlane16_swap(mn, mn, false, false);
+    mn = min(a[0], a[1]);
+    a = __builtin_amdgcn_permlane32_swap(mn, mn, false, false);
+    mn = min(a[0], a[1]);
+    auto b = __builtin_amdgcn_permlane16_swap(mx, mx, false, false);
+    mx = max(b[0], b[1]);
+    b = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
+    mx = max(b[0], b[1]);
+}
+
 __device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, uint32_t *misc)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, m, 64));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, m, 64));
-    }
+    wave_minmax(mn, mx);
     if (lane == 0) {
         misc[16 + wv] = mn;
         misc[24 + wv] = mx;
@@ -456,12 +474,14 @@ __device__ void select_topk(const float *__restrict__ vals, const int32_t *__res
 
 // rank-th largest key (1 <= rank <= cnt) of keys[0, cnt) in LDS: a radix
 // select over three digit levels (12, 12 and 8 bits).
-__device__ uint32_t lds_select_rank(const uint32_t *keys, int cnt, uint32_t rank, const TkSmem &sm)
+// With levels == 2 the low 8 bits are not resolved: the result is the lower
+// edge of the 256-key bucket holding the rank-th key (a key at most that rank).
+__device__ uint32_t lds_select_rank(const uint32_t *keys, int cnt, uint32_t rank, const TkSmem &sm, int levels = 3)
 {
     const int tid = threadIdx.x;
     uint32_t prefix = 0u, pmask = 0u, need = rank;
 #pragma unroll 1
-    for (int lv = 0; lv < 3; ++lv) {
+    for (int lv = 0; lv < levels; ++lv) {
         const int sh = lv == 0 ? 20 : (lv == 1 ? 8 : 0);
         const uint32_t dm = lv == 2 ? 0xFFu : 0xFFFu;
         for (int b = tid; b < kBins; b += kTkThreads)
@@ -483,6 +503,44 @@ __device__ uint32_t lds_select_rank(const uint32_t *keys, int cnt, uint32_t rank
     return prefix;
 }
 
+// A key at most the rank-th largest of keys[0, cnt) (rank >= 1), within 2^-12
+// of the keys' range above it: a 4096-bin histogram over the keys' actual range
+// [min, max] (so the bins, and their LDS atomics, spread out), then one over
+// the bin holding that rank.  Returns the lower edge of the final bin.
+__device__ uint32_t lds_window_select(const uint32_t *keys, int cnt, uint32_t rank, const TkSmem &sm)
+{
+    const int tid = threadIdx.x;
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+    for (int c = tid; c < cnt; c += kTkThreads) {
+        mn = min(mn, keys[c]);
+        mx = max(mx, keys[c]);
+    }
+    block_minmax(mn, mx, sm.misc);
+    uint32_t lo = mn, span = mx - mn, need = rank;     // the window [lo, lo + span]
+#pragma unroll 1
+    for (int lv = 0; lv < 2; ++lv) {
+        const int sh = max(0, bitlen(span) - 12);       // (span >> sh) < 4096
+        for (int b = tid; b < kBins; b += kTkThreads)
+            sm.hist[b] = 0u;
+        __syncthreads();
+        for (int c = tid; c < cnt; c += kTkThreads) {
+            const uint32_t k = keys[c];
+            if (k >= lo && k - lo <= span)
+                atomicAdd(&sm.hist[(k - lo) >> sh], 1u);
+        }
+        __syncthreads();
+        int b;
+        uint32_t gt;
+        find_bin(sm, need, b, gt);
+        need -= gt;
+        lo += (uint32_t)b << sh;
+        if (sh == 0)
+            break;
+        span = (1u << sh) - 1u;                         // the chosen bin
+    }
+    return lo;
+}
+
 // Single-pass selection for long rows (slot j has position idx0 + j).  A
 // sample of 64 (128 on long rows) runs of 64 consecutive slots, spread evenly
 // over the row, gives a threshold: the sample key whose rank is the K-th key's
@@ -498,7 +556,7 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
                                  int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (n < 2 * kSample || !pad4 || (((uintptr_t)vals) & 15u) != 0)
+    if (n < 2 * kSample || n >= (1 << 25) || !pad4 || (((uintptr_t)vals) & 15u) != 0)
         return false;
     // the sample: 64 runs, or 128 on segments of at least 16 runs per wave
     // step (the K-th key's expected rank in it then doubles, so the same
@@ -509,28 +567,6 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
     const int rlow = (int)(rexp + 4.0f * sqrtf(rexp) + 4.0f) + 1;
     if (rlow >= S)
         return false;
-
-    // ---- 1. sample -> threshold (the sample sits in the pair area)
-    auto sample = [&](auto runs_c) {
-        constexpr int RUNS = decltype(runs_c)::value;
-        // all of the wave's runs in flight at once
-        float sv[RUNS / kTkWaves];
-#pragma unroll
-        for (int i = 0; i < RUNS / kTkWaves; ++i) {
-            const int r = wv + kTkWaves * i;
-            sv[i] = vals[(int)(((int64_t)r * (n - 64)) / (RUNS - 1)) + lane];
-        }
-#pragma unroll
-        for (int i = 0; i < RUNS / kTkWaves; ++i)
-            sm.ckey[(wv + kTkWaves * i) * 64 + lane] = fkey(sv[i]);
-    };
-    static_assert(kSampleBig <= 2 * kCap, "the sample fits in ckey and cidx");
-    if (big)
-        sample(std::integral_constant<int, kSampleBig / 64>{});
-    else
-        sample(std::integral_constant<int, kSample / 64>{});
-    __syncthreads();
-    const uint32_t thr = lds_select_rank(sm.ckey, S, (uint32_t)rlow, sm);
 
     // ---- 2. one pass, streamed per wave: wave w scans its own contiguous chunk
     // of the segment in slot order and appends the slots with key >= thr to its
@@ -567,6 +603,40 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
             v[4 * u + 3] = f.w;
         }
     };
+    // the pass's first loads do not depend on the threshold: two steps are
+    // issued now, so that they arrive while the sample is selected (three
+    // would cost a workgroup per CU in registers)
+    float buf[TD][16];
+#pragma unroll
+    for (int d = 0; d < TD - 1; ++d)
+        load(d, buf[d]);
+
+    // ---- 1. sample -> threshold (the sample sits in the pair area)
+    auto sample = [&](auto runs_c) {
+        constexpr int RUNS = decltype(runs_c)::value;
+        // all of the wave's runs in flight at once
+        float sv[RUNS / kTkWaves];
+#pragma unroll
+        for (int i = 0; i < RUNS / kTkWaves; ++i) {
+            const int r = wv + kTkWaves * i;
+            // (32-bit: r * (n - 64) < 2^32 for n < 2^25; the division by a
+            // constant is a multiply-high)
+            sv[i] = vals[(int)(((uint32_t)r * (uint32_t)(n - 64)) / (uint32_t)(RUNS - 1)) + lane];
+        }
+#pragma unroll
+        for (int i = 0; i < RUNS / kTkWaves; ++i)
+            sm.ckey[(wv + kTkWaves * i) * 64 + lane] = fkey(sv[i]);
+    };
+    static_assert(kSampleBig <= 2 * kCap, "the sample fits in ckey and cidx");
+    if (big)
+        sample(std::integral_constant<int, kSampleBig / 64>{});
+    else
+        sample(std::integral_constant<int, kSample / 64>{});
+    __syncthreads();
+    // (a threshold a little below the exact sample key only keeps a few more
+    // slots)
+    const uint32_t thr = lds_window_select(sm.ckey, S, (uint32_t)rlow, sm);
+
     u32x2 *const pairs = (u32x2 *)sm.ckey;     // the pair area (ckey, cidx, hist)
     u32x2 *rgn = pairs + wv * RC;
     uint32_t wcount = 0;                        // kept slots of this wave so far
@@ -600,10 +670,7 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
             wcount += (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
         }
     };
-    float buf[TD][16];
-#pragma unroll
-    for (int d = 0; d < TD; ++d)
-        load(d, buf[d]);
+    load(TD - 1, buf[TD - 1]);
     for (int s0 = 0; s0 < nsteps; s0 += TD) {
 #pragma unroll
         for (int d = 0; d < TD; ++d) {
@@ -650,7 +717,13 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
         }
     __syncthreads();
     // ---- 3. exact K-th key among the kept slots (all K winners are among them)
-    finish_select(thr, 0xFFFFFFFFu, base, 0u, (uint32_t)K, false, K, gidx, gval, sm, true);
+    // the window [thr, largest kept key] (no kept key is above it), so that the
+    // finish's histograms spread over the keys' actual range
+    uint32_t kmn = 0xFFFFFFFFu, kmx = 0u;
+    for (int c = tid; c < (int)base; c += kTkThreads)
+        kmx = max(kmx, sm.ckey[c]);
+    block_minmax(kmn, kmx, sm.misc);
+    finish_select(thr, kmx, base, 0u, (uint32_t)K, false, K, gidx, gval, sm, true);
     return true;
 }
 

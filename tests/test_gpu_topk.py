@@ -1,8 +1,9 @@
 """GPU Top-K on crafted score rows, bit-exact against the oracle's brute force.
 
 The rows kernel and the chunked kernels try a single pass whose threshold comes
-from a sample of 64 runs of 64 consecutive slots; when the kept count misses
-[K, capacity] they fall back to the general selection.  These rows drive both
+from a sample of 64 (128 on rows of 32K slots or more) runs of 64 consecutive
+slots; when the kept count misses [K, capacity] they fall back to the general
+selection.  These rows drive both
 branches: plain random rows, constant rows and coarse alphabets (massive
 ties), ramps, rows whose large values sit exactly on (or exactly off) the
 sampled runs, and signed zeros.
@@ -22,14 +23,20 @@ if not torch.cuda.is_available():
 from indexer_top_sparse_relu_amd import binding as B  # noqa: E402
 
 DEV = "cuda"
-RUNS = 64
+
+
+def sample_runs(n):
+    """Runs of 64 slots the single-pass sample reads: 64 runs, or 128 on rows of
+    at least 32768 slots."""
+    return 128 if n >= 32768 else 64
 
 
 def sampled_mask(n):
-    """Slots the single-pass sample reads: run r starts at r*(n-64)//63."""
+    """Slots the single-pass sample reads: run r starts at r*(n-64)//(runs-1)."""
+    runs = sample_runs(n)
     m = np.zeros(n, bool)
-    for r in range(RUNS):
-        j = (r * (n - 64)) // (RUNS - 1)
+    for r in range(runs):
+        j = (r * (n - 64)) // (runs - 1)
         m[j:j + 64] = True
     return m
 
