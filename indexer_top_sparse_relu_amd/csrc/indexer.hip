@@ -71,6 +71,7 @@ template <int H> struct IdxShape {
 
 constexpr int kIdxWaves = 4;
 constexpr int kIdxTileKeys = 64;
+constexpr int kIdxLinTileKeys = 128;   // key tile of the fp8 linear-term path
 constexpr int kIdxMaxChunk = 8192;     // keys per prefill workgroup, at most
 
 typedef __attribute__((address_space(3))) float lds_f32;
@@ -95,10 +96,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     constexpr bool LIN = (DT == 2) && (H >= 16) && (MT % 2 == 0) && (D == 128);
     __shared__ __align__(16) uint8_t lds_k[2][LIN ? 16 : kIdxTileKeys * RBP];
     __shared__ float lds_ks[2][LIN ? 1 : kIdxTileKeys];
-    __shared__ __align__(16) uint8_t lkr0[LIN ? kIdxTileKeys * 128 : 16];
-    __shared__ __align__(16) uint8_t lkr1[LIN ? kIdxTileKeys * 128 : 16];
-    __shared__ __align__(16) uint8_t lkr2[LIN ? kIdxTileKeys * 128 : 16];
-    __shared__ float lksr[LIN ? 3 * kIdxWaves * kIdxTileKeys : 1];
+    __shared__ __align__(16) uint8_t lkr0[LIN ? kIdxLinTileKeys * 128 : 16];
+    __shared__ __align__(16) uint8_t lkr1[LIN ? kIdxLinTileKeys * 128 : 16];
+    __shared__ __align__(16) uint8_t lkr2[LIN ? kIdxLinTileKeys * 128 : 16];
+    __shared__ float lksr[LIN ? 3 * kIdxWaves * kIdxLinTileKeys : 1];
     __shared__ int lpt[LIN ? kIdxMaxChunk / 16 + 2 : 1];
     constexpr int LTS = 128 + 16;                // padded term row (bank spread, as RBP)
     __shared__ __align__(16) uint8_t lterm[LIN ? kIdxWaves * 32 * LTS : 16];
@@ -279,41 +280,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         const int sal = myscl[col];
         const uint8_t *arow = myterm + col * LTS + half * X::LB;
 
-        // Key tiles: a ring of KST stages of 64 rows x 128 bytes, filled by direct
-        // global->LDS loads (no registers).  The 16-byte chunk c of row r sits at
-        // chunk position c ^ ((r >> 1) & 7): the B-operand reads (16 rows of one
-        // chunk per LDS phase) then hit 16 distinct bank groups.  Wave wv loads
-        // the 1 KB blocks wv and wv + 4 (8 rows each) and its own copy of the
-        // tile's 64 key scales.  Positions past the chunk are clamped to its last
-        // key, so every tile, also one past the end, is a full, in-bounds load.
+        // Key tiles: a ring of KST stages of LT = 128 rows x 128 bytes, filled by
+        // direct global->LDS loads (no registers).  The 16-byte chunk c of row r
+        // sits at chunk position c ^ ((r >> 1) & 7): the B-operand reads (16 rows
+        // of one chunk per LDS phase) then hit 16 distinct bank groups.  Wave wv
+        // loads the 1 KB blocks wv + 4m, m = 0..3 (8 rows each), and its own copy
+        // of the tile's 128 key scales (two loads of 64).  Positions past the
+        // chunk are clamped to its last key, so every tile, also one past the
+        // end, is a full, in-bounds load.
         constexpr int KST = 3;
+        constexpr int LT = kIdxLinTileKeys;
+        constexpr int NB = LT / 8 / kIdxWaves;          // 1 KB row blocks per wave per tile
+        constexpr int NS = LT / 64;                     // key-scale loads per wave per tile
+        const int ntiles = (kb1 - kb0 + LT - 1) / LT;
         auto stage = [&](int st) -> lds_u8 * {
             return st == 0 ? (lds_u8 *)lkr0 : st == 1 ? (lds_u8 *)lkr1 : (lds_u8 *)lkr2;
         };
         lds_f32 *const LKS = (lds_f32 *)lksr;
-        // The lane's three key positions of tile tt (two rows of the key tile
-        // and one key scale) and their physical pages.  The pages are read from
-        // LDS one tile ahead of the loads, inside the previous tile's MFMA work,
-        // so the issue itself waits on nothing.
-        struct Pg { int a, b, c; };
+        // The lane's key positions of tile tt (NB rows of the key tile, NS key
+        // scales) and their physical pages.  The pages are read from LDS one
+        // tile ahead of the loads, inside the previous tile's MFMA work, so the
+        // issue itself waits on nothing.
+        struct Pg { int p[NB + NS]; };
+        auto krow_of = [&](int m, int ln) { return (kIdxWaves * m + wv) * 8 + (ln >> 3); };
         auto kpos = [&](int tt, int ln, int which) {
-            const int t0 = kb0 + tt * kIdxTileKeys;
-            const int r = which == 0 ? wv * 8 + (ln >> 3) : which == 1 ? (kIdxWaves + wv) * 8 + (ln >> 3) : ln;
+            const int t0 = kb0 + tt * LT;
+            const int r = which < NB ? krow_of(which, ln) : 64 * (which - NB) + ln;
             return min(t0 + r, kb1 - 1);
         };
         auto pages = [&](int tt, int ln) {
-            return Pg{lpt[(kpos(tt, ln, 0) >> pshift) - pg0], lpt[(kpos(tt, ln, 1) >> pshift) - pg0],
-                      lpt[(kpos(tt, ln, 2) >> pshift) - pg0]};
+            Pg g;
+#pragma unroll
+            for (int w = 0; w < NB + NS; ++w)
+                g.p[w] = lpt[(kpos(tt, ln, w) >> pshift) - pg0];
+            return g;
         };
         auto issue = [&](int tt, int ln, const Pg &pg) {
             const int st = tt % KST;
-            const int r0 = wv * 8 + (ln >> 3), r1 = (kIdxWaves + wv) * 8 + (ln >> 3);
-            const int64_t p0 = ((int64_t)pg.a << pshift) + (kpos(tt, ln, 0) & pmask);
-            const int64_t p1 = ((int64_t)pg.b << pshift) + (kpos(tt, ln, 1) & pmask);
-            const int64_t p2 = ((int64_t)pg.c << pshift) + (kpos(tt, ln, 2) & pmask);
-            dma_b128(k_idx + p0 * 128 + ((ln & 7) ^ ((r0 >> 1) & 7)) * 16, stage(st) + wv * 1024);
-            dma_b128(k_idx + p1 * 128 + ((ln & 7) ^ ((r1 >> 1) & 7)) * 16, stage(st) + (kIdxWaves + wv) * 1024);
-            dma_b32(k_scale + p2, (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * 64));
+#pragma unroll
+            for (int m = 0; m < NB; ++m) {
+                const int r = krow_of(m, ln);
+                const int64_t pr = ((int64_t)pg.p[m] << pshift) + (kpos(tt, ln, m) & pmask);
+                dma_b128(k_idx + pr * 128 + ((ln & 7) ^ ((r >> 1) & 7)) * 16,
+                         stage(st) + (kIdxWaves * m + wv) * 1024);
+            }
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                const int64_t pr = ((int64_t)pg.p[NB + q] << pshift) + (kpos(tt, ln, NB + q) & pmask);
+                dma_b32(k_scale + pr, (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * LT + 64 * q));
+            }
         };
 
         // Scores go out through a buffer resource spanning this wave's token rows:
@@ -356,25 +371,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         issue(0, lane, pages(0, lane));
         issue(1, lane, pages(1, lane));
         Pg pg_next = pages(2, lane);
+        // memory operations per wave: NL loads per tile, NST score stores per
+        // tile iteration (one fewer in the first)
+        constexpr int NL = NB + NS, NST = 2 * (LT / 32);
         for (int it = 0; it < ntiles; ++it) {
-            // Tile it was issued two iterations back (3 ops per wave); since then
-            // each iteration issued 3 loads and 4 stores (3 in the first), which
-            // may stay in flight.
+            // Tile it was issued two iterations back; since then came the next
+            // tile's loads and the stores of up to two iterations, which may stay
+            // in flight.
             if (it == 0)
-                asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
             else if (it == 1)
-                asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL + NST - 1) : "memory");
             else if (it == 2)
-                asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NST - 1 + NL + NST) : "memory");
             else
-                asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+                asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NST + NL + NST) : "memory");
             __syncthreads();
             const int ln = opaque(lane);
             issue(it + 2, ln, pg_next);
             const int st = it % KST;
-            const int t0 = kb0 + it * kIdxTileKeys;
+            const int t0 = kb0 + it * LT;
 #pragma unroll
-            for (int nt = 0; nt < kIdxTileKeys / 32; ++nt) {
+            for (int nt = 0; nt < LT / 32; ++nt) {
                 const int r = nt * 32 + (ln & 31);
                 const lds_u8 *brow = stage(st) + r * 128;
                 const int f = (r >> 1) & 7, hf = ln >> 5;
@@ -387,7 +405,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                     bop[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 }
                 const int s = t0 + r;
-                const float ks_s = LKS[(st * kIdxWaves + wv) * 64 + r];
+                const float ks_s = LKS[(st * kIdxWaves + wv) * LT + r];
                 // linear term first, reduced to one value per lane right away
                 float La = 0.0f, Lb = 0.0f;
                 {
