@@ -231,10 +231,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         // rows: the weighted query qbar is split into 8 fp8 terms, term t scaled
         // by 2^e_t, and each row's 2^e_t is applied by the MFMA's per-row block
         // scale.  Eight terms carry qbar to full fp32 precision.
-        // Row layout of the 32-row term tile: token tt's term t sits at row
-        // 8*(2*(tt/2) + t/4) + 4*(tt%2) + t%4, so in the 32x32 output the terms of
-        // token tt land in the lanes of half tt%2 (registers 0-7 for tt < 2,
-        // 8-15 for tt >= 2): the lanes that write that token's scores.
+        // Four tokens per wave: the 32-row term tile is a 32x32x64 MFMA A
+        // operand, token tt's term t at row 8*(2*(tt/2) + t/4) + 4*(tt%2) + t%4,
+        // so in the 32x32 output the terms of token tt land in the lanes of half
+        // tt%2 (registers 0-7 for tt < 2, 8-15 for tt >= 2): the lanes that write
+        // that token's scores.  Two tokens per wave: the 16 term rows (row
+        // 8*tt + t) are a 16x16x128 MFMA A operand, half the MFMA work of a
+        // 32-row tile; see the key loop for how its output reaches the writers.
         uint8_t *myterm = lterm + wv * 32 * LTS;
         int *myscl = lscl + wv * 32;
         for (int e = lane; e < 32 * LTS / 16; e += 64)
@@ -269,7 +272,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                     const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(r0, -e), ldexpf(r1, -e), 0, false);
                     r0 -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 0), e);
                     r1 -= ldexpf(__builtin_amdgcn_cvt_f32_fp8(pk, 1), e);
-                    const int row = 8 * (2 * (tt >> 1) + (t >> 2)) + 4 * (tt & 1) + (t & 3);
+                    const int row = TPW == 2 ? 8 * tt + t : 8 * (2 * (tt >> 1) + (t >> 2)) + 4 * (tt & 1) + (t & 3);
                     *(uint16_t *)(myterm + row * LTS + 2 * lane) = (uint16_t)pk;
                     if (lane == 0)
                         myscl[row] = e + 122;                  // with B's 2^-5: 2^(e - 10)
@@ -277,8 +280,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             }
         }
         __syncthreads();
-        const int sal = myscl[col];
-        const uint8_t *arow = myterm + col * LTS + half * X::LB;
+        const int sal = myscl[TPW == 2 ? (lane & 15) : col];
+        const uint8_t *arow = TPW == 2 ? myterm + (lane & 15) * LTS + (lane >> 4) * 32 : myterm + col * LTS + half * X::LB;
 
         // Key tiles: a ring of KST stages of LT = 128 rows x 128 bytes, filled by
         // direct global->LDS loads (no registers).  The 16-byte chunk c of row r
@@ -408,7 +411,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                 const float ks_s = LKS[(st * kIdxWaves + wv) * LT + r];
                 // linear term first, reduced to one value per lane right away
                 float La = 0.0f, Lb = 0.0f;
-                {
+                if constexpr (TPW == 2) {
+                    // Two 16x16x128 MFMAs, keys 0-15 (P) and 16-31 (Q) of the
+                    // N-tile.  Output lane l holds key l%16 and term rows
+                    // 4*(l/16)..+3, so lane row g (16 lanes) holds token g/2's
+                    // terms 4*(g%2)..+3.  After summing its 4 registers, a lane
+                    // needs its partner l^16: v_permlane16_swap(P, Q) gives
+                    // (P row0, Q row0, P row2, Q row2) and (P row1, Q row1, P row3,
+                    // Q row3), whose sum is token g/2's linear term for key l%32,
+                    // in the lanes that write it.
+                    const i32x8 at = *(const i32x8 *)arow;
+                    f32x4 pq[2];
+#pragma unroll
+                    for (int w2 = 0; w2 < 2; ++w2) {
+                        const int rq = nt * 32 + 16 * w2 + (ln & 15);
+                        const lds_u8 *bq = stage(st) + rq * 128;
+                        const int fq = (rq >> 1) & 7, c = 2 * (ln >> 4);
+                        const i32x4 lo = *(const __attribute__((address_space(3))) i32x4 *)(bq + 16 * (c ^ fq));
+                        const i32x4 hi = *(const __attribute__((address_space(3))) i32x4 *)(bq + 16 * ((c + 1) ^ fq));
+                        pq[w2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                            at, i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, f32x4{}, 0, 0, 0,
+                            sal, 0, 122);
+                    }
+                    const float sp = (pq[0][0] + pq[0][1]) + (pq[0][2] + pq[0][3]);
+                    const float sq = (pq[1][0] + pq[1][1]) + (pq[1][2] + pq[1][3]);
+                    const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sp), __float_as_uint(sq), false, false);
+                    La = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+                } else {
                     f32x16 cl = f32x16{};
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)

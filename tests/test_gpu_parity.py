@@ -138,6 +138,14 @@ def test_chunked_prefill_mla_reduced():
     full_check(spec, "mla-prefill-reduced", attn_rows=P.sample_tokens(333, 48, seed=4))
 
 
+@pytest.mark.parametrize("h_i", [8, 16, 32])
+def test_chunked_prefill_mla_fp8_indexer_head_counts(h_i):
+    """fp8 indexer at other head counts: 8 (packed-fp16 epilogue), 16 (four tokens per
+    wave, 32-row linear-term tile), 32 (two tokens per wave, 16-row linear-term tile)."""
+    spec = W.chunked_prefill_mla(cached=3000, T=333).replace(H_I=h_i, seed=40 + h_i)
+    full_check(spec, f"mla-prefill-h{h_i}", attn_rows=P.sample_tokens(333, 16, seed=8))
+
+
 def test_chunked_prefill_mla_full_size_sampled():
     spec = W.chunked_prefill_mla()
     P.say(f"[mla-prefill-full] T={spec.T} ctx={spec.max_ctx}")
