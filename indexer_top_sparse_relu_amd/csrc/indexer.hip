@@ -148,18 +148,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     for (int mt = 0; mt < MT; ++mt) {
         const int R = mt * 32 + col;              // operand row of this lane
         const int tl = wv * TPW + R / H, h = R % H;
-        const bool ok = tl < ntok;
-        const uint8_t *src = q_idx + ((int64_t)(tok0 + (ok ? tl : 0)) * H + h) * RB;
+        // Rows of tokens past the tile's end read the tile's first token: their
+        // products are finite, only ever summed into their own token (whose
+        // weights are zero), and never stored.
+        const uint8_t *src = q_idx + ((int64_t)(tok0 + (tl < ntok ? tl : 0)) * H + h) * RB;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-            typename X::Op v = X::load(src + ks * X::KS * X::ELEM + half * X::LB);
-            a[mt][ks] = ok ? v : typename X::Op{};
-        }
+        for (int ks = 0; ks < NKS; ++ks)
+            a[mt][ks] = X::load(src + ks * X::KS * X::ELEM + half * X::LB);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int Ro = mt * 32 + mfma32_row(i, lane);
             const int to = wv * TPW + Ro / H;
-            const float wv_ = to < ntok ? w[(int64_t)(tok0 + to) * H + Ro % H] : 0.0f;
+            // unconditional load (clamped token), then select: no branch per weight
+            const float wl = w[(int64_t)(tok0 + min(to, ntok - 1)) * H + Ro % H];
+            const float wv_ = to < ntok ? wl : 0.0f;
             if constexpr (F16E) {
                 if (i & 1)
                     wp[mt][i >> 1][1] = (_Float16)wv_;
@@ -169,6 +171,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                 wr[mt][i] = wv_;
             }
         }
+    }
+    if constexpr (LIN) {
+        // opaque from here on, so the selects above are not redone inside the key loop
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                asm volatile("" : "+v"(wr[mt][i]));
     }
     float qs[TPW];
 #pragma unroll
@@ -255,13 +265,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             if (tl >= ntok)
                 break;
             const int tok = tok0 + tl;
-            float r0 = 0.0f, r1 = 0.0f;             // qbar at dims 2*lane, 2*lane+1
+            // qbar at dims 2*lane, 2*lane+1: the H loads are all issued before
+            // the first use, so the sum waits for one memory round trip
             const uint8_t *qp = q_idx + (int64_t)tok * H * 128 + 2 * lane;
+            const float *wt = w + (int64_t)tok * H;
+            int pq[H];
+#pragma unroll
+            for (int h = 0; h < H; ++h)
+                pq[h] = *(const uint16_t *)(qp + h * 128);
+            float r0 = 0.0f, r1 = 0.0f;
+#pragma unroll
             for (int h = 0; h < H; ++h) {
-                const float wh = w[(int64_t)tok * H + h];
-                const int pr = *(const uint16_t *)(qp + h * 128);
-                r0 = fmaf(wh, __builtin_amdgcn_cvt_f32_fp8(pr, 0), r0);
-                r1 = fmaf(wh, __builtin_amdgcn_cvt_f32_fp8(pr, 1), r1);
+                r0 = fmaf(wt[h], __builtin_amdgcn_cvt_f32_fp8(pq[h], 0), r0);
+                r1 = fmaf(wt[h], __builtin_amdgcn_cvt_f32_fp8(pq[h], 1), r1);
             }
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -318,20 +334,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                 g.p[w] = lpt[(kpos(tt, ln, w) >> pshift) - pg0];
             return g;
         };
-        auto issue = [&](int tt, int ln, const Pg &pg) {
+        // load w of tile tt: row block w (w < NB) or key-scale load w - NB
+        auto issue_part = [&](int tt, int ln, const Pg &pg, int w) {
             const int st = tt % KST;
-#pragma unroll
-            for (int m = 0; m < NB; ++m) {
-                const int r = krow_of(m, ln);
-                const int64_t pr = ((int64_t)pg.p[m] << pshift) + (kpos(tt, ln, m) & pmask);
+            const int64_t pr = ((int64_t)pg.p[w] << pshift) + (kpos(tt, ln, w) & pmask);
+            if (w < NB) {
+                const int r = krow_of(w, ln);
                 dma_b128(k_idx + pr * 128 + ((ln & 7) ^ ((r >> 1) & 7)) * 16,
-                         stage(st) + (kIdxWaves * m + wv) * 1024);
+                         stage(st) + (kIdxWaves * w + wv) * 1024);
+            } else {
+                dma_b32(k_scale + pr, (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * LT + 64 * (w - NB)));
             }
+        };
+        auto issue = [&](int tt, int ln, const Pg &pg) {
 #pragma unroll
-            for (int q = 0; q < NS; ++q) {
-                const int64_t pr = ((int64_t)pg.p[NB + q] << pshift) + (kpos(tt, ln, NB + q) & pmask);
-                dma_b32(k_scale + pr, (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * LT + 64 * q));
-            }
+            for (int w = 0; w < NB + NS; ++w)
+                issue_part(tt, ln, pg, w);
         };
 
         // Scores go out through a buffer resource spanning this wave's token rows:
@@ -394,19 +412,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             issue(it + 2, ln, pg_next);
             const int st = it % KST;
             const int t0 = kb0 + it * LT;
-#pragma unroll
-            for (int nt = 0; nt < LT / 32; ++nt) {
+            // B operands of N-tile nt (the key rows and, with two tokens per
+            // wave, the 16-key halves for the linear-term MFMAs), read from LDS
+            // one N-tile ahead, under the previous N-tile's epilogue
+            struct Bt {
+                typename X::Op bop[NKS];
+            };
+            auto load_b = [&](int nt) {
+                Bt b;
                 const int r = nt * 32 + (ln & 31);
                 const lds_u8 *brow = stage(st) + r * 128;
                 const int f = (r >> 1) & 7, hf = ln >> 5;
-                typename X::Op bop[NKS];
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
                     const int c = 2 * hf + 4 * ks;
                     const i32x4 lo = *(const __attribute__((address_space(3))) i32x4 *)(brow + 16 * (c ^ f));
                     const i32x4 hi = *(const __attribute__((address_space(3))) i32x4 *)(brow + 16 * ((c + 1) ^ f));
-                    bop[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    b.bop[ks] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
                 }
+                return b;
+            };
+            auto load_bq = [&](int nt, int w2) {
+                const int rq = nt * 32 + 16 * w2 + (ln & 15);
+                const lds_u8 *bq = stage(st) + rq * 128;
+                const int fq = (rq >> 1) & 7, c = 2 * (ln >> 4);
+                const i32x4 lo = *(const __attribute__((address_space(3))) i32x4 *)(bq + 16 * (c ^ fq));
+                const i32x4 hi = *(const __attribute__((address_space(3))) i32x4 *)(bq + 16 * ((c + 1) ^ fq));
+                return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            };
+            Bt cur = load_b(0);
+#pragma unroll
+            for (int nt = 0; nt < LT / 32; ++nt) {
+                const int r = nt * 32 + (ln & 31);
+                const typename X::Op *bop = cur.bop;
                 const int s = t0 + r;
                 const float ks_s = LKS[(st * kIdxWaves + wv) * LT + r];
                 // linear term first, reduced to one value per lane right away
@@ -423,16 +461,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                     const i32x8 at = *(const i32x8 *)arow;
                     f32x4 pq[2];
 #pragma unroll
-                    for (int w2 = 0; w2 < 2; ++w2) {
-                        const int rq = nt * 32 + 16 * w2 + (ln & 15);
-                        const lds_u8 *bq = stage(st) + rq * 128;
-                        const int fq = (rq >> 1) & 7, c = 2 * (ln >> 4);
-                        const i32x4 lo = *(const __attribute__((address_space(3))) i32x4 *)(bq + 16 * (c ^ fq));
-                        const i32x4 hi = *(const __attribute__((address_space(3))) i32x4 *)(bq + 16 * ((c + 1) ^ fq));
-                        pq[w2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                            at, i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}, f32x4{}, 0, 0, 0,
-                            sal, 0, 122);
-                    }
+                    for (int w2 = 0; w2 < 2; ++w2)
+                        pq[w2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, load_bq(nt, w2), f32x4{}, 0,
+                                                                                  0, 0, sal, 0, 122);
                     const float sp = (pq[0][0] + pq[0][1]) + (pq[0][2] + pq[0][3]);
                     const float sq = (pq[1][0] + pq[1][1]) + (pq[1][2] + pq[1][3]);
                     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sp), __float_as_uint(sq), false, false);
@@ -466,6 +497,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                     for (int ks = 0; ks < NKS; ++ks)
                         c1[m] = X::mma(a[MH + m][ks], bop[ks], c1[m]);
                 }
+                if (nt + 1 < LT / 32)
+                    cur = load_b(nt + 1);
                 epi(c0, 0, s, ks_s, La);
                 if (nt == 0)
                     pg_next = pages(it + 3, ln);
