@@ -72,7 +72,8 @@ template <int H> struct IdxShape {
 constexpr int kIdxWaves = 4;
 constexpr int kIdxTileKeys = 64;
 constexpr int kIdxLinTileKeys = 128;   // key tile of the fp8 linear-term path
-constexpr int kIdxMaxChunk = 8192;     // keys per prefill workgroup, at most
+constexpr int kIdxMaxChunk = 17408;    // keys per prefill workgroup, at most
+constexpr int kIdxChunkTarget = 17408; // prefill chunks: this many keys or fewer, eight at a time
 
 typedef __attribute__((address_space(3))) float lds_f32;
 
@@ -102,7 +103,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     __shared__ float lksr[LIN ? 3 * kIdxWaves * kIdxLinTileKeys : 1];
     __shared__ int lpt[LIN ? kIdxMaxChunk / 16 + 2 : 1];
     constexpr int LTS = 128 + 16;                // padded term row (bank spread, as RBP)
-    __shared__ __align__(16) uint8_t lterm[LIN ? kIdxWaves * 32 * LTS : 16];
+    constexpr int TROWS = TPW == 2 ? 16 : 32;  // used rows of a wave's term tile
+    __shared__ __align__(16) uint8_t lterm[LIN ? kIdxWaves * TROWS * LTS : 16];
     __shared__ int lscl[LIN ? kIdxWaves * 32 : 1];
 
     // ---- workgroup -> (token tile, key chunk): chunk c always runs on XCD c % 8
@@ -248,9 +250,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         // that token's scores.  Two tokens per wave: the 16 term rows (row
         // 8*tt + t) are a 16x16x128 MFMA A operand, half the MFMA work of a
         // 32-row tile; see the key loop for how its output reaches the writers.
-        uint8_t *myterm = lterm + wv * 32 * LTS;
+        uint8_t *myterm = lterm + wv * TROWS * LTS;
         int *myscl = lscl + wv * 32;
-        for (int e = lane; e < 32 * LTS / 16; e += 64)
+        for (int e = lane; e < TROWS * LTS / 16; e += 64)
             ((i32x4 *)myterm)[e] = i32x4{0, 0, 0, 0};
         if (lane < 32)
             myscl[lane] = 127;
@@ -811,7 +813,7 @@ static hipError_t launch_indexer_t(const Batch &bt, const void *q_idx, const flo
     if (bt.max_q >= 8) {
         constexpr int TQ = kIdxWaves * IdxShape<H>::TPW;
         // key chunks: a multiple of 8 (one set per XCD) once the context is long
-        int n_chunks = bt.max_ctx > 8192 ? 8 * ((bt.max_ctx + 8 * 8192 - 1) / (8 * 8192)) : 1;
+        int n_chunks = bt.max_ctx > 8192 ? 8 * ((bt.max_ctx + 8 * kIdxChunkTarget - 1) / (8 * kIdxChunkTarget)) : 1;
         int key_chunk = (bt.max_ctx + n_chunks - 1) / n_chunks;
         key_chunk = (key_chunk + kIdxTileKeys - 1) / kIdxTileKeys * kIdxTileKeys;
         n_chunks = (bt.max_ctx + key_chunk - 1) / key_chunk;
