@@ -162,15 +162,19 @@ __device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, uint32_
     __syncthreads();
 }
 
-// Bin b with sum(hist[b+1..]) < need <= sum(hist[b..]); *gt = sum(hist[b+1..]).
-// Requires 1 <= need <= sum(hist).  Each thread owns 8 consecutive bins.
+// Bin b of hist[0, NB) with sum(hist[b+1..]) < need <= sum(hist[b..]);
+// *gt = sum(hist[b+1..]).  Requires 1 <= need <= sum(hist).  Each thread owns
+// NB / 512 consecutive bins.
+template <int NB>
 __device__ __forceinline__ void find_bin(const TkSmem &sm, uint32_t need, int &b_out, uint32_t &gt_out)
 {
+    constexpr int BT = NB / kTkThreads;
+    static_assert(NB % kTkThreads == 0, "bins per thread");
     const int t = threadIdx.x;
-    uint32_t h[8], local = 0;
+    uint32_t h[BT], local = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        h[j] = sm.hist[t * 8 + j];
+    for (int j = 0; j < BT; ++j) {
+        h[j] = sm.hist[t * BT + j];
         local += h[j];
     }
     uint32_t total;
@@ -179,9 +183,9 @@ __device__ __forceinline__ void find_bin(const TkSmem &sm, uint32_t need, int &b
     if (need > above && need <= above + local) {
         uint32_t acc = above;
 #pragma unroll
-        for (int j = 7; j >= 0; --j) {
+        for (int j = BT - 1; j >= 0; --j) {
             if (acc + h[j] >= need) {
-                sm.misc[40] = (uint32_t)(t * 8 + j);
+                sm.misc[40] = (uint32_t)(t * BT + j);
                 sm.misc[41] = acc;
                 break;
             }
@@ -199,7 +203,8 @@ __device__ __forceinline__ void find_bin(const TkSmem &sm, uint32_t need, int &b
 // in slot order.  Resolves the exact K-th key inside LDS (ties to the lowest
 // slots), then merges the two ascending runs into gidx (and gval).
 // direct (only with above == 0): the K selected slots go straight to gidx/gval
-// in slot order, without the okey/oidx staging.
+// in slot order, without the okey/oidx staging.  NB: histogram bins in sm.hist.
+template <int NB>
 __device__ void finish_select(uint32_t lo, uint32_t hi, uint32_t cnt, uint32_t above, uint32_t need, bool single,
                               int K, int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm,
                               bool direct = false)
@@ -210,10 +215,12 @@ __device__ void finish_select(uint32_t lo, uint32_t hi, uint32_t cnt, uint32_t a
         const int C = (int)min(cnt, (uint32_t)kCap);
         uint32_t wl = lo, wh = hi, needw = need;
         bool all_in = false;
-        // each pass narrows a window of width W to at most W / 4096 (or stops): <= 3 passes
-        for (int pass = 0; pass < 4 && wl != wh && !all_in; ++pass) {
-            const int sh = max(0, bitlen(wh - wl) - 12);
-            for (int b = tid; b < kBins; b += kTkThreads)
+        // each pass narrows a window of width W to at most W / NB (or stops)
+        constexpr int LB = __builtin_ctz(NB);
+        static_assert((NB & (NB - 1)) == 0, "power-of-two bins");
+        for (int pass = 0; pass < (32 + LB - 1) / LB && wl != wh && !all_in; ++pass) {
+            const int sh = max(0, bitlen(wh - wl) - LB);
+            for (int b = tid; b < NB; b += kTkThreads)
                 sm.hist[b] = 0u;
             __syncthreads();
             for (int c = tid; c < C; c += kTkThreads) {
@@ -224,7 +231,7 @@ __device__ void finish_select(uint32_t lo, uint32_t hi, uint32_t cnt, uint32_t a
             __syncthreads();
             int bsel;
             uint32_t gt;
-            find_bin(sm, needw, bsel, gt);
+            find_bin<NB>(sm, needw, bsel, gt);
             const uint32_t hb = sm.hist[bsel];
             needw -= gt;
             const uint64_t nlo = (uint64_t)wl + ((uint64_t)bsel << sh);
@@ -399,7 +406,7 @@ __device__ void select_topk(const float *__restrict__ vals, const int32_t *__res
         }
         int bsel;
         uint32_t gt;
-        find_bin(sm, need, bsel, gt);
+        find_bin<kBins>(sm, need, bsel, gt);
         cnt = sm.hist[bsel];
         const uint64_t nlo = (uint64_t)lo + ((uint64_t)bsel << sh);
         const uint64_t nhi = min((uint64_t)hi, nlo + ((1ull << sh) - 1ull));
@@ -469,46 +476,18 @@ __device__ void select_topk(const float *__restrict__ vals, const int32_t *__res
         __syncthreads();
     }
 
-    finish_select(lo, hi, cnt, above, need, single, K, gidx, gval, sm);
+    finish_select<kBins>(lo, hi, cnt, above, need, single, K, gidx, gval, sm);
 }
 
-// rank-th largest key (1 <= rank <= cnt) of keys[0, cnt) in LDS: a radix
-// select over three digit levels (12, 12 and 8 bits).
-// With levels == 2 the low 8 bits are not resolved: the result is the lower
-// edge of the 256-key bucket holding the rank-th key (a key at most that rank).
-__device__ uint32_t lds_select_rank(const uint32_t *keys, int cnt, uint32_t rank, const TkSmem &sm, int levels = 3)
-{
-    const int tid = threadIdx.x;
-    uint32_t prefix = 0u, pmask = 0u, need = rank;
-#pragma unroll 1
-    for (int lv = 0; lv < levels; ++lv) {
-        const int sh = lv == 0 ? 20 : (lv == 1 ? 8 : 0);
-        const uint32_t dm = lv == 2 ? 0xFFu : 0xFFFu;
-        for (int b = tid; b < kBins; b += kTkThreads)
-            sm.hist[b] = 0u;
-        __syncthreads();
-        for (int c = tid; c < cnt; c += kTkThreads) {
-            const uint32_t k = keys[c];
-            if ((k & pmask) == prefix)
-                atomicAdd(&sm.hist[(k >> sh) & dm], 1u);
-        }
-        __syncthreads();
-        int b;
-        uint32_t gt;
-        find_bin(sm, need, b, gt);
-        need -= gt;
-        prefix |= (uint32_t)b << sh;
-        pmask |= dm << sh;
-    }
-    return prefix;
-}
-
-// A key at most the rank-th largest of keys[0, cnt) (rank >= 1), within 2^-12
-// of the keys' range above it: a 4096-bin histogram over the keys' actual range
-// [min, max] (so the bins, and their LDS atomics, spread out), then one over
-// the bin holding that rank.  Returns the lower edge of the final bin.
+// A key at most the rank-th largest of keys[0, cnt) (rank >= 1), within a
+// factor 1/NB^2 of the keys' range above it: an NB-bin histogram over the keys'
+// actual range [min, max] (so the bins, and their LDS atomics, spread out),
+// then one over the bin holding that rank.  Returns the lower edge of the final
+// bin.
+template <int NB>
 __device__ uint32_t lds_window_select(const uint32_t *keys, int cnt, uint32_t rank, const TkSmem &sm)
 {
+    constexpr int LB = __builtin_ctz(NB);
     const int tid = threadIdx.x;
     uint32_t mn = 0xFFFFFFFFu, mx = 0u;
     for (int c = tid; c < cnt; c += kTkThreads) {
@@ -519,8 +498,8 @@ __device__ uint32_t lds_window_select(const uint32_t *keys, int cnt, uint32_t ra
     uint32_t lo = mn, span = mx - mn, need = rank;     // the window [lo, lo + span]
 #pragma unroll 1
     for (int lv = 0; lv < 2; ++lv) {
-        const int sh = max(0, bitlen(span) - 12);       // (span >> sh) < 4096
-        for (int b = tid; b < kBins; b += kTkThreads)
+        const int sh = max(0, bitlen(span) - LB);       // (span >> sh) < NB
+        for (int b = tid; b < NB; b += kTkThreads)
             sm.hist[b] = 0u;
         __syncthreads();
         for (int c = tid; c < cnt; c += kTkThreads) {
@@ -531,7 +510,7 @@ __device__ uint32_t lds_window_select(const uint32_t *keys, int cnt, uint32_t ra
         __syncthreads();
         int b;
         uint32_t gt;
-        find_bin(sm, need, b, gt);
+        find_bin<NB>(sm, need, b, gt);
         need -= gt;
         lo += (uint32_t)b << sh;
         if (sh == 0)
@@ -551,7 +530,9 @@ __device__ uint32_t lds_window_select(const uint32_t *keys, int cnt, uint32_t ra
 // written out.  Returns false, having written nothing, when the kept count
 // falls outside [K, kCap] (or a wave's share overflows its LDS region); the
 // caller then runs the general selection, so the result never depends on the
-// sample.
+// sample.  NB: histogram bins at sm.hist (the pair area is ckey, cidx and those
+// bins); TD: wave steps of loads in flight.
+template <int NB, int TD>
 __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad4, int idx0, int K,
                                  int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
 {
@@ -576,9 +557,8 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
     // from ballots (no LDS traffic).  A region that overflows sends the
     // segment to the general path.
     constexpr int WST = 1024;                   // slots per wave step: 4 runs of 64 lanes x 4
-    constexpr int PC = kCap + kBins / 2;        // (key, index) pairs in ckey, cidx, hist
+    constexpr int PC = kCap + NB / 2;           // (key, index) pairs in ckey, cidx, hist
     constexpr int RC = PC / kTkWaves;           // region pairs per wave
-    constexpr int TD = 3;                       // wave steps in flight
     static_assert(PC % kTkThreads == 0, "concatenation: every thread moves PC / kTkThreads pairs");
     const int wchunk = (n + kTkWaves * WST - 1) / (kTkWaves * WST) * WST;
     const int c0 = min(n, wv * wchunk), c1 = min(n, c0 + wchunk);
@@ -603,9 +583,8 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
             v[4 * u + 3] = f.w;
         }
     };
-    // the pass's first loads do not depend on the threshold: two steps are
-    // issued now, so that they arrive while the sample is selected (three
-    // would cost a workgroup per CU in registers)
+    // the pass's first loads do not depend on the threshold: TD - 1 steps are
+    // issued now, so that they arrive while the sample is selected
     float buf[TD][16];
 #pragma unroll
     for (int d = 0; d < TD - 1; ++d)
@@ -635,7 +614,7 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
     __syncthreads();
     // (a threshold a little below the exact sample key only keeps a few more
     // slots)
-    const uint32_t thr = lds_window_select(sm.ckey, S, (uint32_t)rlow, sm);
+    const uint32_t thr = lds_window_select<NB>(sm.ckey, S, (uint32_t)rlow, sm);
 
     u32x2 *const pairs = (u32x2 *)sm.ckey;     // the pair area (ckey, cidx, hist)
     u32x2 *rgn = pairs + wv * RC;
@@ -723,7 +702,7 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
     for (int c = tid; c < (int)base; c += kTkThreads)
         kmx = max(kmx, sm.ckey[c]);
     block_minmax(kmn, kmx, sm.misc);
-    finish_select(thr, kmx, base, 0u, (uint32_t)K, false, K, gidx, gval, sm, true);
+    finish_select<NB>(thr, kmx, base, 0u, (uint32_t)K, false, K, gidx, gval, sm, true);
     return true;
 }
 
@@ -749,7 +728,10 @@ static size_t tk_smem_bytes(int K)
 }
 
 // The single pass alone needs no output staging (its selection is written
-// straight out): 48.25 KB, three workgroups per CU instead of two.
+// straight out): 48.25 KB, three workgroups per CU instead of two.  (With
+// 1024-bin histograms, 36.25 KB, and two steps of loads in flight, four fit;
+// measured at the benchmark that was 2% slower: the selects need one more
+// histogram level and the pass has fewer loads in flight.)
 __device__ __forceinline__ TkSmem tk_smem_fast()
 {
     extern __shared__ __align__(16) uint32_t tk_lds[];
@@ -781,7 +763,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_fast_kernel(Batch bt, co
     int32_t *o = out + (int64_t)row * K;
     // rows start 16-byte aligned and can be read up to a multiple of 4 slots
     // when the row stride is a multiple of 4 floats
-    if (!select_topk_fast(vals, n, (ld & 3) == 0, 0, K, o, nullptr, sm) && threadIdx.x == 0)
+    if (!select_topk_fast<kBins, 3>(vals, n, (ld & 3) == 0, 0, K, o, nullptr, sm) && threadIdx.x == 0)
         o[0] = kTkPending;
 }
 
@@ -812,7 +794,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(Batch bt, const 
     const int64_t o = (int64_t)row * cand_ld + (int64_t)c * K;
     const TkSmem sm = tk_smem(K);
     const float *vals = scores + (int64_t)row * ld + j0;
-    if (!select_topk_fast(vals, len, (ld & 3) == 0, j0, K, cidx + o, cval + o, sm))
+    if (!select_topk_fast<kBins, 3>(vals, len, (ld & 3) == 0, j0, K, cidx + o, cval + o, sm))
         select_topk<false>(vals, nullptr, len, j0, K, cidx + o, cval + o, sm);
 }
 
