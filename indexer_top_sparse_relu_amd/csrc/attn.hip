@@ -358,11 +358,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int j1 = min(K, j0 + split_len);
     const int nslots = max(0, j1 - j0);
     const int32_t *irow = idx + (int64_t)tok * K + j0;
+    // Q^T operand: head h, dims 16ks + 8hq .. +7.  Issued first, so that its
+    // loads overlap the slot resolution below; the rare rerun loads it again.
+    struct QOp {
+        bf16x8 v[NKQ];
+    };
+    auto load_q = [&]() {
+        QOp r;
+        const uint16_t *qp = q + ((int64_t)tok * Hq + h) * DQK + 8 * hq;
+#pragma unroll
+        for (int ks = 0; ks < NKQ; ++ks)
+            r.v[ks] = *(const bf16x8 *)(qp + 16 * ks);
+        return r;
+    };
+    const QOp q0 = load_q();
     const int row0 = (int)phys_row(bt, b, 0);      // a valid row of this sequence
     {
-        for (int j = tid; j < nslots; j += 64 * NW) {
-            const int s = irow[j];
-            prow[j] = s >= 0 ? (int)phys_row(bt, b, s) : -1 - row0;
+        // every slot's index, then every page-table entry: two memory round
+        // trips in all (reads past the list re-read slot 0 and are dropped)
+        constexpr int PS = kMaxSplit / (64 * NW);
+        int sv[PS];
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            const int j = tid + 64 * NW * u;
+            sv[u] = irow[j < nslots ? j : 0];
+        }
+        int pg[PS];
+#pragma unroll
+        for (int u = 0; u < PS; ++u)
+            pg[u] = bt.page_table[(int64_t)b * bt.max_pages + ((sv[u] >= 0 ? sv[u] : 0) >> bt.page_shift)];
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            const int j = tid + 64 * NW * u;
+            const int pr = (pg[u] << bt.page_shift) + (sv[u] & ((1 << bt.page_shift) - 1));
+            if (j < nslots)
+                prow[j] = sv[u] >= 0 ? pr : -1 - row0;
         }
     }
     f32x16 o[NDT];
@@ -414,17 +444,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // One pass over the index list.  mode 0: reference from the first valid
     // keys, accumulate into oa; mode 1: exact maximum only (m_true), no P V;
     // mode 2: reference m_ref as given, accumulate into oa.
-    auto run = [&](f32x16 (&oa)[NDT], const int mode) {
-    // Q^T operand: head h, dims 16ks + 8hq .. +7.  Loaded per pass, so that
-    // nothing of it is live in the epilogue (the rare rerun loads it again).
+    auto run = [&](f32x16 (&oa)[NDT], const int mode, const QOp &qo) {
+    const bf16x8 *qop = qo.v;
     bool have_ref = false;      // mode 0: the reference has been set from some valid key
-    bf16x8 qop[NKQ];
-    {
-        const uint16_t *qp = q + ((int64_t)tok * Hq + h) * DQK + 8 * hq;
-#pragma unroll
-        for (int ks = 0; ks < NKQ; ++ks)
-            qop[ks] = *(const bf16x8 *)(qp + 16 * ks);
-    }
     // Every pass issues exactly KCB loads per wave for each of the tiles
     // 0 .. ntiles+2: past the end of the list src_of falls back to a valid row
     // of the sequence and the data lands in a ring buffer nobody reads.  The
@@ -707,14 +729,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     return !(l_tot <= 0x1p64f) || probe != 0.0f;
     };
 
-    run(o, 0);
+    run(o, 0, q0);
     over = store(o);
     if (__syncthreads_or(over)) {
         // rare: some head's terms outgrew 2^64 relative to its first keys; find
         // the exact maximum, then rerun with it as the reference (terms <= 1).
         // The max-only pass does not touch o; o is cleared only after it, so no
         // second accumulator array is ever live.
-        run(o, 1);
+        run(o, 1, load_q());
         __syncthreads();
         m_ref = m_true;
         l_run = 0.0f;
@@ -722,7 +744,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
             o[dt] = f32x16{};
-        run(o, 2);
+        run(o, 2, load_q());
         store(o);
     }
 }
