@@ -31,7 +31,9 @@
  *   - causal candidates of query token i are positions s <= pos(i);
  *   - Top-K orders by (score descending, position ascending);
  *   - rows with n <= K take all n positions, the rest of the row is -1;
- *   - output gate  y = o * sigmoid(G), G per channel or per head.
+ *   - output gate  y = o * sigmoid(G), G per channel or per head;
+ *   - cache append: fp8 indexer keys as e4m3fn codes with a per-token scale
+ *     max|x| / 448, nearest-even, saturating (see that section).
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -356,5 +358,101 @@ void orc_dense_attn(const orc_batch *bt, int dtype, const void *q, int Hq, int d
             }
             free(logit);
         }
+    }
+}
+
+/* ------------------------------------------- cache append + fp8 quantisation
+ * The step before the path: the new tokens' rows go into the paged caches.
+ * [HAT §5 item 2]: the cache organisation decides indexing efficiency;
+ * [F2S "Engineering Considerations" item 1]: paged cache management is on
+ * the critical path; [HAT §5 item 3]: the indexer is sensitive to numeric
+ * range in low precision.
+ * Reading (the pages fix no format): an fp8 indexer key is stored as OCP
+ * e4m3fn codes with one fp32 scale per token, s = max_d |x_d| / 448 (448 is
+ * the largest e4m3fn value), code_d = e4m3fn(x_d / s) rounded to nearest,
+ * ties to the even code, saturating at +-448.  s and x_d / s are single
+ * precision operations: they decide an integer code, so the oracle takes
+ * them in the kernel's precision.  A row of zeros gets s = 0 and codes 0. */
+
+/* e4m3fn code of y: the representable value nearest to y, ties to the code
+ * with an even mantissa; |y| >= 448 gives +-448; NaN gives S.1111.111. */
+uint8_t orc_fp8_encode(float y)
+{
+    if (isnan(y))
+        return 0x7F;
+    int sign = signbit(y) ? 1 : 0;
+    double a = fabs((double)y);
+    if (a >= 448.0)
+        return (uint8_t)((sign << 7) | 0x7E);
+    /* binade [2^E, 2^(E+1)) holds 8 steps of 2^(E-3) for E >= -6; below 2^-6
+     * (subnormals) the step stays 2^-9 */
+    int E = a > 0.0 ? ilogb(a) : -6;
+    if (E < -6)
+        E = -6;
+    double q = ldexp(1.0, E - 3);
+    double r = rint(a / q);               /* a / q is exact; rint: nearest, ties to even */
+    double v = r * q;                     /* <= 448 since a < 448 */
+    int ef, mant;
+    if (v < ldexp(1.0, -6)) {
+        ef = 0;
+        mant = (int)(v / ldexp(1.0, -9));
+    } else {
+        int E2 = ilogb(v);
+        ef = E2 + 7;
+        mant = (int)(v / ldexp(1.0, E2 - 3)) - 8;
+    }
+    return (uint8_t)((sign << 7) | (ef << 3) | mant);
+}
+
+static float loadf(int dtype, const void *base, int64_t i)
+{
+    return dtype == ORC_F32 ? ((const float *)base)[i] : (float)orc_bf16(((const uint16_t *)base)[i]);
+}
+
+/* One fp8 scale per row of x [rows, cols] (bf16 or f32), codes per element. */
+void orc_quantize_rows(int src_dtype, const void *x, int64_t rows, int64_t cols, uint8_t *codes, float *scales)
+{
+    for (int64_t r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int64_t c = 0; c < cols; ++c) {
+            float v = fabsf(loadf(src_dtype, x, r * cols + c));
+            amax = v > amax ? v : amax;
+        }
+        const float s = amax / 448.0f;
+        scales[r] = s;
+        for (int64_t c = 0; c < cols; ++c) {
+            const float v = loadf(src_dtype, x, r * cols + c);
+            codes[r * cols + c] = amax > 0.0f ? orc_fp8_encode(v / s) : 0;
+        }
+    }
+}
+
+/* Write new token i's rows at the physical row of its position pos(i):
+ *   k_cache[row, 0:d_qk] = k_new[i, :]; v_cache[row, 0:d_v] = v_new[i, :]
+ *   (v_new NULL: the latent layout, V is part of the K row);
+ *   k_idx_cache[row, :] = k_idx_new[i, :] (copied when idx_dtype ==
+ *   src_dtype) or its fp8 codes with k_scale_cache[row] = its scale.
+ * Caches are raw element arrays indexed by physical row (row stride
+ * row_stride elements for K/V, d_i for the indexer keys). */
+void orc_cache_append(const orc_batch *bt, int64_t T, int kv_dtype, const void *k_new, int d_qk, const void *v_new,
+                      int d_v, void *k_cache, void *v_cache, int64_t row_stride, int src_dtype,
+                      const void *k_idx_new, int d_i, int idx_dtype, void *k_idx_cache, float *k_scale_cache)
+{
+    const int64_t esz = kv_dtype == ORC_F32 ? 4 : 2;
+    const int64_t isz = src_dtype == ORC_F32 ? 4 : 2;
+    for (int64_t i = 0; i < T; ++i) {
+        int b;
+        const int64_t pos = pos_of(bt, i, &b);
+        const int64_t row = phys_row(bt, b, pos);
+        memcpy((char *)k_cache + row * row_stride * esz, (const char *)k_new + i * d_qk * esz, (size_t)(d_qk * esz));
+        if (v_new)
+            memcpy((char *)v_cache + row * row_stride * esz, (const char *)v_new + i * d_v * esz,
+                   (size_t)(d_v * esz));
+        if (idx_dtype == ORC_FP8)
+            orc_quantize_rows(src_dtype, (const char *)k_idx_new + i * d_i * isz, 1, d_i,
+                              (uint8_t *)k_idx_cache + row * d_i, k_scale_cache + row);
+        else
+            memcpy((char *)k_idx_cache + row * d_i * isz, (const char *)k_idx_new + i * d_i * isz,
+                   (size_t)(d_i * isz));
     }
 }

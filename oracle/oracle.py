@@ -70,6 +70,11 @@ def lib():
                                       vp, ctypes.c_int, vp, ctypes.c_int, dbl, vp, i64, vp, vp]
         L.orc_dense_attn.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, i64,
                                      vp, ctypes.c_int, dbl, vp, i64, vp]
+        L.orc_fp8_encode.restype = ctypes.c_uint8
+        L.orc_fp8_encode.argtypes = [ctypes.c_float]
+        L.orc_quantize_rows.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp]
+        L.orc_cache_append.argtypes = [vp, i64, ctypes.c_int, vp, ctypes.c_int, vp, ctypes.c_int, vp, vp, i64,
+                                       ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, vp]
         _lib = L
     return _lib
 
@@ -224,3 +229,42 @@ def pipeline(inp: Inputs, K: int, rows=None, scale: Optional[float] = None):
     idx = topk(sc, n, K)
     out = sparse_attn(inp, idx, rows, scale)
     return sc, idx, out
+
+
+# ------------------------------------------------ cache append + fp8 quantisation
+
+def fp8_encode(y) -> np.ndarray:
+    """e4m3fn codes of float32 values: nearest, ties to even, saturating at +-448."""
+    y = np.ascontiguousarray(y, dtype=np.float32).ravel()
+    return np.array([lib().orc_fp8_encode(float(v)) for v in y], dtype=np.uint8)
+
+
+def quantize_rows(x: np.ndarray, src_dtype: str):
+    """Per-row fp8 quantisation of x [rows, cols] (f32 values, or raw bf16 bits as uint16):
+    returns (codes uint8 [rows, cols], scales float32 [rows]) with scale = max|x| / 448."""
+    x = np.ascontiguousarray(x)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols), np.uint8)
+    scales = np.zeros(rows, np.float32)
+    lib().orc_quantize_rows(DT[src_dtype], x.ctypes.data, rows, cols, codes.ctypes.data, scales.ctypes.data)
+    return codes, scales
+
+
+def cache_append(*, q_start, ctx_len, page_table, page_size, kv_dtype, k_new, v_new, k_cache, v_cache,
+                 src_dtype, k_idx_new, idx_dtype, k_idx_cache, k_scale_cache=None):
+    """Apply the cache append in place to host raw arrays.  Caches are indexed by physical row:
+    k_cache / v_cache [rows, row_stride], k_idx_cache [rows, d_i], k_scale_cache [rows]."""
+    q_start = _c(q_start, np.int32)
+    ctx_len = _c(ctx_len, np.int32)
+    page_table = _c(page_table, np.int32)
+    bt = _Batch(int(ctx_len.shape[0]), int(page_size), int(page_table.shape[1]), 0,
+                q_start.ctypes.data, ctx_len.ctypes.data, page_table.ctypes.data)
+    for a in (k_cache, v_cache, k_idx_cache, k_scale_cache):
+        if a is not None and not a.flags.c_contiguous:
+            raise ValueError("caches must be contiguous (they are written in place)")
+    k_new, v_new, k_idx_new = _c(k_new), _c(v_new), _c(k_idx_new)
+    T = int(q_start[-1])
+    lib().orc_cache_append(ctypes.byref(bt), T, DT[kv_dtype], _p(k_new), int(k_new.shape[-1]), _p(v_new),
+                           0 if v_new is None else int(v_new.shape[-1]), _p(k_cache), _p(v_cache),
+                           int(k_cache.shape[-1]), DT[src_dtype], _p(k_idx_new), int(k_idx_new.shape[-1]),
+                           DT[idx_dtype], _p(k_idx_cache), _p(k_scale_cache))

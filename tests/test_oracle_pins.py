@@ -484,3 +484,130 @@ def test_small_k_pipeline_selects_planted_needle():
     inp.k_idx.reshape(-1, spec.d_I)[s] = 10.0 * inp.q_idx[i].sum(0)
     sc, idx, _ = O.pipeline(inp, spec.K, rows=[i])
     assert s in idx[0]
+
+
+# ------------------------------------------------ cache append + fp8 quantisation
+
+def _fp8_finite_codes():
+    tab = O.fp8_table()
+    return [c for c in range(256) if not math.isnan(tab[c])], tab
+
+
+def test_fp8_encode_round_trips_every_finite_code():
+    codes, tab = _fp8_finite_codes()
+    got = O.fp8_encode(np.array([tab[c] for c in codes], np.float32))
+    # -0 keeps its sign bit; every other finite value encodes back to its own code
+    assert list(got) == codes
+
+
+def test_fp8_encode_midpoints_round_to_the_even_code():
+    codes, tab = _fp8_finite_codes()
+    pos = sorted(c for c in codes if c < 0x80)            # 0x00 .. 0x7E, ascending values
+    for lo, hi in zip(pos[:-1], pos[1:]):
+        mid = np.float32((tab[lo] + tab[hi]) / 2)          # exact: one bit more than e4m3 has
+        assert float(mid) == (tab[lo] + tab[hi]) / 2
+        even = lo if (lo & 1) == 0 else hi
+        above = np.nextafter(mid, np.float32(np.inf))
+        below = np.nextafter(mid, np.float32(0))
+        got = O.fp8_encode([mid, above, below, -mid])
+        assert list(got) == [even, hi, lo, even | 0x80], (lo, hi, float(mid))
+
+
+def test_fp8_encode_matches_torch_in_range_and_saturates():
+    rng = np.random.default_rng(7)
+    y = np.concatenate([rng.uniform(-448, 448, 4000), rng.standard_normal(4000) * 0.01,
+                        rng.standard_normal(2000) * 2.0 ** rng.integers(-12, 8, 2000)]).astype(np.float32)
+    y = y[np.abs(y) <= 448]
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp8_encode(y), want)
+    big = O.fp8_encode([448.0, 449.0, 463.9, 464.0, 1e30, -1e30, -500.0])
+    assert list(big) == [0x7E] * 5 + [0xFE] * 2
+    assert O.fp8_encode([np.nan])[0] == 0x7F
+
+
+def test_quantize_rows_scale_and_codes_closed_forms():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((6, 64)).astype(np.float32)
+    x[0] = 0.0                                          # zero row: scale 0, codes 0
+    x[1, 5] = -448.0                                    # amax 448: scale exactly 1, codes = e4m3fn(x)
+    x[1] = np.clip(x[1], -448, 448)
+    codes, scales = O.quantize_rows(x, "f32")
+    assert scales[0] == 0 and not codes[0].any()
+    assert scales[1] == 1.0 and np.array_equal(codes[1], O.fp8_encode(x[1]))
+    amax = np.abs(x).max(axis=1)
+    assert np.array_equal(scales[2:], (amax[2:] / np.float32(448)).astype(np.float32))
+    # every row reaches +-448 at its largest element
+    tab = O.fp8_table()
+    for r in range(2, 6):
+        j = int(np.argmax(np.abs(x[r])))
+        assert abs(tab[codes[r, j]]) == 448.0
+
+
+def test_quantize_rows_power_of_two_invariance_and_error_bound():
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((4, 128)) * 3).astype(np.float32)
+    c0, s0 = O.quantize_rows(x, "f32")
+    for k in (-20, -3, 5, 40):
+        ck, sk = O.quantize_rows((x * np.float32(2.0 ** k)).astype(np.float32), "f32")
+        assert np.array_equal(ck, c0) and np.array_equal(sk, (s0 * np.float32(2.0 ** k)).astype(np.float32))
+    tab = O.fp8_table()
+    deq = tab[c0] * s0[:, None]
+    y = x / s0[:, None]
+    normal = np.abs(y) >= 2.0 ** -6
+    # half a step: 2^-4 relative in the normal range, 2^-10 * s below it
+    assert np.all(np.abs(deq - x)[normal] <= (2.0 ** -4) * np.abs(x)[normal] * (1 + 1e-6))
+    assert np.all(np.abs(deq - x)[~normal] <= (2.0 ** -10) * np.broadcast_to(s0[:, None], x.shape)[~normal] * 1.0001)
+
+
+def test_quantize_rows_bf16_input_equals_f32_of_the_same_values():
+    rng = np.random.default_rng(10)
+    bits = (rng.integers(0, 2 ** 16, (3, 32)) & 0xFF7F | 0x3C00).astype(np.uint16)   # finite, moderate
+    vals = np.array([[O.bf16_value(int(b)) for b in row] for row in bits], np.float32)
+    cb, sb = O.quantize_rows(bits, "bf16")
+    cf, sf = O.quantize_rows(vals, "f32")
+    assert np.array_equal(cb, cf) and np.array_equal(sb, sf)
+
+
+def test_cache_append_writes_the_rows_the_position_rule_names():
+    # two sequences over 4-row pages with a shuffled page table:
+    #   seq 0: ctx 6, 2 new tokens -> positions 4, 5; its pages are [3, 0] -> rows 0, 1
+    #   seq 1: ctx 3, 3 new tokens -> positions 0, 1, 2; its page is [2]    -> rows 8, 9, 10
+    q_start = np.array([0, 2, 5], np.int32)
+    ctx_len = np.array([6, 3], np.int32)
+    page_table = np.array([[3, 0], [2, 1]], np.int32)
+    rows_expected = [0, 1, 8, 9, 10]
+    R, dqk, dv, di = 16, 8, 4, 16
+    rng = np.random.default_rng(11)
+    k_new = rng.integers(0, 2 ** 16, (5, dqk)).astype(np.uint16)
+    v_new = rng.integers(0, 2 ** 16, (5, dv)).astype(np.uint16)
+    kidx = (rng.standard_normal((5, di)) * 2).astype(np.float32)
+    k_cache = np.full((R, dqk), 7, np.uint16)
+    v_cache = np.full((R, dqk), 9, np.uint16)
+    kic = np.full((R, di), 5, np.uint8)
+    ksc = np.full(R, -1.0, np.float32)
+    O.cache_append(q_start=q_start, ctx_len=ctx_len, page_table=page_table, page_size=4, kv_dtype="bf16",
+                   k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, src_dtype="f32",
+                   k_idx_new=kidx, idx_dtype="fp8", k_idx_cache=kic, k_scale_cache=ksc)
+    codes, scales = O.quantize_rows(kidx, "f32")
+    for i, r in enumerate(rows_expected):
+        assert np.array_equal(k_cache[r], k_new[i])
+        assert np.array_equal(v_cache[r, :dv], v_new[i]) and np.all(v_cache[r, dv:] == 9)
+        assert np.array_equal(kic[r], codes[i]) and ksc[r] == scales[i]
+    others = [r for r in range(R) if r not in rows_expected]
+    assert np.all(k_cache[others] == 7) and np.all(v_cache[others] == 9)
+    assert np.all(kic[others] == 5) and np.all(ksc[others] == -1.0)
+
+
+def test_cache_append_copies_same_dtype_keys_and_skips_v_for_latent_rows():
+    q_start = np.array([0, 1], np.int32)
+    ctx_len = np.array([5], np.int32)
+    page_table = np.array([[0, 1]], np.int32)         # identity: position 4 -> row 4
+    k_cache = np.zeros((8, 6), np.float32)
+    kic = np.zeros((8, 4), np.uint16)
+    k_new = np.arange(6, dtype=np.float32)[None] + 1
+    kidx = np.array([[1, 2, 3, 4]], np.uint16)
+    O.cache_append(q_start=q_start, ctx_len=ctx_len, page_table=page_table, page_size=4, kv_dtype="f32",
+                   k_new=k_new, v_new=None, k_cache=k_cache, v_cache=k_cache, src_dtype="bf16",
+                   k_idx_new=kidx, idx_dtype="bf16", k_idx_cache=kic)
+    assert np.array_equal(k_cache[4], k_new[0]) and not np.delete(k_cache, 4, axis=0).any()
+    assert np.array_equal(kic[4], kidx[0]) and not np.delete(kic, 4, axis=0).any()
