@@ -170,6 +170,49 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype,
                                 float softmax_scale, void *out, float *lse,
                                 void *workspace, size_t workspace_bytes, sa_stream_t stream);
 
+/*
+ * Cache append (the step before the path): writes the new tokens' rows into
+ * the paged caches.  [HAT §5 item 2]: the cache organisation decides indexing
+ * efficiency; [F2S "Engineering Considerations" item 1]: paged cache
+ * management is on the critical path; [HAT §5 item 3]: low-precision ranges
+ * need care in the indexer.
+ *
+ * Query token i (position pos(i) of its sequence, the sa_batch rule, i.e. the
+ * cache already counts it in ctx_len) goes to physical row
+ *     r = page_table[b * max_pages + pos / page_size] * page_size + pos % page_size:
+ *     k_cache[r, 0:d_qk] = k_new[i, :]
+ *     v_cache[r, 0:d_v]  = v_new[i, :]      (v_new NULL: latent layout, V is the
+ *                                            first d_v elements of the K row)
+ *     k_idx_cache[r, :]  = k_idx_new[i, :]  (idx_dtype == src_dtype: copied), or
+ *     fp8 (idx_dtype SA_FP8_E4M3): k_scale_cache[r] = s = max_d |k_idx_new[i, d]| / 448
+ *         and k_idx_cache[r, d] = e4m3fn(k_idx_new[i, d] / s), nearest even,
+ *         saturating at +-448, both operations in fp32; a zero row gives s = 0
+ *         and codes 0.  This is the format sparse_indexer_scores reads.
+ * Other rows are not touched.  Positions of one call must be distinct rows.
+ *
+ *   k_new, v_new   [T, d_qk], [T, d_v] in kv_dtype (SA_F32 or SA_BF16)
+ *   k_cache, v_cache  as in sparse_gated_attn_fwd (kv_row_stride elements per row)
+ *   k_idx_new      [T, d_i] in src_dtype (SA_F32 or SA_BF16); finite values
+ *   k_idx_cache    [num_pages, page_size, d_i] in idx_dtype
+ *   k_scale_cache  [num_pages, page_size] fp32 (fp8 only, else ignored)
+ * Requires d_qk, d_v and kv_row_stride rows of whole 16-byte units, d_i even
+ * (and <= 1024 for fp8), 16-byte aligned base pointers.
+ */
+sa_status sparse_cache_append(const sa_batch *batch, sa_dtype kv_dtype, const void *k_new, int32_t d_qk,
+                              const void *v_new, int32_t d_v, void *k_cache, void *v_cache, int64_t kv_row_stride,
+                              sa_dtype src_dtype, const void *k_idx_new, int32_t d_i, sa_dtype idx_dtype,
+                              void *k_idx_cache, float *k_scale_cache, sa_stream_t stream);
+
+/*
+ * fp8 quantisation of the rows of x [rows, cols] (src_dtype SA_F32 or
+ * SA_BF16, finite values), by the rule of sparse_cache_append: scales[r] =
+ * max|x[r, :]| / 448, codes[r, c] = e4m3fn(x[r, c] / scales[r]).  For the
+ * indexer queries, rows = T and cols = n_heads * head_dim give q_idx and
+ * q_scale.  cols a multiple of 8; x 16-byte and codes 8-byte aligned.
+ */
+sa_status sparse_quantize_fp8_rows(sa_dtype src_dtype, const void *x, int64_t rows, int32_t cols,
+                                   uint8_t *codes, float *scales, sa_stream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char *sa_status_string(sa_status s);
 

@@ -20,7 +20,8 @@ SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_ELAUNCH = 0, -1, -2, -3, -4
 
 EXPORTS = ("sparse_indexer_scores", "sparse_topk_workspace_size", "sparse_topk",
-           "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sa_status_string", "sa_abi_version")
+           "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sparse_cache_append",
+           "sparse_quantize_fp8_rows", "sa_status_string", "sa_abi_version")
 
 _DT = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: SA_FP8_E4M3}
 
@@ -71,6 +72,11 @@ def lib() -> ctypes.CDLL:
         L.sparse_gated_attn_fwd.restype = ctypes.c_int
         L.sparse_gated_attn_fwd.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp, i32,
                                             ctypes.c_float, vp, vp, vp, sz, vp]
+        L.sparse_cache_append.restype = ctypes.c_int
+        L.sparse_cache_append.argtypes = [bp, ctypes.c_int, vp, i32, vp, i32, vp, vp, i64, ctypes.c_int, vp, i32,
+                                          ctypes.c_int, vp, vp, vp]
+        L.sparse_quantize_fp8_rows.restype = ctypes.c_int
+        L.sparse_quantize_fp8_rows.argtypes = [ctypes.c_int, vp, i64, i32, vp, vp, vp]
         L.sa_status_string.restype = ctypes.c_char_p
         L.sa_status_string.argtypes = [ctypes.c_int]
         L.sa_abi_version.restype = i32
@@ -157,6 +163,31 @@ def sparse_gated_attn_fwd(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor
                                      _ptr(gate), per_channel, ctypes.c_float(scale), _ptr(out), _ptr(lse),
                                      _ptr(workspace), wsb, _stream(stream))
     _check("sparse_gated_attn_fwd", st)
+
+
+def sparse_cache_append(batch: SaBatch, k_new: torch.Tensor, k_cache: torch.Tensor, k_idx_new: torch.Tensor,
+                        k_idx_cache: torch.Tensor, v_new: Optional[torch.Tensor] = None,
+                        v_cache: Optional[torch.Tensor] = None, k_scale_cache: Optional[torch.Tensor] = None,
+                        stream=None) -> None:
+    """Write the new tokens' K (and V) rows and indexer keys at their positions' cache rows.
+
+    k_cache / v_cache [pages, page_size, row_stride]; k_idx_cache [pages, page_size, d_i] whose dtype picks
+    copy (same as k_idx_new) or fp8 quantisation (float8_e4m3fn, scales into k_scale_cache)."""
+    v_cache = k_cache if v_cache is None else v_cache
+    st = lib().sparse_cache_append(ctypes.byref(batch), _DT[k_new.dtype], _ptr(k_new), k_new.shape[-1],
+                                   _ptr(v_new), 0 if v_new is None else v_new.shape[-1], _ptr(k_cache),
+                                   _ptr(v_cache), k_cache.stride(-2), _DT[k_idx_new.dtype], _ptr(k_idx_new),
+                                   k_idx_new.shape[-1], _DT[k_idx_cache.dtype], _ptr(k_idx_cache),
+                                   _ptr(k_scale_cache), _stream(stream))
+    _check("sparse_cache_append", st)
+
+
+def sparse_quantize_fp8_rows(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    """Per-row fp8 quantisation of x [rows, cols] into codes (uint8 or float8_e4m3fn) and scales [rows]."""
+    rows, cols = x.reshape(x.shape[0], -1).shape
+    st = lib().sparse_quantize_fp8_rows(_DT[x.dtype], _ptr(x), rows, cols, _ptr(codes), _ptr(scales),
+                                        _stream(stream))
+    _check("sparse_quantize_fp8_rows", st)
 
 
 class Pipeline:

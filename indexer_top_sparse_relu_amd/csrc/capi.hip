@@ -151,6 +151,57 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const voi
                                     workspace, (hipStream_t)stream));
 }
 
+sa_status sparse_cache_append(const sa_batch *batch, sa_dtype kv_dtype, const void *k_new, int32_t d_qk,
+                              const void *v_new, int32_t d_v, void *k_cache, void *v_cache, int64_t kv_row_stride,
+                              sa_dtype src_dtype, const void *k_idx_new, int32_t d_i, sa_dtype idx_dtype,
+                              void *k_idx_cache, float *k_scale_cache, sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (kv_dtype != SA_F32 && kv_dtype != SA_BF16)
+        return SA_EINVAL;
+    if (src_dtype != SA_F32 && src_dtype != SA_BF16)
+        return SA_EINVAL;
+    if (idx_dtype != src_dtype && idx_dtype != SA_FP8_E4M3)
+        return SA_EINVAL;
+    if (!k_new || !k_cache || !k_idx_new || !k_idx_cache || (v_new && !v_cache))
+        return SA_EINVAL;
+    if (idx_dtype == SA_FP8_E4M3 && !k_scale_cache)
+        return SA_EINVAL;
+    if (d_qk < 1 || d_i < 2 || (d_i & 1) || (v_new && d_v < 1))
+        return SA_EINVAL;
+    if (kv_row_stride < d_qk || (v_new && kv_row_stride < d_v))
+        return SA_EINVAL;
+    const int esz = kv_dtype == SA_BF16 ? 2 : 4;
+    if ((d_qk * esz) % 16 || (v_new && (d_v * esz) % 16) || (kv_row_stride * esz) % 16)
+        return SA_EINVAL;
+    if (!aligned16(k_new) || !aligned16(k_cache) || (v_new && (!aligned16(v_new) || !aligned16(v_cache))))
+        return SA_EINVAL;
+    if (!aligned16(k_idx_new) || !aligned16(k_idx_cache))
+        return SA_EINVAL;
+    if (idx_dtype == SA_FP8_E4M3 && d_i > 2 * 64 * 8)
+        return SA_EUNSUPPORTED;
+    return launched(sa::launch_cache_append(bt, esz, k_new, d_qk, v_new, d_v, k_cache, v_cache, kv_row_stride,
+                                            src_dtype == SA_F32 ? 1 : 0, k_idx_new, d_i,
+                                            idx_dtype == SA_FP8_E4M3 ? 1 : 0, k_idx_cache, k_scale_cache,
+                                            (hipStream_t)stream));
+}
+
+sa_status sparse_quantize_fp8_rows(sa_dtype src_dtype, const void *x, int64_t rows, int32_t cols, uint8_t *codes,
+                                   float *scales, sa_stream_t stream)
+{
+    if (src_dtype != SA_F32 && src_dtype != SA_BF16)
+        return SA_EINVAL;
+    if (!x || !codes || !scales || rows < 1 || rows > 0x7fffffff || cols < 8 || (cols & 7))
+        return SA_EINVAL;
+    if (!aligned16(x) || (((uintptr_t)codes) & 7u))
+        return SA_EINVAL;
+    return launched(sa::launch_quantize_rows(x, src_dtype == SA_F32 ? 1 : 0, rows, cols, codes, scales,
+                                             (hipStream_t)stream));
+}
+
 const char *sa_status_string(sa_status s)
 {
     switch (s) {

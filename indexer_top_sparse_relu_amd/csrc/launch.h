@@ -39,4 +39,11 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &plan, const v
                        const int32_t *indices, int k, const void *gate, int per_channel, float scale,
                        void *out, float *lse, void *ws, hipStream_t st);
 
+// cache append + fp8 quantisation
+hipError_t launch_cache_append(const Batch &bt, int kv_esz, const void *k_new, int d_qk, const void *v_new, int d_v,
+                               void *k_cache, void *v_cache, int64_t row_stride, int src_f32, const void *kidx_new,
+                               int d_i, int fp8, void *kidx_cache, float *kscale_cache, hipStream_t st);
+hipError_t launch_quantize_rows(const void *x, int src_f32, int64_t rows, int cols, uint8_t *codes, float *scales,
+                                hipStream_t st);
+
 } // namespace sa
