@@ -111,6 +111,58 @@ def cpu_baseline(wl, sample_tokens: int):
                       f"full indexer + Top-K + gated attention in fp64, {dt:.1f} s"}
 
 
+def before_path(wl, steps: int, stream):
+    """The step before the path, timed apart (not part of the step above): the cache append
+    of the batch's new tokens (latent K rows in bf16 and fp8 indexer keys quantised from bf16,
+    into copies of the caches) and the fp8 quantisation of the indexer queries from bf16.
+    Algorithmic bytes: every input read once and every output written once."""
+    import torch
+
+    from indexer_top_sparse_relu_amd import binding as B
+
+    s = wl.spec
+    if s.idx_dtype != "fp8":
+        return None
+    g = torch.Generator(device="cuda").manual_seed(5)
+    k_cache, k_idx = wl.k_cache.clone(), wl.k_idx.clone()
+    k_scale = wl.k_scale.clone()
+    ae = 2 if s.attn_dtype == "bf16" else 4
+    k_new = torch.randn(s.T, s.d_qk, device="cuda", generator=g).to(wl.k_cache.dtype)
+    v_new = None if s.mla else torch.randn(s.T, s.d_v, device="cuda", generator=g).to(wl.k_cache.dtype)
+    v_cache = None if s.mla else wl.v_cache.clone()
+    kidx_new = torch.randn(s.T, s.d_I, device="cuda", generator=g).to(torch.bfloat16)
+    q_bf16 = torch.randn(s.T, s.H_I * s.d_I, device="cuda", generator=g).to(torch.bfloat16)
+    codes = torch.empty(s.T, s.H_I * s.d_I, device="cuda", dtype=torch.uint8)
+    scales = torch.empty(s.T, device="cuda", dtype=torch.float32)
+    bt = B.batch_of(wl)
+
+    def append():
+        B.sparse_cache_append(bt, k_new, k_cache, kidx_new, k_idx, v_new=v_new, v_cache=v_cache,
+                              k_scale_cache=k_scale, stream=stream)
+
+    def quant():
+        B.sparse_quantize_fp8_rows(q_bf16, codes, scales, stream=stream)
+
+    kv_bytes = s.d_qk * ae + (0 if s.mla else s.d_v * ae)
+    work = {"cache_append": (append, s.T * (2 * kv_bytes + 2 * s.d_I + s.d_I + 4)),
+            "quantize_q": (quant, s.T * (2 * s.H_I * s.d_I + s.H_I * s.d_I + 4))}
+    out = {}
+    for name, (fn, nbytes) in work.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        ach = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"], "unit": "GB/s",
+                     "frac": ach / PEAK["hbm_GBs"], "ms": ms, "bytes": nbytes}
+    return out
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -219,6 +271,7 @@ def main(argv=None):
         "roofline": roof,
         "stages": rl,
     }
+    line["before_path"] = before_path(wl, args.steps, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(line), flush=True)

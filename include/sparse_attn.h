@@ -195,8 +195,8 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype,
  *   k_idx_new      [T, d_i] in src_dtype (SA_F32 or SA_BF16); finite values
  *   k_idx_cache    [num_pages, page_size, d_i] in idx_dtype
  *   k_scale_cache  [num_pages, page_size] fp32 (fp8 only, else ignored)
- * Requires d_qk, d_v and kv_row_stride rows of whole 16-byte units, d_i even
- * (and <= 1024 for fp8), 16-byte aligned base pointers.
+ * Requires d_qk, d_v and kv_row_stride rows of whole 16-byte units (K and V
+ * rows of at most 4 KB), d_i even and <= 1024, 16-byte aligned base pointers.
  */
 sa_status sparse_cache_append(const sa_batch *batch, sa_dtype kv_dtype, const void *k_new, int32_t d_qk,
                               const void *v_new, int32_t d_v, void *k_cache, void *v_cache, int64_t kv_row_stride,

@@ -48,7 +48,11 @@ __device__ __forceinline__ float2 load_pair(const void *src, int src_f32, int64_
 
 // One wave per new token: its K row (and V row when separate) go to the
 // physical row of its position, its indexer key is copied or quantised.
-// Row byte counts are multiples of 16; d_i is even and at most 2 * 64 * 8.
+// Row byte counts are multiples of 16 and at most kRowPieces * 1 KB; d_i is
+// even and at most 2 * 64 * 8.  The sources are read before the destination
+// row is known (they do not depend on it), so the page-table lookup and the
+// source loads share one memory round trip.
+constexpr int kRowPieces = 4;
 __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
     Batch bt, const uint8_t *__restrict__ k_new, int krow_bytes, const uint8_t *__restrict__ v_new, int vrow_bytes,
     uint8_t *__restrict__ k_cache, uint8_t *__restrict__ v_cache, int64_t stride_bytes, const void *__restrict__ kidx_new,
@@ -58,34 +62,58 @@ __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
     const int tok = blockIdx.x * kAppendWaves + (threadIdx.x >> 6);
     if (tok >= bt.total_q)
         return;
-    const int b = seq_of_token(bt, tok);
-    const int64_t row = phys_row(bt, b, pos_of_token(bt, b, tok));
-
-    for (int o = 16 * lane; o < krow_bytes; o += 16 * 64)
-        *(u32x4 *)(k_cache + row * stride_bytes + o) = *(const u32x4 *)(k_new + (int64_t)tok * krow_bytes + o);
-    if (v_new)
-        for (int o = 16 * lane; o < vrow_bytes; o += 16 * 64)
-            *(u32x4 *)(v_cache + row * stride_bytes + o) = *(const u32x4 *)(v_new + (int64_t)tok * vrow_bytes + o);
-
-    const int npair = d_i / 2;
-    if (!fp8) {
-        // same dtype: a plain copy of the key row, 4 bytes (one pair of bf16, or one f32) at a time
-        const int words = src_f32 ? d_i : npair;
-        const uint32_t *src = (const uint32_t *)kidx_new + (int64_t)tok * words;
-        uint32_t *dst = (uint32_t *)kidx_cache + row * words;
-        for (int w = lane; w < words; w += 64)
-            dst[w] = src[w];
-        return;
+    u32x4 kp[kRowPieces], vp[kRowPieces];
+#pragma unroll
+    for (int u = 0; u < kRowPieces; ++u) {
+        const int o = 16 * lane + 1024 * u;
+        if (o < krow_bytes)
+            kp[u] = *(const u32x4 *)(k_new + (int64_t)tok * krow_bytes + o);
+        if (v_new && o < vrow_bytes)
+            vp[u] = *(const u32x4 *)(v_new + (int64_t)tok * vrow_bytes + o);
     }
-    constexpr int PU = 8;                         // pairs per lane, at most
+    constexpr int PU = 8;                         // key pairs per lane, at most
+    const int npair = d_i / 2;
     float2 x[PU];
-    float amax = 0.0f;
+    uint32_t cw[2 * PU];                          // same-dtype copy: 4-byte words
+    const int words = src_f32 ? d_i : npair;
 #pragma unroll
     for (int u = 0; u < PU; ++u) {
         const int p = lane + 64 * u;
-        x[u] = p < npair ? load_pair(kidx_new, src_f32, (int64_t)tok * npair + p) : make_float2(0.0f, 0.0f);
-        amax = fmaxf(amax, fmaxf(fabsf(x[u].x), fabsf(x[u].y)));
+        if (fp8) {
+            x[u] = p < npair ? load_pair(kidx_new, src_f32, (int64_t)tok * npair + p) : make_float2(0.0f, 0.0f);
+        } else {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int w = lane + 64 * (2 * u + h);
+                cw[2 * u + h] = w < words ? ((const uint32_t *)kidx_new)[(int64_t)tok * words + w] : 0u;
+            }
+        }
     }
+
+    const int b = seq_of_token(bt, tok);
+    const int64_t row = phys_row(bt, b, pos_of_token(bt, b, tok));
+#pragma unroll
+    for (int u = 0; u < kRowPieces; ++u) {
+        const int o = 16 * lane + 1024 * u;
+        if (o < krow_bytes)
+            *(u32x4 *)(k_cache + row * stride_bytes + o) = kp[u];
+        if (v_new && o < vrow_bytes)
+            *(u32x4 *)(v_cache + row * stride_bytes + o) = vp[u];
+    }
+    if (!fp8) {
+        uint32_t *dst = (uint32_t *)kidx_cache + row * words;
+#pragma unroll
+        for (int u = 0; u < 2 * PU; ++u) {
+            const int w = lane + 64 * u;
+            if (w < words)
+                dst[w] = cw[u];
+        }
+        return;
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int u = 0; u < PU; ++u)
+        amax = fmaxf(amax, fmaxf(fabsf(x[u].x), fabsf(x[u].y)));
     amax = wave_max(amax);
     const float s = amax / 448.0f;
     uint16_t *dst = (uint16_t *)(kidx_cache + row * d_i);
@@ -100,8 +128,11 @@ __global__ __launch_bounds__(64 * kAppendWaves) void cache_append_kernel(
 }
 
 // One workgroup per row of x [rows, cols] (cols a multiple of 8): the row's
-// maximum, then its codes, 8 per thread and step.  The second read of the
-// row hits the L2.
+// maximum, then its codes, 8 per thread and step.  Rows of at most
+// 8 * kQuantThreads * kQuantHeld elements stay in registers between the two
+// steps (one read of the row); longer rows are read twice (the second time
+// from the L2).
+constexpr int kQuantHeld = 4;
 __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void *__restrict__ x, int src_f32,
                                                                       int cols, uint8_t *__restrict__ codes,
                                                                       float *__restrict__ scales)
@@ -127,13 +158,31 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void
             }
         }
     };
+    const bool held = cols <= 8 * kQuantThreads * kQuantHeld;
+    float hv[kQuantHeld][8];
     float amax = 0.0f;
-    for (int c = 8 * tid; c < cols; c += 8 * kQuantThreads) {
-        float v[8];
-        load8(c, v);
+    if (held) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            amax = fmaxf(amax, fabsf(v[e]));
+        for (int u = 0; u < kQuantHeld; ++u) {
+            const int c = 8 * tid + 8 * kQuantThreads * u;
+            if (c < cols)
+                load8(c, hv[u]);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    hv[u][e] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                amax = fmaxf(amax, fabsf(hv[u][e]));
+        }
+    } else {
+        for (int c = 8 * tid; c < cols; c += 8 * kQuantThreads) {
+            float v[8];
+            load8(c, v);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                amax = fmaxf(amax, fabsf(v[e]));
+        }
     }
     amax = wave_max(amax);
     if (lane == 0)
@@ -143,15 +192,27 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_rows_kernel(const void
     for (int w = 0; w < kQuantThreads / 64; ++w)
         amax = fmaxf(amax, wmax[w]);
     const float s = amax / 448.0f;
-    for (int c = 8 * tid; c < cols; c += 8 * kQuantThreads) {
-        float v[8];
-        load8(c, v);
+    auto put8 = [&](int c, const float (&v)[8]) {
         u32x2 out = {0u, 0u};
         if (amax > 0.0f) {
             out.x = fp8_pair(v[0] / s, v[1] / s) | (fp8_pair(v[2] / s, v[3] / s) << 16);
             out.y = fp8_pair(v[4] / s, v[5] / s) | (fp8_pair(v[6] / s, v[7] / s) << 16);
         }
         *(u32x2 *)(codes + r * cols + c) = out;
+    };
+    if (held) {
+#pragma unroll
+        for (int u = 0; u < kQuantHeld; ++u) {
+            const int c = 8 * tid + 8 * kQuantThreads * u;
+            if (c < cols)
+                put8(c, hv[u]);
+        }
+    } else {
+        for (int c = 8 * tid; c < cols; c += 8 * kQuantThreads) {
+            float v[8];
+            load8(c, v);
+            put8(c, v);
+        }
     }
     if (tid == 0)
         scales[r] = s;

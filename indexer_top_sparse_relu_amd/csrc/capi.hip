@@ -181,7 +181,7 @@ sa_status sparse_cache_append(const sa_batch *batch, sa_dtype kv_dtype, const vo
         return SA_EINVAL;
     if (!aligned16(k_idx_new) || !aligned16(k_idx_cache))
         return SA_EINVAL;
-    if (idx_dtype == SA_FP8_E4M3 && d_i > 2 * 64 * 8)
+    if (d_i > 2 * 64 * 8 || d_qk * esz > 4096 || (v_new && d_v * esz > 4096))
         return SA_EUNSUPPORTED;
     return launched(sa::launch_cache_append(bt, esz, k_new, d_qk, v_new, d_v, k_cache, v_cache, kv_row_stride,
                                             src_dtype == SA_F32 ? 1 : 0, k_idx_new, d_i,
