@@ -33,7 +33,9 @@
  *   - rows with n <= K take all n positions, the rest of the row is -1;
  *   - output gate  y = o * sigmoid(G), G per channel or per head;
  *   - cache append: fp8 indexer keys as e4m3fn codes with a per-token scale
- *     max|x| / 448, nearest-even, saturating (see that section).
+ *     max|x| / 448, nearest-even, saturating (see that section);
+ *   - block-level selection: blocks are pages, pooled keys are block means,
+ *     block scores sum the query heads' dots (see that section).
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -454,5 +456,94 @@ void orc_cache_append(const orc_batch *bt, int64_t T, int kv_dtype, const void *
         else
             memcpy((char *)k_idx_cache + row * d_i * isz, (const char *)k_idx_new + i * d_i * isz,
                    (size_t)(d_i * isz));
+    }
+}
+
+/* --------------------------------------------- block-level selection
+ * [SEL §3.2], pseudocode: pool the keys by block, score the blocks with the
+ * queries, keep the top-k blocks, gather them and run exact attention within
+ * them; [SAD §3] "block sparsity with top-k routing": query-to-block relevance
+ * at block granularity, only the top blocks take part in the fine-grained
+ * computation; [SEL §4.1]: the effective length drops from N to k*b.
+ * Readings (the pages fix none of these):
+ *   - a block is one page of the paged cache (b = page_size): block j of
+ *     sequence b covers positions [j*b, min((j+1)*b, L_b));
+ *   - the pooled key of a block is the mean of its K rows (first d_qk
+ *     elements of each cache row);
+ *   - the query heads share one selection (they share a KV head, [SAD §2]),
+ *     so a block's score sums their dots:
+ *         S[i, j] = sum_h q[i,h,:] . kbar_j
+ *     over the candidate blocks of token i, those whose first position is
+ *     <= pos(i);
+ *   - the selected blocks' positions s <= pos(i) form the index list of the
+ *     exact attention (a2-a5 unchanged). */
+
+/* kbar[page, :] for every page a sequence uses, indexed by physical page. */
+void orc_block_pool(const orc_batch *bt, int dtype, const void *k_cache, int dqk, int64_t row_stride, double *kbar)
+{
+    const int ps = bt->page_size;
+    for (int b = 0; b < bt->num_seqs; ++b) {
+        const int64_t L = bt->ctx_len[b];
+        const int64_t nb = (L + ps - 1) / ps;
+        for (int64_t j = 0; j < nb; ++j) {
+            const int64_t page = bt->page_table[(int64_t)b * bt->max_pages + j];
+            const int64_t len = (L - j * ps) < ps ? (L - j * ps) : ps;
+            for (int d = 0; d < dqk; ++d) {
+                double sum = 0.0;
+                for (int64_t t = 0; t < len; ++t)
+                    sum += load(dtype, k_cache, (page * ps + t) * row_stride + d);
+                kbar[page * dqk + d] = sum / (double)len;
+            }
+        }
+    }
+}
+
+/* S[r, j] for the candidate blocks j of token rows[r]; the rest of the row is left untouched. */
+void orc_block_scores(const orc_batch *bt, int dtype, const void *q, int Hq, int dqk, const double *kbar,
+                      const int64_t *rows, int64_t nrows, double *scores, int64_t ld)
+{
+    const int ps = bt->page_size;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t i = rows[r];
+        int b;
+        const int64_t pos = pos_of(bt, i, &b);
+        for (int64_t j = 0; j <= pos / ps; ++j) {
+            const int64_t page = bt->page_table[(int64_t)b * bt->max_pages + j];
+            double s = 0.0;
+            for (int h = 0; h < Hq; ++h) {
+                double dot = 0.0;
+                for (int d = 0; d < dqk; ++d)
+                    dot += load(dtype, q, (i * Hq + h) * (int64_t)dqk + d) * kbar[page * dqk + d];
+                s += dot;
+            }
+            scores[r * ld + j] = s;
+        }
+    }
+}
+
+/* Positions of the selected blocks (blk[r, :], block ids, -1 = none) that are
+ * <= pos(rows[r]), in the order the blocks are listed, then -1 up to kb*b. */
+void orc_block_expand(const orc_batch *bt, const int32_t *blk, int kb, const int64_t *rows, int64_t nrows,
+                      int32_t *out)
+{
+    const int ps = bt->page_size;
+    const int64_t w = (int64_t)kb * ps;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int b;
+        const int64_t pos = pos_of(bt, rows[r], &b);
+        int64_t n = 0;
+        for (int k = 0; k < kb; ++k) {
+            const int32_t j = blk[r * kb + k];
+            if (j < 0)
+                continue;
+            for (int t = 0; t < ps; ++t) {
+                const int64_t p = (int64_t)j * ps + t;
+                if (p <= pos)
+                    out[r * w + n++] = (int32_t)p;
+            }
+        }
+        for (; n < w; ++n)
+            out[r * w + n] = -1;
     }
 }

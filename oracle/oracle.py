@@ -70,6 +70,9 @@ def lib():
                                       vp, ctypes.c_int, vp, ctypes.c_int, dbl, vp, i64, vp, vp]
         L.orc_dense_attn.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int, i64,
                                      vp, ctypes.c_int, dbl, vp, i64, vp]
+        L.orc_block_pool.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, vp]
+        L.orc_block_scores.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i64]
+        L.orc_block_expand.argtypes = [vp, vp, ctypes.c_int, vp, i64, vp]
         L.orc_fp8_encode.restype = ctypes.c_uint8
         L.orc_fp8_encode.argtypes = [ctypes.c_float]
         L.orc_quantize_rows.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp]
@@ -268,3 +271,54 @@ def cache_append(*, q_start, ctx_len, page_table, page_size, kv_dtype, k_new, v_
                            0 if v_new is None else int(v_new.shape[-1]), _p(k_cache), _p(v_cache),
                            int(k_cache.shape[-1]), DT[src_dtype], _p(k_idx_new), int(k_idx_new.shape[-1]),
                            DT[idx_dtype], _p(k_idx_cache), _p(k_scale_cache))
+
+
+# ------------------------------------------------------ block-level selection
+
+def block_pool(inp: Inputs) -> np.ndarray:
+    """Mean K row (first d_qk elements) of every block a sequence uses, [num_pages, d_qk] float64,
+    indexed by physical page (a block is one page); pages no sequence uses stay NaN."""
+    rows = inp.k_cache.reshape(-1, inp.row_stride).shape[0]
+    kbar = np.full((rows // inp.page_size, inp.d_qk), np.nan, dtype=np.float64)
+    lib().orc_block_pool(ctypes.byref(inp._bt), DT[inp.attn_dtype], _p(inp.k_cache), inp.d_qk, inp.row_stride,
+                         kbar.ctypes.data)
+    return kbar
+
+
+def block_row_lengths(inp: Inputs, rows=None) -> np.ndarray:
+    """Candidate blocks of each token: those whose first position is <= pos."""
+    return (row_lengths(inp, rows) - 1) // inp.page_size + 1
+
+
+def block_scores(inp: Inputs, kbar: np.ndarray, rows=None, ld: Optional[int] = None) -> np.ndarray:
+    """S[i, j] = sum_h q[i,h,:] . kbar[page of block j], [len(rows), ld]; NaN beyond the candidates."""
+    rows = _rows(inp, rows)
+    ld = int(ld or int(inp.page_table.shape[1]))
+    kbar = np.ascontiguousarray(kbar, dtype=np.float64)
+    out = np.full((rows.shape[0], ld), np.nan, dtype=np.float64)
+    lib().orc_block_scores(ctypes.byref(inp._bt), DT[inp.attn_dtype], _p(inp.q), inp.Hq, inp.d_qk,
+                           kbar.ctypes.data, rows.ctypes.data, rows.shape[0], out.ctypes.data, ld)
+    return out
+
+
+def block_expand(inp: Inputs, blk: np.ndarray, rows=None) -> np.ndarray:
+    """Positions (<= pos) of the listed blocks, in block order, then -1: [len(rows), kb * page_size]."""
+    rows = _rows(inp, rows)
+    blk = np.ascontiguousarray(blk, dtype=np.int32)
+    kb = blk.shape[1]
+    out = np.zeros((rows.shape[0], kb * inp.page_size), dtype=np.int32)
+    lib().orc_block_expand(ctypes.byref(inp._bt), blk.ctypes.data, kb, rows.ctypes.data, rows.shape[0],
+                           out.ctypes.data)
+    return out
+
+
+def block_pipeline(inp: Inputs, kb: int, rows=None, scale: Optional[float] = None):
+    """Pool -> block scores -> top-kb blocks -> expansion -> gated sparse attention, all in the oracle."""
+    rows = _rows(inp, rows)
+    kbar = block_pool(inp)
+    sc = block_scores(inp, kbar, rows)
+    nb = block_row_lengths(inp, rows)
+    blk = topk(sc, nb, kb)
+    idx = block_expand(inp, blk, rows)
+    out = sparse_attn(inp, idx, rows, scale)
+    return sc, blk, idx, out

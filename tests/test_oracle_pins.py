@@ -611,3 +611,97 @@ def test_cache_append_copies_same_dtype_keys_and_skips_v_for_latent_rows():
                    k_idx_new=kidx, idx_dtype="bf16", k_idx_cache=kic)
     assert np.array_equal(k_cache[4], k_new[0]) and not np.delete(k_cache, 4, axis=0).any()
     assert np.array_equal(kic[4], kidx[0]) and not np.delete(kic, 4, axis=0).any()
+
+
+# ------------------------------------------------------ block-level selection
+
+def _paged_attn_inputs(rng, q_lens, ctx_lens, ps, Hq=3, d=8, dv=8, shuffle=True):
+    """f32 attention inputs over a shuffled page table (rows of the caches are physical rows)."""
+    B_ = len(q_lens)
+    npg = [(L + ps - 1) // ps for L in ctx_lens]
+    perm = rng.permutation(sum(npg)) if shuffle else np.arange(sum(npg))
+    pt = np.zeros((B_, max(npg)), np.int32)
+    off = 0
+    for b, n in enumerate(npg):
+        pt[b, :n] = perm[off:off + n]
+        off += n
+    inp, q, kc, vc, g = attn_inputs(rng, 0, 0, Hq, d, dv, page_size=ps, q_lens=list(q_lens),
+                                    ctx_lens=list(ctx_lens))
+    inp.page_table = np.ascontiguousarray(pt)
+    inp._bt = O._Batch(inp.B, ps, int(pt.shape[1]), 0, inp.q_start.ctypes.data, inp.ctx_len.ctypes.data,
+                       inp.page_table.ctypes.data)
+    return inp
+
+
+def test_block_pool_is_the_mean_of_the_blocks_valid_rows():
+    rng = np.random.default_rng(40)
+    inp = _paged_attn_inputs(rng, [3, 2], [13, 6], ps=4)
+    kc = inp.k_cache.reshape(-1, inp.row_stride)
+    kbar = O.block_pool(inp)
+    for b, L in enumerate(inp.ctx_len):
+        for j in range((L + 3) // 4):
+            page = inp.page_table[b, j]
+            n = min(4, L - 4 * j)
+            want = kc[page * 4: page * 4 + n, :inp.d_qk].astype(np.float64).mean(axis=0)
+            assert np.allclose(kbar[page], want, rtol=1e-14, atol=1e-15), (b, j)
+    # rows past a sequence's end do not enter its last block
+    page = inp.page_table[0, 3]                 # positions 12..15 of seq 0; only 12 is valid
+    kc[page * 4 + 1: page * 4 + 4] = 1e30
+    assert np.allclose(O.block_pool(inp)[page], kc[page * 4, :inp.d_qk])
+
+
+def test_block_scores_sum_of_head_dots_over_candidate_blocks():
+    rng = np.random.default_rng(41)
+    inp = _paged_attn_inputs(rng, [5, 1], [11, 9], ps=4, Hq=3)
+    kbar = O.block_pool(inp)
+    sc = O.block_scores(inp, kbar, ld=8)
+    nb = O.block_row_lengths(inp)
+    pos = O.row_lengths(inp) - 1
+    assert list(nb) == [p // 4 + 1 for p in pos]
+    qbar = inp.q.astype(np.float64).sum(axis=1)                     # [T, d]
+    for i in range(inp.T):
+        b = 0 if i < 5 else 1
+        pages = inp.page_table[b, :nb[i]]
+        want = kbar[pages] @ qbar[i]                                 # numpy matmul of the same operands
+        assert np.allclose(sc[i, :nb[i]], want, rtol=1e-12, atol=1e-14)
+        assert np.all(np.isnan(sc[i, nb[i]:]))
+
+
+def test_block_expand_hand_example():
+    rng = np.random.default_rng(42)
+    inp = _paged_attn_inputs(rng, [1], [10], ps=4)                   # pos = 9: blocks 0, 1, 2 (2 is partial)
+    blk = np.array([[0, 2, -1]], np.int32)
+    got = O.block_expand(inp, blk)
+    assert list(got[0]) == [0, 1, 2, 3, 8, 9] + [-1] * 6
+
+
+def test_block_pipeline_with_every_block_is_dense_gated_attention():
+    """kb >= the number of blocks keeps every causal position: block-sparse attention equals dense causal
+    gated attention (written separately in the oracle) and torch SDPA."""
+    rng = np.random.default_rng(43)
+    inp = _paged_attn_inputs(rng, [6, 3], [23, 10], ps=4, Hq=2, d=8, dv=8)
+    sc, blk, idx, out = O.block_pipeline(inp, kb=8, scale=0.3)
+    dense = O.dense_attn(inp, scale=0.3)
+    assert np.allclose(out, dense, rtol=1e-12, atol=1e-15)
+    n = O.row_lengths(inp)
+    for i in range(inp.T):
+        assert sorted(idx[i][idx[i] >= 0]) == list(range(n[i]))
+
+
+def test_block_pipeline_selects_the_planted_block():
+    """One block's keys point along every query's head sum: with kb = 1 it is always chosen, and the
+    attention runs over exactly its causal positions."""
+    rng = np.random.default_rng(44)
+    ps = 4
+    inp = _paged_attn_inputs(rng, [4], [40], ps=ps, Hq=2, d=8, dv=8, shuffle=True)
+    qbar = inp.q.sum(axis=1)
+    u = qbar.mean(axis=0)
+    kc = inp.k_cache.reshape(-1, inp.row_stride)
+    page = inp.page_table[0, 5]                                      # block 5: positions 20..23
+    kc[page * ps: page * ps + ps, :inp.d_qk] = 50.0 * u / np.linalg.norm(u)
+    assert np.all(qbar @ u > 0)
+    sc, blk, idx, out = O.block_pipeline(inp, kb=1, scale=0.3)
+    assert np.all(blk[:, 0] == 5)
+    assert np.all(idx[:, :ps] == np.arange(20, 24)) and np.all(idx[:, ps:] == -1)
+    ref = O.sparse_attn(inp, np.tile(np.arange(20, 24, dtype=np.int32), (inp.T, 1)), scale=0.3)
+    assert np.allclose(out, ref, rtol=0, atol=0)
