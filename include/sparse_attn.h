@@ -171,6 +171,48 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype,
                                 void *workspace, size_t workspace_bytes, sa_stream_t stream);
 
 /*
+ * Block-level selection, the pages' second variant.  [SEL §3.2] pseudocode:
+ * pool the keys by block, score the blocks with the queries, keep the top-k
+ * blocks, gather them, exact attention within them; [SAD §3]: block sparsity
+ * with top-k routing, query-to-block relevance at block granularity; [SEL
+ * §4.1-4.2]: the effective length becomes k*b, and block sparsity is the form
+ * that most easily turns into real speed-ups.
+ *
+ * Readings (the pages fix none): a block is one page of the paged cache
+ * (b = page_size); its pooled key is the mean of its K rows; the query heads
+ * share one selection (they share a KV head, [SAD §2]), so the score of block
+ * j for token i is  S[i, j] = (sum_h q[i,h,:]) . kbar_j  over the candidate
+ * blocks j <= pos(i) / page_size.  The flow, all on `stream`:
+ *   sparse_block_pool   -> kbar        [num_pages, d_qk] fp32, row = physical page
+ *   sparse_block_scores -> S           [T, ld] fp32, row i: entries [0, pos_i / page_size + 1)
+ *   sparse_block_topk   -> block ids   [T, kb] (a2's rule on block rows: ascending, then -1)
+ *   sparse_block_expand -> positions   [T, kb * page_size] (the causal positions of the
+ *                                       selected blocks, ascending, then -1)
+ *   sparse_gated_attn_fwd over those positions with k = kb * page_size.
+ *
+ * sparse_block_pool: for every sequence b and block j < ceil(ctx_len[b] /
+ *   page_size), kbar[page_table[b, j], :] = mean of the block's rows s <
+ *   ctx_len[b] of k_cache (first d_qk elements, dtype SA_F32 or SA_BF16),
+ *   summed in fp32.  Pages no sequence uses are not written.
+ * sparse_block_scores: needs a workspace of sparse_block_scores_workspace_size
+ *   bytes (T * d_qk fp32); d_qk a multiple of 32; ld_scores >= the most blocks
+ *   of any sequence.  Products accumulate in fp32 (MFMA).
+ * sparse_block_topk: 1 <= kb <= 4096; workspace as sparse_topk's.
+ * sparse_block_expand: kb * page_size <= 65536.
+ */
+sa_status sparse_block_pool(const sa_batch *batch, sa_dtype dtype, const void *k_cache, int32_t d_qk,
+                            int64_t kv_row_stride, float *k_blocks, sa_stream_t stream);
+size_t sparse_block_scores_workspace_size(const sa_batch *batch, int32_t d_qk);
+sa_status sparse_block_scores(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
+                              int32_t d_qk, const float *k_blocks, float *scores, int64_t ld_scores,
+                              void *workspace, size_t workspace_bytes, sa_stream_t stream);
+size_t sparse_block_topk_workspace_size(const sa_batch *batch, int32_t kb);
+sa_status sparse_block_topk(const sa_batch *batch, const float *scores, int64_t ld_scores, int32_t kb,
+                            int32_t *block_idx, void *workspace, size_t workspace_bytes, sa_stream_t stream);
+sa_status sparse_block_expand(const sa_batch *batch, const int32_t *block_idx, int32_t kb, int32_t *indices,
+                              sa_stream_t stream);
+
+/*
  * Cache append (the step before the path): writes the new tokens' rows into
  * the paged caches.  [HAT §5 item 2]: the cache organisation decides indexing
  * efficiency; [F2S "Engineering Considerations" item 1]: paged cache

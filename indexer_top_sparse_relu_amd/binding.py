@@ -20,7 +20,9 @@ SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_ELAUNCH = 0, -1, -2, -3, -4
 
 EXPORTS = ("sparse_indexer_scores", "sparse_topk_workspace_size", "sparse_topk",
-           "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sparse_cache_append",
+           "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sparse_block_pool",
+           "sparse_block_scores_workspace_size", "sparse_block_scores", "sparse_block_topk_workspace_size",
+           "sparse_block_topk", "sparse_block_expand", "sparse_cache_append",
            "sparse_quantize_fp8_rows", "sa_status_string", "sa_abi_version")
 
 _DT = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: SA_FP8_E4M3}
@@ -72,6 +74,18 @@ def lib() -> ctypes.CDLL:
         L.sparse_gated_attn_fwd.restype = ctypes.c_int
         L.sparse_gated_attn_fwd.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp, i32,
                                             ctypes.c_float, vp, vp, vp, sz, vp]
+        L.sparse_block_pool.restype = ctypes.c_int
+        L.sparse_block_pool.argtypes = [bp, ctypes.c_int, vp, i32, i64, vp, vp]
+        L.sparse_block_scores_workspace_size.restype = sz
+        L.sparse_block_scores_workspace_size.argtypes = [bp, i32]
+        L.sparse_block_scores.restype = ctypes.c_int
+        L.sparse_block_scores.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i64, vp, sz, vp]
+        L.sparse_block_topk_workspace_size.restype = sz
+        L.sparse_block_topk_workspace_size.argtypes = [bp, i32]
+        L.sparse_block_topk.restype = ctypes.c_int
+        L.sparse_block_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
+        L.sparse_block_expand.restype = ctypes.c_int
+        L.sparse_block_expand.argtypes = [bp, vp, i32, vp, vp]
         L.sparse_cache_append.restype = ctypes.c_int
         L.sparse_cache_append.argtypes = [bp, ctypes.c_int, vp, i32, vp, i32, vp, vp, i64, ctypes.c_int, vp, i32,
                                           ctypes.c_int, vp, vp, vp]
@@ -163,6 +177,47 @@ def sparse_gated_attn_fwd(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor
                                      _ptr(gate), per_channel, ctypes.c_float(scale), _ptr(out), _ptr(lse),
                                      _ptr(workspace), wsb, _stream(stream))
     _check("sparse_gated_attn_fwd", st)
+
+
+def sparse_block_pool(batch: SaBatch, k_cache: torch.Tensor, d_qk: int, k_blocks: torch.Tensor, stream=None) -> None:
+    """Mean K row of every block (page) a sequence uses, into k_blocks [num_pages, d_qk] fp32."""
+    st = lib().sparse_block_pool(ctypes.byref(batch), _DT[k_cache.dtype], _ptr(k_cache), int(d_qk),
+                                 k_cache.stride(-2), _ptr(k_blocks), _stream(stream))
+    _check("sparse_block_pool", st)
+
+
+def sparse_block_scores_workspace_size(batch: SaBatch, d_qk: int) -> int:
+    return int(lib().sparse_block_scores_workspace_size(ctypes.byref(batch), int(d_qk)))
+
+
+def sparse_block_scores(batch: SaBatch, q: torch.Tensor, k_blocks: torch.Tensor, scores: torch.Tensor,
+                        workspace: torch.Tensor, stream=None) -> None:
+    """Block scores (sum of the query heads' dots with each candidate block's pooled key) into scores [T, ld]."""
+    T, Hq, dqk = q.shape
+    wsb = workspace.numel() * workspace.element_size()
+    st = lib().sparse_block_scores(ctypes.byref(batch), _DT[q.dtype], _ptr(q), Hq, dqk, _ptr(k_blocks),
+                                   _ptr(scores), scores.stride(0), _ptr(workspace), wsb, _stream(stream))
+    _check("sparse_block_scores", st)
+
+
+def sparse_block_topk_workspace_size(batch: SaBatch, kb: int) -> int:
+    return int(lib().sparse_block_topk_workspace_size(ctypes.byref(batch), int(kb)))
+
+
+def sparse_block_topk(batch: SaBatch, scores: torch.Tensor, kb: int, block_idx: torch.Tensor,
+                      workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Top-kb candidate blocks of each token (ascending block ids, then -1) into block_idx [T, kb]."""
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().sparse_block_topk(ctypes.byref(batch), _ptr(scores), scores.stride(0), int(kb), _ptr(block_idx),
+                                 _ptr(workspace), wsb, _stream(stream))
+    _check("sparse_block_topk", st)
+
+
+def sparse_block_expand(batch: SaBatch, block_idx: torch.Tensor, indices: torch.Tensor, stream=None) -> None:
+    """Causal positions of the selected blocks into indices [T, kb * page_size] (ascending, then -1)."""
+    st = lib().sparse_block_expand(ctypes.byref(batch), _ptr(block_idx), block_idx.shape[1], _ptr(indices),
+                                   _stream(stream))
+    _check("sparse_block_expand", st)
 
 
 def sparse_cache_append(batch: SaBatch, k_new: torch.Tensor, k_cache: torch.Tensor, k_idx_new: torch.Tensor,

@@ -1,0 +1,194 @@
+// Block-level selection (gfx950): pooled block keys, block scores and the
+// expansion of the selected blocks to positions.  The Top-K over block scores
+// is the a2 kernel with block row lengths, and the attention is a3-a5
+// unchanged, over the expanded index list.
+//
+// Pages (by title):
+//   [SEL] "Hybrid Attention Architecture Evolution in LLMs: From Full
+//          Attention to Sparse Selection", §3.2 (pseudocode: pool the keys by
+//          block, score the blocks, keep the top-k blocks, gather them, exact
+//          attention) and §4.1-4.2 (effective length k*b; block sparsity is
+//          the form that turns into real speed-ups).
+//   [SAD] "Sparse Attention and Hybrid Attention Architecture Design in Large
+//          Language Models", §3 (block sparsity with top-k routing: relevance
+//          between queries and key blocks at block granularity) and §2 (query
+//          heads share a KV head).
+//
+// Readings: a block is one page of the paged cache, its pooled key the mean of
+// its K rows, and the block score of token i sums its query heads' dots,
+// S[i, j] = (sum_h q[i,h,:]) . kbar_j, over the blocks that start at or
+// before pos(i) (one selection shared by the heads of the KV head).
+#include "launch.h"
+#include "sa_device.h"
+
+namespace sa {
+
+constexpr int kBlkThreads = 256;
+constexpr int kBlkTok = 32;          // tokens per score tile (MFMA rows)
+constexpr int kBlkCols = 128;        // blocks per score tile (4 waves x 32 MFMA columns)
+
+__device__ __forceinline__ float load_elem(const uint8_t *base, int f32, int64_t i)
+{
+    return f32 ? ((const float *)base)[i] : __uint_as_float((uint32_t)((const uint16_t *)base)[i] << 16);
+}
+
+// One workgroup per (block j, sequence b): the mean of the block's valid K
+// rows (fp32 sums in position order), written at k_blocks[page].  Threads own
+// consecutive dims, so every row read is coalesced.
+__global__ __launch_bounds__(kBlkThreads) void block_pool_kernel(Batch bt, const uint8_t *__restrict__ k_cache,
+                                                                 int f32, int d_qk, int64_t row_stride,
+                                                                 float *__restrict__ k_blocks)
+{
+    const int j = blockIdx.x, b = blockIdx.y;
+    const int ps = 1 << bt.page_shift;
+    const int L = bt.ctx_len[b];
+    if (j >= ((L + ps - 1) >> bt.page_shift))
+        return;
+    const int64_t page = bt.page_table[(int64_t)b * bt.max_pages + j];
+    const int len = min(ps, L - j * ps);
+    for (int d = threadIdx.x; d < d_qk; d += kBlkThreads) {
+        float s = 0.0f;
+        for (int t = 0; t < len; ++t)
+            s += load_elem(k_cache, f32, (page * ps + t) * row_stride + d);
+        k_blocks[page * d_qk + d] = s / (float)len;
+    }
+}
+
+// qbar[i, :] = sum over the query heads of q[i, h, :] (fp32, heads in order);
+// one workgroup per token.
+__global__ __launch_bounds__(kBlkThreads) void qbar_kernel(const uint8_t *__restrict__ q, int f32, int Hq, int d_qk,
+                                                           float *__restrict__ qbar)
+{
+    const int64_t i = blockIdx.x;
+    for (int d = threadIdx.x; d < d_qk; d += kBlkThreads) {
+        float s = 0.0f;
+        for (int h = 0; h < Hq; ++h)
+            s += load_elem(q, f32, (i * Hq + h) * d_qk + d);
+        qbar[i * d_qk + d] = s;
+    }
+}
+
+// Block scores on fp32 MFMA (32x32x2): a workgroup takes 32 consecutive
+// tokens of one sequence and 128 blocks (32 per wave).  Over each 32-dim
+// chunk of d_qk, lane half hf supplies dims 16hf .. 16hf+15 of its token row
+// (A) and block row (B) to 16 MFMAs, so both operands are contiguous 64-byte
+// loads; the next chunk's loads are issued before this chunk's MFMAs.  Tokens
+// past the tile and blocks past the sequence read row 0 and are not stored.
+__global__ __launch_bounds__(kBlkThreads) void block_scores_kernel(Batch bt, const float *__restrict__ qbar, int d_qk,
+                                                                   const float *__restrict__ k_blocks,
+                                                                   float *__restrict__ scores, int64_t ld,
+                                                                   int n_tiles_max)
+{
+    int tile = blockIdx.x;
+    if (tile >= n_tiles_max)
+        return;
+    int b = 0;
+    for (; b < bt.num_seqs; ++b) {
+        const int nq = bt.q_start[b + 1] - bt.q_start[b];
+        const int nt = (nq + kBlkTok - 1) / kBlkTok;
+        if (tile < nt)
+            break;
+        tile -= nt;
+    }
+    if (b >= bt.num_seqs)
+        return;
+    const int q0 = bt.q_start[b], nq = bt.q_start[b + 1] - q0;
+    const int tok0 = q0 + tile * kBlkTok;
+    const int ntok = min(kBlkTok, nq - tile * kBlkTok);
+    const int pos0 = bt.ctx_len[b] - nq + tile * kBlkTok;        // position of token tok0
+    const int nb_max = ((pos0 + ntok - 1) >> bt.page_shift) + 1;  // candidate blocks of the tile's last token
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int j0 = blockIdx.y * kBlkCols + wv * 32;
+    if (j0 >= nb_max)
+        return;
+    const int col = lane & 31, hf = lane >> 5;
+    const int tr = col < ntok ? col : 0;
+    const int jb = j0 + col < nb_max ? j0 + col : 0;
+    const float *arow = qbar + (int64_t)(tok0 + tr) * d_qk + 16 * hf;
+    const float *brow = k_blocks + (int64_t)bt.page_table[(int64_t)b * bt.max_pages + jb] * d_qk + 16 * hf;
+    const int nch = d_qk / 32;
+    f32x4 a[2][4], bb[2][4];
+    auto load = [&](int c, int buf) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            a[buf][u] = *(const f32x4 *)(arow + 32 * c + 4 * u);
+            bb[buf][u] = *(const f32x4 *)(brow + 32 * c + 4 * u);
+        }
+    };
+    f32x16 acc = f32x16{};
+    load(0, 0);
+    for (int c = 0; c < nch; ++c) {
+        const int cur = c & 1;
+        if (c + 1 < nch)
+            load(c + 1, cur ^ 1);
+#pragma unroll
+        for (int m = 0; m < 16; ++m)
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[cur][m >> 2][m & 3], bb[cur][m >> 2][m & 3], acc, 0, 0, 0);
+    }
+    // output: lane holds block column j0 + col, token rows 8*(i/4) + 4*hf + i%4
+    const int j = j0 + col;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 8 * (i >> 2) + 4 * hf + (i & 3);
+        if (r < ntok && j <= ((pos0 + r) >> bt.page_shift))
+            scores[(int64_t)(tok0 + r) * ld + j] = acc[i];
+    }
+}
+
+// One wave per token: slot e of its kb * page_size index row is position
+// blk*page_size + t of selected block k = e / page_size (t = e % page_size),
+// or -1 past the token's position or for an empty block slot.  The Top-K
+// lists blocks in ascending order with empty slots last, and only the block
+// holding pos(i) can be cut, so the rows come out as ascending positions
+// followed by -1.
+__global__ __launch_bounds__(kBlkThreads) void block_expand_kernel(Batch bt, const int32_t *__restrict__ blk, int kb,
+                                                                   int32_t *__restrict__ out)
+{
+    const int tok = blockIdx.x * (kBlkThreads / 64) + (threadIdx.x >> 6);
+    if (tok >= bt.total_q)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int b = seq_of_token(bt, tok);
+    const int pos = pos_of_token(bt, b, tok);
+    const int sh = bt.page_shift;
+    const int width = kb << sh;
+    for (int e = lane; e < width; e += 64) {
+        const int j = blk[(int64_t)tok * kb + (e >> sh)];
+        const int p = (j << sh) + (e & ((1 << sh) - 1));
+        out[(int64_t)tok * width + e] = (j >= 0 && p <= pos) ? p : -1;
+    }
+}
+
+hipError_t launch_block_pool(const Batch &bt, int dtype, const void *k_cache, int d_qk, int64_t row_stride,
+                             float *k_blocks, hipStream_t st)
+{
+    const int max_blocks = (bt.max_ctx + (1 << bt.page_shift) - 1) >> bt.page_shift;
+    hipLaunchKernelGGL(block_pool_kernel, dim3(max_blocks, bt.num_seqs), dim3(kBlkThreads), 0, st, bt,
+                       (const uint8_t *)k_cache, dtype == 0 ? 1 : 0, d_qk, row_stride, k_blocks);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_scores(const Batch &bt, int dtype, const void *q, int Hq, int d_qk, const float *k_blocks,
+                               float *scores, int64_t ld, float *qbar, hipStream_t st)
+{
+    hipLaunchKernelGGL(qbar_kernel, dim3(bt.total_q), dim3(kBlkThreads), 0, st, (const uint8_t *)q,
+                       dtype == 0 ? 1 : 0, Hq, d_qk, qbar);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int max_blocks = (bt.max_ctx + (1 << bt.page_shift) - 1) >> bt.page_shift;
+    const int n_tiles_max = (bt.total_q + kBlkTok - 1) / kBlkTok + bt.num_seqs - 1;
+    hipLaunchKernelGGL(block_scores_kernel, dim3(n_tiles_max, (max_blocks + kBlkCols - 1) / kBlkCols),
+                       dim3(kBlkThreads), 0, st, bt, qbar, d_qk, k_blocks, scores, ld, n_tiles_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_expand(const Batch &bt, const int32_t *blk, int kb, int32_t *indices, hipStream_t st)
+{
+    const int per = kBlkThreads / 64;
+    hipLaunchKernelGGL(block_expand_kernel, dim3((bt.total_q + per - 1) / per), dim3(kBlkThreads), 0, st, bt, blk,
+                       kb, indices);
+    return hipGetLastError();
+}
+
+} // namespace sa

@@ -151,6 +151,106 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const voi
                                     workspace, (hipStream_t)stream));
 }
 
+sa_status sparse_block_pool(const sa_batch *batch, sa_dtype dtype, const void *k_cache, int32_t d_qk,
+                            int64_t kv_row_stride, float *k_blocks, sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (dtype != SA_F32 && dtype != SA_BF16)
+        return SA_EINVAL;
+    if (!k_cache || !k_blocks || d_qk < 1 || kv_row_stride < d_qk)
+        return SA_EINVAL;
+    if (!aligned16(k_cache) || !aligned16(k_blocks))
+        return SA_EINVAL;
+    return launched(sa::launch_block_pool(bt, (int)dtype, k_cache, d_qk, kv_row_stride, k_blocks,
+                                          (hipStream_t)stream));
+}
+
+size_t sparse_block_scores_workspace_size(const sa_batch *batch, int32_t d_qk)
+{
+    sa::Batch bt;
+    if (make_batch(batch, &bt) != SA_OK || d_qk < 1)
+        return 0;
+    return (size_t)bt.total_q * (size_t)d_qk * 4u;
+}
+
+sa_status sparse_block_scores(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
+                              int32_t d_qk, const float *k_blocks, float *scores, int64_t ld_scores,
+                              void *workspace, size_t workspace_bytes, sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (dtype != SA_F32 && dtype != SA_BF16)
+        return SA_EINVAL;
+    if (!q || !k_blocks || !scores || n_q_heads < 1 || d_qk < 32 || (d_qk % 32))
+        return SA_EINVAL;
+    const int64_t max_blocks = (bt.max_ctx + (1 << bt.page_shift) - 1) >> bt.page_shift;
+    if (ld_scores < max_blocks)
+        return SA_EINVAL;
+    if (!aligned16(q) || !aligned16(k_blocks) || !aligned16(scores))
+        return SA_EINVAL;
+    const size_t need = (size_t)bt.total_q * (size_t)d_qk * 4u;
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+        return SA_EWORKSPACE;
+    return launched(sa::launch_block_scores(bt, (int)dtype, q, n_q_heads, d_qk, k_blocks, scores, ld_scores,
+                                            (float *)workspace, (hipStream_t)stream));
+}
+
+// A batch whose rows are block rows: lengths (pos >> page_shift) + 1, the
+// longest ceil(max_ctx / page_size).
+static sa::TopkPlan block_topk_plan(const sa::Batch &bt, int32_t kb)
+{
+    const int max_blocks = (bt.max_ctx + (1 << bt.page_shift) - 1) >> bt.page_shift;
+    return sa::topk_plan(bt.total_q, max_blocks, kb);
+}
+
+size_t sparse_block_topk_workspace_size(const sa_batch *batch, int32_t kb)
+{
+    sa::Batch bt;
+    if (make_batch(batch, &bt) != SA_OK || kb < 1)
+        return 0;
+    return block_topk_plan(bt, kb).ws_bytes;
+}
+
+sa_status sparse_block_topk(const sa_batch *batch, const float *scores, int64_t ld_scores, int32_t kb,
+                            int32_t *block_idx, void *workspace, size_t workspace_bytes, sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (!scores || !block_idx || kb < 1)
+        return SA_EINVAL;
+    if (kb > 4096)
+        return SA_EUNSUPPORTED;
+    const int64_t max_blocks = (bt.max_ctx + (1 << bt.page_shift) - 1) >> bt.page_shift;
+    if (ld_scores < max_blocks || (ld_scores & 3) || !aligned16(scores))
+        return SA_EINVAL;
+    const sa::TopkPlan plan = block_topk_plan(bt, kb);
+    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+        return SA_EWORKSPACE;
+    if (plan.chunked && bt.total_q > 65535)
+        return SA_EUNSUPPORTED;
+    return launched(sa::launch_topk(bt, plan, scores, ld_scores, kb, block_idx, workspace, (hipStream_t)stream,
+                                    bt.page_shift));
+}
+
+sa_status sparse_block_expand(const sa_batch *batch, const int32_t *block_idx, int32_t kb, int32_t *indices,
+                              sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (!block_idx || !indices || kb < 1 || ((int64_t)kb << bt.page_shift) > 65536)
+        return SA_EINVAL;
+    return launched(sa::launch_block_expand(bt, block_idx, kb, indices, (hipStream_t)stream));
+}
+
 sa_status sparse_cache_append(const sa_batch *batch, sa_dtype kv_dtype, const void *k_new, int32_t d_qk,
                               const void *v_new, int32_t d_v, void *k_cache, void *v_cache, int64_t kv_row_stride,
                               sa_dtype src_dtype, const void *k_idx_new, int32_t d_i, sa_dtype idx_dtype,

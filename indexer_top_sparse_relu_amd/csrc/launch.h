@@ -23,8 +23,10 @@ struct TopkPlan {
     size_t ws_bytes;  // workspace the plan needs
 };
 TopkPlan topk_plan(int total_q, int max_ctx, int k);
+// len_shift 0: row i holds the pos_i + 1 position scores; len_shift > 0: the
+// (pos_i >> len_shift) + 1 scores of its candidate blocks
 hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *scores, int64_t ld, int k,
-                       int32_t *indices, void *ws, hipStream_t st);
+                       int32_t *indices, void *ws, hipStream_t st, int len_shift = 0);
 
 // a3-a5
 struct AttnPlan {
@@ -38,6 +40,13 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &plan, const v
                        const void *k_cache, const void *v_cache, int d_v, int64_t row_stride,
                        const int32_t *indices, int k, const void *gate, int per_channel, float scale,
                        void *out, float *lse, void *ws, hipStream_t st);
+
+// block-level selection
+hipError_t launch_block_pool(const Batch &bt, int dtype, const void *k_cache, int d_qk, int64_t row_stride,
+                             float *k_blocks, hipStream_t st);
+hipError_t launch_block_scores(const Batch &bt, int dtype, const void *q, int Hq, int d_qk, const float *k_blocks,
+                               float *scores, int64_t ld, float *qbar, hipStream_t st);
+hipError_t launch_block_expand(const Batch &bt, const int32_t *blk, int kb, int32_t *indices, hipStream_t st);
 
 // cache append + fp8 quantisation
 hipError_t launch_cache_append(const Batch &bt, int kv_esz, const void *k_new, int d_qk, const void *v_new, int d_v,

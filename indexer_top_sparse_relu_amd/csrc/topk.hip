@@ -752,12 +752,21 @@ constexpr int32_t kTkPending = INT32_MIN;   // first output slot of a row left t
 // LDS, more workgroups per CU); a row it cannot finish gets kTkPending in its
 // first output slot and is selected by the general path in the second launch,
 // whose workgroups return at once for every other row.
+// A row's length: pos + 1 scores of positions (len_shift 0), or the
+// (pos >> len_shift) + 1 scores of the blocks of 2^len_shift positions that
+// start at or before pos.
+__device__ __forceinline__ int row_length(const Batch &bt, int row, int len_shift)
+{
+    const int b = seq_of_token(bt, row);
+    return (pos_of_token(bt, b, row) >> len_shift) + 1;
+}
+
 __global__ __launch_bounds__(kTkThreads) void topk_rows_fast_kernel(Batch bt, const float *__restrict__ scores,
-                                                                    int64_t ld, int K, int32_t *__restrict__ out)
+                                                                    int64_t ld, int K, int32_t *__restrict__ out,
+                                                                    int len_shift)
 {
     const int row = blockIdx.x;
-    const int b = seq_of_token(bt, row);
-    const int n = pos_of_token(bt, b, row) + 1;
+    const int n = row_length(bt, row, len_shift);
     const TkSmem sm = tk_smem_fast();
     const float *vals = scores + (int64_t)row * ld;
     int32_t *o = out + (int64_t)row * K;
@@ -768,14 +777,14 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_fast_kernel(Batch bt, co
 }
 
 __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(Batch bt, const float *__restrict__ scores,
-                                                               int64_t ld, int K, int32_t *__restrict__ out)
+                                                               int64_t ld, int K, int32_t *__restrict__ out,
+                                                               int len_shift)
 {
     const int row = blockIdx.x;
     int32_t *o = out + (int64_t)row * K;
     if (o[0] != kTkPending)     // (read by every thread before any is written)
         return;
-    const int b = seq_of_token(bt, row);
-    const int n = pos_of_token(bt, b, row) + 1;
+    const int n = row_length(bt, row, len_shift);
     const TkSmem sm = tk_smem(K);
     const float *vals = scores + (int64_t)row * ld;
     select_topk<false>(vals, nullptr, n, 0, K, o, nullptr, sm);
@@ -784,11 +793,11 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(Batch bt, const f
 // Stage 1: blockIdx.x = chunk, blockIdx.y = row; per-chunk top-K with scores.
 __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(Batch bt, const float *__restrict__ scores,
                                                                 int64_t ld, int K, int chunk, int64_t cand_ld,
-                                                                int32_t *__restrict__ cidx, float *__restrict__ cval)
+                                                                int32_t *__restrict__ cidx, float *__restrict__ cval,
+                                                                int len_shift)
 {
     const int c = blockIdx.x, row = blockIdx.y;
-    const int b = seq_of_token(bt, row);
-    const int n = pos_of_token(bt, b, row) + 1;
+    const int n = row_length(bt, row, len_shift);
     const int j0 = c * chunk;
     const int len = max(0, min(chunk, n - j0));
     const int64_t o = (int64_t)row * cand_ld + (int64_t)c * K;
@@ -831,7 +840,7 @@ TopkPlan topk_plan(int total_q, int max_ctx, int k)
 }
 
 hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *scores, int64_t ld, int k,
-                       int32_t *indices, void *ws, hipStream_t st)
+                       int32_t *indices, void *ws, hipStream_t st, int len_shift)
 {
     if (k < 1 || k > kMaxK)
         return hipErrorInvalidValue;
@@ -848,9 +857,9 @@ hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *score
     }
     if (!plan.chunked) {
         hipLaunchKernelGGL(topk_rows_fast_kernel, dim3(bt.total_q), dim3(kTkThreads), kTkSmemFast, st, bt, scores,
-                           ld, k, indices);
+                           ld, k, indices, len_shift);
         hipLaunchKernelGGL(topk_rows_kernel, dim3(bt.total_q), dim3(kTkThreads), smem, st, bt, scores, ld, k,
-                           indices);
+                           indices, len_shift);
         return hipGetLastError();
     }
     const int64_t cand_ld = ((int64_t)plan.n_chunks * k + 63) / 64 * 64;
@@ -859,7 +868,7 @@ hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *score
     if (bt.total_q > 65535)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(topk_chunk_kernel, dim3(plan.n_chunks, bt.total_q), dim3(kTkThreads), smem, st, bt, scores,
-                       ld, k, plan.chunk, cand_ld, cidx, cval);
+                       ld, k, plan.chunk, cand_ld, cidx, cval, len_shift);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
