@@ -163,6 +163,79 @@ def before_path(wl, steps: int, stream):
     return out
 
 
+def block_variant(wl, steps: int, stream, kb: int):
+    """The pages' block-level variant on the same workload, timed apart from the step above:
+    pooled block keys, block scores, top-kb blocks, their expansion to positions, and the same
+    gated attention over kb * page_size positions.  Stage rooflines use algorithmic work:
+    pooling reads every cache row once; scoring is 2 * d_qk flops per (token, candidate block)
+    on fp32 MFMA plus one read of q; the attention counts its selected positions as the step does."""
+    import torch
+
+    from indexer_top_sparse_relu_amd import binding as B
+
+    s = wl.spec
+    bt = B.batch_of(wl)
+    ps = s.page_size
+    n_pages = wl.k_cache.shape[0]
+    max_blocks = (s.max_ctx + ps - 1) // ps
+    ld = (max_blocks + 3) // 4 * 4
+    kbar = torch.empty((n_pages, s.d_qk), device="cuda")
+    scores = torch.empty((s.T, ld), device="cuda")
+    ws = torch.empty(B.sparse_block_scores_workspace_size(bt, s.d_qk), dtype=torch.uint8, device="cuda")
+    blk = torch.empty((s.T, kb), dtype=torch.int32, device="cuda")
+    tw = B.sparse_block_topk_workspace_size(bt, kb)
+    tws = torch.empty(tw, dtype=torch.uint8, device="cuda") if tw else None
+    idx = torch.empty((s.T, kb * ps), dtype=torch.int32, device="cuda")
+    out = torch.empty((s.T, s.Hq, s.d_v), device="cuda", dtype=wl.q.dtype)
+    aw = B.sparse_gated_attn_workspace_size(bt, s.Hq, s.d_v, kb * ps)
+    aws = torch.empty(aw, dtype=torch.uint8, device="cuda") if aw else None
+    stages = {
+        "pool": lambda: B.sparse_block_pool(bt, wl.k_cache, s.d_qk, kbar, stream=stream),
+        "scores": lambda: B.sparse_block_scores(bt, wl.q, kbar, scores, ws, stream=stream),
+        "topk": lambda: B.sparse_block_topk(bt, scores, kb, blk, tws, stream=stream),
+        "expand": lambda: B.sparse_block_expand(bt, blk, idx, stream=stream),
+        "attn": lambda: B.sparse_gated_attn_fwd(bt, wl.q, wl.k_cache, wl.v_cache, s.d_v, idx, wl.gate, out,
+                                                softmax_scale=s.softmax_scale, workspace=aws, stream=stream),
+    }
+    for fn in stages.values():
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for k, fn in enumerate(stages.values()):
+            fn()
+            ev[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = {name: sum(e[k].elapsed_time(e[k + 1]) for e in ev) / steps for k, name in enumerate(stages)}
+    step_ms = sum(e[0].elapsed_time(e[-1]) for e in ev) / steps
+    ae = 2 if s.attn_dtype == "bf16" else 4
+    nb = [((L - nq + j) // ps) + 1 for nq, L in zip(s.q_lens, s.ctx_lens) for j in range(nq)]
+    n_valid = int((idx >= 0).sum().item())
+    cache_rows = sum(s.ctx_lens)
+    work = {
+        "pool": ("hbm", cache_rows * s.d_qk * ae + sum((L + ps - 1) // ps for L in s.ctx_lens) * s.d_qk * 4),
+        "scores": ("mfma_fp32", 2.0 * s.d_qk * sum(nb)),
+        "topk": ("hbm", sum(nb) * 4 + s.T * kb * 4),
+        "expand": ("hbm", s.T * kb * 4 + s.T * kb * ps * 4),
+        "attn": ("mfma", 2.0 * s.Hq * n_valid * (s.d_qk + s.d_v)),
+    }
+    rl = {}
+    for name, (kind, w) in work.items():
+        t = ms[name] * 1e-3
+        if kind == "hbm":
+            ach = w / t / 1e9
+            rl[name] = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"], "unit": "GB/s"}
+        else:
+            peak = PEAK["fp32_TFLOPs"] if kind == "mfma_fp32" or s.attn_dtype != "bf16" else PEAK["bf16_TFLOPs"]
+            ach = w / t / 1e12
+            rl[name] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s"}
+        rl[name]["frac"] = rl[name]["achieved"] / rl[name]["peak"]
+        rl[name]["ms"] = ms[name]
+    return {"kb": kb, "block": ps, "positions": kb * ps, "ms_per_step": step_ms,
+            "query_tokens_per_s": s.T / (step_ms * 1e-3), "stages": rl}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -272,6 +345,7 @@ def main(argv=None):
         "stages": rl,
     }
     line["before_path"] = before_path(wl, args.steps, stream)
+    line["block_variant"] = block_variant(wl, args.steps, stream, kb=max(1, spec.K // spec.page_size))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(line), flush=True)

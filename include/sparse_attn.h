@@ -194,9 +194,11 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype,
  *   page_size), kbar[page_table[b, j], :] = mean of the block's rows s <
  *   ctx_len[b] of k_cache (first d_qk elements, dtype SA_F32 or SA_BF16),
  *   summed in fp32.  Pages no sequence uses are not written.
+ *   Rows of whole 16-byte units, at most 4 KB (d_qk <= 2048 bf16, 1024 f32).
  * sparse_block_scores: needs a workspace of sparse_block_scores_workspace_size
- *   bytes (T * d_qk fp32); d_qk a multiple of 32; ld_scores >= the most blocks
- *   of any sequence.  Products accumulate in fp32 (MFMA).
+ *   bytes (T * d_qk fp32); d_qk a multiple of 32, rows of at most 4 KB;
+ *   ld_scores >= the most blocks of any sequence.  Products accumulate in fp32
+ *   (MFMA).
  * sparse_block_topk: 1 <= kb <= 4096; workspace as sparse_topk's.
  * sparse_block_expand: kb * page_size <= 65536.
  */

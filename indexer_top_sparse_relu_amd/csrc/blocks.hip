@@ -32,13 +32,83 @@ __device__ __forceinline__ float load_elem(const uint8_t *base, int f32, int64_t
     return f32 ? ((const float *)base)[i] : __uint_as_float((uint32_t)((const uint16_t *)base)[i] << 16);
 }
 
+constexpr int kSumChunks = 4;       // 16-byte chunks per lane and row: rows of up to 4 KB
+
+// Column sums (fp32) of nrows rows of `dims` elements (bf16 or f32), row r at
+// base + r * row_bytes_stride, into out[0, dims) of LDS.  Wave w takes rows
+// w, w + 4, ...; a lane takes 16-byte chunks lane, lane + 64, ... of each
+// row, so every load is a coalesced 16-byte access; the four waves' partial
+// sums meet in LDS.
+__device__ void sum_rows(const uint8_t *__restrict__ base, int64_t row_bytes_stride, int nrows, int dims, int f32,
+                         float *part /* LDS [4][dims] */, float *out /* LDS [dims] */)
+{
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int per = f32 ? 4 : 8;                    // elements per 16-byte chunk
+    const int nch = dims / per;
+    float acc[kSumChunks][8];
+#pragma unroll
+    for (int k = 0; k < kSumChunks; ++k)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            acc[k][e] = 0.0f;
+#pragma unroll 4
+    for (int r = wv; r < nrows; r += 4) {
+        const uint8_t *row = base + r * row_bytes_stride;
+#pragma unroll
+        for (int k = 0; k < kSumChunks; ++k) {
+            const int c = lane + 64 * k;
+            if (c < nch) {
+                const u32x4 w = *(const u32x4 *)(row + 16 * c);
+                if (f32) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[k][e] += __uint_as_float(w[e]);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        acc[k][2 * e] += __uint_as_float(w[e] << 16);
+                        acc[k][2 * e + 1] += __uint_as_float(w[e] & 0xFFFF0000u);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < kSumChunks; ++k) {
+        const int c = lane + 64 * k;
+        if (c < nch) {
+            if (f32) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    part[wv * dims + c * 4 + e] = acc[k][e];
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    part[wv * dims + c * 8 + e] = acc[k][e];
+            }
+        }
+    }
+    __syncthreads();
+    for (int d = threadIdx.x; d < dims; d += kBlkThreads)
+        out[d] = (part[d] + part[dims + d]) + (part[2 * dims + d] + part[3 * dims + d]);
+    __syncthreads();
+}
+
+// LDS of sum_rows: 4 partial rows and the sums, 5 * dims floats, sized at
+// launch so that short rows leave room for more workgroups per CU.
+__device__ __forceinline__ float *sum_lds()
+{
+    extern __shared__ __align__(16) float blk_lds[];
+    return blk_lds;
+}
+
 // One workgroup per (block j, sequence b): the mean of the block's valid K
-// rows (fp32 sums in position order), written at k_blocks[page].  Threads own
-// consecutive dims, so every row read is coalesced.
+// rows (fp32 sums), written at k_blocks[page].
 __global__ __launch_bounds__(kBlkThreads) void block_pool_kernel(Batch bt, const uint8_t *__restrict__ k_cache,
                                                                  int f32, int d_qk, int64_t row_stride,
                                                                  float *__restrict__ k_blocks)
 {
+    float *part = sum_lds(), *sums = part + 4 * d_qk;
     const int j = blockIdx.x, b = blockIdx.y;
     const int ps = 1 << bt.page_shift;
     const int L = bt.ctx_len[b];
@@ -46,26 +116,23 @@ __global__ __launch_bounds__(kBlkThreads) void block_pool_kernel(Batch bt, const
         return;
     const int64_t page = bt.page_table[(int64_t)b * bt.max_pages + j];
     const int len = min(ps, L - j * ps);
-    for (int d = threadIdx.x; d < d_qk; d += kBlkThreads) {
-        float s = 0.0f;
-        for (int t = 0; t < len; ++t)
-            s += load_elem(k_cache, f32, (page * ps + t) * row_stride + d);
-        k_blocks[page * d_qk + d] = s / (float)len;
-    }
+    const int esz = f32 ? 4 : 2;
+    sum_rows(k_cache + page * ps * row_stride * esz, row_stride * esz, len, d_qk, f32, part, sums);
+    for (int d = threadIdx.x; d < d_qk; d += kBlkThreads)
+        k_blocks[page * d_qk + d] = sums[d] / (float)len;
 }
 
-// qbar[i, :] = sum over the query heads of q[i, h, :] (fp32, heads in order);
-// one workgroup per token.
+// qbar[i, :] = sum over the query heads of q[i, h, :] (fp32); one workgroup
+// per token.
 __global__ __launch_bounds__(kBlkThreads) void qbar_kernel(const uint8_t *__restrict__ q, int f32, int Hq, int d_qk,
                                                            float *__restrict__ qbar)
 {
+    float *part = sum_lds(), *sums = part + 4 * d_qk;
     const int64_t i = blockIdx.x;
-    for (int d = threadIdx.x; d < d_qk; d += kBlkThreads) {
-        float s = 0.0f;
-        for (int h = 0; h < Hq; ++h)
-            s += load_elem(q, f32, (i * Hq + h) * d_qk + d);
-        qbar[i * d_qk + d] = s;
-    }
+    const int esz = f32 ? 4 : 2;
+    sum_rows(q + i * Hq * d_qk * esz, (int64_t)d_qk * esz, Hq, d_qk, f32, part, sums);
+    for (int d = threadIdx.x; d < d_qk; d += kBlkThreads)
+        qbar[i * d_qk + d] = sums[d];
 }
 
 // Block scores on fp32 MFMA (32x32x2): a workgroup takes 32 consecutive
@@ -163,7 +230,7 @@ hipError_t launch_block_pool(const Batch &bt, int dtype, const void *k_cache, in
                              float *k_blocks, hipStream_t st)
 {
     const int max_blocks = (bt.max_ctx + (1 << bt.page_shift) - 1) >> bt.page_shift;
-    hipLaunchKernelGGL(block_pool_kernel, dim3(max_blocks, bt.num_seqs), dim3(kBlkThreads), 0, st, bt,
+    hipLaunchKernelGGL(block_pool_kernel, dim3(max_blocks, bt.num_seqs), dim3(kBlkThreads), 5 * d_qk * 4, st, bt,
                        (const uint8_t *)k_cache, dtype == 0 ? 1 : 0, d_qk, row_stride, k_blocks);
     return hipGetLastError();
 }
@@ -171,7 +238,7 @@ hipError_t launch_block_pool(const Batch &bt, int dtype, const void *k_cache, in
 hipError_t launch_block_scores(const Batch &bt, int dtype, const void *q, int Hq, int d_qk, const float *k_blocks,
                                float *scores, int64_t ld, float *qbar, hipStream_t st)
 {
-    hipLaunchKernelGGL(qbar_kernel, dim3(bt.total_q), dim3(kBlkThreads), 0, st, (const uint8_t *)q,
+    hipLaunchKernelGGL(qbar_kernel, dim3(bt.total_q), dim3(kBlkThreads), 5 * d_qk * 4, st, (const uint8_t *)q,
                        dtype == 0 ? 1 : 0, Hq, d_qk, qbar);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -160,10 +160,14 @@ sa_status sparse_block_pool(const sa_batch *batch, sa_dtype dtype, const void *k
         return st;
     if (dtype != SA_F32 && dtype != SA_BF16)
         return SA_EINVAL;
-    if (!k_cache || !k_blocks || d_qk < 1 || kv_row_stride < d_qk)
+    const int esz = dtype == SA_BF16 ? 2 : 4;
+    if (!k_cache || !k_blocks || d_qk < 1 || kv_row_stride < d_qk || (d_qk * esz) % 16 ||
+        (kv_row_stride * esz) % 16)
         return SA_EINVAL;
     if (!aligned16(k_cache) || !aligned16(k_blocks))
         return SA_EINVAL;
+    if (d_qk * esz > 4096)
+        return SA_EUNSUPPORTED;
     return launched(sa::launch_block_pool(bt, (int)dtype, k_cache, d_qk, kv_row_stride, k_blocks,
                                           (hipStream_t)stream));
 }
@@ -188,6 +192,8 @@ sa_status sparse_block_scores(const sa_batch *batch, sa_dtype dtype, const void 
         return SA_EINVAL;
     if (!q || !k_blocks || !scores || n_q_heads < 1 || d_qk < 32 || (d_qk % 32))
         return SA_EINVAL;
+    if (d_qk * (dtype == SA_BF16 ? 2 : 4) > 4096)
+        return SA_EUNSUPPORTED;
     const int64_t max_blocks = (bt.max_ctx + (1 << bt.page_shift) - 1) >> bt.page_shift;
     if (ld_scores < max_blocks)
         return SA_EINVAL;
