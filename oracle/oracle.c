@@ -35,7 +35,9 @@
  *   - cache append: fp8 indexer keys as e4m3fn codes with a per-token scale
  *     max|x| / 448, nearest-even, saturating (see that section);
  *   - block-level selection: blocks are pages, pooled keys are block means,
- *     block scores sum the query heads' dots (see that section).
+ *     block scores sum the query heads' dots (see that section);
+ *   - branch fusion: the local branch is causal attention over the last w
+ *     positions, fused as g * sparse + (1 - g) * local (see that section).
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -546,4 +548,44 @@ void orc_block_expand(const orc_batch *bt, const int32_t *blk, int kb, const int
         for (; n < w; ++n)
             out[r * w + n] = -1;
     }
+}
+
+/* ------------------------------------------ branch fusion with a local branch
+ * [SAD §3] pseudocode and §4 "branch fusion gating": a sparse branch and a
+ * sliding-window local branch, combined by a sigmoid gate,
+ *     y = g * sparse_out + (1 - g) * local_out,  g = sigmoid(G);
+ * the local branch keeps nearby context whatever the selection.
+ * Readings: the local branch is exact causal softmax attention of token i over
+ * the window positions max(0, pos(i) - w + 1) .. pos(i), with the same q, K,
+ * V and softmax scale; G is per head or per channel like the output gate.
+ * Each branch is the path's attention with its gate at +inf (sigmoid = 1):
+ * the fusion applies the gate once. */
+
+/* The window positions of each listed token, ascending, then -1 up to w. */
+void orc_window_indices(const orc_batch *bt, int w, const int64_t *rows, int64_t nrows, int32_t *out)
+{
+    for (int64_t r = 0; r < nrows; ++r) {
+        int b;
+        const int64_t pos = pos_of(bt, rows[r], &b);
+        const int64_t lo = pos - w + 1 > 0 ? pos - w + 1 : 0;
+        int64_t n = 0;
+        for (int64_t s = lo; s <= pos; ++s)
+            out[r * w + n++] = (int32_t)s;
+        for (; n < w; ++n)
+            out[r * w + n] = -1;
+    }
+}
+
+/* y[r, h, c] = g * a + (1 - g) * b with g = sigmoid(G) of token rows[r]
+ * (a, b, y: [nrows, Hq, dv] double; G raw in dtype, [T, Hq, dv] or [T, Hq]). */
+void orc_branch_fuse(int dtype, const double *a, const double *b, const void *gate, int per_channel, int Hq, int dv,
+                     const int64_t *rows, int64_t nrows, double *y)
+{
+    for (int64_t r = 0; r < nrows; ++r)
+        for (int h = 0; h < Hq; ++h)
+            for (int c = 0; c < dv; ++c) {
+                const double g = gate_of(dtype, gate, per_channel, rows[r], h, Hq, dv, c);
+                const int64_t e = (r * Hq + h) * (int64_t)dv + c;
+                y[e] = g * a[e] + (1.0 - g) * b[e];
+            }
 }

@@ -73,6 +73,9 @@ def lib():
         L.orc_block_pool.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, i64, vp]
         L.orc_block_scores.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, vp, i64, vp, i64]
         L.orc_block_expand.argtypes = [vp, vp, ctypes.c_int, vp, i64, vp]
+        L.orc_window_indices.argtypes = [vp, ctypes.c_int, vp, i64, vp]
+        L.orc_branch_fuse.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64,
+                                      vp]
         L.orc_fp8_encode.restype = ctypes.c_uint8
         L.orc_fp8_encode.argtypes = [ctypes.c_float]
         L.orc_quantize_rows.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp]
@@ -322,3 +325,46 @@ def block_pipeline(inp: Inputs, kb: int, rows=None, scale: Optional[float] = Non
     idx = block_expand(inp, blk, rows)
     out = sparse_attn(inp, idx, rows, scale)
     return sc, blk, idx, out
+
+
+# ------------------------------------------ branch fusion with a local branch
+
+def window_indices(inp: Inputs, w: int, rows=None) -> np.ndarray:
+    """Positions max(0, pos - w + 1) .. pos of each token, ascending, then -1: [len(rows), w]."""
+    rows = _rows(inp, rows)
+    out = np.zeros((rows.shape[0], int(w)), dtype=np.int32)
+    lib().orc_window_indices(ctypes.byref(inp._bt), int(w), rows.ctypes.data, rows.shape[0], out.ctypes.data)
+    return out
+
+
+def ungated(inp: Inputs) -> Inputs:
+    """The same inputs with a per-head gate of +inf (sigmoid = 1): attention without its output gate."""
+    import copy
+    u = copy.copy(inp)
+    inf = np.full((inp.T, inp.Hq), np.inf, dtype=np.float32)
+    if inp.attn_dtype == "bf16":
+        inf = (inf.view(np.uint32) >> 16).astype(np.uint16)
+    u.gate = np.ascontiguousarray(inf)
+    u.gate_per_channel = False
+    return u
+
+
+def branch_fuse(inp: Inputs, a: np.ndarray, b: np.ndarray, rows=None) -> np.ndarray:
+    """g * a + (1 - g) * b with g = sigmoid(G) of the inputs' gate, [len(rows), Hq, d_v]."""
+    rows = _rows(inp, rows)
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    b = np.ascontiguousarray(b, dtype=np.float64)
+    y = np.zeros_like(a)
+    lib().orc_branch_fuse(DT[inp.attn_dtype], a.ctypes.data, b.ctypes.data, _p(inp.gate), int(inp.gate_per_channel),
+                          inp.Hq, inp.d_v, rows.ctypes.data, rows.shape[0], y.ctypes.data)
+    return y
+
+
+def fused_pipeline(inp: Inputs, K: int, w: int, rows=None, scale: Optional[float] = None):
+    """Indexer -> Top-K -> ungated sparse attention, ungated window attention, then the gated fusion."""
+    rows = _rows(inp, rows)
+    sc, idx, _ = pipeline(inp, K, rows, scale)
+    u = ungated(inp)
+    a = sparse_attn(u, idx, rows, scale)
+    b = sparse_attn(u, window_indices(inp, w, rows), rows, scale)
+    return idx, a, b, branch_fuse(inp, a, b, rows)

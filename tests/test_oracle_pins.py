@@ -705,3 +705,58 @@ def test_block_pipeline_selects_the_planted_block():
     assert np.all(idx[:, :ps] == np.arange(20, 24)) and np.all(idx[:, ps:] == -1)
     ref = O.sparse_attn(inp, np.tile(np.arange(20, 24, dtype=np.int32), (inp.T, 1)), scale=0.3)
     assert np.allclose(out, ref, rtol=0, atol=0)
+
+
+# ------------------------------------------ branch fusion with a local branch
+
+def test_window_indices_hand_example():
+    rng = np.random.default_rng(50)
+    inp = _paged_attn_inputs(rng, [3], [10], ps=4)          # positions 7, 8, 9
+    got = O.window_indices(inp, 4)
+    assert got.tolist() == [[4, 5, 6, 7], [5, 6, 7, 8], [6, 7, 8, 9]]
+    inp2 = _paged_attn_inputs(rng, [2], [2], ps=4)          # positions 0, 1
+    assert O.window_indices(inp2, 4).tolist() == [[0, -1, -1, -1], [0, 1, -1, -1]]
+
+
+def test_window_attention_is_banded_causal_sdpa():
+    """The local branch against torch SDPA with a banded causal mask (f32 inputs, float64 math)."""
+    rng = np.random.default_rng(51)
+    T, L, Hq, d, w = 12, 30, 2, 8, 5
+    inp, q, kc, vc, g = attn_inputs(rng, T, L, Hq, d, d, page_size=8)
+    u = O.ungated(inp)
+    out = O.sparse_attn(u, O.window_indices(inp, w), scale=0.4)
+    pos = np.arange(L - T, L)
+    qt = torch.from_numpy(q.astype(np.float64)).transpose(0, 1)
+    kt = torch.from_numpy(kc[:L].astype(np.float64))[None].expand(Hq, -1, -1)
+    vt = torch.from_numpy(vc[:L].astype(np.float64))[None].expand(Hq, -1, -1)
+    s = torch.arange(L)[None, :]
+    p = torch.from_numpy(pos)[:, None]
+    mask = (s <= p) & (s >= p - w + 1)
+    ref = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask[None], scale=0.4).transpose(0, 1).numpy()
+    assert np.allclose(out, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_branch_fuse_limits_and_midpoint():
+    rng = np.random.default_rng(52)
+    inp, q, kc, vc, g = attn_inputs(rng, 4, 9, 2, 8, 8, page_size=4)
+    a = rng.standard_normal((4, 2, 8))
+    b = rng.standard_normal((4, 2, 8))
+    for G, want in ((80.0, a), (-80.0, b), (0.0, (a + b) / 2)):
+        inp.gate = np.full_like(inp.gate, G)
+        assert np.allclose(O.branch_fuse(inp, a, b), want, rtol=1e-15, atol=1e-30), G
+    # per-head gate broadcasts over channels
+    inp.gate = rng.standard_normal((4, 2)).astype(np.float32)
+    inp.gate_per_channel = False
+    gg = 1.0 / (1.0 + np.exp(-inp.gate.astype(np.float64)))[..., None]
+    assert np.allclose(O.branch_fuse(inp, a, b), gg * a + (1 - gg) * b, rtol=1e-14)
+
+
+def test_fused_pipeline_with_full_branches_is_dense_attention():
+    """K >= n and w >= n: both branches see every causal position, so any gate mix is dense attention."""
+    import indexer_top_sparse_relu_amd.workloads as W
+    spec = W.tiny_prefill_fp32().replace(q_lens=(48,), ctx_lens=(48,), K=48)
+    inp = O.Inputs.from_workload(W.generate(spec, "cpu"))
+    idx, a, b, y = O.fused_pipeline(inp, spec.K, 48, scale=spec.softmax_scale)
+    dense = O.dense_attn(O.ungated(inp), scale=spec.softmax_scale)
+    assert np.allclose(a, dense, rtol=1e-12, atol=1e-15) and np.allclose(b, dense, rtol=1e-12, atol=1e-15)
+    assert np.allclose(y, dense, rtol=1e-12, atol=1e-15)
