@@ -215,6 +215,30 @@ sa_status sparse_block_expand(const sa_batch *batch, const int32_t *block_idx, i
                               sa_stream_t stream);
 
 /*
+ * Branch fusion with a sliding-window local branch.  [SAD §3] pseudocode: a
+ * sparse branch, a sliding-window branch so that nearby context is never
+ * lost, and y = g * sparse_out + (1 - g) * local_out with g = sigmoid(...);
+ * [SAD §4] "branch fusion gating".  Readings: the local branch is exact causal
+ * attention over positions max(0, pos(i) - window + 1) .. pos(i) with the
+ * same q, K, V and softmax scale; G is per head or per channel.
+ * The flow, all on `stream`:
+ *   o_sparse = sparse_gated_attn_fwd over the Top-K indices, and
+ *   o_local  = sparse_gated_attn_fwd over sparse_window_indices(window),
+ *              both with a per-head gate of +inf (sigmoid(+inf) = 1: ungated);
+ *   out      = sparse_branch_fuse(o_sparse, o_local, G).
+ *
+ * sparse_window_indices: indices [T, window] = the window's positions,
+ *   ascending, then -1 (rows shorter than the window).  1 <= window <= 65536.
+ * sparse_branch_fuse: out = g * o_sparse + (1 - g) * o_local, g = sigmoid(G),
+ *   elementwise over rows x d_v (rows = T * n_q_heads), in fp32, rounded to
+ *   dtype (bf16 to nearest even).  gate_logits is [rows, d_v] when
+ *   gate_per_channel, else [rows]; d_v a multiple of 8; 16-byte aligned.
+ */
+sa_status sparse_window_indices(const sa_batch *batch, int32_t window, int32_t *indices, sa_stream_t stream);
+sa_status sparse_branch_fuse(sa_dtype dtype, int64_t rows, int32_t d_v, const void *o_sparse, const void *o_local,
+                             const void *gate_logits, int32_t gate_per_channel, void *out, sa_stream_t stream);
+
+/*
  * Cache append (the step before the path): writes the new tokens' rows into
  * the paged caches.  [HAT §5 item 2]: the cache organisation decides indexing
  * efficiency; [F2S "Engineering Considerations" item 1]: paged cache

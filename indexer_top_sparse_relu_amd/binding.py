@@ -22,7 +22,8 @@ SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_ELAUNCH = 0, -1, -2, -3, -4
 EXPORTS = ("sparse_indexer_scores", "sparse_topk_workspace_size", "sparse_topk",
            "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sparse_block_pool",
            "sparse_block_scores_workspace_size", "sparse_block_scores", "sparse_block_topk_workspace_size",
-           "sparse_block_topk", "sparse_block_expand", "sparse_cache_append",
+           "sparse_block_topk", "sparse_block_expand", "sparse_window_indices", "sparse_branch_fuse",
+           "sparse_cache_append",
            "sparse_quantize_fp8_rows", "sa_status_string", "sa_abi_version")
 
 _DT = {torch.float32: SA_F32, torch.bfloat16: SA_BF16, torch.float8_e4m3fn: SA_FP8_E4M3}
@@ -86,6 +87,10 @@ def lib() -> ctypes.CDLL:
         L.sparse_block_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
         L.sparse_block_expand.restype = ctypes.c_int
         L.sparse_block_expand.argtypes = [bp, vp, i32, vp, vp]
+        L.sparse_window_indices.restype = ctypes.c_int
+        L.sparse_window_indices.argtypes = [bp, i32, vp, vp]
+        L.sparse_branch_fuse.restype = ctypes.c_int
+        L.sparse_branch_fuse.argtypes = [ctypes.c_int, i64, i32, vp, vp, vp, i32, vp, vp]
         L.sparse_cache_append.restype = ctypes.c_int
         L.sparse_cache_append.argtypes = [bp, ctypes.c_int, vp, i32, vp, i32, vp, vp, i64, ctypes.c_int, vp, i32,
                                           ctypes.c_int, vp, vp, vp]
@@ -218,6 +223,22 @@ def sparse_block_expand(batch: SaBatch, block_idx: torch.Tensor, indices: torch.
     st = lib().sparse_block_expand(ctypes.byref(batch), _ptr(block_idx), block_idx.shape[1], _ptr(indices),
                                    _stream(stream))
     _check("sparse_block_expand", st)
+
+
+def sparse_window_indices(batch: SaBatch, window: int, indices: torch.Tensor, stream=None) -> None:
+    """The last `window` positions of each token (ascending, then -1) into indices [T, window]."""
+    st = lib().sparse_window_indices(ctypes.byref(batch), int(window), _ptr(indices), _stream(stream))
+    _check("sparse_window_indices", st)
+
+
+def sparse_branch_fuse(o_sparse: torch.Tensor, o_local: torch.Tensor, gate: torch.Tensor, out: torch.Tensor,
+                       stream=None) -> None:
+    """out = g * o_sparse + (1 - g) * o_local, g = sigmoid(gate); outputs [T, Hq, d_v], gate [T, Hq(, d_v)]."""
+    T, Hq, dv = o_sparse.shape
+    per_channel = 1 if gate.dim() == 3 else 0
+    st = lib().sparse_branch_fuse(_DT[o_sparse.dtype], T * Hq, dv, _ptr(o_sparse), _ptr(o_local), _ptr(gate),
+                                  per_channel, _ptr(out), _stream(stream))
+    _check("sparse_branch_fuse", st)
 
 
 def sparse_cache_append(batch: SaBatch, k_new: torch.Tensor, k_cache: torch.Tensor, k_idx_new: torch.Tensor,

@@ -257,6 +257,31 @@ sa_status sparse_block_expand(const sa_batch *batch, const int32_t *block_idx, i
     return launched(sa::launch_block_expand(bt, block_idx, kb, indices, (hipStream_t)stream));
 }
 
+sa_status sparse_window_indices(const sa_batch *batch, int32_t window, int32_t *indices, sa_stream_t stream)
+{
+    sa::Batch bt;
+    sa_status st = make_batch(batch, &bt);
+    if (st != SA_OK)
+        return st;
+    if (!indices || window < 1 || window > 65536)
+        return SA_EINVAL;
+    return launched(sa::launch_window_indices(bt, window, indices, (hipStream_t)stream));
+}
+
+sa_status sparse_branch_fuse(sa_dtype dtype, int64_t rows, int32_t d_v, const void *o_sparse, const void *o_local,
+                             const void *gate_logits, int32_t gate_per_channel, void *out, sa_stream_t stream)
+{
+    if (dtype != SA_F32 && dtype != SA_BF16)
+        return SA_EINVAL;
+    if (!o_sparse || !o_local || !gate_logits || !out || rows < 1 || d_v < 8 || (d_v % 8))
+        return SA_EINVAL;
+    if (!aligned16(o_sparse) || !aligned16(o_local) || !aligned16(out) ||
+        (gate_per_channel && !aligned16(gate_logits)))
+        return SA_EINVAL;
+    return launched(sa::launch_branch_fuse((int)dtype, rows, d_v, o_sparse, o_local, gate_logits,
+                                           gate_per_channel ? 1 : 0, out, (hipStream_t)stream));
+}
+
 sa_status sparse_cache_append(const sa_batch *batch, sa_dtype kv_dtype, const void *k_new, int32_t d_qk,
                               const void *v_new, int32_t d_v, void *k_cache, void *v_cache, int64_t kv_row_stride,
                               sa_dtype src_dtype, const void *k_idx_new, int32_t d_i, sa_dtype idx_dtype,

@@ -48,6 +48,11 @@ hipError_t launch_block_scores(const Batch &bt, int dtype, const void *q, int Hq
                                float *scores, int64_t ld, float *qbar, hipStream_t st);
 hipError_t launch_block_expand(const Batch &bt, const int32_t *blk, int kb, int32_t *indices, hipStream_t st);
 
+// branch fusion with a local branch
+hipError_t launch_window_indices(const Batch &bt, int w, int32_t *indices, hipStream_t st);
+hipError_t launch_branch_fuse(int dtype, int64_t rows, int dv, const void *a, const void *b, const void *gate,
+                              int per_channel, void *y, hipStream_t st);
+
 // cache append + fp8 quantisation
 hipError_t launch_cache_append(const Batch &bt, int kv_esz, const void *k_new, int d_qk, const void *v_new, int d_v,
                                void *k_cache, void *v_cache, int64_t row_stride, int src_f32, const void *kidx_new,
