@@ -236,6 +236,72 @@ def block_variant(wl, steps: int, stream, kb: int):
             "query_tokens_per_s": s.T / (step_ms * 1e-3), "stages": rl}
 
 
+def branch_fusion(wl, pl, steps: int, stream, window: int):
+    """Branch fusion with a sliding-window local branch on the same workload, timed apart from the
+    step: the sparse branch (the step's attention over its Top-K indices, ungated), the window
+    list, the local branch (the same attention over the last `window` positions, ungated) and the
+    fusion y = g * sparse + (1 - g) * local.  The indexer and Top-K are the step's and are not
+    repeated here."""
+    import torch
+
+    from indexer_top_sparse_relu_amd import binding as B
+
+    s = wl.spec
+    bt = pl.batch
+    inf = torch.full((s.T, s.Hq), float("inf"), device="cuda").to(wl.q.dtype)
+    win = torch.empty((s.T, window), dtype=torch.int32, device="cuda")
+    o_s = torch.empty((s.T, s.Hq, s.d_v), device="cuda", dtype=wl.q.dtype)
+    o_l = torch.empty_like(o_s)
+    y = torch.empty_like(o_s)
+    ws = {}
+    for k in (s.K, window):
+        n = B.sparse_gated_attn_workspace_size(bt, s.Hq, s.d_v, k)
+        ws[k] = torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+    stages = {
+        "sparse_branch": lambda: B.sparse_gated_attn_fwd(bt, wl.q, wl.k_cache, wl.v_cache, s.d_v, pl.indices, inf,
+                                                         o_s, softmax_scale=s.softmax_scale, workspace=ws[s.K],
+                                                         stream=stream),
+        "window": lambda: B.sparse_window_indices(bt, window, win, stream=stream),
+        "local_branch": lambda: B.sparse_gated_attn_fwd(bt, wl.q, wl.k_cache, wl.v_cache, s.d_v, win, inf, o_l,
+                                                        softmax_scale=s.softmax_scale, workspace=ws[window],
+                                                        stream=stream),
+        "fuse": lambda: B.sparse_branch_fuse(o_s, o_l, wl.gate, y, stream=stream),
+    }
+    for fn in stages.values():
+        fn()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record(stream)
+        for k, fn in enumerate(stages.values()):
+            fn()
+            ev[i][k + 1].record(stream)
+    torch.cuda.synchronize()
+    ms = {name: sum(e[k].elapsed_time(e[k + 1]) for e in ev) / steps for k, name in enumerate(stages)}
+    ae = 2 if s.attn_dtype == "bf16" else 4
+    n_sparse = int((pl.indices >= 0).sum().item())
+    n_local = int((win >= 0).sum().item())
+    gate_elems = s.Hq * (s.d_v if s.gate_per_channel else 1)
+    peak_mma = PEAK["bf16_TFLOPs"] if s.attn_dtype == "bf16" else PEAK["fp32_TFLOPs"]
+    work = {
+        "sparse_branch": ("mfma", 2.0 * s.Hq * n_sparse * (s.d_qk + s.d_v)),
+        "window": ("hbm", s.T * window * 4),
+        "local_branch": ("mfma", 2.0 * s.Hq * n_local * (s.d_qk + s.d_v)),
+        "fuse": ("hbm", s.T * (3 * s.Hq * s.d_v * ae + gate_elems * ae)),
+    }
+    rl = {}
+    for name, (kind, w) in work.items():
+        t = ms[name] * 1e-3
+        if kind == "hbm":
+            rl[name] = {"bound": "hbm", "achieved": w / t / 1e9, "peak": PEAK["hbm_GBs"], "unit": "GB/s"}
+        else:
+            rl[name] = {"bound": "mfma", "achieved": w / t / 1e12, "peak": peak_mma, "unit": "TFLOP/s"}
+        rl[name]["frac"] = rl[name]["achieved"] / rl[name]["peak"]
+        rl[name]["ms"] = ms[name]
+    total = sum(ms.values())
+    return {"window": window, "ms_attention_and_fusion": total, "stages": rl}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -346,6 +412,7 @@ def main(argv=None):
     }
     line["before_path"] = before_path(wl, args.steps, stream)
     line["block_variant"] = block_variant(wl, args.steps, stream, kb=max(1, spec.K // spec.page_size))
+    line["branch_fusion"] = branch_fusion(wl, pl, args.steps, stream, window=512)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(line), flush=True)
