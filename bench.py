@@ -310,6 +310,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="chunked_prefill_mla_128k")
     ap.add_argument("--cpu-sample", type=int, default=192, help="query tokens the oracle baseline runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time only the step (no cache append, block variant or branch fusion runs), so that "
+                         "a profile of this process holds the step's kernels alone")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a copy kernel of known size (for HBM counter calibration)")
     args = ap.parse_args(argv)
@@ -410,9 +413,10 @@ def main(argv=None):
         "roofline": roof,
         "stages": rl,
     }
-    line["before_path"] = before_path(wl, args.steps, stream)
-    line["block_variant"] = block_variant(wl, args.steps, stream, kb=max(1, spec.K // spec.page_size))
-    line["branch_fusion"] = branch_fusion(wl, pl, args.steps, stream, window=512)
+    if not args.step_only:
+        line["before_path"] = before_path(wl, args.steps, stream)
+        line["block_variant"] = block_variant(wl, args.steps, stream, kb=max(1, spec.K // spec.page_size))
+        line["branch_fusion"] = branch_fusion(wl, pl, args.steps, stream, window=512)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(line), flush=True)
