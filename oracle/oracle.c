@@ -37,7 +37,9 @@
  *   - block-level selection: blocks are pages, pooled keys are block means,
  *     block scores sum the query heads' dots (see that section);
  *   - branch fusion: the local branch is causal attention over the last w
- *     positions, fused as g * sparse + (1 - g) * local (see that section).
+ *     positions, fused as g * sparse + (1 - g) * local (see that section);
+ *   - backward: gradients of the attention and the gate over fixed indices,
+ *     scatter-added into the cache rows (see that section).
  */
 #define _GNU_SOURCE
 #include <math.h>
@@ -588,4 +590,111 @@ void orc_branch_fuse(int dtype, const double *a, const double *b, const void *ga
                 const int64_t e = (r * Hq + h) * (int64_t)dv + c;
                 y[e] = g * a[e] + (1.0 - g) * b[e];
             }
+}
+
+/* ------------------------------------------ backward over fixed indices
+ * The training-side pass the pages imply for the selected set ([HAT §3.3]:
+ * exact attention over kv_history[idx] times the gate; [F2S] pseudocode: the
+ * indices come from a non-differentiable Top-K, so gradients flow through the
+ * attention and the gate only, not through the selection or the indexer).
+ * For token i, head h, valid entries s_j of idx[i, :], with the forward's
+ *     z_j = scale q.K_j, P_j = softmax(z)_j, o = sum_j P_j V_j, y = o * g, g = sigmoid(G):
+ *     dG   = dy * o * g * (1 - g)           (per channel; summed over c per head)
+ *     do   = dy * g
+ *     dP_j = do . V_j,  D = sum_j P_j dP_j,  dz_j = P_j (dP_j - D)
+ *     dq  += scale * sum_j dz_j K_j
+ *     dK[row(s_j)] += scale * dz_j q,   dV[row(s_j)] += P_j do   (scatter-add)
+ * All in double from the exactly decoded inputs; dK and dV are indexed by
+ * physical cache row (row stride row_stride), and for the latent layout the
+ * caller passes the same array for both. */
+void orc_sparse_attn_bwd(const orc_batch *bt, int dtype, const void *q, int Hq, int dqk, const void *k_cache,
+                         const void *v_cache, int dv, int64_t row_stride, const int32_t *idx, int K, const void *gate,
+                         int gate_per_channel, double scale, const void *dy, int64_t T, double *dq, double *dk,
+                         double *dvv, double *dgate)
+{
+    double *z = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double *dp = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    double *o = (double *)malloc(sizeof(double) * (size_t)dv);
+    double *dov = (double *)malloc(sizeof(double) * (size_t)dv);
+    for (int64_t i = 0; i < T; ++i) {
+        const int b = seq_of(bt, i);
+        const int32_t *sel = idx + i * (int64_t)K;
+        for (int h = 0; h < Hq; ++h) {
+            const int64_t qo = (i * Hq + h) * (int64_t)dqk;
+            double m = -INFINITY;
+            for (int j = 0; j < K; ++j) {
+                if (sel[j] < 0)
+                    continue;
+                const int64_t pr = phys_row(bt, b, sel[j]);
+                double dot = 0.0;
+                for (int d = 0; d < dqk; ++d)
+                    dot += load(dtype, q, qo + d) * load(dtype, k_cache, pr * row_stride + d);
+                z[j] = scale * dot;
+                if (z[j] > m)
+                    m = z[j];
+            }
+            double l = 0.0;
+            for (int j = 0; j < K; ++j)
+                if (sel[j] >= 0)
+                    l += exp(z[j] - m);
+            for (int c = 0; c < dv; ++c)
+                o[c] = 0.0;
+            for (int j = 0; j < K; ++j) {
+                if (sel[j] < 0)
+                    continue;
+                z[j] = exp(z[j] - m) / l;            /* z now holds P_j */
+                const int64_t pr = phys_row(bt, b, sel[j]);
+                for (int c = 0; c < dv; ++c)
+                    o[c] += z[j] * load(dtype, v_cache, pr * row_stride + c);
+            }
+            const int64_t yo = (i * Hq + h) * (int64_t)dv;
+            double dgh = 0.0;
+            for (int c = 0; c < dv; ++c) {
+                const double g = gate_of(dtype, gate, gate_per_channel, i, h, Hq, dv, c);
+                const double dyc = load(dtype, dy, yo + c);
+                dov[c] = dyc * g;
+                const double dgc = dyc * o[c] * g * (1.0 - g);
+                if (gate_per_channel)
+                    dgate[yo + c] = dgc;
+                else
+                    dgh += dgc;
+            }
+            if (!gate_per_channel)
+                dgate[i * Hq + h] = dgh;
+            if (l <= 0.0) {
+                for (int d = 0; d < dqk; ++d)
+                    dq[qo + d] = 0.0;
+                continue;
+            }
+            double D = 0.0;
+            for (int j = 0; j < K; ++j) {
+                if (sel[j] < 0)
+                    continue;
+                const int64_t pr = phys_row(bt, b, sel[j]);
+                double s = 0.0;
+                for (int c = 0; c < dv; ++c)
+                    s += dov[c] * load(dtype, v_cache, pr * row_stride + c);
+                dp[j] = s;
+                D += z[j] * s;
+            }
+            for (int d = 0; d < dqk; ++d)
+                dq[qo + d] = 0.0;
+            for (int j = 0; j < K; ++j) {
+                if (sel[j] < 0)
+                    continue;
+                const int64_t pr = phys_row(bt, b, sel[j]);
+                const double dz = z[j] * (dp[j] - D);
+                for (int d = 0; d < dqk; ++d) {
+                    dq[qo + d] += scale * dz * load(dtype, k_cache, pr * row_stride + d);
+                    dk[pr * row_stride + d] += scale * dz * load(dtype, q, qo + d);
+                }
+                for (int c = 0; c < dv; ++c)
+                    dvv[pr * row_stride + c] += z[j] * dov[c];
+            }
+        }
+    }
+    free(dov);
+    free(o);
+    free(dp);
+    free(z);
 }

@@ -76,6 +76,8 @@ def lib():
         L.orc_window_indices.argtypes = [vp, ctypes.c_int, vp, i64, vp]
         L.orc_branch_fuse.argtypes = [ctypes.c_int, vp, vp, vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, i64,
                                       vp]
+        L.orc_sparse_attn_bwd.argtypes = [vp, ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp, vp, ctypes.c_int,
+                                          i64, vp, ctypes.c_int, vp, ctypes.c_int, dbl, vp, i64, vp, vp, vp, vp]
         L.orc_fp8_encode.restype = ctypes.c_uint8
         L.orc_fp8_encode.argtypes = [ctypes.c_float]
         L.orc_quantize_rows.argtypes = [ctypes.c_int, vp, i64, i64, vp, vp]
@@ -368,3 +370,29 @@ def fused_pipeline(inp: Inputs, K: int, w: int, rows=None, scale: Optional[float
     a = sparse_attn(u, idx, rows, scale)
     b = sparse_attn(u, window_indices(inp, w, rows), rows, scale)
     return idx, a, b, branch_fuse(inp, a, b, rows)
+
+
+# ------------------------------------------------- backward over fixed indices
+
+def sparse_attn_bwd(inp: Inputs, idx: np.ndarray, dy: np.ndarray, scale: Optional[float] = None):
+    """Gradients of the gated sparse attention of every token over idx [T, K], for the upstream
+    gradient dy [T, Hq, d_v] (raw bits for bf16): returns (dq [T, Hq, d_qk], dk [rows, row_stride],
+    dv [rows, row_stride], dgate like the gate), all float64; dk/dv are indexed by physical cache row
+    and are the same array for the latent layout (V inside the K row)."""
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    dy = np.ascontiguousarray(dy)
+    T = inp.T
+    if idx.shape[0] != T:
+        raise ValueError("idx needs one row per token")
+    scale = float(scale if scale is not None else 1.0 / np.sqrt(inp.d_qk))
+    rows = inp.k_cache.reshape(-1, inp.row_stride).shape[0]
+    same = inp.v_cache is inp.k_cache or (inp.v_cache.ctypes.data == inp.k_cache.ctypes.data)
+    dq = np.zeros((T, inp.Hq, inp.d_qk), dtype=np.float64)
+    dk = np.zeros((rows, inp.row_stride), dtype=np.float64)
+    dv = dk if same else np.zeros((rows, inp.row_stride), dtype=np.float64)
+    dg = np.zeros((T, inp.Hq, inp.d_v) if inp.gate_per_channel else (T, inp.Hq), dtype=np.float64)
+    lib().orc_sparse_attn_bwd(ctypes.byref(inp._bt), DT[inp.attn_dtype], _p(inp.q), inp.Hq, inp.d_qk,
+                              _p(inp.k_cache), _p(inp.v_cache), inp.d_v, inp.row_stride, idx.ctypes.data,
+                              idx.shape[1], _p(inp.gate), int(inp.gate_per_channel), scale, dy.ctypes.data, T,
+                              dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, dg.ctypes.data)
+    return dq, dk, dv, dg

@@ -760,3 +760,64 @@ def test_fused_pipeline_with_full_branches_is_dense_attention():
     dense = O.dense_attn(O.ungated(inp), scale=spec.softmax_scale)
     assert np.allclose(a, dense, rtol=1e-12, atol=1e-15) and np.allclose(b, dense, rtol=1e-12, atol=1e-15)
     assert np.allclose(y, dense, rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------- backward over fixed indices
+
+def _torch_gated_attn_grads(q, kc, vc, idx, gate, dy, scale, per_channel, same):
+    """torch float64 autograd of y = softmax(scale q K_sel^T) V_sel * sigmoid(G), loss = sum(y * dy)."""
+    qt = torch.tensor(q, dtype=torch.float64, requires_grad=True)
+    kt = torch.tensor(kc, dtype=torch.float64, requires_grad=True)
+    vt = kt if same else torch.tensor(vc, dtype=torch.float64, requires_grad=True)
+    gt = torch.tensor(gate, dtype=torch.float64, requires_grad=True)
+    dv = dy.shape[-1]
+    loss = 0.0
+    for i in range(q.shape[0]):
+        sel = torch.from_numpy(idx[i][idx[i] >= 0].astype(np.int64))
+        if sel.numel() == 0:
+            continue
+        K_ = kt.index_select(0, sel)[:, :q.shape[2]]
+        V_ = vt.index_select(0, sel)[:, :dv]
+        p = torch.softmax(scale * qt[i] @ K_.T, dim=-1)               # [H, n]
+        o = p @ V_                                                      # [H, dv]
+        g = torch.sigmoid(gt[i] if per_channel else gt[i][:, None])
+        loss = loss + (o * g * torch.from_numpy(dy[i].astype(np.float64))).sum()
+    loss.backward()
+    dk = kt.grad.numpy()
+    return qt.grad.numpy(), dk, (dk if same else vt.grad.numpy()), gt.grad.numpy()
+
+
+@pytest.mark.parametrize("per_channel,mla", [(True, False), (False, False), (True, True)])
+def test_backward_matches_torch_autograd(per_channel, mla):
+    rng = np.random.default_rng(60)
+    T, Hq, d, dv = 5, 3, 8, 8 if not mla else 6
+    inp, q, kc, vc, g = attn_inputs(rng, T, 20, Hq, d, dv, page_size=4, mla=mla, per_channel=per_channel)
+    K = 7
+    idx = np.full((T, K), -1, np.int32)
+    n = O.row_lengths(inp)
+    for i in range(T):
+        m = min(K - 1, n[i])                               # leave at least one padding slot
+        idx[i, :m] = np.sort(rng.choice(n[i], size=m, replace=False))
+    dy = rng.standard_normal((T, Hq, dv)).astype(np.float32)
+    dq, dk, dvv, dg = O.sparse_attn_bwd(inp, idx, dy, scale=0.35)
+    kfull = inp.k_cache.reshape(-1, inp.row_stride)
+    vfull = inp.v_cache.reshape(-1, inp.row_stride)
+    tq, tk, tv, tg = _torch_gated_attn_grads(q, kfull, vfull, idx, inp.gate, dy, 0.35, per_channel, mla)
+    assert np.allclose(dq, tq, rtol=1e-10, atol=1e-13)
+    assert np.allclose(dk, tk, rtol=1e-10, atol=1e-13)
+    assert np.allclose(dvv, tv, rtol=1e-10, atol=1e-13)
+    assert np.allclose(dg, tg, rtol=1e-10, atol=1e-13)
+
+
+def test_backward_of_a_single_index_is_the_gated_row():
+    """K = 1: y = V[s] * sigmoid(G), so dq = 0, dK = 0, dV[s] = sum over tokens of dy * g."""
+    rng = np.random.default_rng(61)
+    T, Hq, d = 3, 2, 8
+    inp, q, kc, vc, g = attn_inputs(rng, T, 10, Hq, d, d, page_size=4)
+    idx = np.array([[4], [4], [6]], np.int32)
+    dy = rng.standard_normal((T, Hq, d)).astype(np.float32)
+    dq, dk, dvv, dg = O.sparse_attn_bwd(inp, idx, dy)
+    sg = 1 / (1 + np.exp(-inp.gate.astype(np.float64)))
+    assert np.allclose(dq, 0, atol=1e-15) and np.allclose(dk, 0, atol=1e-15)
+    assert np.allclose(dvv[4, :d], (dy[0] * sg[0]).sum(0) + (dy[1] * sg[1]).sum(0), rtol=1e-12)
+    assert np.allclose(dvv[6, :d], (dy[2] * sg[2]).sum(0), rtol=1e-12)
