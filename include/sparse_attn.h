@@ -215,6 +215,34 @@ sa_status sparse_block_expand(const sa_batch *batch, const int32_t *block_idx, i
                               sa_stream_t stream);
 
 /*
+ * Backward over fixed indices (training).  [HAT §3.3]: exact attention over
+ * kv_history[idx], scaled by the gate; [F2S "Fine-Grained Sparse Attention:
+ * Indexer Plus Top-K"]: the indices come from a Top-K, which passes no
+ * gradient, so only the attention and the gate are differentiated.  For the
+ * forward of sparse_gated_attn_fwd (its output `out` and log-sum-exp `lse`
+ * are inputs here) and an upstream gradient d_out:
+ *     d_gate = d_out * out * (1 - g)               (per channel; summed over c per head)
+ *     do = d_out * g,  D = d_out . out,  dP_j = do . V_j,  dS_j = P_j (dP_j - D),
+ *     P_j = exp(softmax_scale * q . K_j - lse)
+ *     d_q = softmax_scale * sum_j dS_j K_j                      (written)
+ *     d_k_cache[row(s_j)] += softmax_scale * dS_j q             (scatter-added)
+ *     d_v_cache[row(s_j)] += P_j do                             (scatter-added)
+ * summed over every (token, head) that selected the row.  The caller zeroes
+ * d_k_cache and d_v_cache ([num_pages, page_size, kv_row_stride] fp32; the
+ * same array when v_cache == k_cache).  d_q is [T, n_q_heads, d_qk] fp32,
+ * d_gate fp32 shaped like the gate.  P, dS and do enter the MFMAs rounded to
+ * bf16; sums are fp32; the scatter uses float atomics, so its summation order
+ * (and the last bits of d_k/d_v) varies between runs.
+ * Supported: SA_BF16, d_qk = d_v in {64, 128}, n_q_heads in {16, 32, 64}.
+ */
+sa_status sparse_gated_attn_bwd(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
+                                int32_t d_qk, const void *k_cache, const void *v_cache, int32_t d_v,
+                                int64_t kv_row_stride, const int32_t *indices, int32_t k, const void *gate_logits,
+                                int32_t gate_per_channel, float softmax_scale, const void *out, const float *lse,
+                                const void *d_out, float *d_q, float *d_k_cache, float *d_v_cache, float *d_gate,
+                                sa_stream_t stream);
+
+/*
  * Branch fusion with a sliding-window local branch.  [SAD §3] pseudocode: a
  * sparse branch, a sliding-window branch so that nearby context is never
  * lost, and y = g * sparse_out + (1 - g) * local_out with g = sigmoid(...);

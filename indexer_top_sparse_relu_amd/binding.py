@@ -22,7 +22,8 @@ SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_ELAUNCH = 0, -1, -2, -3, -4
 EXPORTS = ("sparse_indexer_scores", "sparse_topk_workspace_size", "sparse_topk",
            "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sparse_block_pool",
            "sparse_block_scores_workspace_size", "sparse_block_scores", "sparse_block_topk_workspace_size",
-           "sparse_block_topk", "sparse_block_expand", "sparse_window_indices", "sparse_branch_fuse",
+           "sparse_block_topk", "sparse_block_expand", "sparse_gated_attn_bwd", "sparse_window_indices",
+           "sparse_branch_fuse",
            "sparse_cache_append",
            "sparse_quantize_fp8_rows", "sa_status_string", "sa_abi_version")
 
@@ -87,6 +88,9 @@ def lib() -> ctypes.CDLL:
         L.sparse_block_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
         L.sparse_block_expand.restype = ctypes.c_int
         L.sparse_block_expand.argtypes = [bp, vp, i32, vp, vp]
+        L.sparse_gated_attn_bwd.restype = ctypes.c_int
+        L.sparse_gated_attn_bwd.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp, i32,
+                                            ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
         L.sparse_window_indices.restype = ctypes.c_int
         L.sparse_window_indices.argtypes = [bp, i32, vp, vp]
         L.sparse_branch_fuse.restype = ctypes.c_int
@@ -223,6 +227,23 @@ def sparse_block_expand(batch: SaBatch, block_idx: torch.Tensor, indices: torch.
     st = lib().sparse_block_expand(ctypes.byref(batch), _ptr(block_idx), block_idx.shape[1], _ptr(indices),
                                    _stream(stream))
     _check("sparse_block_expand", st)
+
+
+def sparse_gated_attn_bwd(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, d_v: int,
+                          indices: torch.Tensor, gate: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                          d_out: torch.Tensor, d_q: torch.Tensor, d_k_cache: torch.Tensor, d_v_cache: torch.Tensor,
+                          d_gate: torch.Tensor, softmax_scale: Optional[float] = None, stream=None) -> None:
+    """Gradients of the gated sparse attention over fixed indices: d_q and d_gate written, d_k_cache and
+    d_v_cache (fp32, zeroed by the caller, the same tensor for a shared cache) scatter-added."""
+    T, Hq, dqk = q.shape
+    per_channel = 1 if gate.dim() == 3 else 0
+    scale = float(softmax_scale if softmax_scale is not None else dqk ** -0.5)
+    st = lib().sparse_gated_attn_bwd(ctypes.byref(batch), _DT[q.dtype], _ptr(q), Hq, dqk, _ptr(k_cache),
+                                     _ptr(v_cache), int(d_v), k_cache.stride(-2), _ptr(indices), indices.shape[1],
+                                     _ptr(gate), per_channel, ctypes.c_float(scale), _ptr(out), _ptr(lse),
+                                     _ptr(d_out), _ptr(d_q), _ptr(d_k_cache), _ptr(d_v_cache), _ptr(d_gate),
+                                     _stream(stream))
+    _check("sparse_gated_attn_bwd", st)
 
 
 def sparse_window_indices(batch: SaBatch, window: int, indices: torch.Tensor, stream=None) -> None:

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["capi.hip", "indexer.hip", "topk.hip", "attn.hip", "append.hip", "blocks.hip", "fusion.hip"]
+SOURCES = ["capi.hip", "indexer.hip", "topk.hip", "attn.hip", "append.hip", "blocks.hip", "fusion.hip", "attn_bwd.hip"]
 # per-source code generation options: the indexer keeps MFMA accumulators in
 # arch VGPRs, where its VALU epilogue reads them without v_accvgpr_read copies,
 # and assumes finite values (scores are defined for finite inputs), so max(x, 0)

@@ -48,6 +48,13 @@ hipError_t launch_block_scores(const Batch &bt, int dtype, const void *q, int Hq
                                float *scores, int64_t ld, float *qbar, hipStream_t st);
 hipError_t launch_block_expand(const Batch &bt, const int32_t *blk, int kb, int32_t *indices, hipStream_t st);
 
+// backward over fixed indices
+int attn_bwd_supported(int dtype, int Hq, int d_qk, int d_v);
+hipError_t launch_attn_bwd(const Batch &bt, int Hq, int D, const void *q, const void *kc, const void *vc,
+                           int64_t rs, const int32_t *idx, int K, const void *gate, int per_channel, float scale,
+                           const void *y, const float *lse, const void *dy, float *dq, float *dk, float *dv,
+                           float *dgate, hipStream_t st);
+
 // branch fusion with a local branch
 hipError_t launch_window_indices(const Batch &bt, int w, int32_t *indices, hipStream_t st);
 hipError_t launch_branch_fuse(int dtype, int64_t rows, int dv, const void *a, const void *b, const void *gate,
