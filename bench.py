@@ -302,6 +302,54 @@ def branch_fusion(wl, pl, steps: int, stream, window: int):
     return {"window": window, "ms_attention_and_fusion": total, "stages": rl}
 
 
+def backward_pass(steps: int, stream):
+    """The backward over fixed indices on the bf16 prefill workload (8192 tokens, 32 query heads of
+    128 dims, K = 2048), timed apart from the step: the forward (indexer, Top-K, attention with its
+    log-sum-exp) runs once to produce the indices, the output and lse, then sparse_gated_attn_bwd is
+    timed.  Algorithmic work: 2 * H_q * (3 d_qk + 2 d_v) flops per (token, selected position) for
+    the S, dq and dK contractions over d_qk and the dP and dV ones over d_v (S is recomputed),
+    against the bf16 peak."""
+    import torch
+
+    from indexer_top_sparse_relu_amd import binding as B
+    from indexer_top_sparse_relu_amd import workloads as W
+
+    spec = W.CONFIGS["prefill_bf16_8k"]()
+    wl = W.generate(spec, "cuda")
+    pl = B.Pipeline(wl)
+    pl.run(stream)
+    torch.cuda.synchronize()
+    g = torch.Generator(device="cuda").manual_seed(7)
+    dy = torch.randn(pl.out.shape, device="cuda", generator=g).to(torch.bfloat16)
+    shared = wl.v_cache.data_ptr() == wl.k_cache.data_ptr()
+    dk = torch.zeros((wl.k_cache.shape[0], wl.k_cache.shape[1], wl.kv_row_stride), device="cuda")
+    dv = dk if shared else torch.zeros_like(dk)
+    dq = torch.empty(wl.q.shape, device="cuda")
+    dg = torch.empty(wl.gate.shape, device="cuda")
+
+    def bwd():
+        B.sparse_gated_attn_bwd(pl.batch, wl.q, wl.k_cache, wl.v_cache, spec.d_v, pl.indices, wl.gate, pl.out,
+                                pl.lse, dy, dq, dk, dv, dg, softmax_scale=spec.softmax_scale, stream=stream)
+
+    bwd()
+    torch.cuda.synchronize()
+    n = max(1, min(steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        bwd()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n
+    n_valid = int((pl.indices >= 0).sum().item())
+    flops = 2.0 * spec.Hq * n_valid * (3 * spec.d_qk + 2 * spec.d_v)     # S, dq, dK over d_qk; dP, dV over d_v
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"workload": spec.name, "ms": ms, "query_tokens_per_s": spec.T / (ms * 1e-3),
+            "atomic_adds": n_valid * (spec.d_qk + spec.d_v),
+            "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK["bf16_TFLOPs"], "unit": "TFLOP/s",
+                         "frac": ach / PEAK["bf16_TFLOPs"]}}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -417,6 +465,7 @@ def main(argv=None):
         line["before_path"] = before_path(wl, args.steps, stream)
         line["block_variant"] = block_variant(wl, args.steps, stream, kb=max(1, spec.K // spec.page_size))
         line["branch_fusion"] = branch_fusion(wl, pl, args.steps, stream, window=512)
+        line["backward"] = backward_pass(args.steps, stream)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
     print(json.dumps(line), flush=True)
