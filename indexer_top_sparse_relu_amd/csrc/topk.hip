@@ -47,6 +47,7 @@
 namespace sa {
 
 constexpr int kTkThreads = 512;
+static_assert(kTkThreads <= 1024, "misc holds per-wave slots for at most 16 waves");
 constexpr int kTkWaves = kTkThreads / 64;
 constexpr int kBins = 4096;
 constexpr int kCap = 4096;      // LDS slots for the window's candidates
@@ -149,7 +150,7 @@ __device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, uint32_
     wave_minmax(mn, mx);
     if (lane == 0) {
         misc[16 + wv] = mn;
-        misc[24 + wv] = mx;
+        misc[32 + wv] = mx;
     }
     __syncthreads();
     mn = 0xFFFFFFFFu;
@@ -157,7 +158,7 @@ __device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, uint32_
 #pragma unroll
     for (int w = 0; w < kTkWaves; ++w) {
         mn = min(mn, misc[16 + w]);
-        mx = max(mx, misc[24 + w]);
+        mx = max(mx, misc[32 + w]);
     }
     __syncthreads();
 }
@@ -185,16 +186,16 @@ __device__ __forceinline__ void find_bin(const TkSmem &sm, uint32_t need, int &b
 #pragma unroll
         for (int j = BT - 1; j >= 0; --j) {
             if (acc + h[j] >= need) {
-                sm.misc[40] = (uint32_t)(t * BT + j);
-                sm.misc[41] = acc;
+                sm.misc[48] = (uint32_t)(t * BT + j);
+                sm.misc[49] = acc;
                 break;
             }
             acc += h[j];
         }
     }
     __syncthreads();
-    b_out = (int)sm.misc[40];
-    gt_out = sm.misc[41];
+    b_out = (int)sm.misc[48];
+    gt_out = sm.misc[49];
     __syncthreads();
 }
 
