@@ -68,12 +68,17 @@ typedef enum {
  * Its causal candidates are the n = pos + 1 positions 0..pos (self-inclusive).
  * Logical position s of sequence b lives at physical cache row
  *     page_table[b * max_pages + s / page_size] * page_size + s % page_size.
- * Decode is the case of one new token per sequence.
+ * Decode is the case of one new token per sequence.  A sequence may have no
+ * new tokens (q_start[b+1] == q_start[b]); it then takes part only through its
+ * cached pages.  A batch with T = 0 is valid: every entry point that takes a
+ * batch checks it and returns SA_OK without launching anything (workspace
+ * sizes are 0), except sparse_block_pool, which pools the cached pages as for
+ * any other batch.
  */
 typedef struct {
     int32_t num_seqs;          /* (host) B >= 1 */
-    int32_t total_q;           /* (host) T = q_start[B] >= 1 */
-    int32_t max_q;             /* (host) max_b (q_start[b+1] - q_start[b]) */
+    int32_t total_q;           /* (host) T = q_start[B] >= 0 */
+    int32_t max_q;             /* (host) max_b (q_start[b+1] - q_start[b]); >= 1, or 0 when T = 0 */
     int32_t max_ctx;           /* (host) max_b ctx_len[b]; sizes grids and bounds score rows */
     int32_t page_size;         /* (host) tokens per page: power of two, 16..4096 */
     int32_t max_pages;         /* (host) row stride of page_table, >= ceil(max_ctx / page_size) */
@@ -261,6 +266,7 @@ sa_status sparse_gated_attn_bwd(const sa_batch *batch, sa_dtype dtype, const voi
  *   elementwise over rows x d_v (rows = T * n_q_heads), in fp32, rounded to
  *   dtype (bf16 to nearest even).  gate_logits is [rows, d_v] when
  *   gate_per_channel, else [rows]; d_v a multiple of 8; 16-byte aligned.
+ *   rows = 0 returns SA_OK and launches nothing.
  */
 sa_status sparse_window_indices(const sa_batch *batch, int32_t window, int32_t *indices, sa_stream_t stream);
 sa_status sparse_branch_fuse(sa_dtype dtype, int64_t rows, int32_t d_v, const void *o_sparse, const void *o_local,
@@ -305,6 +311,7 @@ sa_status sparse_cache_append(const sa_batch *batch, sa_dtype kv_dtype, const vo
  * max|x[r, :]| / 448, codes[r, c] = e4m3fn(x[r, c] / scales[r]).  For the
  * indexer queries, rows = T and cols = n_heads * head_dim give q_idx and
  * q_scale.  cols a multiple of 8; x 16-byte and codes 8-byte aligned.
+ * rows = 0 returns SA_OK and launches nothing.
  */
 sa_status sparse_quantize_fp8_rows(sa_dtype src_dtype, const void *x, int64_t rows, int32_t cols,
                                    uint8_t *codes, float *scales, sa_stream_t stream);

@@ -21,9 +21,15 @@ int log2_exact(int x)
     return s;
 }
 
+// A valid batch with no query tokens (T = 0): the entry points return SA_OK
+// without launching anything.  Never returned to a caller.
+constexpr sa_status kEmptyBatch = (sa_status)1;
+
 sa_status make_batch(const sa_batch *in, sa::Batch *out)
 {
-    if (!in || in->num_seqs < 1 || in->total_q < 1 || in->max_q < 1 || in->max_ctx < 1 || in->max_pages < 1)
+    if (!in || in->num_seqs < 1 || in->total_q < 0 || in->max_ctx < 1 || in->max_pages < 1)
+        return SA_EINVAL;
+    if (in->total_q > 0 ? in->max_q < 1 : in->max_q != 0)
         return SA_EINVAL;
     if (!in->q_start || !in->ctx_len || !in->page_table)
         return SA_EINVAL;
@@ -43,7 +49,7 @@ sa_status make_batch(const sa_batch *in, sa::Batch *out)
     out->q_start = in->q_start;
     out->ctx_len = in->ctx_len;
     out->page_table = in->page_table;
-    return SA_OK;
+    return in->total_q == 0 ? kEmptyBatch : SA_OK;
 }
 
 sa_status launched(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ELAUNCH; }
@@ -60,7 +66,7 @@ sa_status sparse_indexer_scores(const sa_batch *batch, sa_dtype dtype, const voi
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (dtype != SA_F32 && dtype != SA_BF16 && dtype != SA_FP8_E4M3)
         return SA_EINVAL;
     if (!q_idx || !weights || !k_idx_cache || !scores || n_heads < 1 || head_dim < 1)
@@ -91,7 +97,7 @@ sa_status sparse_topk(const sa_batch *batch, const float *scores, int64_t ld_sco
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (!scores || !indices || k < 1)
         return SA_EINVAL;
     if (k > 4096)
@@ -123,7 +129,7 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const voi
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (dtype != SA_F32 && dtype != SA_BF16)
         return SA_EINVAL;
     if (!q || !k_cache || !v_cache || !indices || !gate_logits || !out)
@@ -156,7 +162,7 @@ sa_status sparse_block_pool(const sa_batch *batch, sa_dtype dtype, const void *k
 {
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
-    if (st != SA_OK)
+    if (st != SA_OK && st != kEmptyBatch)      // pooling depends on the cached pages only
         return st;
     if (dtype != SA_F32 && dtype != SA_BF16)
         return SA_EINVAL;
@@ -187,7 +193,7 @@ sa_status sparse_block_scores(const sa_batch *batch, sa_dtype dtype, const void 
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (dtype != SA_F32 && dtype != SA_BF16)
         return SA_EINVAL;
     if (!q || !k_blocks || !scores || n_q_heads < 1 || d_qk < 32 || (d_qk % 32))
@@ -228,7 +234,7 @@ sa_status sparse_block_topk(const sa_batch *batch, const float *scores, int64_t 
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (!scores || !block_idx || kb < 1)
         return SA_EINVAL;
     if (kb > 4096)
@@ -251,7 +257,7 @@ sa_status sparse_block_expand(const sa_batch *batch, const int32_t *block_idx, i
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (!block_idx || !indices || kb < 1 || ((int64_t)kb << bt.page_shift) > 65536)
         return SA_EINVAL;
     return launched(sa::launch_block_expand(bt, block_idx, kb, indices, (hipStream_t)stream));
@@ -267,7 +273,7 @@ sa_status sparse_gated_attn_bwd(const sa_batch *batch, sa_dtype dtype, const voi
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (dtype != SA_F32 && dtype != SA_BF16)
         return SA_EINVAL;
     if (!q || !k_cache || !v_cache || !indices || !gate_logits || !out || !lse || !d_out || !d_q || !d_k_cache ||
@@ -293,7 +299,7 @@ sa_status sparse_window_indices(const sa_batch *batch, int32_t window, int32_t *
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (!indices || window < 1 || window > 65536)
         return SA_EINVAL;
     return launched(sa::launch_window_indices(bt, window, indices, (hipStream_t)stream));
@@ -304,6 +310,8 @@ sa_status sparse_branch_fuse(sa_dtype dtype, int64_t rows, int32_t d_v, const vo
 {
     if (dtype != SA_F32 && dtype != SA_BF16)
         return SA_EINVAL;
+    if (rows == 0)
+        return SA_OK;
     if (!o_sparse || !o_local || !gate_logits || !out || rows < 1 || d_v < 8 || (d_v % 8))
         return SA_EINVAL;
     if (!aligned16(o_sparse) || !aligned16(o_local) || !aligned16(out) ||
@@ -321,7 +329,7 @@ sa_status sparse_cache_append(const sa_batch *batch, sa_dtype kv_dtype, const vo
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
     if (st != SA_OK)
-        return st;
+        return st == kEmptyBatch ? SA_OK : st;
     if (kv_dtype != SA_F32 && kv_dtype != SA_BF16)
         return SA_EINVAL;
     if (src_dtype != SA_F32 && src_dtype != SA_BF16)
@@ -356,6 +364,8 @@ sa_status sparse_quantize_fp8_rows(sa_dtype src_dtype, const void *x, int64_t ro
 {
     if (src_dtype != SA_F32 && src_dtype != SA_BF16)
         return SA_EINVAL;
+    if (rows == 0)
+        return SA_OK;
     if (!x || !codes || !scales || rows < 1 || rows > 0x7fffffff || cols < 8 || (cols & 7))
         return SA_EINVAL;
     if (!aligned16(x) || (((uintptr_t)codes) & 7u))

@@ -67,7 +67,9 @@ def test_indexer_argument_errors(B):
     assert idx_call(B, batch(B, page_size=48)) == B.SA_EINVAL          # not a power of two
     assert idx_call(B, batch(B, page_size=8)) == B.SA_EINVAL           # below 16
     assert idx_call(B, batch(B, max_pages=1)) == B.SA_EINVAL           # table too short for max_ctx
-    assert idx_call(B, batch(B, total_q=0)) == B.SA_EINVAL
+    assert idx_call(B, batch(B, total_q=0)) == B.SA_EINVAL            # T = 0 needs max_q = 0
+    assert idx_call(B, batch(B, total_q=-1)) == B.SA_EINVAL
+    assert idx_call(B, batch(B, max_q=0)) == B.SA_EINVAL              # T > 0 needs max_q >= 1
     assert idx_call(B, batch(B, q_start=None)) == B.SA_EINVAL
     assert idx_call(B, ok, ld=64) == B.SA_EINVAL                       # ld < max_ctx
     assert idx_call(B, ok, ld=130) == B.SA_EINVAL                      # ld not a multiple of 4
@@ -124,6 +126,33 @@ def test_attention_argument_errors(B):
     need = L.sparse_gated_attn_workspace_size(ctypes.byref(dec), 128, 512, 2048)
     assert need > 0
     assert call(bt=dec, H=128, dqk=576, dv=512, rs=576, kc=FAKE, vc=FAKE, k=2048) == B.SA_EWORKSPACE
+
+
+def test_empty_batch_is_a_no_op(B):
+    """T = 0 passes validation and returns SA_OK without touching a pointer or the GPU."""
+    L = B.lib()
+    e = ctypes.byref(batch(B, total_q=0, max_q=0))
+    f = ctypes.c_float(0.1)
+    assert L.sparse_indexer_scores(e, 2, None, 64, 128, None, None, None, None, None, 0, None) == B.SA_OK
+    assert L.sparse_topk_workspace_size(e, 2048) == 0
+    assert L.sparse_topk(e, None, 0, 2048, None, None, 0, None) == B.SA_OK
+    assert L.sparse_gated_attn_workspace_size(e, 128, 512, 2048) == 0
+    assert L.sparse_gated_attn_fwd(e, 1, None, 128, 576, None, None, 512, 576, None, 2048, None, 1, f, None, None,
+                                   None, 0, None) == B.SA_OK
+    assert L.sparse_block_scores_workspace_size(e, 128) == 0
+    assert L.sparse_block_scores(e, 1, None, 16, 128, None, None, 0, None, 0, None) == B.SA_OK
+    assert L.sparse_block_topk_workspace_size(e, 16) == 0
+    assert L.sparse_block_topk(e, None, 0, 16, None, None, 0, None) == B.SA_OK
+    assert L.sparse_block_expand(e, None, 16, None, None) == B.SA_OK
+    assert L.sparse_gated_attn_bwd(e, 1, None, 16, 128, None, None, 128, 128, None, 64, None, 1, f, None, None,
+                                   None, None, None, None, None, None) == B.SA_OK
+    assert L.sparse_window_indices(e, 64, None, None) == B.SA_OK
+    assert L.sparse_cache_append(e, 1, None, 128, None, 128, None, None, 128, 1, None, 128, 2, None, None,
+                                 None) == B.SA_OK
+    assert L.sparse_branch_fuse(1, 0, 128, None, None, None, 1, None, None) == B.SA_OK
+    assert L.sparse_quantize_fp8_rows(1, None, 0, 128, None, None, None) == B.SA_OK
+    # pooling depends on the cached pages only: it still validates its arguments
+    assert L.sparse_block_pool(e, 1, None, 128, 128, None, None) == B.SA_EINVAL
 
 
 def test_binding_fails_loudly_without_library(B, monkeypatch, tmp_path):

@@ -97,6 +97,24 @@ def test_prefill_bf16_multi_sequence_per_head_gate():
     full_check(spec, "prefill-multi")
 
 
+def test_sequences_without_new_tokens():
+    """Sequences with a cached context but no new tokens, first, between and last in the batch."""
+    spec = W.prefill_bf16().replace(q_lens=(0, 90, 0, 41, 0), ctx_lens=(500, 90, 300, 700, 64), K=128,
+                                    paged_random=True, seed=22)
+    full_check(spec, "prefill-empty-seqs")
+
+
+def test_decode_with_sequences_without_new_tokens():
+    spec = W.decode_bf16(B=6, lo=100, hi=3000).replace(q_lens=(0, 1, 1, 0, 1, 0), K=512, seed=24)
+    full_check(spec, "decode-empty-seqs")
+
+
+def test_fp8_latent_with_sequences_without_new_tokens():
+    spec = W.chunked_prefill_mla(cached=3000, T=333).replace(q_lens=(0, 200, 0, 133),
+                                                            ctx_lens=(900, 3200, 64, 1500), seed=23)
+    full_check(spec, "mla-empty-seqs", attn_rows=P.sample_tokens(333, 24, seed=23))
+
+
 def test_prefill_bf16_full_size_sampled():
     spec = W.prefill_bf16()
     P.say(f"[prefill-full] {spec.name} T={spec.T}")
