@@ -50,6 +50,9 @@ def causal_lengths(spec):
     return out
 
 
+METRIC = "query tokens/s (indexer+TopK+sparse attn) at 128K ctx, K=2048; % HBM/MFMA peak"
+
+
 def algorithmic_work(spec, n_valid):
     """Per-step algorithmic work of each stage: flops of the contractions, and the bytes the
     method must move (inputs read once, outputs written once)."""
@@ -414,13 +417,15 @@ def main(argv=None):
     rl = {}
     for st, ms in stage_ms.items():
         w = work[st]
+        peak = None
         if st == "indexer":
             peak = PEAK["fp8_TFLOPs"] if spec.idx_dtype == "fp8" else PEAK["bf16_TFLOPs"] if spec.idx_dtype == "bf16" \
                 else PEAK["fp32_TFLOPs"]
-            ach = w["flops"] / (ms * 1e-3) / 1e12
-            rl[st] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
         elif st == "attn":
             peak = PEAK["bf16_TFLOPs"] if spec.attn_dtype == "bf16" else PEAK["fp32_TFLOPs"]
+        # a contraction whose flops per algorithmic byte fall below the ridge point (peak flops over
+        # peak bandwidth) is bound by HBM: decode, where every key row is used by one query token
+        if peak is not None and w["flops"] / w["bytes"] >= peak * 1e12 / (PEAK["hbm_GBs"] * 1e9):
             ach = w["flops"] / (ms * 1e-3) / 1e12
             rl[st] = {"bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s", "frac": ach / peak}
         else:
@@ -441,7 +446,8 @@ def main(argv=None):
 
     tokens = spec.T
     line = {
-        "metric": "query tokens/s (indexer+TopK+sparse attn) at 128K ctx, K=2048; % HBM/MFMA peak",
+        "metric": METRIC if spec.name == "chunked_prefill_mla_128k" else
+        f"query tokens/s (indexer+TopK+sparse attn), {spec.name}, K={spec.K}; % HBM/MFMA peak",
         "value": tokens / (step_ms * 1e-3),
         "unit": "query_tokens/s",
         "n_gpus": 1,
