@@ -101,7 +101,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     __shared__ __align__(16) uint8_t lkr1[LIN ? kIdxLinTileKeys * 128 : 16];
     __shared__ __align__(16) uint8_t lkr2[LIN ? kIdxLinTileKeys * 128 : 16];
     __shared__ float lksr[LIN ? 3 * kIdxWaves * kIdxLinTileKeys : 1];
-    __shared__ int lpt[LIN ? kIdxMaxChunk / 16 + 2 : 1];
+    __shared__ int lpt[kIdxMaxChunk / 16 + 2];
     constexpr int LTS = 128 + 16;                // padded term row (bank spread, as RBP)
     constexpr int TROWS = TPW == 2 ? 16 : 32;  // used rows of a wave's term tile
     __shared__ __align__(16) uint8_t lterm[LIN ? kIdxWaves * TROWS * LTS : 16];
@@ -189,6 +189,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         qs[t] = ((FP8 && tl < ntok) ? q_scale[tok0 + tl] : 1.0f) * IdxEpi<DT>::UNSCALE;
     }
 
+    // Physical page of every page the chunk touches, staged once in LDS, so a
+    // tile's key loads never wait on a page-table load.
+    const int pshift = bt.page_shift, pmask = (1 << pshift) - 1;
+    const int pg0 = kb0 >> pshift;
+    {
+        const int npg = ((kb1 - 1) >> pshift) - pg0 + 1;
+        for (int i = tid; i < npg; i += 256)
+            lpt[i] = bt.page_table[(int64_t)b * bt.max_pages + pg0 + i];
+    }
+    auto krow = [&](int s) -> int64_t { return ((int64_t)lpt[(s >> pshift) - pg0] << pshift) + (s & pmask); };
+
     // ---- key tile staging: thread -> (key, 32-byte part)
     constexpr int PARTS = RB / 32;
     constexpr int LOADS = (kIdxTileKeys * PARTS + 255) / 256;
@@ -201,7 +212,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             const int kk = e / PARTS, p = e % PARTS;
             const int s = t0 + kk;
             if (kk < kIdxTileKeys && s < kb1) {
-                const i32x4 *src = (const i32x4 *)(k_idx + phys_row(bt, b, s) * RB + p * 32);
+                const i32x4 *src = (const i32x4 *)(k_idx + krow(s) * RB + p * 32);
                 stage[u][0] = src[0];
                 stage[u][1] = src[1];
             } else {
@@ -211,7 +222,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         }
         if (FP8 && tid < kIdxTileKeys) {
             const int s = t0 + tid;
-            stage_ks = s < kb1 ? k_scale[phys_row(bt, b, s)] : 0.0f;
+            stage_ks = s < kb1 ? k_scale[krow(s)] : 0.0f;
         }
     };
     auto lstore = [&](int buf) {
@@ -231,6 +242,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
 
     const int ntiles = (kb1 - kb0 + kIdxTileKeys - 1) / kIdxTileKeys;
     if constexpr (!LIN) {
+        __syncthreads();                         // the staged page ids
         gload(kb0);
         lstore(0);
         __syncthreads();
@@ -256,12 +268,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             ((i32x4 *)myterm)[e] = i32x4{0, 0, 0, 0};
         if (lane < 32)
             myscl[lane] = 127;
-        // physical page of every page the chunk touches
-        const int pshift = bt.page_shift, pmask = (1 << pshift) - 1;
-        const int pg0 = kb0 >> pshift;
-        const int npg = ((kb1 - 1) >> pshift) - pg0 + 1;
-        for (int i = tid; i < npg; i += 256)
-            lpt[i] = bt.page_table[(int64_t)b * bt.max_pages + pg0 + i];
         for (int tt = 0; tt < TPW; ++tt) {
             const int tl = wv * TPW + tt;
             if (tl >= ntok)
@@ -523,6 +529,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         // while the VALU epilogue of the other half (of this or the previous
         // 32-key N-tile) runs, with no extra accumulator registers.
         constexpr int MH = MT / 2, TH = TPW / 2;
+        // Scores leave through a buffer resource over this wave's token rows; a
+        // masked lane gets an offset past the end, which the hardware drops.
+        // With no branch around the stores the compiler counts them exactly, and
+        // the wait for the next tile's loads leaves this tile's stores in flight.
+        const int wt0 = min(wv * TPW, ntok - 1);
+        const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+            scores + (int64_t)(tok0 + wt0) * ld, 0, (int)(TPW * ld * 4), 0x00020000);
         auto epi = [&](const f32x16 (&c)[MH], int gh, int s, float ks_s) {
             float acc[TH];
 #pragma unroll
@@ -555,8 +568,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                 const int tw = t0w + (TH > 1 ? half : 0);
                 const float v = (TH > 1 && half) ? acc[t1] * qs[gh * TH + t1] : acc[t0w] * qs[gh * TH + t0w];
                 const int tl = wv * TPW + gh * TH + tw;
-                if ((TH > 1 || half == 0) && tw < TH && tl < ntok && s <= pos0 + tl && s < kb1)
-                    scores[(int64_t)(tok0 + tl) * ld + s] = v * ks_s;
+                const bool ok = (TH > 1 || half == 0) && tw < TH && tl < ntok && s <= pos0 + tl && s < kb1;
+                const uint32_t off = ok ? (uint32_t)(((int64_t)(tl - wt0) * ld + s) * 4) : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v * ks_s), srs, off, 0, 0);
             }
         };
         f32x16 c0[MH], c1[MH];
@@ -812,8 +826,9 @@ static hipError_t launch_indexer_t(const Batch &bt, const void *q_idx, const flo
 {
     if (bt.max_q >= 8) {
         constexpr int TQ = kIdxWaves * IdxShape<H>::TPW;
-        // key chunks: a multiple of 8 (one set per XCD) once the context is long
-        int n_chunks = bt.max_ctx > 8192 ? 8 * ((bt.max_ctx + 8 * kIdxChunkTarget - 1) / (8 * kIdxChunkTarget)) : 1;
+        // key chunks: a multiple of 8, since chunk c runs on XCD c % 8 (fewer
+        // chunks would leave XCDs idle); short contexts give short chunks
+        int n_chunks = 8 * ((bt.max_ctx + 8 * kIdxChunkTarget - 1) / (8 * kIdxChunkTarget));
         int key_chunk = (bt.max_ctx + n_chunks - 1) / n_chunks;
         key_chunk = (key_chunk + kIdxTileKeys - 1) / kIdxTileKeys * kIdxTileKeys;
         n_chunks = (bt.max_ctx + key_chunk - 1) / key_chunk;
