@@ -83,7 +83,7 @@ template <int DT, int H, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void indexer_tile_kernel(
     Batch bt, const uint8_t *__restrict__ q_idx, const float *__restrict__ q_scale,
     const float *__restrict__ w, const uint8_t *__restrict__ k_idx, const float *__restrict__ k_scale,
-    float *__restrict__ scores, int64_t ld, int key_chunk, int n_chunks, int n_tiles_max)
+    float *__restrict__ scores, int64_t ld, int key_chunk, int n_chunks, int n_tiles_max, int rotate)
 {
     typedef IdxT<DT> X;
     constexpr int MT = IdxShape<H>::MT, TPW = IdxShape<H>::TPW;
@@ -107,14 +107,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     __shared__ __align__(16) uint8_t lterm[LIN ? kIdxWaves * TROWS * LTS : 16];
     __shared__ int lscl[LIN ? kIdxWaves * 32 : 1];
 
-    // ---- workgroup -> (token tile, key chunk): chunk c always runs on XCD c % 8
+    // ---- workgroup -> (token tile, key chunk).  Consecutive workgroups go to
+    // consecutive XCDs.  Without rotation chunk c always runs on XCD c % 8, so
+    // its k^I rows stay in one L2.  With rotation (all keys fit in one L2, and
+    // n_chunks is a multiple of 8) token tile t puts chunk c on XCD (c - t) % 8,
+    // so that causal prefill, where early tiles see only the first chunks,
+    // spreads its work evenly over the XCDs.
     const int bid = blockIdx.x;
     const int xcd = bid & 7, j = bid >> 3;
-    const int cpx = (n_chunks - xcd + 7) >> 3;   // chunks owned by this XCD
-    if (cpx <= 0)
-        return;
-    const int chunk = xcd + 8 * (j % cpx);
-    int tile = j / cpx;
+    int chunk, tile;
+    if (rotate) {
+        const int cpx = n_chunks >> 3;
+        tile = j / cpx;
+        chunk = ((xcd + tile) & 7) + 8 * (j % cpx);
+    } else {
+        const int cpx = (n_chunks - xcd + 7) >> 3;   // chunks owned by this XCD
+        if (cpx <= 0)
+            return;
+        chunk = xcd + 8 * (j % cpx);
+        tile = j / cpx;
+    }
     if (tile >= n_tiles_max)
         return;
     int b = 0;
@@ -839,9 +851,12 @@ static hipError_t launch_indexer_t(const Batch &bt, const void *q_idx, const flo
         const int64_t grid = 8LL * cpx_max * n_tiles_max;
         if (grid > 0x7fffffff)
             return hipErrorInvalidValue;
+        // rotate the chunk -> XCD map when every chunk's keys fit in one L2 together
+        const int64_t key_bytes = (int64_t)n_chunks * key_chunk * D * IdxT<DT>::ELEM;
+        const int rotate = n_chunks % 8 == 0 && key_bytes <= (2 << 20);
         hipLaunchKernelGGL((indexer_tile_kernel<DT, H, D>), dim3((unsigned)grid), dim3(256), 0, st, bt,
                            (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx, k_scale, scores, ld,
-                           key_chunk, n_chunks, n_tiles_max);
+                           key_chunk, n_chunks, n_tiles_max, rotate);
     } else {
         // enough workgroups to cover the GPU even for a handful of sequences
         int key_chunk = 2048;

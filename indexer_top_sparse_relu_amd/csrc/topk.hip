@@ -538,7 +538,7 @@ __device__ bool select_topk_fast(const float *__restrict__ vals, int n, bool pad
                                  int32_t *__restrict__ gidx, float *__restrict__ gval, const TkSmem &sm)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (n < 2 * kSample || n >= (1 << 25) || !pad4 || (((uintptr_t)vals) & 15u) != 0)
+    if (n < kSample || n >= (1 << 25) || !pad4 || (((uintptr_t)vals) & 15u) != 0)
         return false;
     // the sample: 64 runs, or 128 on segments of at least 16 runs per wave
     // step (the K-th key's expected rank in it then doubles, so the same
