@@ -20,6 +20,7 @@ struct TopkPlan {
     int chunked;      // 1: per-chunk selection followed by a merge pass
     int chunk;        // chunk length (positions) when chunked
     int n_chunks;     // chunks per row when chunked
+    int group;        // chunk lists per first-level merge (n_chunks: one merge level)
     size_t ws_bytes;  // workspace the plan needs
 };
 TopkPlan topk_plan(int total_q, int max_ctx, int k);

@@ -808,20 +808,27 @@ __global__ __launch_bounds__(kTkThreads) void topk_chunk_kernel(Batch bt, const 
         select_topk<false>(vals, nullptr, len, j0, K, cidx + o, cval + o, sm);
 }
 
-// Stage 2: one workgroup per row over the concatenated chunk winners.
-__global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(int K, int n_cand, int64_t cand_ld,
+// Stage 2: blockIdx.y = row, blockIdx.x = group: the top K of the group's
+// candidates [g*gc, min(n_cand, (g+1)*gc)) of the row, written at
+// row*out_ld + g*K (values too when oval is set).  With many chunks a first
+// level merges groups of chunk lists in parallel and a second level merges
+// the group winners; both keep position order, so ties still go to the lower
+// position.
+__global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(int K, int n_cand, int gc, int64_t cand_ld,
                                                                 const int32_t *__restrict__ cidx,
-                                                                const float *__restrict__ cval,
-                                                                int32_t *__restrict__ out)
+                                                                const float *__restrict__ cval, int64_t out_ld,
+                                                                int32_t *__restrict__ oidx, float *__restrict__ oval)
 {
-    const int row = blockIdx.x;
-    const int64_t o = (int64_t)row * cand_ld;
-    select_topk<true>(cval + o, cidx + o, n_cand, 0, K, out + (int64_t)row * K, nullptr, tk_smem(K));
+    const int g = blockIdx.x, row = blockIdx.y;
+    const int64_t o = (int64_t)row * cand_ld + (int64_t)g * gc;
+    const int len = min(gc, n_cand - g * gc);
+    const int64_t w = (int64_t)row * out_ld + (int64_t)g * K;
+    select_topk<true>(cval + o, cidx + o, len, 0, K, oidx + w, oval ? oval + w : nullptr, tk_smem(K));
 }
 
 TopkPlan topk_plan(int total_q, int max_ctx, int k)
 {
-    TopkPlan p{0, 0, 1, 0};
+    TopkPlan p{0, 0, 1, 1, 0};
     // Few rows cannot fill 256 CUs: cut long rows into chunks (>= 4 * k each).
     if (total_q < 256 && max_ctx > 16384) {
         const int want_chunks = (512 + total_q - 1) / total_q;
@@ -833,8 +840,20 @@ TopkPlan topk_plan(int total_q, int max_ctx, int k)
             p.chunked = 1;
             p.chunk = chunk;
             p.n_chunks = n_chunks;
+            // one merge workgroup per row over every chunk list leaves most CUs
+            // idle when the lists are many: merge groups of about sqrt(n_chunks)
+            // lists first
+            int group = n_chunks;
+            if (n_chunks >= 8) {
+                group = 1;
+                while (group * group < n_chunks)
+                    ++group;
+            }
+            p.group = group;
+            const int n_groups = (n_chunks + group - 1) / group;
             const int64_t cand_ld = ((int64_t)n_chunks * k + 63) / 64 * 64;
-            p.ws_bytes = (size_t)total_q * (size_t)cand_ld * 8u;
+            const int64_t cand2_ld = n_groups > 1 ? ((int64_t)n_groups * k + 63) / 64 * 64 : 0;
+            p.ws_bytes = (size_t)total_q * (size_t)(cand_ld + cand2_ld) * 8u;
         }
     }
     return p;
@@ -873,8 +892,24 @@ hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *score
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(topk_merge_kernel, dim3(bt.total_q), dim3(kTkThreads), smem, st, k,
-                       (int)(plan.n_chunks * k), cand_ld, cidx, cval, indices);
+    const int n_cand = plan.n_chunks * k;
+    const int n_groups = (plan.n_chunks + plan.group - 1) / plan.group;
+    if (n_groups == 1) {
+        hipLaunchKernelGGL(topk_merge_kernel, dim3(1, bt.total_q), dim3(kTkThreads), smem, st, k, n_cand, n_cand,
+                           cand_ld, cidx, cval, (int64_t)k, indices, (float *)nullptr);
+        return hipGetLastError();
+    }
+    // two levels: group winners (indices and values) after the chunk lists
+    const int64_t cand2_ld = ((int64_t)n_groups * k + 63) / 64 * 64;
+    int32_t *gidx = (int32_t *)((char *)ws + (size_t)bt.total_q * (size_t)cand_ld * 8u);
+    float *gval = (float *)((char *)gidx + (size_t)bt.total_q * (size_t)cand2_ld * 4u);
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(n_groups, bt.total_q), dim3(kTkThreads), smem, st, k, n_cand,
+                       plan.group * k, cand_ld, cidx, cval, cand2_ld, gidx, gval);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(1, bt.total_q), dim3(kTkThreads), smem, st, k, n_groups * k,
+                       n_groups * k, cand2_ld, gidx, gval, (int64_t)k, indices, (float *)nullptr);
     return hipGetLastError();
 }
 
