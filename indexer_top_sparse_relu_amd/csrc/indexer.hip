@@ -74,6 +74,7 @@ constexpr int kIdxTileKeys = 64;
 constexpr int kIdxLinTileKeys = 128;   // key tile of the fp8 linear-term path
 constexpr int kIdxMaxChunk = 17408;    // keys per prefill workgroup, at most
 constexpr int kIdxChunkTarget = 17408; // prefill chunks: this many keys or fewer, eight at a time
+constexpr int kIdxTokChunk = 2048;     // keys per decode workgroup, at most
 
 typedef __attribute__((address_space(3))) float lds_f32;
 
@@ -765,27 +766,39 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
     }
     const float qs = (FP8 ? q_scale[tok] : 1.0f) * IdxEpi<DT>::UNSCALE;
 
+    // Physical page of every page the chunk touches, staged once in LDS: a
+    // key load then waits on an LDS read, not on a page-table load (a global
+    // load would have to drain every key load issued before it).
+    __shared__ int lpt[kIdxTokChunk / 16 + 2];
+    const int pshift = bt.page_shift, pmask = (1 << pshift) - 1;
+    const int pg0 = kb0 >> pshift;
+    {
+        const int npg = ((kb1 - 1) >> pshift) - pg0 + 1;
+        for (int i = tid; i < npg; i += 256)
+            lpt[i] = bt.page_table[(int64_t)b * bt.max_pages + pg0 + i];
+    }
+    __syncthreads();
+
     const int ntiles = (kb1 - kb0 + 31) / 32;
-    // two operand slots, software-pipelined; the loop is unrolled by two so
-    // every register array index is a compile-time constant
-    typename X::Op b0[NKS], b1[NKS];
-    float ks0 = 0.0f, ks1 = 0.0f;
+    // operand slots, software-pipelined; the loop is unrolled by the slot count
+    // so every register array index is a compile-time constant.  Loads have no
+    // branch: a key past the chunk rereads its last key (never stored), and a
+    // tile past the end rereads the last tile, so the compiler's waits count
+    // the loads in flight exactly.
+    typename X::Op b0[NKS], b1[NKS], b2[NKS];
+    float ks0 = 0.0f, ks1 = 0.0f, ks2 = 0.0f;
     auto gload = [&](typename X::Op (&bo)[NKS], float &ksv, int t) {
-        const int s = kb0 + t * 32 + col;
-        if (s < kb1) {
-            const int64_t pr = phys_row(bt, b, s);
-            const uint8_t *src = k_idx + pr * RB + half * X::LB;
+        const int s = min(kb0 + min(t, ntiles - 1) * 32 + col, kb1 - 1);
+        const int64_t pr = ((int64_t)lpt[(s >> pshift) - pg0] << pshift) + (s & pmask);
+        const uint8_t *src = k_idx + pr * RB + half * X::LB;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                bo[ks] = X::load(src + ks * X::KS * X::ELEM);
-            ksv = FP8 ? k_scale[pr] : 1.0f;
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-                bo[ks] = typename X::Op{};
-            ksv = 0.0f;
-        }
+        for (int ks = 0; ks < NKS; ++ks)
+            bo[ks] = X::load(src + ks * X::KS * X::ELEM);
+        ksv = FP8 ? k_scale[pr] : 1.0f;
     };
+    // scores leave through a buffer resource over the token's score row
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)tok * ld, 0,
+                                                                         (int)(ld * 4), 0x00020000);
     auto compute = [&](typename X::Op (&bo)[NKS], float ksv, int t) {
         f32x16 c[MT];
 #pragma unroll
@@ -811,23 +824,41 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
             }
         }
         acc = sum_halves(acc);
+        // a masked lane (or a tile past the end) stores past the resource's end,
+        // which the hardware drops
         const int s = kb0 + t * 32 + col;
-        if (half == 0 && s < kb1)
-            scores[(int64_t)tok * ld + s] = acc * qs * ksv;
+        const uint32_t off = (half == 0 && s < kb1) ? (uint32_t)s * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc * qs * ksv), srs, off, 0, 0);
     };
     constexpr int W = kIdxWaves;
     int t = wv;
-    if (t < ntiles)
+    if constexpr (FP8) {
+        // fp8 (the long-context layout): three slots in flight
         gload(b0, ks0, t);
-    for (; t < ntiles; t += 2 * W) {
-        if (t + W < ntiles)
+        gload(b1, ks1, t + W);
+        for (; t < ntiles; t += 3 * W) {
+            gload(b2, ks2, t + 2 * W);
+            compute(b0, ks0, t);
+            gload(b0, ks0, t + 3 * W);
+            if (t + W < ntiles)
+                compute(b1, ks1, t + W);
+            gload(b1, ks1, t + 4 * W);
+            if (t + 2 * W < ntiles)
+                compute(b2, ks2, t + 2 * W);
+        }
+    } else {
+        // two slots: the third costs a wave per SIMD of occupancy here
+        gload(b0, ks0, t);
+        for (; t < ntiles; t += 2 * W) {
             gload(b1, ks1, t + W);
-        compute(b0, ks0, t);
-        if (t + 2 * W < ntiles)
+            compute(b0, ks0, t);
             gload(b0, ks0, t + 2 * W);
-        if (t + W < ntiles)
-            compute(b1, ks1, t + W);
+            if (t + W < ntiles)
+                compute(b1, ks1, t + W);
+        }
     }
+    // the last loads of the ring are never used: let them land before the wave ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // ------------------------------------------------------------------ launch
@@ -859,12 +890,12 @@ static hipError_t launch_indexer_t(const Batch &bt, const void *q_idx, const flo
                            key_chunk, n_chunks, n_tiles_max, rotate);
     } else {
         // enough workgroups to cover the GPU even for a handful of sequences
-        int key_chunk = 2048;
+        int key_chunk = kIdxTokChunk;
         const int64_t want = 2048;
         while (key_chunk > 256 && (int64_t)bt.total_q * ((bt.max_ctx + key_chunk - 1) / key_chunk) < want)
             key_chunk >>= 1;
         const int n_chunks = (bt.max_ctx + key_chunk - 1) / key_chunk;
-        if (bt.total_q > 65535)
+        if (bt.total_q > 65535 || ld * 4 >= (1LL << 31))
             return hipErrorInvalidValue;
         hipLaunchKernelGGL((indexer_token_kernel<DT, H, D>), dim3(n_chunks, bt.total_q), dim3(256), 0, st, bt,
                            (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx, k_scale, scores, ld,
