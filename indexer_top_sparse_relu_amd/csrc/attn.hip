@@ -42,6 +42,7 @@ namespace sa {
 
 constexpr int kTK = 64;                 // keys per LDS tile
 constexpr int kMaxSplit = 2048;         // index slots one workgroup resolves up front
+constexpr int kMaxCombine = 64;         // splits one combine workgroup merges (one lane each)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
@@ -757,19 +758,33 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(int Hq, int DV, int n
     const int tok = blockIdx.x, h = blockIdx.y;
     const float *pp = part + ((int64_t)tok * n_split * Hq + h) * (DV + 4);
     const int64_t sstride = (int64_t)Hq * (DV + 4);
-    float M = -INFINITY;
-    for (int s = 0; s < n_split; ++s)
-        M = fmaxf(M, pp[s * sstride + DV]);
-    const float base = M == -INFINITY ? 0.0f : M;
-    float L = 0.0f;
-    for (int s = 0; s < n_split; ++s)
-        L += pp[s * sstride + DV + 1] * exp2f(pp[s * sstride + DV] - base);
+    // wave 0, one lane per split: the splits' (max, sum) pairs are loaded at
+    // once, and each split's weight 2^(m_s - M) is kept in LDS
+    __shared__ float wsh[kMaxCombine];
+    __shared__ float ml[2];
+    if (threadIdx.x < 64) {
+        const int s = threadIdx.x;
+        const float m = s < n_split ? pp[s * sstride + DV] : -INFINITY;
+        const float l = s < n_split ? pp[s * sstride + DV + 1] : 0.0f;
+        const float Mw = wave_max(m);
+        const float w = s < n_split ? exp2f(m - (Mw == -INFINITY ? 0.0f : Mw)) : 0.0f;
+        const float Lw = wave_sum(l * w);
+        if (s < n_split)
+            wsh[s] = w;
+        if (s == 0) {
+            ml[0] = Mw;
+            ml[1] = Lw;
+        }
+    }
+    __syncthreads();
+    const float M = ml[0], L = ml[1];
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int64_t ob = ((int64_t)tok * Hq + h) * DV;
     for (int c = threadIdx.x; c < DV; c += blockDim.x) {
         float acc = 0.0f;
+#pragma unroll 8
         for (int s = 0; s < n_split; ++s)
-            acc += pp[s * sstride + c] * exp2f(pp[s * sstride + DV] - base);
+            acc += pp[s * sstride + c] * wsh[s];
         float gl;
         const int64_t gi = per_channel ? ob + c : (int64_t)tok * Hq + h;
         if (is_bf16)
@@ -980,6 +995,8 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const voi
     }
     if (e != hipSuccess || pl.n_split == 1)
         return e;
+    if (pl.n_split > kMaxCombine)
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(bt.total_q, Hq), dim3(128), 0, st, Hq, d_v, pl.n_split,
                        part, gate, per_channel, dtype == 1 ? 1 : 0, out, lse);
     return hipGetLastError();
