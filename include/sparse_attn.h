@@ -27,7 +27,7 @@
  *     by the *_workspace_size queries.
  *   - Argument errors are detected on the host before any launch and return
  *     SA_EINVAL (bad value / NULL / shape) or SA_EUNSUPPORTED (a valid request
- *     this build has no kernel for); nothing is launched then.  A failed
+ *     the library has no kernel for); nothing is launched then.  A failed
  *     launch returns SA_ELAUNCH.  Device-side data (page ids, index values,
  *     lengths inside q_start / ctx_len) is trusted and not range-checked.
  */
