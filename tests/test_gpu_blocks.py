@@ -81,8 +81,9 @@ def check_blocks(spec, kb, tag, attn_rows=None):
     # attention over the GPU's expanded positions
     rows = np.arange(spec.T) if attn_rows is None else np.asarray(attn_rows)
     ref_out = O.sparse_attn(inp, e_idx[rows], rows, spec.softmax_scale)
-    w2 = P.check_attn(out.float().cpu().numpy()[rows], ref_out, P.RTOL[spec.attn_dtype])
-    P.say(f"[{tag}] ok: worst block-score rel {w1:.2e}, worst attn rel {w2:.2e}")
+    w2 = P.check_attn(out.float().cpu().numpy()[rows], ref_out, P.RTOL[spec.attn_dtype],
+                      P.attn_floor(inp, e_idx[rows], rows, spec.softmax_scale))
+    P.say(f"[{tag}] ok: worst block-score rel {w1:.2e}, worst attn {w2:.2f} of the bound")
 
 
 def test_block_selection_latent_prefill():

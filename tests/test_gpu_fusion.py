@@ -58,10 +58,16 @@ def check_fused(spec, w, tag, rows=None):
     a = O.sparse_attn(u, idx[rows], rows, spec.softmax_scale)
     b = O.sparse_attn(u, win[rows], rows, spec.softmax_scale)
     tol = P.RTOL[spec.attn_dtype]
-    P.check_attn(o_s.float().cpu().numpy()[rows], a, tol, "sparse branch")
-    P.check_attn(o_l.float().cpu().numpy()[rows], b, tol, "local branch")
+    fa = P.attn_floor(u, idx[rows], rows, spec.softmax_scale)
+    fb = P.attn_floor(u, win[rows], rows, spec.softmax_scale)
+    P.check_attn(o_s.float().cpu().numpy()[rows], a, tol, fa, "sparse branch")
+    P.check_attn(o_l.float().cpu().numpy()[rows], b, tol, fb, "local branch")
     ref = O.branch_fuse(inp, a, b, rows)
-    worst = P.check_attn(y.float().cpu().numpy()[rows], ref, tol, "fused output")
+    # the fusion's floor: both branches' floors plus their rounding to the output type
+    a_abs = P.attn_abs(u, idx[rows], rows, spec.softmax_scale)
+    b_abs = P.attn_abs(u, win[rows], rows, spec.softmax_scale)
+    worst = P.check_attn(y.float().cpu().numpy()[rows], ref, tol, P.fused_floor(inp, fa, fb, a_abs, b_abs, rows),
+                         "fused output")
     P.say(f"[{tag}] ok: worst fused rel {worst:.2e}")
 
 

@@ -55,10 +55,10 @@ def full_check(spec, tag, attn_rows=None):
     rows = np.arange(spec.T) if attn_rows is None else np.asarray(attn_rows)
     ref_out, ref_lse = O.sparse_attn(inp, idx[rows], rows, spec.softmax_scale, with_lse=True)
     out = pl.out.float().cpu().numpy()[rows]
-    w2 = P.check_attn(out, ref_out, P.RTOL[spec.attn_dtype])
+    w2 = P.check_attn(out, ref_out, P.RTOL[spec.attn_dtype], P.attn_floor(inp, idx[rows], rows, spec.softmax_scale))
     lse = pl.lse.cpu().numpy()[rows]
     assert P.close(lse, ref_lse, P.RTOL[spec.attn_dtype]).all()
-    P.say(f"[{tag}] ok: worst score rel {w1:.2e}, worst attn rel {w2:.2e}, recall {rec:.4f}")
+    P.say(f"[{tag}] ok: worst score rel {w1:.2e}, worst attn {w2:.2f} of the bound, recall {rec:.4f}")
     return wl, pl
 
 
@@ -80,7 +80,10 @@ def test_k_covering_context_equals_dense_control():
     pl = run(wl)
     inp = O.Inputs.from_workload(wl)
     dense = O.dense_attn(inp, scale=spec.softmax_scale)
-    P.check_attn(pl.out.cpu().numpy(), dense, P.RTOL["f32"], "dense control")
+    n = P.token_geometry(spec)[2]
+    every = np.where(np.arange(spec.K)[None, :] < n[:, None], np.arange(spec.K)[None, :], -1)
+    fl = P.attn_floor(inp, every, None, spec.softmax_scale)
+    P.check_attn(pl.out.cpu().numpy(), dense, P.RTOL["f32"], fl, "dense control")
 
 
 # ------------------------------------------------------------ prefill bf16
@@ -134,7 +137,8 @@ def test_prefill_bf16_full_size_sampled():
     arows = P.sample_tokens(spec.T, 16, seed=3)
     ainp, aidx = P.attn_inputs(wl, arows, idx[arows])
     ref_out = O.sparse_attn(ainp, aidx, None, spec.softmax_scale)
-    P.check_attn(pl.out.float().cpu().numpy()[arows], ref_out, P.RTOL["bf16"])
+    P.check_attn(pl.out.float().cpu().numpy()[arows], ref_out, P.RTOL["bf16"],
+                 P.attn_floor(ainp, aidx, None, spec.softmax_scale))
 
 
 # ------------------------------------------------------------- decode bf16
@@ -165,6 +169,9 @@ def test_chunked_prefill_mla_fp8_indexer_head_counts(h_i):
 
 
 def test_chunked_prefill_mla_full_size_sampled():
+    """The benchmark's own launch at full size: Top-K bit-exact on 512 rows (the first and
+    last 64 among them), scores and the selection rule on 128 rows (first and last 16),
+    attention element by element on 64 rows (first and last 16)."""
     spec = W.chunked_prefill_mla()
     P.say(f"[mla-prefill-full] T={spec.T} ctx={spec.max_ctx}")
     wl = W.generate(spec, DEV)
@@ -172,20 +179,23 @@ def test_chunked_prefill_mla_full_size_sampled():
     seq, pos, n = P.token_geometry(spec)
     idx = pl.indices.cpu().numpy()
     P.check_idx_invariants(idx, n, spec.K)
-    rows = P.sample_tokens(spec.T, 96, seed=5, edge=16)
-    sc_rows = pl.scores[torch.as_tensor(rows, device=DEV)].cpu().numpy()
-    P.check_topk_exact(idx[rows], sc_rows, n[rows], spec.K)
-    srows = P.sample_tokens(spec.T, 6, seed=6, edge=1)
-    inp = P.indexer_inputs(wl, srows)
-    ref = O.indexer(inp, ld=pl.ld)
+    rows = P.sample_tokens(spec.T, 512, seed=5, edge=64)
+    for part in np.array_split(np.asarray(rows), 8):
+        sc_rows = pl.scores[torch.as_tensor(part, device=DEV)].cpu().numpy()
+        P.check_topk_exact(idx[part], sc_rows, n[part], spec.K)
+    P.say(f"[mla-prefill-full] Top-K exact on {len(rows)} rows")
+    inp = O.Inputs.from_workload(wl)
+    srows = np.asarray(P.sample_tokens(spec.T, 128, seed=6, edge=16))
+    ref = O.indexer(inp, rows=srows, ld=pl.ld)
     sc = pl.scores[torch.as_tensor(srows, device=DEV)].cpu().numpy()
-    P.check_scores(sc, ref, n[srows], P.RTOL["fp8"])
+    w1 = P.check_scores(sc, ref, n[srows], P.RTOL["fp8"])
     rec = P.check_selection(idx[srows], ref, n[srows], spec.K)
-    arows = P.sample_tokens(spec.T, 8, seed=7, edge=1)
-    ainp, aidx = P.attn_inputs(wl, arows, idx[arows])
-    ref_out = O.sparse_attn(ainp, aidx, None, spec.softmax_scale)
-    w2 = P.check_attn(pl.out.float().cpu().numpy()[arows], ref_out, P.RTOL["bf16"])
-    P.say(f"[mla-prefill-full] ok: recall {rec:.4f}, worst attn rel {w2:.2e}")
+    P.say(f"[mla-prefill-full] scores and selection on {len(srows)} rows: worst rel {w1:.2e}, recall {rec:.4f}")
+    arows = np.asarray(P.sample_tokens(spec.T, 64, seed=7, edge=16))
+    ref_out = O.sparse_attn(inp, idx[arows], arows, spec.softmax_scale)
+    w2 = P.check_attn(pl.out[torch.as_tensor(arows, device=DEV)].float().cpu().numpy(), ref_out, P.RTOL["bf16"],
+                      P.attn_floor(inp, idx[arows], arows, spec.softmax_scale))
+    P.say(f"[mla-prefill-full] ok: attention on {len(arows)} rows, worst {w2:.2f} of the bound")
 
 
 def test_long_decode_mla_reduced_with_ties():
@@ -243,8 +253,9 @@ def test_long_decode_mla_full_size_sampled():
     arows = list(range(spec.T))
     ainp, aidx = P.attn_inputs(wl, arows, idx)
     ref_out = O.sparse_attn(ainp, aidx, None, spec.softmax_scale)
-    w2 = P.check_attn(pl.out.float().cpu().numpy(), ref_out, P.RTOL["bf16"])
-    P.say(f"[long-decode-full] ok: worst attn rel {w2:.2e}")
+    w2 = P.check_attn(pl.out.float().cpu().numpy(), ref_out, P.RTOL["bf16"],
+                      P.attn_floor(ainp, aidx, None, spec.softmax_scale))
+    P.say(f"[long-decode-full] ok: worst attn {w2:.2f} of the bound")
 
 
 # --------------------------------------------------------------- properties
@@ -312,6 +323,6 @@ def test_latent_attention_logit_far_above_first_keys(mode):
     ref_out, ref_lse = O.sparse_attn(ainp, aidx, None, spec.softmax_scale, with_lse=True)
     out = pl.out.float().cpu().numpy()
     assert np.isfinite(out).all()
-    w = P.check_attn(out, ref_out, P.RTOL["bf16"])
+    w = P.check_attn(out, ref_out, P.RTOL["bf16"], P.attn_floor(ainp, aidx, None, spec.softmax_scale))
     assert P.close(pl.lse.cpu().numpy(), ref_lse, P.RTOL["bf16"]).all()
-    P.say(f"[rerun-{mode}] ok: worst attn rel {w:.2e}")
+    P.say(f"[rerun-{mode}] ok: worst attn {w:.2f} of the bound")
