@@ -106,8 +106,12 @@ typedef struct {
  *   scores     [T, ld_scores] fp32; row i gets entries [0, n_i) and nothing
  *              else is written.  ld_scores >= max_ctx and a multiple of 4.
  * Supported (dtype, n_heads, head_dim): f32 with head_dim 32; bf16 with
- * head_dim 64; fp8 with head_dim 128; n_heads in {4, 8, 16, 32, 64}.
- * Scores are finite for finite inputs.
+ * head_dim 64 or 128; fp8 with head_dim 128; n_heads in {4, 8, 16, 32, 64}.
+ * Any other shape returns SA_EUNSUPPORTED.  Weights may be of any finite
+ * magnitude: where the fp8 epilogue multiplies in fp16, each token's weights
+ * are scaled by a power of two that keeps them in fp16's normal range and the
+ * factor is given back in fp32.  Scores are finite for finite inputs whose
+ * exact scores are within fp32 range.
  */
 sa_status sparse_indexer_scores(const sa_batch *batch, sa_dtype dtype,
                                 const void *q_idx, int32_t n_heads, int32_t head_dim,
@@ -127,7 +131,7 @@ sa_status sparse_indexer_scores(const sa_batch *batch, sa_dtype dtype,
  * the min(k, n_i) selected positions in ascending order, then -1.
  * Scores must be finite.  1 <= k <= 4096.
  *   workspace: >= sparse_topk_workspace_size(batch, k) bytes (may be 0 bytes;
- *   then workspace may be NULL), 256-byte aligned.  Results are deterministic.
+ *   then workspace may be NULL), 16-byte aligned.  Results are deterministic.
  */
 size_t sparse_topk_workspace_size(const sa_batch *batch, int32_t k);
 sa_status sparse_topk(const sa_batch *batch, const float *scores, int64_t ld_scores,

@@ -910,7 +910,6 @@ int attn_supported_layout(int dtype, int d_qk, int d_v, int aliased)
     if (dtype == 1 && d_qk == 576 && d_v == 512)
         return aliased;
     return 1;
-    return 0;
 }
 
 AttnPlan attn_plan(int total_q, int Hq, int d_v, int k)

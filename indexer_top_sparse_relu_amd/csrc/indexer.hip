@@ -158,6 +158,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     constexpr bool F16E = IdxEpi<DT>::F16 && H >= 8 && !LIN;
     typename X::Op a[MT][NKS];
     float wr[MT][F16E ? 1 : 16];
+    float wt[MT][F16E ? 16 : 1];
     f16x2 wp[MT][F16E ? 8 : 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -177,15 +178,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             // unconditional load (clamped token), then select: no branch per weight
             const float wl = w[(int64_t)(tok0 + min(to, ntok - 1)) * H + Ro % H];
             const float wv_ = to < ntok ? wl : 0.0f;
-            if constexpr (F16E) {
-                if (i & 1)
-                    wp[mt][i >> 1][1] = (_Float16)wv_;
-                else
-                    wp[mt][i >> 1][0] = (_Float16)wv_;
-            } else {
+            if constexpr (F16E)
+                wt[mt][i] = wv_;
+            else
                 wr[mt][i] = wv_;
-            }
         }
+    }
+    // fp16 weights: each token's weights are scaled by a power of two that puts
+    // their largest magnitude in [2^14, 2^15) (no overflow, no subnormals for
+    // 28 binades below it); the factor is given back through the score scale
+    int wsh[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+        wsh[t] = 0;
+    if constexpr (F16E) {
+        float tmax[TPW];
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            tmax[t] = 0.0f;
+        // with H >= 8 the token of register i is the same in both lane halves
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                tmax[(mt * 32 + 8 * (i >> 2)) / H] = fmaxf(tmax[(mt * 32 + 8 * (i >> 2)) / H], fabsf(wt[mt][i]));
+#pragma unroll
+        for (int t = 0; t < TPW; ++t)
+            wsh[t] = f16_weight_shift(fmaxf(tmax[t], __shfl_xor(tmax[t], 32, 64)));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                wp[mt][i >> 1][i & 1] = (_Float16)ldexpf(wt[mt][i], wsh[(mt * 32 + 8 * (i >> 2)) / H]);
     }
     if constexpr (LIN) {
         // opaque from here on, so the selects above are not redone inside the key loop
@@ -199,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int tl = wv * TPW + t;
-        qs[t] = ((FP8 && tl < ntok) ? q_scale[tok0 + tl] : 1.0f) * IdxEpi<DT>::UNSCALE;
+        qs[t] = ldexpf(((FP8 && tl < ntok) ? q_scale[tok0 + tl] : 1.0f) * IdxEpi<DT>::UNSCALE, -wsh[t]);
     }
 
     // Physical page of every page the chunk touches, staged once in LDS, so a
@@ -739,6 +763,7 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
     constexpr bool F16E = IdxEpi<DT>::F16 && H >= 8;
     typename X::Op a[MT][NKS];
     float wr[MT][F16E ? 1 : 16];
+    float wt[MT][F16E ? 16 : 1];
     f16x2 wp[MT][F16E ? 8 : 1];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -754,17 +779,31 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
         for (int i = 0; i < 16; ++i) {
             const int ho = mt * 32 + mfma32_row(i, lane);
             const float wv_ = ho < H ? w[(int64_t)tok * H + ho] : 0.0f;
-            if constexpr (F16E) {
-                if (i & 1)
-                    wp[mt][i >> 1][1] = (_Float16)wv_;
-                else
-                    wp[mt][i >> 1][0] = (_Float16)wv_;
-            } else {
+            if constexpr (F16E)
+                wt[mt][i] = wv_;
+            else
                 wr[mt][i] = wv_;
-            }
         }
     }
-    const float qs = (FP8 ? q_scale[tok] : 1.0f) * IdxEpi<DT>::UNSCALE;
+    // fp16 weights: scaled by the power of two that puts the token's largest
+    // |w| in [2^14, 2^15), given back through the score scale (a lane half
+    // holds every register's head of its half; the other half the rest)
+    int wsh = 0;
+    if constexpr (F16E) {
+        float m = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                m = fmaxf(m, fabsf(wt[mt][i]));
+        wsh = f16_weight_shift(fmaxf(m, __shfl_xor(m, 32, 64)));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                wp[mt][i >> 1][i & 1] = (_Float16)ldexpf(wt[mt][i], wsh);
+    }
+    const float qs = ldexpf((FP8 ? q_scale[tok] : 1.0f) * IdxEpi<DT>::UNSCALE, -wsh);
 
     // Physical page of every page the chunk touches, staged once in LDS: a
     // key load then waits on an LDS read, not on a page-table load (a global

@@ -144,6 +144,13 @@ __device__ __forceinline__ float relu_dot2(float x0, float x1, f16x2 w, float ac
     return __builtin_amdgcn_fdot2(x, w, acc, false);
 }
 
+// Power-of-two exponent that moves m > 0 into [2^14, 2^15): fp16 weights scaled
+// by it neither overflow nor go subnormal within 28 binades below m.
+__device__ __forceinline__ int f16_weight_shift(float m)
+{
+    return m > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(m) : 0;
+}
+
 // A copy of v that the compiler cannot see through.  Lane-derived addresses
 // computed from it inside a loop body are recomputed there (a few VALU ops)
 // instead of being hoisted and kept live across the loop, where register

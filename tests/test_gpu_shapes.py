@@ -1,0 +1,129 @@
+"""GPU parity of every shape the C ABI accepts.
+
+The library accepts a fixed set of (dtype, heads, head_dim) shapes for the
+indexer and of (dtype, d_qk, d_v, layout, query heads) for the attention, each
+served by a template instance of a kernel.  Every accepted shape runs here, in
+both launch forms (prefill: the tile kernel / one workgroup per index list;
+decode: the token kernel / split index lists with the combine), at small sizes
+that the oracle checks on every row.  Shapes outside the set are rejected on
+the host (tests/test_abi.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from tests import parity as P
+from indexer_top_sparse_relu_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from indexer_top_sparse_relu_amd import binding as B  # noqa: E402
+
+DEV = "cuda"
+
+INDEXER_SHAPES = [(dt, h, d) for dt, d in (("f32", 32), ("bf16", 64), ("bf16", 128), ("fp8", 128))
+                  for h in (4, 8, 16, 32, 64)]
+
+
+def _base(mode, seed):
+    """Prefill: two sequences with cached prefixes (tile kernels); decode: five sequences
+    with one new token each (token kernels, split index lists)."""
+    spec = W.prefill_bf16().replace(K=96, seed=seed)
+    if mode == "prefill":
+        return spec.replace(q_lens=(70, 45), ctx_lens=(700, 45), paged_random=True)
+    return spec.replace(q_lens=(1,) * 5, ctx_lens=(90, 1500, 3100, 640, 2200), paged_random=True)
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("dt,h,d", INDEXER_SHAPES, ids=[f"{a}-h{b}-d{c}" for a, b, c in INDEXER_SHAPES])
+def test_indexer_shape(dt, h, d, mode):
+    spec = _base(mode, seed=100 + h + d).replace(idx_dtype=dt, H_I=h, d_I=d, name=f"indexer-{dt}-{h}x{d}")
+    P.say(f"[indexer {dt} {h}x{d} {mode}] T={spec.T} max_ctx={spec.max_ctx}")
+    wl = W.generate(spec, DEV)
+    pl = B.Pipeline(wl)
+    pl.scores.fill_(float("nan"))
+    pl.indices.fill_(-7)
+    pl.indexer()
+    pl.topk()
+    torch.cuda.synchronize()
+    inp = O.Inputs.from_workload(wl)
+    n = P.token_geometry(spec)[2]
+    sc = pl.scores.cpu().numpy()
+    ref = O.indexer(inp, ld=pl.ld)
+    w1 = P.check_scores(sc, ref, n, P.RTOL[dt])
+    for r in range(spec.T):
+        assert np.all(np.isnan(sc[r, n[r]:])), f"row {r} written past n"
+    idx = pl.indices.cpu().numpy()
+    P.check_idx_invariants(idx, n, spec.K)
+    P.check_topk_exact(idx, sc, n, spec.K)
+    rec = P.check_selection(idx, ref, n, spec.K)
+    P.say(f"[indexer {dt} {h}x{d} {mode}] ok: worst score rel {w1:.2e}, recall {rec:.4f}")
+
+
+# (dtype, d_qk, d_v, shared K/V row, query heads): every kernel instance the library
+# dispatches to -- fp32 per head; bf16 MQA rows of 128 with 1, 2, 4 or 8 waves of 16
+# heads, separate or shared; the 576/512 latent row on the general kernel (heads not a
+# multiple of 128) and on the latent kernel (multiples of 128)
+ATTN_SHAPES = [
+    ("f32", 32, 32, False, 3), ("f32", 64, 64, False, 1), ("f32", 128, 128, False, 5), ("f32", 64, 64, True, 2),
+    ("bf16", 128, 128, False, 16), ("bf16", 128, 128, False, 48), ("bf16", 128, 128, False, 64),
+    ("bf16", 128, 128, False, 128), ("bf16", 128, 128, True, 32),
+    ("bf16", 576, 512, True, 16), ("bf16", 576, 512, True, 64), ("bf16", 576, 512, True, 256),
+]
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("dt,dqk,dv,mla,hq", ATTN_SHAPES,
+                         ids=[f"{a}-{b}x{c}-{'shared' if d else 'sep'}-h{e}" for a, b, c, d, e in ATTN_SHAPES])
+def test_attention_shape(dt, dqk, dv, mla, hq, mode):
+    spec = _base(mode, seed=200 + hq + dqk).replace(attn_dtype=dt, d_qk=dqk, d_v=dv, mla=mla, Hq=hq,
+                                                  gate_per_channel=(hq % 2 == 0), name=f"attn-{dt}-{dqk}")
+    P.say(f"[attn {dt} {dqk}/{dv} {'shared' if mla else 'separate'} h{hq} {mode}] T={spec.T}")
+    wl = W.generate(spec, DEV)
+    pl = B.Pipeline(wl)
+    pl.out.fill_(float("nan"))
+    pl.indexer()
+    pl.topk()
+    pl.attn()
+    torch.cuda.synchronize()
+    inp = O.Inputs.from_workload(wl)
+    idx = pl.indices.cpu().numpy()
+    ref, ref_lse = O.sparse_attn(inp, idx, None, spec.softmax_scale, with_lse=True)
+    w = P.check_attn(pl.out.float().cpu().numpy(), ref, P.RTOL[dt], P.attn_floor(inp, idx, None, spec.softmax_scale))
+    assert P.close(pl.lse.cpu().numpy(), ref_lse, P.RTOL[dt]).all(), "lse"
+    P.say(f"[attn {dt} {dqk}/{dv} h{hq} {mode}] ok: worst {w:.2f} of the bound")
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("h", [8, 64])
+def test_fp8_indexer_weight_range(h, mode):
+    """Weights far from 1: per-token factors from 1e-9 to 1e9 and, within a token, heads
+    spread over 2^20.  The fp8 epilogue multiplies in fp16 (8 heads at prefill, every head
+    count at decode): its per-token power-of-two weight scaling keeps every score within
+    the tolerance, with no overflow and no subnormal weights."""
+    spec = _base(mode, seed=300 + h).replace(idx_dtype="fp8", H_I=h, d_I=128, name=f"indexer-fp8-wrange-{h}")
+    P.say(f"[indexer fp8 weight range h{h} {mode}] T={spec.T}")
+    wl = W.generate(spec, DEV)
+    g = torch.Generator(device=DEV).manual_seed(17)
+    tok = 10.0 ** (torch.rand(spec.T, device=DEV, generator=g) * 18.0 - 9.0)
+    head = 2.0 ** (torch.rand(spec.T, h, device=DEV, generator=g) * 20.0 - 10.0)
+    wl.w.mul_(tok[:, None] * head)
+    pl = B.Pipeline(wl)
+    pl.scores.fill_(float("nan"))
+    pl.indexer()
+    pl.topk()
+    torch.cuda.synchronize()
+    inp = O.Inputs.from_workload(wl)
+    n = P.token_geometry(spec)[2]
+    sc = pl.scores.cpu().numpy()
+    assert np.all(np.isfinite(np.concatenate([sc[r, :n[r]] for r in range(spec.T)])))
+    ref = O.indexer(inp, ld=pl.ld)
+    w1 = P.check_scores(sc, ref, n, P.RTOL["fp8"])
+    idx = pl.indices.cpu().numpy()
+    P.check_topk_exact(idx, sc, n, spec.K)
+    P.check_selection(idx, ref, n, spec.K)
+    P.say(f"[indexer fp8 weight range h{h} {mode}] ok: worst score rel {w1:.2e}")
