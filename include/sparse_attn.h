@@ -22,9 +22,11 @@
  *   - Pointers are DEVICE pointers unless marked (host).  Tensors are dense
  *     row-major; base pointers are 16-byte aligned.
  *   - Every call is asynchronous on `stream` (a hipStream_t); the library
- *     never allocates, frees or synchronises and keeps no global state, so it
- *     is reentrant.  The caller owns every buffer, including workspaces sized
- *     by the *_workspace_size queries.
+ *     never allocates, frees or synchronises, so it is reentrant.  The caller
+ *     owns every buffer, including workspaces sized by the *_workspace_size
+ *     queries.  The one exception to "the caller owns every buffer" is
+ *     sparse_gated_attn_fwd_noalloc, whose scratch is a static device array
+ *     of the library (see there).
  *   - Argument errors are detected on the host before any launch and return
  *     SA_EINVAL (bad value / NULL / shape) or SA_EUNSUPPORTED (a valid request
  *     the library has no kernel for); nothing is launched then.  A failed
@@ -178,6 +180,35 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype,
                                 const void *gate_logits, int32_t gate_per_channel,
                                 float softmax_scale, void *out, float *lse,
                                 void *workspace, size_t workspace_bytes, sa_stream_t stream);
+
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): sparse_gated_attn_fwd with
+ * the same arguments, results and errors, minus the workspace.  Where the
+ * index list is split over workgroups (decode, few tokens), the partial
+ * results go to a static device array of SA_NOALLOC_SCRATCH_BYTES per GPU,
+ * which the library holds from its first use on that GPU until the process
+ * ends.  The call allocates nothing: no hipMalloc, no hipFree, no allocating
+ * library routine.  The stream must belong to the current device.
+ *   - A batch whose partials need more than SA_NOALLOC_SCRATCH_BYTES (the
+ *     bytes sparse_gated_attn_workspace_size reports) returns SA_EWORKSPACE
+ *     before anything is launched; sparse_gated_attn_fwd with a caller
+ *     workspace serves it.
+ *   - Every call on one GPU shares that GPU's array, and the array keeps the
+ *     last call's contents (the kernels write every partial before reading
+ *     it, so nothing needs clearing).  Calls that overlap in time on one GPU
+ *     (two streams, or two host threads) race on the array and must be
+ *     serialised by the caller.
+ */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+sa_status sparse_gated_attn_fwd_noalloc(const sa_batch *batch, sa_dtype dtype,
+                                        const void *q, int32_t n_q_heads, int32_t d_qk,
+                                        const void *k_cache, const void *v_cache, int32_t d_v,
+                                        int64_t kv_row_stride,
+                                        const int32_t *indices, int32_t k,
+                                        const void *gate_logits, int32_t gate_per_channel,
+                                        float softmax_scale, void *out, float *lse,
+                                        sa_stream_t stream);
 
 /*
  * Block-level selection, the pages' second variant.  [SEL §3.2] pseudocode:

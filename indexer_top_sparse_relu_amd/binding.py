@@ -20,7 +20,8 @@ SA_F32, SA_BF16, SA_FP8_E4M3 = 0, 1, 2
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_EWORKSPACE, SA_ELAUNCH = 0, -1, -2, -3, -4
 
 EXPORTS = ("sparse_indexer_scores", "sparse_topk_workspace_size", "sparse_topk",
-           "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sparse_block_pool",
+           "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sparse_gated_attn_fwd_noalloc",
+           "sparse_block_pool",
            "sparse_block_scores_workspace_size", "sparse_block_scores", "sparse_block_topk_workspace_size",
            "sparse_block_topk", "sparse_block_expand", "sparse_gated_attn_bwd", "sparse_window_indices",
            "sparse_branch_fuse",
@@ -76,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.sparse_gated_attn_fwd.restype = ctypes.c_int
         L.sparse_gated_attn_fwd.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp, i32,
                                             ctypes.c_float, vp, vp, vp, sz, vp]
+        L.sparse_gated_attn_fwd_noalloc.restype = ctypes.c_int
+        L.sparse_gated_attn_fwd_noalloc.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp,
+                                                    i32, ctypes.c_float, vp, vp, vp]
         L.sparse_block_pool.restype = ctypes.c_int
         L.sparse_block_pool.argtypes = [bp, ctypes.c_int, vp, i32, i64, vp, vp]
         L.sparse_block_scores_workspace_size.restype = sz
@@ -186,6 +190,21 @@ def sparse_gated_attn_fwd(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor
                                      _ptr(gate), per_channel, ctypes.c_float(scale), _ptr(out), _ptr(lse),
                                      _ptr(workspace), wsb, _stream(stream))
     _check("sparse_gated_attn_fwd", st)
+
+
+def sparse_gated_attn_fwd_noalloc(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  d_v: int, indices: torch.Tensor, gate: torch.Tensor, out: torch.Tensor,
+                                  softmax_scale: Optional[float] = None, lse: Optional[torch.Tensor] = None,
+                                  stream=None) -> None:
+    """sparse_gated_attn_fwd with the library's static per-GPU scratch instead of a workspace."""
+    T, Hq, dqk = q.shape
+    per_channel = 1 if gate.dim() == 3 else 0
+    scale = float(softmax_scale if softmax_scale is not None else dqk ** -0.5)
+    st = lib().sparse_gated_attn_fwd_noalloc(ctypes.byref(batch), _DT[q.dtype], _ptr(q), Hq, dqk, _ptr(k_cache),
+                                             _ptr(v_cache), int(d_v), k_cache.stride(-2), _ptr(indices),
+                                             indices.shape[1], _ptr(gate), per_channel, ctypes.c_float(scale),
+                                             _ptr(out), _ptr(lse), _stream(stream))
+    _check("sparse_gated_attn_fwd_noalloc", st)
 
 
 def sparse_block_pool(batch: SaBatch, k_cache: torch.Tensor, d_qk: int, k_blocks: torch.Tensor, stream=None) -> None:

@@ -1,11 +1,20 @@
 // extern "C" entry points of libsparse_attn.so: argument validation on the
-// host, then kernel launches on the caller's stream.  No allocation, no
-// synchronisation, no global state.  The operations and their citations are
-// documented in sparse_attn.h.
+// host, then kernel launches on the caller's stream.  No allocation and no
+// synchronisation; the only global state is the per-device address of the
+// static scratch array of the no-allocation attention entry point.  The
+// operations and their citations are documented in sparse_attn.h.
 #include "sparse_attn.h"
+
+#include <mutex>
 
 #include "launch.h"
 #include "sa_device.h"
+
+// Scratch of sparse_gated_attn_fwd_noalloc: split-attention partials for
+// callers that cannot allocate.  Every GPU the library runs on holds its own
+// copy until the process ends.  In host code this name is only a stand-in for
+// the symbol: kernels get the device address from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[SA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -53,6 +62,35 @@ sa_status make_batch(const sa_batch *in, sa::Batch *out)
 }
 
 sa_status launched(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ELAUNCH; }
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+sa_status scratch_of_current_device(hipStream_t stream, void **ptr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return SA_ELAUNCH;
+    if (stream) {
+        int sdev = -1;
+        if (hipStreamGetDevice(stream, &sdev) != hipSuccess)
+            return SA_EINVAL;
+        if (sdev != dev)                 // the stream must belong to the current device
+            return SA_EINVAL;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return SA_ELAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return SA_OK;
+}
 
 } // namespace
 
@@ -120,11 +158,11 @@ size_t sparse_gated_attn_workspace_size(const sa_batch *batch, int32_t n_q_heads
     return sa::attn_plan(bt.total_q, n_q_heads, d_v, k).ws_bytes;
 }
 
-sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
-                                int32_t d_qk, const void *k_cache, const void *v_cache, int32_t d_v,
-                                int64_t kv_row_stride, const int32_t *indices, int32_t k, const void *gate_logits,
-                                int32_t gate_per_channel, float softmax_scale, void *out, float *lse,
-                                void *workspace, size_t workspace_bytes, sa_stream_t stream)
+static sa_status attn_fwd_checked(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
+                                  int32_t d_qk, const void *k_cache, const void *v_cache, int32_t d_v,
+                                  int64_t kv_row_stride, const int32_t *indices, int32_t k, const void *gate_logits,
+                                  int32_t gate_per_channel, float softmax_scale, void *out, float *lse,
+                                  void *workspace, size_t workspace_bytes, bool static_scratch, sa_stream_t stream)
 {
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
@@ -150,11 +188,41 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const voi
         !sa::attn_supported_layout((int)dtype, d_qk, d_v, k_cache == v_cache))
         return SA_EUNSUPPORTED;
     const sa::AttnPlan plan = sa::attn_plan(bt.total_q, n_q_heads, d_v, k);
-    if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace)))
+    if (static_scratch) {
+        if (plan.ws_bytes > SA_NOALLOC_SCRATCH_BYTES)
+            return SA_EWORKSPACE;
+        if (plan.ws_bytes > 0) {
+            st = scratch_of_current_device((hipStream_t)stream, &workspace);
+            if (st != SA_OK)
+                return st;
+        }
+    } else if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes || !aligned16(workspace))) {
         return SA_EWORKSPACE;
+    }
     return launched(sa::launch_attn((int)dtype, bt, plan, q, n_q_heads, d_qk, k_cache, v_cache, d_v, kv_row_stride,
                                     indices, k, gate_logits, gate_per_channel ? 1 : 0, softmax_scale, out, lse,
                                     workspace, (hipStream_t)stream));
+}
+
+sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
+                                int32_t d_qk, const void *k_cache, const void *v_cache, int32_t d_v,
+                                int64_t kv_row_stride, const int32_t *indices, int32_t k, const void *gate_logits,
+                                int32_t gate_per_channel, float softmax_scale, void *out, float *lse,
+                                void *workspace, size_t workspace_bytes, sa_stream_t stream)
+{
+    return attn_fwd_checked(batch, dtype, q, n_q_heads, d_qk, k_cache, v_cache, d_v, kv_row_stride, indices, k,
+                            gate_logits, gate_per_channel, softmax_scale, out, lse, workspace, workspace_bytes,
+                            false, stream);
+}
+
+sa_status sparse_gated_attn_fwd_noalloc(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
+                                        int32_t d_qk, const void *k_cache, const void *v_cache, int32_t d_v,
+                                        int64_t kv_row_stride, const int32_t *indices, int32_t k,
+                                        const void *gate_logits, int32_t gate_per_channel, float softmax_scale,
+                                        void *out, float *lse, sa_stream_t stream)
+{
+    return attn_fwd_checked(batch, dtype, q, n_q_heads, d_qk, k_cache, v_cache, d_v, kv_row_stride, indices, k,
+                            gate_logits, gate_per_channel, softmax_scale, out, lse, nullptr, 0, true, stream);
 }
 
 sa_status sparse_block_pool(const sa_batch *batch, sa_dtype dtype, const void *k_cache, int32_t d_qk,

@@ -160,3 +160,25 @@ def test_binding_fails_loudly_without_library(B, monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         B.lib()
+
+
+def test_noalloc_attention_rejects_batches_beyond_its_scratch(B):
+    """The no-allocation entry point checks its static scratch limit on the host: a decode batch
+    whose split partials need more than SA_NOALLOC_SCRATCH_BYTES returns SA_EWORKSPACE before any
+    HIP call, and argument errors are those of sparse_gated_attn_fwd."""
+    L = B.lib()
+    f = ctypes.c_float(1.0 / 24)
+
+    def call(bt, H=128, dqk=576, dv=512, k=2048, gate=FAKE):
+        return L.sparse_gated_attn_fwd_noalloc(ctypes.byref(bt), 1, FAKE, H, dqk, FAKE, FAKE, dv, dqk, FAKE, k,
+                                               gate, 1, f, FAKE, None, None)
+
+    big = batch(B, num_seqs=200, total_q=200, max_q=1)
+    need = L.sparse_gated_attn_workspace_size(ctypes.byref(big), 128, 512, 2048)
+    assert need > (128 << 20)
+    assert call(big) == B.SA_EWORKSPACE
+    assert call(batch(B), gate=None) == B.SA_EINVAL
+    assert call(batch(B), H=24) == B.SA_EUNSUPPORTED
+    e = batch(B, total_q=0, max_q=0)
+    assert L.sparse_gated_attn_fwd_noalloc(ctypes.byref(e), 1, None, 128, 576, None, None, 512, 576, None, 2048, None,
+                                           1, f, None, None, None) == B.SA_OK
