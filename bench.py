@@ -27,6 +27,7 @@ if ROOT not in sys.path:
 PEAK = {"hbm_GBs": 8000.0, "fp8_TFLOPs": 5000.0, "bf16_TFLOPs": 2500.0, "fp32_TFLOPs": 157.3}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 COPY_ELEMS = 1 << 28          # calibration copy: 2^28 fp32 = 1 GiB read + 1 GiB written
+FLUSH_BYTES = 512 << 20       # written between timed steps: twice the 256 MB MALL
 
 
 def calibration_copy():
@@ -53,9 +54,11 @@ def causal_lengths(spec):
 METRIC = "query tokens/s (indexer+TopK+sparse attn) at 128K ctx, K=2048; % HBM/MFMA peak"
 
 
-def algorithmic_work(spec, n_valid):
+def algorithmic_work(spec, n_valid, n_unique_rows):
     """Per-step algorithmic work of each stage: flops of the contractions, and the bytes the
-    method must move (inputs read once, outputs written once)."""
+    method must move (inputs read once, outputs written once).  The attention reads each cache
+    row it touches once (n_unique_rows distinct rows over the whole step), not once per query
+    token that selects it: at prefill a row shared by many tokens is one HBM read."""
     pairs = int(sum(causal_lengths(spec)))
     esz = {"fp8": 1, "bf16": 2, "f32": 4}
     ie, ae = esz[spec.idx_dtype], esz[spec.attn_dtype]
@@ -69,9 +72,130 @@ def algorithmic_work(spec, n_valid):
                     + keys * (spec.d_I * ie + scale_b) + pairs * 4},
         "topk": {"bytes": pairs * 4 + spec.T * spec.K * 4},
         "attn": {"flops": 2.0 * spec.Hq * n_valid * (spec.d_qk + spec.d_v),
-                 "bytes": n_valid * kv_row + spec.T * (spec.Hq * spec.d_qk + gate_elems + spec.Hq * spec.d_v) * ae
-                 + spec.T * spec.K * 4},
+                 "bytes": n_unique_rows * kv_row
+                 + spec.T * (spec.Hq * spec.d_qk + gate_elems + spec.Hq * spec.d_v) * ae + spec.T * spec.K * 4,
+                 "gathered_bytes": n_valid * kv_row},
     }
+
+
+def unique_rows(wl, indices):
+    """Distinct physical cache rows the step's index lists touch (outside the timed region)."""
+    import torch
+
+    s = wl.spec
+    seq = torch.repeat_interleave(torch.arange(s.B, device=indices.device),
+                                  torch.tensor(s.q_lens, device=indices.device))
+    acc = torch.empty(0, dtype=torch.long, device=indices.device)
+    for t0 in range(0, s.T, 512):
+        idx = indices[t0:t0 + 512].long()
+        b = seq[t0:t0 + 512, None].expand_as(idx)
+        ok = idx >= 0
+        rows = wl.page_table[b[ok], idx[ok] // s.page_size].long() * s.page_size + idx[ok] % s.page_size
+        acc = torch.unique(torch.cat([acc, rows]))
+    return int(acc.numel())
+
+
+def stats_ms(vals):
+    import statistics
+
+    return {"mean": sum(vals) / len(vals), "median": statistics.median(vals), "min": min(vals), "max": max(vals)}
+
+
+def machine_info():
+    """GPU, ROCm and host facts for the record."""
+    import glob
+    import platform
+
+    import torch
+
+    info = {}
+    try:
+        p = torch.cuda.get_device_properties(0)
+        info["gpu"] = p.name
+        info["gpu_arch"] = getattr(p, "gcnArchName", None)
+        info["gpu_cus"] = p.multi_processor_count
+        info["gpu_mem_GB"] = round(p.total_memory / 1e9, 1)
+    except Exception as e:  # noqa: BLE001
+        info["gpu"] = f"unknown ({e})"
+    info["hip"] = torch.version.hip
+    info["torch"] = torch.__version__
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            info["rocm"] = f.read().strip()
+    except OSError:
+        info["rocm"] = None
+    clocks = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(card, name)) as f:
+                    levels = [l.strip() for l in f if l.strip()]
+            except OSError:
+                continue
+            cur = [l for l in levels if l.endswith("*")]
+            clocks[name[7:]] = {"levels": levels, "current": cur[0] if cur else None}
+        if clocks:
+            break
+    info["clocks"] = clocks or None
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    info["cpu"] = cpu or platform.processor()
+    info["host_cpus"] = os.cpu_count()
+    try:
+        info["host_cpus_usable"] = len(os.sched_getaffinity(0))
+    except AttributeError:
+        info["host_cpus_usable"] = None
+    return info
+
+
+def measured_ceilings(stream):
+    """Ceilings measured on this GPU with library kernels (not the path's): a 1 GiB streaming copy
+    (bytes read + written per second), a bf16 GEMM and an fp8 GEMM (8192^3, hipBLASLt through
+    torch).  Reported beside the published peaks; the roofline fractions use the published ones."""
+    import torch
+
+    out = {}
+
+    def timed(fn, n):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n * 1e-3
+
+    x = torch.empty(1 << 28, device="cuda")
+    y = torch.empty_like(x)
+    t = timed(lambda: y.copy_(x), 10)
+    out["hbm_copy_GBs"] = 2 * x.numel() * 4 / t / 1e9
+    del x, y
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    t = timed(lambda: torch.matmul(a, b), 10)
+    out["bf16_gemm_TFLOPs"] = 2.0 * n ** 3 / t / 1e12
+    try:
+        a8 = a.to(torch.float8_e4m3fn)
+        b8 = b.t().contiguous().to(torch.float8_e4m3fn).t()
+        one = torch.ones((), device="cuda")
+        t = timed(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16), 10)
+        out["fp8_gemm_TFLOPs"] = 2.0 * n ** 3 / t / 1e12
+    except Exception as e:  # noqa: BLE001
+        out["fp8_gemm_TFLOPs"] = None
+        out["fp8_gemm_error"] = str(e)[:120]
+    del a, b
+    torch.cuda.empty_cache()
+    return out
 
 
 def to_np(t):
@@ -86,8 +210,10 @@ def to_np(t):
     return t.numpy()
 
 
-def cpu_baseline(wl, sample_tokens: int):
-    """The oracle (as it stands) on the last `sample_tokens` query tokens of the workload."""
+def cpu_baseline(wl, gpu_indices, sample_tokens: int):
+    """The oracle (as it stands) on the last `sample_tokens` query tokens of the workload, and the
+    recall@K of the GPU's selection against the oracle's on those tokens (the share of the
+    oracle's K positions the GPU also selected, averaged over the rows)."""
     import numpy as np
 
     from oracle import oracle as O
@@ -107,11 +233,18 @@ def cpu_baseline(wl, sample_tokens: int):
                    gate_per_channel=s.gate_per_channel)
     threads = O.set_threads(0)
     t0 = time.perf_counter()
-    O.pipeline(inp, s.K, scale=s.softmax_scale)
+    _, ref_idx, _ = O.pipeline(inp, s.K, scale=s.softmax_scale)
     dt = time.perf_counter() - t0
+    gpu = to_np(gpu_indices[sl])
+    rec = []
+    for r in range(S):
+        want = ref_idx[r][ref_idx[r] >= 0]
+        got = gpu[r][gpu[r] >= 0]
+        rec.append(np.intersect1d(want, got).size / max(1, want.size))
     return {"value": S / dt, "unit": "query_tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"last {S} of {s.T} query tokens (positions {s.ctx_lens[-1] - S}..{s.ctx_lens[-1] - 1}), "
-                      f"full indexer + Top-K + gated attention in fp64, {dt:.1f} s"}
+                      f"full indexer + Top-K + gated attention in fp64, {dt:.1f} s",
+            "recall_at_K": float(np.mean(rec)), "recall_min": float(np.min(rec)), "recall_rows": S}
 
 
 def before_path(wl, steps: int, stream):
@@ -364,6 +497,7 @@ def main(argv=None):
     ap.add_argument("--step-only", action="store_true",
                     help="time only the step (no cache append, block variant or branch fusion runs), so that "
                          "a profile of this process holds the step's kernels alone")
+    ap.add_argument("--no-flush", action="store_true", help="do not evict the caches between timed steps")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a copy kernel of known size (for HBM counter calibration)")
     args = ap.parse_args(argv)
@@ -388,10 +522,15 @@ def main(argv=None):
         pl.run(stream)
     torch.cuda.synchronize()
 
+    # between timed steps a 512 MiB buffer is written on the same stream, outside the event
+    # pairs, so that no step finds its inputs in L2 or the 256 MB MALL left by the previous one
+    flush = torch.empty(FLUSH_BYTES // 4, device="cuda") if not args.no_flush else None
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        if flush is not None:
+            flush.fill_(float(i))
         e = ev[i]
         e[0].record(stream)
         pl.indexer(stream)
@@ -402,17 +541,18 @@ def main(argv=None):
         e[3].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    stage_ms = {
-        "indexer": sum(e[0].elapsed_time(e[1]) for e in ev) / args.steps,
-        "topk": sum(e[1].elapsed_time(e[2]) for e in ev) / args.steps,
-        "attn": sum(e[2].elapsed_time(e[3]) for e in ev) / args.steps,
-    }
-    step_ms = sum(e[0].elapsed_time(e[3]) for e in ev) / args.steps
+    del flush
+    per = {"indexer": [e[0].elapsed_time(e[1]) for e in ev], "topk": [e[1].elapsed_time(e[2]) for e in ev],
+           "attn": [e[2].elapsed_time(e[3]) for e in ev], "step": [e[0].elapsed_time(e[3]) for e in ev]}
+    st_ms = {k: stats_ms(v) for k, v in per.items()}
+    stage_ms = {k: st_ms[k]["mean"] for k in ("indexer", "topk", "attn")}
+    step_ms = st_ms["step"]["median"]
     wall_ms = wall * 1e3 / args.steps
     n_valid = int((pl.indices >= 0).sum().item())
+    n_unique = unique_rows(wl, pl.indices)
     assert torch.isfinite(pl.out.float()).all().item(), "non-finite output"
 
-    work = algorithmic_work(spec, n_valid)
+    work = algorithmic_work(spec, n_valid, n_unique)
     dom = max(stage_ms, key=stage_ms.get)
     rl = {}
     for st, ms in stage_ms.items():
@@ -433,6 +573,15 @@ def main(argv=None):
             rl[st] = {"bound": "hbm", "achieved": ach, "peak": PEAK["hbm_GBs"], "unit": "GB/s",
                       "frac": ach / PEAK["hbm_GBs"]}
         rl[st]["ms"] = ms
+        rl[st]["ms_median"] = st_ms[st]["median"]
+        rl[st]["ms_min"] = st_ms[st]["min"]
+        rl[st]["ms_max"] = st_ms[st]["max"]
+        rl[st]["algorithmic_bytes"] = w["bytes"]
+        if "flops" in w:
+            rl[st]["algorithmic_flops"] = w["flops"]
+    rl["attn"]["gathered_rows_GBs"] = work["attn"]["gathered_bytes"] / (stage_ms["attn"] * 1e-3) / 1e9
+    rl["attn"]["unique_rows"] = n_unique
+    rl["attn"]["selected_slots"] = n_valid
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -440,7 +589,7 @@ def main(argv=None):
         ent = tr.get(spec.name, {}).get(dom)
         if ent and ent.get("source_hash") == source_hash(dom):
             traffic = ent["bytes_per_launch"]
-    roof = {k: v for k, v in rl[dom].items() if k != "ms"}
+    roof = {k: rl[dom][k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     roof["kernel"] = dom
     roof["traffic"] = traffic
 
@@ -454,7 +603,12 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": step_ms,
+        "ms_per_step_stats": st_ms["step"],
         "wall_ms_per_step": wall_ms,
+        "timing": ("HIP events on the kernels' stream around each stage; value and ms_per_step from the median "
+                   "step" + ("" if args.no_flush else f"; a {FLUSH_BYTES >> 20} MiB buffer written between steps, "
+                                                       "outside the events, evicts L2 and the MALL")
+                   + "; roofline achieved from the dominant stage's mean duration"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -467,13 +621,23 @@ def main(argv=None):
         "roofline": roof,
         "stages": rl,
     }
+    line["machine"] = machine_info()
     if not args.step_only:
+        line["measured_ceilings"] = measured_ceilings(stream)
+        c = line["measured_ceilings"]
+        for st, r in rl.items():
+            if r["bound"] == "hbm" and c.get("hbm_copy_GBs"):
+                r["frac_of_measured"] = r["achieved"] / c["hbm_copy_GBs"]
+            elif r["bound"] == "mfma":
+                key = "fp8_gemm_TFLOPs" if (st == "indexer" and spec.idx_dtype == "fp8") else "bf16_gemm_TFLOPs"
+                if c.get(key) and (st == "attn" or spec.idx_dtype != "f32"):
+                    r["frac_of_measured"] = r["achieved"] / c[key]
         line["before_path"] = before_path(wl, args.steps, stream)
         line["block_variant"] = block_variant(wl, args.steps, stream, kb=max(1, spec.K // spec.page_size))
         line["branch_fusion"] = branch_fusion(wl, pl, args.steps, stream, window=512)
         line["backward"] = backward_pass(args.steps, stream)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample)
+        line["cpu_baseline"] = cpu_baseline(wl, pl.indices, args.cpu_sample)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -15,6 +15,15 @@ Usage (from the repository root):
   python -m indexer_top_sparse_relu_amd.profiling stats <dir> --workload W --command "..." --out F.md
   python -m indexer_top_sparse_relu_amd.profiling traffic <fetch_dir> <write_dir> --workload W \
          --copy-bytes N --command-fetch "..." --command-write "..." --json F.json --out F.md
+  python -m indexer_top_sparse_relu_amd.profiling counters <dir> [<dir> ...] --workload W \
+         --command "..." [--command "..."] --out F.md
+
+  counters — `rocprofv3 --pmc` runs with any counters -> per path kernel the
+            median value per dispatch of each counter, plus derived figures
+            when their counters are present: the shader clock (GRBM_GUI_ACTIVE
+            is counted on each of the 8 XCDs), MFMA busy (SQ_VALU_MFMA_BUSY_CYCLES
+            over the SIMD-cycles of the dispatch: it counts on each of a CU's 4 SIMDs), and LDS bank-conflict cycles
+            per LDS-active cycle.
 """
 from __future__ import annotations
 
@@ -131,6 +140,65 @@ def traffic(fetch_dir: str, write_dir: str, copy_bytes: int):
     return res
 
 
+N_XCD = 8
+N_CU = 256
+
+
+def counters(dirs):
+    """{kernel: {counter: median per dispatch}} over the counter output of several runs, plus
+    the median kernel duration of the dispatches (ns) where the output carries timestamps."""
+    out = {}
+    for d in dirs:
+        rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
+        per, dur = {}, {}
+        for r in rows:
+            name = r["Kernel_Name"]
+            if stage_of(name) is None:
+                continue
+            disp = r.get("Dispatch_Id", r.get("Correlation_Id", ""))
+            key = (name, r["Counter_Name"], disp)
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                dur[(name, disp)] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        agg = {}
+        for (name, cn, disp), v in per.items():
+            agg.setdefault((name, cn), []).append(v)
+            if cn == "GRBM_GUI_ACTIVE" and dur.get((name, disp), 0) >= 50000:     # 50 us or longer
+                agg.setdefault((name, "clock_GHz"), []).append(v / N_XCD / dur[(name, disp)])
+        for (name, cn), vs in agg.items():
+            out.setdefault(short_name(name), {})[cn] = statistics.median(vs)
+    for k, c in out.items():
+        g = c.get("GRBM_GUI_ACTIVE")
+        if g:
+            cyc = g / N_XCD                      # cycles of the dispatch (per XCD)
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                c["mfma_busy_frac"] = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * N_CU * 4)
+            if "SQ_BUSY_CU_CYCLES" in c:
+                c["cu_busy_frac"] = c["SQ_BUSY_CU_CYCLES"] / (cyc * N_CU)
+        if c.get("SQ_LDS_IDX_ACTIVE"):
+            c["lds_bank_conflict_per_active"] = c.get("SQ_LDS_BANK_CONFLICT", 0.0) / c["SQ_LDS_IDX_ACTIVE"]
+    return out
+
+
+def _counters_md(workload, commands, res, stats=None):
+    lines = [f"# Counters per dispatch — {workload}", "", "Counter runs (repository root, one MI355X):", "", "```",
+             "export TMPDIR=/tmp", *commands, "```", "",
+             "Median over the dispatches of each kernel.  Derived: `cycles` = GRBM_GUI_ACTIVE / 8 (it counts on each "
+             "of the 8 XCDs); `mfma_busy_frac` = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 256 CUs x 4 SIMDs); `cu_busy_frac` = "
+             "SQ_BUSY_CU_CYCLES / (cycles x 256); `lds_bank_conflict_per_active` = SQ_LDS_BANK_CONFLICT / "
+             "SQ_LDS_IDX_ACTIVE; `clock_GHz` = cycles over the dispatch's own duration (its timestamps in the counter run).", ""]
+    for k, c in res.items():
+        lines.append(f"## `{k}`")
+        lines.append("")
+        lines.append("| counter | value |")
+        lines.append("|---|---|")
+        for cn in sorted(c):
+            v = c[cn]
+            lines.append(f"| {cn} | {v:.4g} |" if isinstance(v, float) else f"| {cn} | {v} |")
+        lines.append("")
+    return "\n".join(lines) + "\n"
+
+
 def _stats_md(workload, command, stats):
     lines = [f"# Kernel stats — {workload}", "", "Command (repository root, one MI355X):", "", "```",
              "export TMPDIR=/tmp", command, "```", "",
@@ -173,7 +241,23 @@ def main(argv=None):
     b.add_argument("--command-write", required=True)
     b.add_argument("--json", required=True)
     b.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("dirs", nargs="+")
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", action="append", required=True)
+    c.add_argument("--stats-dir", default=None, help="a --kernel-trace --stats run of the same command (kernel times)")
+    c.add_argument("--out", required=True)
     args = ap.parse_args(argv)
+    if args.cmd == "counters":
+        res = counters(args.dirs)
+        times = None
+        if args.stats_dir:
+            times = {s["kernel"]: (s["median_ms"] or s["avg_ms"]) for s in kernel_stats(args.stats_dir)}
+        with open(args.out, "w") as f:
+            f.write(_counters_md(args.workload, args.command, res, times))
+        json.dump(res, sys.stdout)
+        print()
+        return 0
     if args.cmd == "stats":
         st = kernel_stats(args.dir)
         with open(args.out, "w") as f:
