@@ -35,6 +35,8 @@
 // softmax sum, multiplies by sigmoid(gate) and rounds to bf16; with a split
 // index list it writes (O, max, sum) partials that a combine kernel merges by
 // log-sum-exp.
+#include <type_traits>
+
 #include "sa_device.h"
 #include "launch.h"
 
@@ -750,6 +752,395 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+// MQA kernel (d_qk = d_v = D = 128, 32 query heads per unit, separate K and V
+// caches or one shared row) on 32x32x16 bf16 MFMA.  A unit is one (token,
+// group of 32 heads, split of the index list) and belongs to one wave; the
+// four waves of a workgroup are independent units (consecutive tokens), so the
+// kernel has no workgroup barrier.  Each wave resolves its slots to physical
+// rows in its own LDS area.  Per 32-key tile:
+//   - the gather: each load instruction covers four whole rows (16 lanes x 16
+//     bytes per 256-byte row).  On gfx950 the address unit's cost grows with
+//     the cache lines an instruction touches: this pattern gathers about 2.5x
+//     faster than loading the MFMA operand layout directly (32 rows x 32
+//     bytes per instruction).  The rows land in VGPRs, two tiles ahead (every
+//     load is compiler-tracked, so its waits are exact), and are written to
+//     the wave's LDS tiles (K, and V unless the row is shared);
+//   - S^T = K Q^T (8 MFMAs, K from LDS, Q^T in VGPRs, a lane holds one head's
+//     column), softmax terms against a fixed per-head reference as in the
+//     latent kernel (exact rerun when a term outgrows 2^64), O^T += V^T P^T
+//     (8 MFMAs, V^T by transpose loads).
+// The LDS tiles use the latent kernel's layout and swizzle (blocks of 8 rows x
+// 8 sixteen-byte chunks, position (c & 7) ^ g(r)), under which its K reads and
+// V transpose reads are conflict-free.
+template <int D, bool SHARED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_mqa_kernel(
+    Batch bt, const uint16_t *__restrict__ q, int Hq, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, int64_t rs, const int32_t *__restrict__ idx, int K,
+    const uint16_t *__restrict__ gate, int per_channel, float scale_log2, uint16_t *__restrict__ out,
+    float *__restrict__ lse, float *__restrict__ part, int n_split, int split_len, int n_units)
+{
+    constexpr int NW = 4;
+    constexpr int NKQ = D / 16;             // S-chain k-steps
+    constexpr int NDT = D / 32;             // 32-dim tiles of O^T
+    constexpr int KCB = D / 64;             // 8-chunk blocks per row
+    constexpr int TK = 32;                  // keys per tile
+    constexpr int TB = TK * D * 2;          // bytes of one K (or V) tile in LDS
+    constexpr int RPI = 64 / (D / 8);       // rows per load instruction (16-byte chunks per row: D / 8)
+    constexpr int NI = TK / RPI;            // load instructions per tile and cache
+    constexpr int NT = SHARED ? 1 : 2;      // LDS tiles per wave (K, V)
+    static_assert(D % 64 == 0 && NKQ % 4 == 0 && 64 % (D / 8) == 0, "dims");
+    constexpr int MAXT = kMaxSplit / TK + 2;   // tiles of a list, plus the two loaded past its end
+    __shared__ __align__(16) uint8_t ltile[NW * NT * TB];
+    __shared__ uint64_t loff[NW * MAXT * TK];  // byte offset of each slot's cache row
+    __shared__ uint32_t lmask[NW * MAXT];     // valid slots of each tile, one bit per key
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int unit = blockIdx.x * NW + wv;
+    if (unit >= n_units)
+        return;
+    const int HG = Hq >> 5;
+    const int sp = unit % n_split;
+    const int rest = unit / n_split;
+    const int hg = rest % HG, tok = rest / HG;
+    const int col = lane & 31, hq = lane >> 5;
+    const int h = hg * 32 + col;
+    const int b = seq_of_token(bt, tok);
+    const int j0 = sp * split_len;
+    const int j1 = min(K, j0 + split_len);
+    const int nslots = max(0, j1 - j0);
+    const int32_t *irow = idx + (int64_t)tok * K + j0;
+    lds_u8 *const tk = (lds_u8 *)ltile + wv * NT * TB;
+    lds_u8 *const tv = SHARED ? tk : tk + TB;
+    uint64_t *const off = loff + wv * MAXT * TK;
+    uint32_t *const msk = lmask + wv * MAXT;
+
+    // Q^T operand: head h, dims 16ks + 8hq .. +7
+    struct QOp {
+        bf16x8 v[NKQ];
+    };
+    auto load_q = [&]() {
+        QOp r;
+        const uint16_t *qp = q + ((int64_t)tok * Hq + h) * D + 8 * hq;
+#pragma unroll
+        for (int ks = 0; ks < NKQ; ++ks)
+            r.v[ks] = *(const bf16x8 *)(qp + 16 * ks);
+        return r;
+    };
+    const QOp q0 = load_q();
+    // leading tiles with every key valid, and the tiles up to the last valid key
+    // (lists from sparse_topk hold their valid positions first, then -1)
+    int nfull = 0, ntiles = 0;
+    {
+        // every slot's index, then every page-table entry (two round trips); each
+        // slot keeps the byte offset of its cache row, and slots past the list or
+        // holding padding keep position 0's row (a valid row: their loads are in
+        // bounds, their keys are masked)
+        const uint64_t rsb = (uint64_t)rs * 2;
+        const int64_t row0 = phys_row(bt, b, 0);
+        constexpr int PS = kMaxSplit / 64 + 1;
+        int sv[PS];
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            const int j = lane + 64 * u;
+            sv[u] = j < nslots ? irow[j] : -1;
+        }
+        int pg[PS];
+#pragma unroll
+        for (int u = 0; u < PS; ++u)
+            pg[u] = bt.page_table[(int64_t)b * bt.max_pages + ((sv[u] >= 0 ? sv[u] : 0) >> bt.page_shift)];
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            const int j = lane + 64 * u;
+            const int64_t pr = sv[u] >= 0 ? ((int64_t)pg[u] << bt.page_shift) + (sv[u] & ((1 << bt.page_shift) - 1))
+                                          : row0;
+            if (j < MAXT * TK)
+                off[j] = (uint64_t)pr * rsb;
+            const uint64_t vb = __ballot(sv[u] >= 0);
+            const uint32_t lo = (uint32_t)vb, hi = (uint32_t)(vb >> 32);
+            if (nfull == 2 * u && lo == 0xFFFFFFFFu)
+                nfull = 2 * u + 1 + (hi == 0xFFFFFFFFu);
+            if (lo)
+                ntiles = 2 * u + 1;
+            if (hi)
+                ntiles = 2 * u + 2;
+            if (lane == 0 && 2 * u < MAXT) {
+                msk[2 * u] = (uint32_t)vb;
+                if (2 * u + 1 < MAXT)
+                    msk[2 * u + 1] = (uint32_t)(vb >> 32);
+            }
+        }
+    }
+    f32x16 o[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        o[dt] = f32x16{};
+    float m_ref = -INFINITY, m_true = -INFINITY, l_run = 0.0f;
+
+    // one tile's gather: instruction i, lane l -> tile row RPI*i + l / (D/8), chunk l % (D/8)
+    struct Stage {
+        i32x4 k[NI];
+        i32x4 v[SHARED ? 1 : NI];
+    };
+    const int lrow = lane / (D / 8), lch = lane % (D / 8);
+    const uint8_t *const kbase = (const uint8_t *)kc + 16 * lch;
+    const uint8_t *const vbase = (const uint8_t *)vc + 16 * lch;
+    auto load_stage = [&](int t) {
+        Stage st;
+        const uint64_t *o = off + t * TK + lrow;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const uint64_t ob = o[RPI * i];
+            st.k[i] = *(const i32x4 *)(kbase + ob);
+            if constexpr (!SHARED)
+                st.v[i] = *(const i32x4 *)(vbase + ob);
+        }
+        return st;
+    };
+    // LDS position of chunk c of tile row r: block (r / 8) * KCB + c / 8, row r % 8
+    // of the block, position (c % 8) ^ g(r).  With r = RPI*i + lrow (RPI = 4),
+    // g(r) = 4*(lrow / 2) + (i % 4), so four lane bases plus constants cover it.
+    static_assert(RPI == 4, "four rows per load instruction");
+    lds_u8 *wbase[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        wbase[c] = tk + (lch >> 3) * 1024 + lrow * 128 + 16 * (((lch & 7) ^ (4 * (lrow >> 1))) ^ c);
+    auto put_stage = [&](const Stage &st) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int cst = (i >> 1) * KCB * 1024 + (i & 1) * 512;
+            *(__attribute__((address_space(3))) i32x4 *)(wbase[i & 3] + cst) = st.k[i];
+            if constexpr (!SHARED)
+                *(__attribute__((address_space(3))) i32x4 *)(wbase[i & 3] + (tv - tk) + cst) = st.v[i];
+        }
+    };
+    // S^T A operand (K row cl, chunk 2ks + hl) and V^T transpose-load bases
+    const int cl = lane & 31, hl = lane >> 5;
+    lds_u8 *kb[4];
+    {
+        lds_u8 *krow = tk + (cl >> 3) * KCB * 1024 + (cl & 7) * 128;
+        const int gh = hl ^ swzg(cl);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            kb[m] = krow + 16 * ((2 * m) ^ gh);
+    }
+    lds_u8 *vb[2][2];
+    {
+        const int G = lane >> 4, i16 = lane & 15;
+        lds_u8 *vrow = tv + (4 * hl + (i16 >> 2)) * 128 + 8 * (i16 & 1) + 16 * (((i16 & 3) >> 1) ^ hl);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int sc = 0; sc < 2; ++sc)
+                vb[a][sc] = vrow + 64 * (a ^ ((i16 >> 3) & 1)) + 32 * ((G & 1) ^ sc);
+    }
+
+    // One pass over the index list.  mode 0: reference from the first valid
+    // keys, accumulate; mode 1: exact maximum only (m_true); mode 2: reference
+    // m_ref as given, accumulate.
+    // The reference is taken from tile 0 (a list's first valid keys) and the
+    // leading full tiles need no key mask, so the steady-state tile step carries
+    // neither: `first` and `partial` are compile-time flags.  (With no valid key
+    // in tile 0 the reference stays -inf; any overflow then takes the rerun.)
+    auto run = [&](f32x16 (&oa)[NDT], const int mode, const QOp &qo) {
+        const bf16x8 *qop = qo.v;
+        // two stages in registers: tile t is written to LDS while t+1 is in flight,
+        // then the stage is reloaded with tile t+2
+        Stage s0 = load_stage(0), s1 = load_stage(1);
+        auto step = [&](int t, Stage &st, auto first_c, auto partial_c) {
+            constexpr bool FIRST = decltype(first_c)::value, PARTIAL = decltype(partial_c)::value;
+            put_stage(st);
+            asm volatile("" ::: "memory");      // the tile's writes precede its reads
+            st = load_stage(t + 2);
+            // ---- S^T = K Q^T: A = K row cl, chunk 2ks + hl
+            // (written as asm so that the accumulator stays in VGPRs, where the
+            // softmax reads it; the AGPRs hold O.  The last MFMA is followed by the
+            // wait states a VALU read of its result needs.)
+            f32x16 s;
+            {
+                constexpr int QD = 4;
+                auto lda = [&](int ks) { return *(lds_bf16x8 *)(kb[ks & 3] + 1024 * (ks >> 2)); };
+                bf16x8 ka[QD];
+#pragma unroll
+                for (int d = 0; d < QD; ++d)
+                    ka[d] = lda(d);
+#pragma unroll
+                for (int ks = 0; ks < NKQ; ++ks) {
+                    if (ks == 0)
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0"
+                                     : "=&v"(s) : "v"(ka[ks % QD]), "v"(qop[ks]));
+                    else if (ks + 1 < NKQ)
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0"
+                                     : "+v"(s) : "v"(ka[ks % QD]), "v"(qop[ks]));
+                    else
+                        asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+                                     "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                                     : "+v"(s) : "v"(ka[ks % QD]), "v"(qop[ks]));
+                    if (ks + QD < NKQ)
+                        ka[ks % QD] = lda(ks + QD);
+                }
+            }
+            // logits in log2 units; keys outside the list get -inf (a term of 0)
+            if constexpr (PARTIAL) {
+                const uint32_t vmask = __builtin_amdgcn_readfirstlane(msk[t]);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    s[i] = ((vmask >> (8 * (i >> 2) + 4 * hl + (i & 3))) & 1) ? s[i] : -INFINITY;
+            }
+            if (mode == 1 || (mode == 0 && FIRST)) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    mx = fmaxf(mx, s[i] * scale_log2);
+                mx = max_halves(mx);
+                if (mode == 1)
+                    m_true = fmaxf(m_true, mx);
+                else
+                    m_ref = mx;
+            }
+            if (mode != 1) {
+                const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+                bf16x8 pop[2];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float pi = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -base));
+                    l_run += pi;
+                    pop[i >> 3][i & 7] = (__bf16)pi;
+                }
+                // ---- O^T += V^T P^T (transpose loads; the latent kernel's V^T mapping)
+                auto ldv = [&](int dt, int j, int sec) {
+                    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                        (lds_bf16x4 *)(vb[dt & 1][sec] + (2 * j + sec) * KCB * 1024 + (dt >> 1) * 1024));
+                };
+                auto vstep = [](int u) { return 2 * (u % NDT) + u / NDT; };
+                auto ldv8 = [&](int stp) {
+                    const bf16x4 lo = ldv(stp >> 1, stp & 1, 0), hi = ldv(stp >> 1, stp & 1, 1);
+                    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                };
+                constexpr int PD = 4;
+                bf16x8 va[PD];
+#pragma unroll
+                for (int d = 0; d < PD; ++d)
+                    va[d] = ldv8(vstep(d));
+#pragma unroll
+                for (int u = 0; u < 2 * NDT; ++u) {
+                    oa[u % NDT] = mma32_bf16(va[u % PD], pop[u / NDT], oa[u % NDT]);
+                    if (u + PD < 2 * NDT)
+                        va[u % PD] = ldv8(vstep(u + PD));
+                }
+            }
+            asm volatile("" ::: "memory");      // the tile's reads precede the next tile's writes
+        };
+        using T_ = std::true_type;
+        using F_ = std::false_type;
+        if (ntiles == 0)
+            return;
+        // tile 0 (stage s0), then the full tiles in pairs (s1, s0), then the tail
+        if (nfull == 0) {
+            step(0, s0, T_{}, T_{});
+            return;
+        }
+        step(0, s0, T_{}, F_{});
+        int t = 1;
+        for (; t + 1 < nfull; t += 2) {
+            step(t, s1, F_{}, F_{});
+            step(t + 1, s0, F_{}, F_{});
+        }
+        if (t < nfull) {
+            step(t, s1, F_{}, F_{});
+            ++t;
+        }
+        for (; t < ntiles; ++t) {       // tiles with some key missing
+            if (t & 1)
+                step(t, s1, F_{}, T_{});
+            else
+                step(t, s0, F_{}, T_{});
+        }
+    };
+
+    // ---- epilogue: lane holds head h, dims 32dt + 8g + 4hq + {0..3} of tile dt
+    auto store = [&](const f32x16 (&oa)[NDT]) {
+        float l_tot = sum_halves(l_run);
+        float probe = 0.0f;                 // turns NaN if any result is not finite
+        if (n_split == 1) {
+            const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
+            const int64_t orow = ((int64_t)tok * Hq + h) * D;
+            if (per_channel) {
+                u32x2 gw[NDT][4];
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        gw[dt][g] = *(const u32x2 *)(gate + orow + 32 * dt + 8 * g + 4 * hq);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float y[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint32_t w = i < 2 ? gw[dt][g].x : gw[dt][g].y;
+                            const float x = bf16_bits_to_f32((uint16_t)(w >> (16 * (i & 1))));
+                            y[i] = oa[dt][4 * g + i] * (inv * __builtin_amdgcn_rcpf(1.0f + __expf(-x)));
+                            probe = fmaf(y[i], 0.0f, probe);
+                        }
+                        const bf16x2 lo = {(__bf16)y[0], (__bf16)y[1]}, hi = {(__bf16)y[2], (__bf16)y[3]};
+                        *(u32x2 *)(out + orow + 32 * dt + 8 * g + 4 * hq) =
+                            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                    }
+            } else {
+                const float gi = inv * sigmoidf_(bf16_bits_to_f32(gate[(int64_t)tok * Hq + h]));
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        float y[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            y[i] = oa[dt][4 * g + i] * gi;
+                            probe = fmaf(y[i], 0.0f, probe);
+                        }
+                        const bf16x2 lo = {(__bf16)y[0], (__bf16)y[1]}, hi = {(__bf16)y[2], (__bf16)y[3]};
+                        *(u32x2 *)(out + orow + 32 * dt + 8 * g + 4 * hq) =
+                            u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                    }
+            }
+            if (lse && hq == 0)
+                lse[(int64_t)tok * Hq + h] = l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
+        } else {
+            float *pp = part + (((int64_t)tok * n_split + sp) * Hq + h) * (D + 4) + 4 * hq;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const f32x4 v4 = f32x4{oa[dt][4 * g], oa[dt][4 * g + 1], oa[dt][4 * g + 2], oa[dt][4 * g + 3]};
+                    probe = fmaf(v4[0] + v4[1] + v4[2] + v4[3], 0.0f, probe);
+                    *(f32x4 *)(pp + 32 * dt + 8 * g) = v4;
+                }
+            if (hq == 0) {
+                pp[D] = m_ref;
+                pp[D + 1] = l_tot;
+            }
+        }
+        return !(l_tot <= 0x1p64f) || probe != 0.0f;
+    };
+
+    run(o, 0, q0);
+    const bool over = store(o);
+    if (__ballot(over) != 0) {
+        // rare: some head's terms outgrew 2^64 relative to its first keys; find
+        // the exact maximum, then rerun with it as the reference (terms <= 1)
+        run(o, 1, load_q());
+        m_ref = m_true;
+        l_run = 0.0f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            o[dt] = f32x16{};
+        run(o, 2, load_q());
+        store(o);
+    }
+}
+
 // Merge split partials by log-sum-exp, then gate; one block per (token, head).
 __global__ __launch_bounds__(128) void attn_combine_kernel(int Hq, int DV, int n_split, const float *__restrict__ part,
                                                           const void *__restrict__ gate, int per_channel, int is_bf16,
@@ -965,7 +1356,24 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const voi
     hipError_t e = hipErrorInvalidValue;
     if (dtype == 1) {
         const bool mla = (k_cache == v_cache) && d_v <= d_qk;
-        if (d_qk == 128 && d_v == 128 && !mla)
+        if (d_qk == 128 && d_v == 128 && Hq % 32 == 0) {
+            // one wave per (token, 32 heads, split)
+            const int64_t units = (int64_t)bt.total_q * (Hq / 32) * pl.n_split;
+            if (units > 0x7fffffffLL)
+                return hipErrorInvalidValue;
+            const dim3 grid((unsigned)((units + 3) / 4));
+#define SA_LAUNCH_MQA(SH)                                                                                       \
+    hipLaunchKernelGGL((attn_mqa_kernel<128, SH>), grid, dim3(256), 0, st, bt, (const uint16_t *)q, Hq,           \
+                       (const uint16_t *)k_cache, (const uint16_t *)v_cache, row_stride, indices, k,              \
+                       (const uint16_t *)gate, per_channel, sl2, (uint16_t *)out, lse, part, pl.n_split, split_len, \
+                       (int)units)
+            if (mla)
+                SA_LAUNCH_MQA(true);
+            else
+                SA_LAUNCH_MQA(false);
+#undef SA_LAUNCH_MQA
+            e = hipGetLastError();
+        } else if (d_qk == 128 && d_v == 128 && !mla)
             e = launch_bf16<128, 128, false>(bt, pl, q, Hq, k_cache, v_cache, row_stride, indices, k, gate,
                                              per_channel, sl2, out, lse, part, split_len, st);
         else if (d_qk == 128 && d_v == 128 && mla)
