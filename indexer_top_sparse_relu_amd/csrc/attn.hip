@@ -1356,8 +1356,10 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const voi
     hipError_t e = hipErrorInvalidValue;
     if (dtype == 1) {
         const bool mla = (k_cache == v_cache) && d_v <= d_qk;
-        if (d_qk == 128 && d_v == 128 && Hq % 32 == 0) {
-            // one wave per (token, 32 heads, split)
+        if (d_qk == 128 && d_v == 128 && Hq % 32 == 0 && pl.n_split == 1) {
+            // one wave per (token, 32 heads); split lists (decode, few tokens) take
+            // attn_bf16_kernel, measured faster there (its workgroups hold 16*NW
+            // heads of a token, and each split is short)
             const int64_t units = (int64_t)bt.total_q * (Hq / 32) * pl.n_split;
             if (units > 0x7fffffffLL)
                 return hipErrorInvalidValue;

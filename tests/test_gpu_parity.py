@@ -291,14 +291,19 @@ def _sharpen_to_last_selected(wl, pl, gain):
         wl.q[t] = q.to(wl.q.dtype).unsqueeze(0).expand(spec.Hq, -1)
 
 
-@pytest.mark.parametrize("mode", ["prefill", "decode-split"])
+@pytest.mark.parametrize("mode", ["prefill", "decode-split", "mqa-prefill", "mqa-shared-prefill"])
 def test_latent_attention_logit_far_above_first_keys(mode):
-    """A logit ~70 nats above the first tile's: the latent kernel must rerun with the exact
-    maximum as its reference and still match the oracle."""
+    """A logit ~70 nats above the first tile's: the latent kernel (and the MQA kernel, with
+    separate or shared K/V rows) must rerun with the exact maximum as its reference and still
+    match the oracle."""
     if mode == "prefill":
         spec = W.chunked_prefill_mla(cached=3000, T=64).replace(seed=61)
-    else:
+    elif mode == "decode-split":
         spec = W.long_decode_mla(B=4, lo=5000, hi=9000, short_at=1).replace(seed=62)
+    else:
+        # 600 tokens x 32 heads: one wave per token, no split lists
+        spec = W.prefill_bf16().replace(q_lens=(600,), ctx_lens=(3000,), K=256, paged_random=True,
+                                        mla=(mode == "mqa-shared-prefill"), seed=63)
     P.say(f"[rerun-{mode}] T={spec.T} max_ctx={spec.max_ctx}")
     wl = W.generate(spec, DEV)
     pl = run(wl, stages=("indexer", "topk"))
