@@ -900,6 +900,197 @@ __global__ __launch_bounds__(256) void indexer_token_kernel(
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// Decode with 128-byte key rows (fp8 x 128, bf16 x 64, f32 x 32): the same
+// work split and epilogue as indexer_token_kernel, but each wave gathers its
+// 32-key tiles into its own LDS ring by direct loads that cover whole rows
+// (8 rows x 128 bytes per load instruction) and reads the MFMA operands from
+// there.  On gfx950 the address unit's cost grows with the cache lines one
+// load instruction touches: loading the operand layout directly (32 keys x 32
+// bytes per instruction) gathers about 2.5x slower.  The ring holds four
+// tiles (three in flight); the loads are issued from asm with exact vmcnt
+// waits, and keys past the chunk re-read its last key, so every tile issues
+// the same loads.  Chunk c of row r sits at position c ^ ((r >> 1) & 7): the
+// operand reads (32 rows of one chunk) hit distinct bank groups.
+template <int DT, int H, int D>
+__global__ __launch_bounds__(256) void indexer_token_lds_kernel(
+    Batch bt, const uint8_t *__restrict__ q_idx, const float *__restrict__ q_scale,
+    const float *__restrict__ w, const uint8_t *__restrict__ k_idx, const float *__restrict__ k_scale,
+    float *__restrict__ scores, int64_t ld, int key_chunk)
+{
+    typedef IdxT<DT> X;
+    constexpr int MT = (H + 31) / 32;
+    constexpr int RB = D * X::ELEM;
+    constexpr int NKS = D / X::KS;
+    constexpr bool FP8 = DT == 2;
+    constexpr int R = 4;                          // tiles in a wave's ring
+    constexpr int TBY = 32 * RB;                  // bytes of one 32-key tile
+    constexpr int NPT = TBY / 1024 + (FP8 ? 1 : 0);   // direct loads per tile per wave
+    static_assert(RB == 128, "128-byte key rows");
+    __shared__ __align__(16) uint8_t lkt[kIdxWaves * R * TBY];
+    __shared__ float lks[kIdxWaves * R * 64];
+    __shared__ int lpt[kIdxTokChunk / 16 + 2];
+
+    const int tok = blockIdx.y;
+    const int b = seq_of_token(bt, tok);
+    const int pos = pos_of_token(bt, b, tok);
+    const int kb0 = blockIdx.x * key_chunk;
+    const int kb1 = min(kb0 + key_chunk, pos + 1);
+    if (kb0 >= kb1)
+        return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = lane >> 5, col = lane & 31;
+
+    constexpr bool F16E = IdxEpi<DT>::F16 && H >= 8;
+    typename X::Op a[MT][NKS];
+    float wr[MT][F16E ? 1 : 16];
+    float wt[MT][F16E ? 16 : 1];
+    f16x2 wp[MT][F16E ? 8 : 1];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+        const int h = mt * 32 + col;
+        const bool ok = h < H;
+        const uint8_t *src = q_idx + ((int64_t)tok * H + (ok ? h : 0)) * RB;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            typename X::Op v = X::load(src + ks * X::KS * X::ELEM + half * X::LB);
+            a[mt][ks] = ok ? v : typename X::Op{};
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int ho = mt * 32 + mfma32_row(i, lane);
+            const float wv_ = ho < H ? w[(int64_t)tok * H + ho] : 0.0f;
+            if constexpr (F16E)
+                wt[mt][i] = wv_;
+            else
+                wr[mt][i] = wv_;
+        }
+    }
+    int wsh = 0;
+    if constexpr (F16E) {
+        float m = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                m = fmaxf(m, fabsf(wt[mt][i]));
+        wsh = f16_weight_shift(fmaxf(m, __shfl_xor(m, 32, 64)));
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                wp[mt][i >> 1][i & 1] = (_Float16)ldexpf(wt[mt][i], wsh);
+    }
+    const float qs = ldexpf((FP8 ? q_scale[tok] : 1.0f) * IdxEpi<DT>::UNSCALE, -wsh);
+
+    const int pshift = bt.page_shift, pmask = (1 << pshift) - 1;
+    const int pg0 = kb0 >> pshift;
+    {
+        const int npg = ((kb1 - 1) >> pshift) - pg0 + 1;
+        for (int i = tid; i < npg; i += 256)
+            lpt[i] = bt.page_table[(int64_t)b * bt.max_pages + pg0 + i];
+    }
+    __syncthreads();
+    // the operand loads of the prologue land before the loop (their registers
+    // are not waited on inside it, where the asm tile loads are in flight)
+    __builtin_amdgcn_s_waitcnt(0x0F70);         // vmcnt(0)
+
+    // this wave's tiles: t = wv, wv + 4, ...; local tile m is global tile wv + 4m
+    const int ntiles = (kb1 - kb0 + 31) / 32;
+    const int nm = (ntiles - wv + kIdxWaves - 1) / kIdxWaves;
+    lds_u8 *const ring = (lds_u8 *)lkt + wv * R * TBY;
+    lds_u8 *const ksr = (lds_u8 *)lks + wv * R * 64 * 4;
+    auto physical = [&](int s) -> int64_t {
+        return ((int64_t)lpt[(s >> pshift) - pg0] << pshift) + (s & pmask);
+    };
+    auto issue = [&](int m, int ln) {
+        const int t0 = kb0 + (wv + kIdxWaves * m) * 32;
+        lds_u8 *dst = ring + (m % R) * TBY;
+#pragma unroll
+        for (int j = 0; j < TBY / 1024; ++j) {
+            const int row = 8 * j + (ln >> 3);
+            const int s = min(t0 + row, kb1 - 1);
+            dma_b128(k_idx + physical(s) * RB + 16 * ((ln & 7) ^ ((row >> 1) & 7)), dst + j * 1024);
+        }
+        if constexpr (FP8) {
+            const int s = min(t0 + (ln & 31), kb1 - 1);
+            dma_b32(k_scale + physical(s), ksr + (m % R) * 256);
+        }
+    };
+    // B operand of k-step ks: bytes ks*KS*ELEM + half*LB .. +LB of key row col
+    const int f = (col >> 1) & 7;
+    auto bload = [&](int m, typename X::Op (&bo)[NKS]) {
+        const lds_u8 *row = ring + (m % R) * TBY + col * 128;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+            const int by = ks * X::KS * X::ELEM + half * X::LB;
+            if constexpr (X::LB == 32) {
+                const int c = by >> 4;
+                const i32x4 lo = *(const __attribute__((address_space(3))) i32x4 *)(row + 16 * (c ^ f));
+                const i32x4 hi = *(const __attribute__((address_space(3))) i32x4 *)(row + 16 * ((c + 1) ^ f));
+                bo[ks] = __builtin_bit_cast(typename X::Op, i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+            } else {
+                const int c = by >> 4;
+                bo[ks] = *(const __attribute__((address_space(3))) typename X::Op *)(row + 16 * (c ^ f) + (by & 15));
+            }
+        }
+    };
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)tok * ld, 0,
+                                                                         (int)(ld * 4), 0x00020000);
+#pragma unroll
+    for (int m = 0; m < R - 1; ++m)
+        issue(m, lane);
+    static_assert(R == 4, "wait counts below");
+    for (int m = 0; m < nm; ++m) {
+        // Tile m's loads were followed by those of tiles m+1 and m+2 and by the
+        // score stores of the iterations since (vmcnt counts stores too): none
+        // before iteration 1, then one, two, and from iteration 3 on three.
+        if (m == 0)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NPT) : "memory");
+        else if (m == 1)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NPT + 1) : "memory");
+        else if (m == 2)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NPT + 2) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * NPT + 3) : "memory");
+        const int ln = opaque(lane);
+        issue(m + R - 1, ln);           // into the buffer of tile m-1, read last iteration
+        typename X::Op bo[NKS];
+        bload(m, bo);
+        const float ksv = FP8 ? *(const __attribute__((address_space(3))) float *)(ksr + (m % R) * 256 + 4 * col)
+                              : 1.0f;
+        f32x16 c[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            c[mt] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                c[mt] = X::mma(a[mt][ks], bo[ks], c[mt]);
+        }
+        float acc = 0.0f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            if constexpr (F16E) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (mt * 32 + 8 * (j >> 1) < H)
+                        acc = relu_dot2(c[mt][2 * j], c[mt][2 * j + 1], wp[mt][j], acc);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (mt * 32 + 8 * (i >> 2) < H)
+                        acc = fmaf(wr[mt][i], fmaxf(c[mt][i], 0.0f), acc);
+            }
+        }
+        acc = sum_halves(acc);
+        const int s = kb0 + (wv + kIdxWaves * m) * 32 + col;
+        const uint32_t off = (half == 0 && s < kb1) ? (uint32_t)s * 4u : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc * qs * ksv), srs, off, 0, 0);
+    }
+    // the ring's last loads land before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
 // ------------------------------------------------------------------ launch
 template <int DT, int H, int D>
 static hipError_t launch_indexer_t(const Batch &bt, const void *q_idx, const float *q_scale, const float *w,
@@ -936,9 +1127,14 @@ static hipError_t launch_indexer_t(const Batch &bt, const void *q_idx, const flo
         const int n_chunks = (bt.max_ctx + key_chunk - 1) / key_chunk;
         if (bt.total_q > 65535 || ld * 4 >= (1LL << 31))
             return hipErrorInvalidValue;
-        hipLaunchKernelGGL((indexer_token_kernel<DT, H, D>), dim3(n_chunks, bt.total_q), dim3(256), 0, st, bt,
-                           (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx, k_scale, scores, ld,
-                           key_chunk);
+        if constexpr (D * IdxT<DT>::ELEM == 128)
+            hipLaunchKernelGGL((indexer_token_lds_kernel<DT, H, D>), dim3(n_chunks, bt.total_q), dim3(256), 0, st,
+                               bt, (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx, k_scale, scores, ld,
+                               key_chunk);
+        else
+            hipLaunchKernelGGL((indexer_token_kernel<DT, H, D>), dim3(n_chunks, bt.total_q), dim3(256), 0, st, bt,
+                               (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx, k_scale, scores, ld,
+                               key_chunk);
     }
     return hipGetLastError();
 }
