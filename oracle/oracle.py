@@ -53,7 +53,8 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        path = build()
+        # ORACLE_LIB names a prebuilt copy (the sanitizer run of the pins builds one)
+        path = os.environ.get("ORACLE_LIB") or build()
         L = ctypes.CDLL(path)
         vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
         L.orc_fp8_e4m3fn.restype = dbl
