@@ -375,9 +375,10 @@ def block_variant(wl, steps: int, stream, kb: int):
 def branch_fusion(wl, pl, steps: int, stream, window: int):
     """Branch fusion with a sliding-window local branch on the same workload, timed apart from the
     step: the sparse branch (the step's attention over its Top-K indices, ungated), the window
-    list, the local branch (the same attention over the last `window` positions, ungated) and the
-    fusion y = g * sparse + (1 - g) * local.  The indexer and Top-K are the step's and are not
-    repeated here."""
+    list, and the local branch (the same attention over the last `window` positions) with the
+    fusion y = g * sparse + (1 - g) * local formed in its epilogue.  The separate form (an
+    ungated local branch written out, then a mix pass over both outputs) is timed beside it.
+    The indexer and Top-K are the step's and are not repeated here."""
     import torch
 
     from indexer_top_sparse_relu_amd import binding as B
@@ -389,6 +390,7 @@ def branch_fusion(wl, pl, steps: int, stream, window: int):
     o_s = torch.empty((s.T, s.Hq, s.d_v), device="cuda", dtype=wl.q.dtype)
     o_l = torch.empty_like(o_s)
     y = torch.empty_like(o_s)
+    y2 = torch.empty_like(o_s)
     ws = {}
     for k in (s.K, window):
         n = B.sparse_gated_attn_workspace_size(bt, s.Hq, s.d_v, k)
@@ -402,6 +404,9 @@ def branch_fusion(wl, pl, steps: int, stream, window: int):
                                                         softmax_scale=s.softmax_scale, workspace=ws[window],
                                                         stream=stream),
         "fuse": lambda: B.sparse_branch_fuse(o_s, o_l, wl.gate, y, stream=stream),
+        "local_branch_fused": lambda: B.sparse_attn_fuse_fwd(bt, wl.q, wl.k_cache, wl.v_cache, s.d_v, win, wl.gate,
+                                                             o_s, y2, softmax_scale=s.softmax_scale,
+                                                             workspace=ws[window], stream=stream),
     }
     for fn in stages.values():
         fn()
@@ -424,6 +429,7 @@ def branch_fusion(wl, pl, steps: int, stream, window: int):
         "window": ("hbm", s.T * window * 4),
         "local_branch": ("mfma", 2.0 * s.Hq * n_local * (s.d_qk + s.d_v)),
         "fuse": ("hbm", s.T * (3 * s.Hq * s.d_v * ae + gate_elems * ae)),
+        "local_branch_fused": ("mfma", 2.0 * s.Hq * n_local * (s.d_qk + s.d_v)),
     }
     rl = {}
     for name, (kind, w) in work.items():
@@ -434,8 +440,9 @@ def branch_fusion(wl, pl, steps: int, stream, window: int):
             rl[name] = {"bound": "mfma", "achieved": w / t / 1e12, "peak": peak_mma, "unit": "TFLOP/s"}
         rl[name]["frac"] = rl[name]["achieved"] / rl[name]["peak"]
         rl[name]["ms"] = ms[name]
-    total = sum(ms.values())
-    return {"window": window, "ms_attention_and_fusion": total, "stages": rl}
+    fused = ms["sparse_branch"] + ms["window"] + ms["local_branch_fused"]
+    separate = ms["sparse_branch"] + ms["window"] + ms["local_branch"] + ms["fuse"]
+    return {"window": window, "ms_attention_and_fusion": fused, "ms_separate_mix_pass": separate, "stages": rl}
 
 
 def backward_pass(steps: int, stream):

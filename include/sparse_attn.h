@@ -308,6 +308,32 @@ sa_status sparse_branch_fuse(sa_dtype dtype, int64_t rows, int32_t d_v, const vo
                              const void *gate_logits, int32_t gate_per_channel, void *out, sa_stream_t stream);
 
 /*
+ * Branch fusion with the mix inside the attention epilogue ([SAD §3]
+ * pseudocode, y = g * sparse + (1 - g) * local; [SAD §4] branch fusion
+ * gating).  Attention of q over the index list (the local branch, e.g.
+ * positions from sparse_window_indices), then, where the output is formed,
+ *     out[i,h,c] = g * other[i,h,c] + (1 - g) * o[c],  g = sigmoid(G)
+ * with o the normalised attention in fp32 (it is not rounded before the mix)
+ * and G per channel or per head as in sparse_gated_attn_fwd.  `other` is the
+ * other branch's output [T, n_q_heads, d_v] in dtype, typically
+ * sparse_gated_attn_fwd of the sparse branch with a per-head gate of +inf
+ * (sigmoid 1: ungated); 16-byte aligned, and it must not overlap `out`
+ * (other NULL, unaligned or equal to out: SA_EINVAL).  This replaces the
+ * local branch's own output and sparse_branch_fuse: one pass fewer over three
+ * [T, H, d_v] tensors, and the local branch is not rounded before the mix.
+ * Shapes, workspace (sparse_gated_attn_workspace_size), lse (of the local
+ * branch) and the other errors as sparse_gated_attn_fwd.
+ */
+sa_status sparse_attn_fuse_fwd(const sa_batch *batch, sa_dtype dtype,
+                               const void *q, int32_t n_q_heads, int32_t d_qk,
+                               const void *k_cache, const void *v_cache, int32_t d_v,
+                               int64_t kv_row_stride,
+                               const int32_t *indices, int32_t k,
+                               const void *gate_logits, int32_t gate_per_channel,
+                               float softmax_scale, const void *other, void *out, float *lse,
+                               void *workspace, size_t workspace_bytes, sa_stream_t stream);
+
+/*
  * Cache append (the step before the path): writes the new tokens' rows into
  * the paged caches.  [HAT §5 item 2]: the cache organisation decides indexing
  * efficiency; [F2S "Engineering Considerations" item 1]: paged cache

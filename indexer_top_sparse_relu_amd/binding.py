@@ -24,7 +24,7 @@ EXPORTS = ("sparse_indexer_scores", "sparse_topk_workspace_size", "sparse_topk",
            "sparse_block_pool",
            "sparse_block_scores_workspace_size", "sparse_block_scores", "sparse_block_topk_workspace_size",
            "sparse_block_topk", "sparse_block_expand", "sparse_gated_attn_bwd", "sparse_window_indices",
-           "sparse_branch_fuse",
+           "sparse_branch_fuse", "sparse_attn_fuse_fwd",
            "sparse_cache_append",
            "sparse_quantize_fp8_rows", "sa_status_string", "sa_abi_version")
 
@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.sparse_gated_attn_fwd.restype = ctypes.c_int
         L.sparse_gated_attn_fwd.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp, i32,
                                             ctypes.c_float, vp, vp, vp, sz, vp]
+        L.sparse_attn_fuse_fwd.restype = ctypes.c_int
+        L.sparse_attn_fuse_fwd.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp, i32,
+                                           ctypes.c_float, vp, vp, vp, vp, sz, vp]
         L.sparse_gated_attn_fwd_noalloc.restype = ctypes.c_int
         L.sparse_gated_attn_fwd_noalloc.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp,
                                                     i32, ctypes.c_float, vp, vp, vp]
@@ -190,6 +193,23 @@ def sparse_gated_attn_fwd(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor
                                      _ptr(gate), per_channel, ctypes.c_float(scale), _ptr(out), _ptr(lse),
                                      _ptr(workspace), wsb, _stream(stream))
     _check("sparse_gated_attn_fwd", st)
+
+
+def sparse_attn_fuse_fwd(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, d_v: int,
+                         indices: torch.Tensor, gate: torch.Tensor, other: torch.Tensor, out: torch.Tensor,
+                         softmax_scale: Optional[float] = None, lse: Optional[torch.Tensor] = None,
+                         workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Attention over `indices` mixed with another branch's output in the epilogue:
+    out = sigmoid(G) * other + (1 - sigmoid(G)) * attention."""
+    T, Hq, dqk = q.shape
+    per_channel = 1 if gate.dim() == 3 else 0
+    scale = float(softmax_scale if softmax_scale is not None else dqk ** -0.5)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib().sparse_attn_fuse_fwd(ctypes.byref(batch), _DT[q.dtype], _ptr(q), Hq, dqk, _ptr(k_cache),
+                                    _ptr(v_cache), int(d_v), k_cache.stride(-2), _ptr(indices), indices.shape[1],
+                                    _ptr(gate), per_channel, ctypes.c_float(scale), _ptr(other), _ptr(out),
+                                    _ptr(lse), _ptr(workspace), wsb, _stream(stream))
+    _check("sparse_attn_fuse_fwd", st)
 
 
 def sparse_gated_attn_fwd_noalloc(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,

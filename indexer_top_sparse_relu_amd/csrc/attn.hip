@@ -62,12 +62,20 @@ typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 // bank span, so a plain modulo model does not predict it).
 __device__ __forceinline__ int swzf(int r) { return r & 7; }
 
+// The epilogue's output from the normalised attention x = o / l and the gate g:
+// the gated output x * g or, given the other branch's output a of a two-branch
+// layer, the branch mix g * a + (1 - g) * x = x + g * (a - x), in fp32.
+__device__ __forceinline__ float gated(float x, float g, const void *mix, float a)
+{
+    return mix ? fmaf(g, a - x, x) : x * g;
+}
+
 template <int DQK, int DV, bool MLA, int NW>
 __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
     Batch bt, const uint16_t *__restrict__ q, int Hq, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, int64_t rs, const int32_t *__restrict__ idx, int K,
     const uint16_t *__restrict__ gate, int per_channel, float scale_log2, uint16_t *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ part, int n_split, int split_len)
+    float *__restrict__ lse, float *__restrict__ part, int n_split, int split_len, const uint16_t *__restrict__ mix)
 {
     constexpr int NT = NW * 64;
     constexpr int NKQ = DQK / 32;           // MFMA steps over d_qk
@@ -283,16 +291,19 @@ __global__ __launch_bounds__(NW * 64) void attn_bf16_kernel(
             gh = sigmoidf_(bf16_bits_to_f32(gate[(int64_t)tok * Hq + h]));
         uint16_t *op = out + ((int64_t)tok * Hq + h) * DV + 4 * g;
         const uint16_t *gp = gate + ((int64_t)tok * Hq + h) * DV + 4 * g;
+        const uint16_t *ap = mix + ((int64_t)tok * Hq + h) * DV + 4 * g;
 #pragma unroll
         for (int mt = 0; mt < NMO; ++mt) {
             uint16_t r[4];
             uint2 gv = per_channel ? *(const uint2 *)(gp + 16 * mt) : uint2{0u, 0u};
+            uint2 av = mix ? *(const uint2 *)(ap + 16 * mt) : uint2{0u, 0u};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const uint32_t gw = i < 2 ? gv.x : gv.y;
                 const float gl = bf16_bits_to_f32((uint16_t)(gw >> (16 * (i & 1))));
                 const float gi = per_channel ? __builtin_amdgcn_rcpf(1.0f + __expf(-gl)) : gh;
-                r[i] = f32_to_bf16_bits(o[mt][i] * inv * gi);
+                const float a = bf16_bits_to_f32((uint16_t)((i < 2 ? av.x : av.y) >> (16 * (i & 1))));
+                r[i] = f32_to_bf16_bits(gated(o[mt][i] * inv, gi, mix, a));
             }
             *(uint2 *)(op + 16 * mt) = uint2{(uint32_t)r[0] | ((uint32_t)r[1] << 16),
                                             (uint32_t)r[2] | ((uint32_t)r[3] << 16)};
@@ -336,7 +347,8 @@ template <int DQK, int DV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_mla_kernel(
     Batch bt, const uint16_t *__restrict__ q, int Hq, const uint16_t *__restrict__ kc, int64_t rs,
     const int32_t *__restrict__ idx, int K, const uint16_t *__restrict__ gate, int per_channel, float scale_log2,
-    uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ part, int n_split, int split_len)
+    uint16_t *__restrict__ out, float *__restrict__ lse, float *__restrict__ part, int n_split, int split_len,
+    const uint16_t *__restrict__ mix)
 {
     constexpr int NW = 4;
     constexpr int NKQ = DQK / 16;           // MFMA k-steps over d_qk
@@ -652,66 +664,119 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         float gh = 0.0f;
         if (!per_channel)
             gh = sigmoidf_(bf16_bits_to_f32(gate[(int64_t)tok * Hq + h]));
-        // The wave's 32 output rows (heads wv*32 .. +31, DV bf16 each) are
-        // staged in LDS, row j at stg + j*ROWB: the gate rows arrive there by
-        // direct loads (contiguous in memory), each lane forms y = o/l * gate
-        // for its 4 x 4 x NDT elements in place, and whole rows leave with
-        // 16-byte stores.  Straight from the O^T layout every access would be
-        // 8 bytes per lane, 64 rows apart.
+        // The wave's 32 output rows (heads wv*32 .. +31, DV bf16 each) leave
+        // through LDS as whole rows (16-byte stores); straight from the O^T
+        // layout every access would be 8 bytes per lane, 64 rows apart.
         constexpr int ROWB = 2 * DV + 16;
         static_assert(4 * 32 * ROWB <= 4 * KCHUNKS * 16 && DV * 2 == 64 * 16, "output staging");
         lds_u8 *stg = (lds_u8 *)lkr + wv * 32 * ROWB;
         const int64_t row0 = (int64_t)tok * Hq + hg * (32 * NW) + wv * 32;
         __syncthreads();                        // every wave is done with the tile ring
-        if (per_channel) {
-            const uint16_t *gsrc = gate + row0 * DV + 8 * lane;
+        if (mix) {
+            // Branch mix: the other branch's rows are read as well, so the
+            // columns go in two halves.  Row j of the staging area holds the
+            // half's gate values (bytes 0..DV) and the other branch's (DV..2DV),
+            // both brought in by direct loads (lanes 0-31 and 32-63 of each
+            // load); y replaces the gate values in place and leaves as whole
+            // half rows.
+            constexpr int HALF = NDT / 2;
+            static_assert(NDT % 2 == 0, "halves");
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const uint16_t *src = (hq ? mix : gate) + row0 * DV + hf * (DV / 2) + 8 * col;
+                if (hq || per_channel) {
+#pragma unroll 8
+                    for (int j = 0; j < 32; ++j)
+                        dma_b128(src + j * DV, stg + j * ROWB);
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this half's rows are in LDS
+                lds_u8 *mh = stg + col * ROWB + 8 * hq;
+#pragma unroll
+                for (int dt = 0; dt < HALF; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        lds_u8 *p = mh + 2 * (32 * dt + 8 * g);
+                        const u32x2 av = *(const lds_u32x2 *)(p + DV);
+                        const u32x2 w = per_channel ? *(const lds_u32x2 *)p : u32x2{0u, 0u};
+                        float y[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int sh = 16 * (i & 1);
+                            float gi = gh;
+                            if (per_channel)
+                                gi = __builtin_amdgcn_rcpf(
+                                    1.0f + __expf(-bf16_bits_to_f32((uint16_t)((i < 2 ? w.x : w.y) >> sh))));
+                            const float a = bf16_bits_to_f32((uint16_t)((i < 2 ? av.x : av.y) >> sh));
+                            y[i] = gated(oa[HALF * hf + dt][4 * g + i] * inv, gi, mix, a);
+                            probe = fmaf(y[i], 0.0f, probe);
+                        }
+                        const bf16x2 lo = {(__bf16)y[0], (__bf16)y[1]}, hi = {(__bf16)y[2], (__bf16)y[3]};
+                        *(lds_u32x2 *)p = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+                    }
+                __builtin_amdgcn_wave_barrier();
+                // two half rows per store instruction
+                uint16_t *oh = out + row0 * DV + hf * (DV / 2) + 8 * col;
+#pragma unroll 8
+                for (int j = 0; j < 32; j += 2)
+                    *(u32x4 *)(oh + (j + hq) * DV) = *(const lds_u32x4 *)(stg + (j + hq) * ROWB + 16 * col);
+                // the stores' reads of the staging area are done before the
+                // next half's loads land there
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            }
+        } else {
+            // row j at stg + j*ROWB: the gate rows arrive there by direct loads
+            // (contiguous in memory), each lane forms y = o/l * gate for its
+            // 4 x 4 x NDT elements in place, and whole rows leave
+            if (per_channel) {
+                const uint16_t *gsrc = gate + row0 * DV + 8 * lane;
+#pragma unroll 8
+                for (int j = 0; j < 32; ++j)
+                    dma_b128(gsrc + j * DV, stg + j * ROWB);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // the gate rows are in LDS
+            lds_u8 *mine = stg + col * ROWB + 8 * hq;
+            auto put4 = [&](int dt, int g, const float (&gi)[4]) {
+                float y[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // (inv * gate first: with o * inv shared by both gate forms the
+                    // compiler would compute all of them up front)
+                    y[i] = oa[dt][4 * g + i] * (inv * gi[i]);
+                    probe = fmaf(y[i], 0.0f, probe);
+                }
+                // bf16 round-to-nearest-even, two values per convert instruction
+                const bf16x2 lo = {(__bf16)y[0], (__bf16)y[1]}, hi = {(__bf16)y[2], (__bf16)y[3]};
+                *(lds_u32x2 *)(mine + 2 * (32 * dt + 8 * g)) =
+                    u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+            };
+            if (per_channel) {
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const u32x2 w = *(const lds_u32x2 *)(mine + 2 * (32 * dt + 8 * g));
+                        float gi[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float x = bf16_bits_to_f32((uint16_t)((i < 2 ? w.x : w.y) >> (16 * (i & 1))));
+                            gi[i] = __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+                        }
+                        put4(dt, g, gi);
+                    }
+            } else {
+                const float gi[4] = {gh, gh, gh, gh};
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+                        put4(dt, g, gi);
+            }
+            __builtin_amdgcn_wave_barrier();
+            uint16_t *orow = out + row0 * DV + 8 * lane;
 #pragma unroll 8
             for (int j = 0; j < 32; ++j)
-                dma_b128(gsrc + j * DV, stg + j * ROWB);
+                *(u32x4 *)(orow + j * DV) = *(const lds_u32x4 *)(stg + j * ROWB + 16 * lane);
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);     // vmcnt(0): the gate rows are in LDS
-        lds_u8 *mine = stg + col * ROWB + 8 * hq;
-        auto put4 = [&](int dt, int g, const float (&gi)[4]) {
-            float y[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                // (inv * gate first: with o * inv shared by both gate forms the
-                // compiler would compute all of them up front)
-                y[i] = oa[dt][4 * g + i] * (inv * gi[i]);
-                probe = fmaf(y[i], 0.0f, probe);
-            }
-            // bf16 round-to-nearest-even, two values per convert instruction
-            const bf16x2 lo = {(__bf16)y[0], (__bf16)y[1]}, hi = {(__bf16)y[2], (__bf16)y[3]};
-            *(lds_u32x2 *)(mine + 2 * (32 * dt + 8 * g)) =
-                u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
-        };
-        if (per_channel) {
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const u32x2 w = *(const lds_u32x2 *)(mine + 2 * (32 * dt + 8 * g));
-                    float gi[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float x = bf16_bits_to_f32((uint16_t)((i < 2 ? w.x : w.y) >> (16 * (i & 1))));
-                        gi[i] = __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-                    }
-                    put4(dt, g, gi);
-                }
-        } else {
-            const float gi[4] = {gh, gh, gh, gh};
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    put4(dt, g, gi);
-        }
-        __builtin_amdgcn_wave_barrier();
-        uint16_t *orow = out + row0 * DV + 8 * lane;
-#pragma unroll 8
-        for (int j = 0; j < 32; ++j)
-            *(u32x4 *)(orow + j * DV) = *(const lds_u32x4 *)(stg + j * ROWB + 16 * lane);
         if (lse && hq == 0)
             lse[(int64_t)tok * Hq + h] = l_tot > 0.0f ? m_ref * kLn2 + __logf(l_tot) : -INFINITY;
     } else {
@@ -777,7 +842,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     Batch bt, const uint16_t *__restrict__ q, int Hq, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, int64_t rs, const int32_t *__restrict__ idx, int K,
     const uint16_t *__restrict__ gate, int per_channel, float scale_log2, uint16_t *__restrict__ out,
-    float *__restrict__ lse, float *__restrict__ part, int n_split, int split_len, int n_units)
+    float *__restrict__ lse, float *__restrict__ part, int n_split, int split_len, int n_units,
+    const uint16_t *__restrict__ mix)
 {
     constexpr int NW = 4;
     constexpr int NKQ = D / 16;             // S-chain k-steps
@@ -1065,6 +1131,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (n_split == 1) {
             const float inv = l_tot > 0.0f ? 1.0f / l_tot : 0.0f;
             const int64_t orow = ((int64_t)tok * Hq + h) * D;
+            u32x2 aw[NDT][4];           // the other branch's output (branch mix only)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    aw[dt][g] = mix ? *(const u32x2 *)(mix + orow + 32 * dt + 8 * g + 4 * hq) : u32x2{0u, 0u};
+            auto a_of = [&](int dt, int g, int i) {
+                return bf16_bits_to_f32((uint16_t)((i < 2 ? aw[dt][g].x : aw[dt][g].y) >> (16 * (i & 1))));
+            };
             if (per_channel) {
                 u32x2 gw[NDT][4];
 #pragma unroll
@@ -1081,7 +1156,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         for (int i = 0; i < 4; ++i) {
                             const uint32_t w = i < 2 ? gw[dt][g].x : gw[dt][g].y;
                             const float x = bf16_bits_to_f32((uint16_t)(w >> (16 * (i & 1))));
-                            y[i] = oa[dt][4 * g + i] * (inv * __builtin_amdgcn_rcpf(1.0f + __expf(-x)));
+                            const float gi = __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+                            y[i] = gated(oa[dt][4 * g + i] * inv, gi, mix, a_of(dt, g, i));
                             probe = fmaf(y[i], 0.0f, probe);
                         }
                         const bf16x2 lo = {(__bf16)y[0], (__bf16)y[1]}, hi = {(__bf16)y[2], (__bf16)y[3]};
@@ -1089,7 +1165,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                             u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
                     }
             } else {
-                const float gi = inv * sigmoidf_(bf16_bits_to_f32(gate[(int64_t)tok * Hq + h]));
+                const float gi = sigmoidf_(bf16_bits_to_f32(gate[(int64_t)tok * Hq + h]));
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -1097,7 +1173,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         float y[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            y[i] = oa[dt][4 * g + i] * gi;
+                            y[i] = gated(oa[dt][4 * g + i] * inv, gi, mix, a_of(dt, g, i));
                             probe = fmaf(y[i], 0.0f, probe);
                         }
                         const bf16x2 lo = {(__bf16)y[0], (__bf16)y[1]}, hi = {(__bf16)y[2], (__bf16)y[3]};
@@ -1144,7 +1220,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 // Merge split partials by log-sum-exp, then gate; one block per (token, head).
 __global__ __launch_bounds__(128) void attn_combine_kernel(int Hq, int DV, int n_split, const float *__restrict__ part,
                                                           const void *__restrict__ gate, int per_channel, int is_bf16,
-                                                          void *__restrict__ out, float *__restrict__ lse)
+                                                          void *__restrict__ out, float *__restrict__ lse,
+                                                          const void *__restrict__ mix)
 {
     const int tok = blockIdx.x, h = blockIdx.y;
     const float *pp = part + ((int64_t)tok * n_split * Hq + h) * (DV + 4);
@@ -1182,7 +1259,10 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(int Hq, int DV, int n
             gl = bf16_bits_to_f32(((const uint16_t *)gate)[gi]);
         else
             gl = ((const float *)gate)[gi];
-        const float y = acc * inv * sigmoidf_(gl);
+        float a = 0.0f;
+        if (mix)
+            a = is_bf16 ? bf16_bits_to_f32(((const uint16_t *)mix)[ob + c]) : ((const float *)mix)[ob + c];
+        const float y = gated(acc * inv, sigmoidf_(gl), mix, a);
         if (is_bf16)
             ((uint16_t *)out)[ob + c] = f32_to_bf16_bits(y);
         else
@@ -1201,7 +1281,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Batch bt, const float *__r
                                                       const float *__restrict__ gate, int per_channel,
                                                       float scale_log2, float *__restrict__ out,
                                                       float *__restrict__ lse, float *__restrict__ part,
-                                                      int n_split, int split_len)
+                                                      int n_split, int split_len, const float *__restrict__ mix)
 {
     constexpr int PER = (D + 63) / 64;
     const int tok = blockIdx.x, h = blockIdx.y, sp = blockIdx.z, lane = threadIdx.x;
@@ -1254,7 +1334,8 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(Batch bt, const float *__r
             const int c = lane + 64 * u;
             if (c < D) {
                 const float gl = per_channel ? gate[((int64_t)tok * Hq + h) * D + c] : gate[(int64_t)tok * Hq + h];
-                out[((int64_t)tok * Hq + h) * D + c] = o[u] * inv * sigmoidf_(gl);
+                const int64_t oi = ((int64_t)tok * Hq + h) * D + c;
+                out[oi] = gated(o[u] * inv, sigmoidf_(gl), mix, mix ? mix[oi] : 0.0f);
             }
         }
         if (lse && lane == 0)
@@ -1325,14 +1406,15 @@ AttnPlan attn_plan(int total_q, int Hq, int d_v, int k)
 template <int DQK, int DV, bool MLA>
 static hipError_t launch_bf16(const Batch &bt, const AttnPlan &pl, const void *q, int Hq, const void *kc,
                               const void *vc, int64_t rs, const int32_t *idx, int K, const void *gate, int pc,
-                              float sl2, void *out, float *lse, float *part, int split_len, hipStream_t st)
+                              float sl2, void *out, float *lse, float *part, int split_len, const void *mix,
+                              hipStream_t st)
 {
     const int nw = bf16_waves(Hq);
     const dim3 grid(bt.total_q, Hq / (16 * nw), pl.n_split);
 #define SA_LAUNCH_NW(NW)                                                                                        \
     hipLaunchKernelGGL((attn_bf16_kernel<DQK, DV, MLA, NW>), grid, dim3(NW * 64), 0, st, bt, (const uint16_t *)q, \
                        Hq, (const uint16_t *)kc, (const uint16_t *)vc, rs, idx, K, (const uint16_t *)gate, pc, sl2, \
-                       (uint16_t *)out, lse, part, pl.n_split, split_len)
+                       (uint16_t *)out, lse, part, pl.n_split, split_len, (const uint16_t *)(pl.n_split == 1 ? mix : nullptr))
     switch (nw) {
     case 8: SA_LAUNCH_NW(8); break;
     case 4: SA_LAUNCH_NW(4); break;
@@ -1346,13 +1428,16 @@ static hipError_t launch_bf16(const Batch &bt, const AttnPlan &pl, const void *q
 hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const void *q, int Hq, int d_qk,
                        const void *k_cache, const void *v_cache, int d_v, int64_t row_stride,
                        const int32_t *indices, int k, const void *gate, int per_channel, float scale, void *out,
-                       float *lse, void *ws, hipStream_t st)
+                       float *lse, void *ws, hipStream_t st, const void *mix)
 {
     if (bt.total_q > 0x7fffffff || pl.n_split > 65535)
         return hipErrorInvalidValue;
     const float sl2 = scale * kLog2e;
     const int split_len = (k + pl.n_split - 1) / pl.n_split;
     float *part = (float *)ws;
+    // the branch mix is applied where the output is formed: by the attention
+    // kernel itself, or by the combine kernel when the list is split
+    const void *kmix = pl.n_split == 1 ? mix : nullptr;
     hipError_t e = hipErrorInvalidValue;
     if (dtype == 1) {
         const bool mla = (k_cache == v_cache) && d_v <= d_qk;
@@ -1368,7 +1453,7 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const voi
     hipLaunchKernelGGL((attn_mqa_kernel<128, SH>), grid, dim3(256), 0, st, bt, (const uint16_t *)q, Hq,           \
                        (const uint16_t *)k_cache, (const uint16_t *)v_cache, row_stride, indices, k,              \
                        (const uint16_t *)gate, per_channel, sl2, (uint16_t *)out, lse, part, pl.n_split, split_len, \
-                       (int)units)
+                       (int)units, (const uint16_t *)kmix)
             if (mla)
                 SA_LAUNCH_MQA(true);
             else
@@ -1377,25 +1462,25 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const voi
             e = hipGetLastError();
         } else if (d_qk == 128 && d_v == 128 && !mla)
             e = launch_bf16<128, 128, false>(bt, pl, q, Hq, k_cache, v_cache, row_stride, indices, k, gate,
-                                             per_channel, sl2, out, lse, part, split_len, st);
+                                             per_channel, sl2, out, lse, part, split_len, mix, st);
         else if (d_qk == 128 && d_v == 128 && mla)
             e = launch_bf16<128, 128, true>(bt, pl, q, Hq, k_cache, v_cache, row_stride, indices, k, gate,
-                                            per_channel, sl2, out, lse, part, split_len, st);
+                                            per_channel, sl2, out, lse, part, split_len, mix, st);
         else if (d_qk == 576 && d_v == 512 && mla && Hq % 128 == 0) {
             hipLaunchKernelGGL((attn_mla_kernel<576, 512>), dim3(bt.total_q, Hq / 128, pl.n_split), dim3(256), 0, st,
                                bt, (const uint16_t *)q, Hq, (const uint16_t *)k_cache, row_stride, indices, k,
                                (const uint16_t *)gate, per_channel, sl2, (uint16_t *)out, lse, part, pl.n_split,
-                               split_len);
+                               split_len, (const uint16_t *)kmix);
             e = hipGetLastError();
         } else if (d_qk == 576 && d_v == 512 && mla)
             e = launch_bf16<576, 512, true>(bt, pl, q, Hq, k_cache, v_cache, row_stride, indices, k, gate,
-                                            per_channel, sl2, out, lse, part, split_len, st);
+                                            per_channel, sl2, out, lse, part, split_len, mix, st);
     } else if (dtype == 0) {
         const dim3 grid(bt.total_q, Hq, pl.n_split);
 #define SA_LAUNCH_F32(D)                                                                                         \
     hipLaunchKernelGGL((attn_f32_kernel<D>), grid, dim3(64), 0, st, bt, (const float *)q, Hq,                     \
                        (const float *)k_cache, (const float *)v_cache, row_stride, indices, k, (const float *)gate, \
-                       per_channel, sl2, (float *)out, lse, part, pl.n_split, split_len)
+                       per_channel, sl2, (float *)out, lse, part, pl.n_split, split_len, (const float *)kmix)
         if (d_qk == 32) SA_LAUNCH_F32(32);
         else if (d_qk == 64) SA_LAUNCH_F32(64);
         else SA_LAUNCH_F32(128);
@@ -1407,7 +1492,7 @@ hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &pl, const voi
     if (pl.n_split > kMaxCombine)
         return hipErrorInvalidValue;
     hipLaunchKernelGGL(attn_combine_kernel, dim3(bt.total_q, Hq), dim3(128), 0, st, Hq, d_v, pl.n_split,
-                       part, gate, per_channel, dtype == 1 ? 1 : 0, out, lse);
+                       part, gate, per_channel, dtype == 1 ? 1 : 0, out, lse, mix);
     return hipGetLastError();
 }
 

@@ -162,7 +162,8 @@ static sa_status attn_fwd_checked(const sa_batch *batch, sa_dtype dtype, const v
                                   int32_t d_qk, const void *k_cache, const void *v_cache, int32_t d_v,
                                   int64_t kv_row_stride, const int32_t *indices, int32_t k, const void *gate_logits,
                                   int32_t gate_per_channel, float softmax_scale, void *out, float *lse,
-                                  void *workspace, size_t workspace_bytes, bool static_scratch, sa_stream_t stream)
+                                  void *workspace, size_t workspace_bytes, bool static_scratch, sa_stream_t stream,
+                                  const void *mix = nullptr)
 {
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
@@ -184,6 +185,8 @@ static sa_status attn_fwd_checked(const sa_batch *batch, sa_dtype dtype, const v
         return SA_EINVAL;
     if (k_cache == v_cache && d_v > d_qk)
         return SA_EINVAL;
+    if (mix && (!aligned16(mix) || mix == out))
+        return SA_EINVAL;
     if (!sa::attn_supported((int)dtype, n_q_heads, d_qk, d_v) ||
         !sa::attn_supported_layout((int)dtype, d_qk, d_v, k_cache == v_cache))
         return SA_EUNSUPPORTED;
@@ -201,7 +204,7 @@ static sa_status attn_fwd_checked(const sa_batch *batch, sa_dtype dtype, const v
     }
     return launched(sa::launch_attn((int)dtype, bt, plan, q, n_q_heads, d_qk, k_cache, v_cache, d_v, kv_row_stride,
                                     indices, k, gate_logits, gate_per_channel ? 1 : 0, softmax_scale, out, lse,
-                                    workspace, (hipStream_t)stream));
+                                    workspace, (hipStream_t)stream, mix));
 }
 
 sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
@@ -213,6 +216,19 @@ sa_status sparse_gated_attn_fwd(const sa_batch *batch, sa_dtype dtype, const voi
     return attn_fwd_checked(batch, dtype, q, n_q_heads, d_qk, k_cache, v_cache, d_v, kv_row_stride, indices, k,
                             gate_logits, gate_per_channel, softmax_scale, out, lse, workspace, workspace_bytes,
                             false, stream);
+}
+
+sa_status sparse_attn_fuse_fwd(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads, int32_t d_qk,
+                               const void *k_cache, const void *v_cache, int32_t d_v, int64_t kv_row_stride,
+                               const int32_t *indices, int32_t k, const void *gate_logits, int32_t gate_per_channel,
+                               float softmax_scale, const void *other, void *out, float *lse, void *workspace,
+                               size_t workspace_bytes, sa_stream_t stream)
+{
+    if (!other)
+        return SA_EINVAL;
+    return attn_fwd_checked(batch, dtype, q, n_q_heads, d_qk, k_cache, v_cache, d_v, kv_row_stride, indices, k,
+                            gate_logits, gate_per_channel, softmax_scale, out, lse, workspace, workspace_bytes,
+                            false, stream, other);
 }
 
 sa_status sparse_gated_attn_fwd_noalloc(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,

@@ -40,7 +40,7 @@ int attn_supported_layout(int dtype, int d_qk, int d_v, int aliased);
 hipError_t launch_attn(int dtype, const Batch &bt, const AttnPlan &plan, const void *q, int Hq, int d_qk,
                        const void *k_cache, const void *v_cache, int d_v, int64_t row_stride,
                        const int32_t *indices, int k, const void *gate, int per_channel, float scale,
-                       void *out, float *lse, void *ws, hipStream_t st);
+                       void *out, float *lse, void *ws, hipStream_t st, const void *mix = nullptr);
 
 // block-level selection
 hipError_t launch_block_pool(const Batch &bt, int dtype, const void *k_cache, int d_qk, int64_t row_stride,

@@ -197,6 +197,20 @@ def fused_floor(inp, fa, fb, a_abs, b_abs, rows=None):
     return O.branch_fuse(inp, fa + u_o * a_abs, fb + u_o * b_abs, rows)
 
 
+def epilogue_mix_floor(inp, fb, a, b_abs, rows=None):
+    """Error floor of y = g a + (1 - g) o with the mix formed where the attention output
+    is: `a` is an input (exact), o the unrounded attention (floor fb, |o| <= b_abs).  The
+    attention's floor enters with weight 1 - g; the fp32 mix adds the sigmoid's error (its
+    exponential's argument G log2(e) is rounded once, the rest a few ulps: (|G| + 4) u32
+    relative) times |a - o|, and the subtraction and fused multiply-add, a few u32 of
+    |a| + |o| more.  The rounding of y itself sits inside rtol |r|."""
+    rows = np.arange(inp.T) if rows is None else np.asarray(rows)
+    shape = (inp.T, inp.Hq, inp.d_v if inp.gate_per_channel else 1)
+    gl = np.abs(_decode(inp.gate, inp.attn_dtype).reshape(shape)[rows])
+    fmix = (gl + 8.0) * U_F32 * (np.abs(a) + b_abs)
+    return O.branch_fuse(inp, np.zeros_like(fb), fb, rows) + fmix
+
+
 # --------------------------------------------------------- host marshalling
 
 def to_np(t: torch.Tensor) -> np.ndarray:

@@ -182,3 +182,21 @@ def test_noalloc_attention_rejects_batches_beyond_its_scratch(B):
     e = batch(B, total_q=0, max_q=0)
     assert L.sparse_gated_attn_fwd_noalloc(ctypes.byref(e), 1, None, 128, 576, None, None, 512, 576, None, 2048, None,
                                            1, f, None, None, None) == B.SA_OK
+
+
+def test_fused_mix_entry_point_checks_the_other_branch(B):
+    """sparse_attn_fuse_fwd: the other branch's output is required, 16-byte aligned and not the
+    output itself; the rest of its checks are those of sparse_gated_attn_fwd."""
+    L = B.lib()
+    f = ctypes.c_float(1.0 / 24)
+    OUT = ctypes.c_void_p(0x20000)
+
+    def call(other, out=OUT, H=128, gate=FAKE):
+        return L.sparse_attn_fuse_fwd(ctypes.byref(batch(B)), 1, FAKE, H, 576, FAKE, FAKE, 512, 576, FAKE, 2048,
+                                      gate, 1, f, other, out, None, FAKE, 1 << 30, None)
+
+    assert call(None) == B.SA_EINVAL
+    assert call(OUT) == B.SA_EINVAL
+    assert call(ctypes.c_void_p(0x30008)) == B.SA_EINVAL
+    assert call(ctypes.c_void_p(0x30000), gate=None) == B.SA_EINVAL
+    assert call(ctypes.c_void_p(0x30000), H=24) == B.SA_EUNSUPPORTED

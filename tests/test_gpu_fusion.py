@@ -4,7 +4,10 @@ The sparse branch runs over the GPU's own Top-K indices (as the other parity
 tests do), the local branch over the window positions (checked bit-exact
 against the oracle's), both ungated through a per-head gate of +inf; the fused
 output is compared with the oracle's double-precision fusion of its own branch
-outputs on the same index sets.
+outputs on the same index sets.  Both forms of the fusion are checked: the
+separate mix pass over the two branch outputs, and the local branch's attention
+with the mix in its epilogue (the sparse branch's output read there, the local
+branch's never rounded).
 """
 import numpy as np
 import pytest
@@ -43,20 +46,26 @@ def run_fused(wl, w):
         outs.append(o)
     y = torch.full_like(outs[0], float("nan"))
     B.sparse_branch_fuse(outs[0], outs[1], wl.gate, y)
+    y2 = torch.full_like(outs[0], float("nan"))
+    lse2 = torch.full((s.T, s.Hq), float("nan"), device=DEV)
+    aw = B.sparse_gated_attn_workspace_size(bt, s.Hq, s.d_v, w)
+    aws = torch.empty(aw, dtype=torch.uint8, device=DEV) if aw else None
+    B.sparse_attn_fuse_fwd(bt, wl.q, wl.k_cache, wl.v_cache, s.d_v, win, wl.gate, outs[0], y2,
+                           softmax_scale=s.softmax_scale, lse=lse2, workspace=aws)
     torch.cuda.synchronize()
-    return pl.indices.cpu().numpy(), win.cpu().numpy(), outs, y
+    return pl.indices.cpu().numpy(), win.cpu().numpy(), outs, y, y2, lse2.cpu().numpy()
 
 
 def check_fused(spec, w, tag, rows=None):
     P.say(f"[{tag}] {spec.name} T={spec.T} B={spec.B} window={w}")
     wl = W.generate(spec, DEV)
-    idx, win, (o_s, o_l), y = run_fused(wl, w)
+    idx, win, (o_s, o_l), y, y2, lse2 = run_fused(wl, w)
     inp = O.Inputs.from_workload(wl)
     rows = np.arange(spec.T) if rows is None else np.asarray(rows)
     assert np.array_equal(win, O.window_indices(inp, w)), "window positions"
     u = O.ungated(inp)
     a = O.sparse_attn(u, idx[rows], rows, spec.softmax_scale)
-    b = O.sparse_attn(u, win[rows], rows, spec.softmax_scale)
+    b, b_lse = O.sparse_attn(u, win[rows], rows, spec.softmax_scale, with_lse=True)
     tol = P.RTOL[spec.attn_dtype]
     fa = P.attn_floor(u, idx[rows], rows, spec.softmax_scale)
     fb = P.attn_floor(u, win[rows], rows, spec.softmax_scale)
@@ -66,9 +75,12 @@ def check_fused(spec, w, tag, rows=None):
     # the fusion's floor: both branches' floors plus their rounding to the output type
     a_abs = P.attn_abs(u, idx[rows], rows, spec.softmax_scale)
     b_abs = P.attn_abs(u, win[rows], rows, spec.softmax_scale)
-    worst = P.check_attn(y.float().cpu().numpy()[rows], ref, tol, P.fused_floor(inp, fa, fb, a_abs, b_abs, rows),
-                         "fused output")
-    P.say(f"[{tag}] ok: worst fused rel {worst:.2e}")
+    ff = P.fused_floor(inp, fa, fb, a_abs, b_abs, rows)
+    worst = P.check_attn(y.float().cpu().numpy()[rows], ref, tol, ff, "fused output")
+    # the epilogue mix rounds one branch fewer, so the same floor bounds it
+    worst2 = P.check_attn(y2.float().cpu().numpy()[rows], ref, tol, ff, "fused in the epilogue")
+    assert P.close(lse2[rows], b_lse, tol).all(), "local branch lse"
+    P.say(f"[{tag}] ok: worst {worst:.2f} (mix pass), {worst2:.2f} (epilogue mix) of the bound")
 
 
 def test_fusion_latent_prefill_per_channel_gate():

@@ -99,6 +99,40 @@ def test_attention_shape(dt, dqk, dv, mla, hq, mode):
 
 
 @pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("dt,dqk,dv,mla,hq", ATTN_SHAPES,
+                         ids=[f"{a}-{b}x{c}-{'shared' if d else 'sep'}-h{e}" for a, b, c, d, e in ATTN_SHAPES])
+def test_epilogue_mix_shape(dt, dqk, dv, mla, hq, mode):
+    """The branch mix formed in the attention epilogue, for every kernel instance: the
+    attention kernel itself mixes when the list is whole, the combine kernel when it is
+    split.  The other branch's output is random data of the output type."""
+    spec = _base(mode, seed=400 + hq + dqk).replace(attn_dtype=dt, d_qk=dqk, d_v=dv, mla=mla, Hq=hq,
+                                                  gate_per_channel=(hq % 2 == 1), name=f"mix-{dt}-{dqk}")
+    P.say(f"[mix {dt} {dqk}/{dv} {'shared' if mla else 'separate'} h{hq} {mode}] T={spec.T}")
+    wl = W.generate(spec, DEV)
+    pl = B.Pipeline(wl)
+    pl.indexer()
+    pl.topk()
+    g = torch.Generator(device=DEV).manual_seed(spec.seed)
+    other = (torch.randn((spec.T, hq, dv), device=DEV, generator=g) * 0.05).to(wl.q.dtype)
+    y = torch.full_like(other, float("nan"))
+    lse = torch.full((spec.T, hq), float("nan"), device=DEV)
+    B.sparse_attn_fuse_fwd(pl.batch, wl.q, wl.k_cache, wl.v_cache, dv, pl.indices, wl.gate, other, y,
+                           softmax_scale=spec.softmax_scale, lse=lse, workspace=pl.attn_ws)
+    torch.cuda.synchronize()
+    inp = O.Inputs.from_workload(wl)
+    idx = pl.indices.cpu().numpy()
+    u = O.ungated(inp)
+    o, o_lse = O.sparse_attn(u, idx, None, spec.softmax_scale, with_lse=True)
+    a = other.float().cpu().numpy()
+    ref = O.branch_fuse(inp, a, o)
+    fb = P.attn_floor(u, idx, None, spec.softmax_scale)
+    floor = P.epilogue_mix_floor(inp, fb, a, P.attn_abs(u, idx, None, spec.softmax_scale))
+    w = P.check_attn(y.float().cpu().numpy(), ref, P.RTOL[dt], floor, "epilogue mix")
+    assert P.close(lse.cpu().numpy(), o_lse, P.RTOL[dt]).all(), "lse"
+    P.say(f"[mix {dt} {dqk}/{dv} h{hq} {mode}] ok: worst {w:.2f} of the bound")
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
 @pytest.mark.parametrize("h", [8, 64])
 def test_fp8_indexer_weight_range(h, mode):
     """Weights far from 1: per-token factors from 1e-9 to 1e9 and, within a token, heads
