@@ -469,10 +469,13 @@ def backward_pass(steps: int, stream):
     dv = dk if shared else torch.zeros_like(dk)
     dq = torch.empty(wl.q.shape, device="cuda")
     dg = torch.empty(wl.gate.shape, device="cuda")
+    nws = B.sparse_gated_attn_bwd_workspace_size(pl.batch, spec.Hq, spec.d_qk, spec.d_v, spec.K)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
 
     def bwd():
         B.sparse_gated_attn_bwd(pl.batch, wl.q, wl.k_cache, wl.v_cache, spec.d_v, pl.indices, wl.gate, pl.out,
-                                pl.lse, dy, dq, dk, dv, dg, softmax_scale=spec.softmax_scale, stream=stream)
+                                pl.lse, dy, dq, dk, dv, dg, softmax_scale=spec.softmax_scale, workspace=ws,
+                                stream=stream)
 
     bwd()
     torch.cuda.synchronize()
@@ -488,7 +491,7 @@ def backward_pass(steps: int, stream):
     flops = 2.0 * spec.Hq * n_valid * (3 * spec.d_qk + 2 * spec.d_v)     # S, dq, dK over d_qk; dP, dV over d_v
     ach = flops / (ms * 1e-3) / 1e12
     return {"workload": spec.name, "ms": ms, "query_tokens_per_s": spec.T / (ms * 1e-3),
-            "atomic_adds": n_valid * (spec.d_qk + spec.d_v),
+            "workspace_bytes": nws,
             "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK["bf16_TFLOPs"], "unit": "TFLOP/s",
                          "frac": ach / PEAK["bf16_TFLOPs"]}}
 

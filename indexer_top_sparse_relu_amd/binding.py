@@ -23,7 +23,8 @@ EXPORTS = ("sparse_indexer_scores", "sparse_topk_workspace_size", "sparse_topk",
            "sparse_gated_attn_workspace_size", "sparse_gated_attn_fwd", "sparse_gated_attn_fwd_noalloc",
            "sparse_block_pool",
            "sparse_block_scores_workspace_size", "sparse_block_scores", "sparse_block_topk_workspace_size",
-           "sparse_block_topk", "sparse_block_expand", "sparse_gated_attn_bwd", "sparse_window_indices",
+           "sparse_block_topk", "sparse_block_expand", "sparse_gated_attn_bwd_workspace_size",
+           "sparse_gated_attn_bwd", "sparse_window_indices",
            "sparse_branch_fuse", "sparse_attn_fuse_fwd",
            "sparse_cache_append",
            "sparse_quantize_fp8_rows", "sa_status_string", "sa_abi_version")
@@ -95,9 +96,11 @@ def lib() -> ctypes.CDLL:
         L.sparse_block_topk.argtypes = [bp, vp, i64, i32, vp, vp, sz, vp]
         L.sparse_block_expand.restype = ctypes.c_int
         L.sparse_block_expand.argtypes = [bp, vp, i32, vp, vp]
+        L.sparse_gated_attn_bwd_workspace_size.restype = sz
+        L.sparse_gated_attn_bwd_workspace_size.argtypes = [bp, i32, i32, i32, i32]
         L.sparse_gated_attn_bwd.restype = ctypes.c_int
         L.sparse_gated_attn_bwd.argtypes = [bp, ctypes.c_int, vp, i32, i32, vp, vp, i32, i64, vp, i32, vp, i32,
-                                            ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp]
+                                            ctypes.c_float, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.sparse_window_indices.restype = ctypes.c_int
         L.sparse_window_indices.argtypes = [bp, i32, vp, vp]
         L.sparse_branch_fuse.restype = ctypes.c_int
@@ -271,18 +274,30 @@ def sparse_block_expand(batch: SaBatch, block_idx: torch.Tensor, indices: torch.
 def sparse_gated_attn_bwd(batch: SaBatch, q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, d_v: int,
                           indices: torch.Tensor, gate: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
                           d_out: torch.Tensor, d_q: torch.Tensor, d_k_cache: torch.Tensor, d_v_cache: torch.Tensor,
-                          d_gate: torch.Tensor, softmax_scale: Optional[float] = None, stream=None) -> None:
+                          d_gate: torch.Tensor, softmax_scale: Optional[float] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None) -> None:
     """Gradients of the gated sparse attention over fixed indices: d_q and d_gate written, d_k_cache and
-    d_v_cache (fp32, zeroed by the caller, the same tensor for a shared cache) scatter-added."""
+    d_v_cache (fp32, zeroed by the caller, the same tensor for a shared cache) added to.  `workspace`
+    (uint8, sparse_gated_attn_bwd_workspace_size bytes, 256-byte aligned) is allocated when not given."""
     T, Hq, dqk = q.shape
     per_channel = 1 if gate.dim() == 3 else 0
     scale = float(softmax_scale if softmax_scale is not None else dqk ** -0.5)
+    K = indices.shape[1]
+    if workspace is None:
+        n = sparse_gated_attn_bwd_workspace_size(batch, Hq, dqk, int(d_v), K)
+        workspace = torch.empty(n, dtype=torch.uint8, device=q.device) if n else None
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib().sparse_gated_attn_bwd(ctypes.byref(batch), _DT[q.dtype], _ptr(q), Hq, dqk, _ptr(k_cache),
-                                     _ptr(v_cache), int(d_v), k_cache.stride(-2), _ptr(indices), indices.shape[1],
+                                     _ptr(v_cache), int(d_v), k_cache.stride(-2), _ptr(indices), K,
                                      _ptr(gate), per_channel, ctypes.c_float(scale), _ptr(out), _ptr(lse),
                                      _ptr(d_out), _ptr(d_q), _ptr(d_k_cache), _ptr(d_v_cache), _ptr(d_gate),
-                                     _stream(stream))
+                                     _ptr(workspace), wsb, _stream(stream))
     _check("sparse_gated_attn_bwd", st)
+
+
+def sparse_gated_attn_bwd_workspace_size(batch: SaBatch, n_q_heads: int, d_qk: int, d_v: int, k: int) -> int:
+    return int(lib().sparse_gated_attn_bwd_workspace_size(ctypes.byref(batch), int(n_q_heads), int(d_qk), int(d_v),
+                                                          int(k)))
 
 
 def sparse_window_indices(batch: SaBatch, window: int, indices: torch.Tensor, stream=None) -> None:

@@ -2,8 +2,9 @@
 //
 // Pages (by title):
 //   [HAT] "Hybrid Attention Architectures: Engineering Trade-offs from Linear
-//          Attention to Gated Sparse Attention", §3.3: exact attention over
-//          kv_history[idx], scaled by the gate.
+//          Attention to Gated Sparse Attention", §3.2 (the gate as a
+//          continuous path for the gradient) and §3.3 (exact attention over
+//          kv_history[idx], scaled by the gate).
 //   [F2S] "From Full Attention to Sparsity: The Evolution of Hybrid Attention
 //          Architectures in Large Language Models", "Fine-Grained Sparse
 //          Attention: Indexer Plus Top-K": the indices come from a Top-K, which
@@ -14,76 +15,68 @@
 //     dG = dy * y * (1 - g)      (= dy * o * g * (1 - g); summed over c per head)
 //     do = dy * g,   D = do . o = dy . y,   dP_j = do . V_j,   dS_j = P_j (dP_j - D)
 //     dq = scale * sum_j dS_j K_j,   dK[row(s_j)] += scale * dS_j q,   dV[row(s_j)] += P_j do
-// P comes back from the forward's log-sum-exp, D and dG from its output y, so
-// no forward pass is repeated.
+// P comes back from the forward's log-sum-exp and D from its output y, so no
+// forward pass is repeated.  P, dS and do enter the MFMAs rounded to bf16;
+// every sum is fp32.
 //
-// One workgroup per token, all its heads, 32 keys per tile, bf16 MFMA
-// (16x16x32) with fp32 accumulation.  Every operand of every contraction is
-// kept in LDS in the layout that makes its MFMA fragment one 16-byte read:
-// Q and dO row-major and transposed, the key tile row-major and transposed,
-// P^T, dS and dS^T per tile.  dq accumulates in registers over the tiles; the
-// tile's dK and dV (summed over the heads by the MFMA) are added to the fp32
-// gradient rows with hardware float atomics, one per (token, key, element).
+// Kernels, in launch order:
+//   attn_bwd_prep_kernel   per token: do (bf16), D, dG, and the transposed
+//                          copies Q^T [d][h] and do^T [d][h] that the
+//                          contractions over heads read.
+//   attn_bwd_mask_kernel   per token (key-major layouts): the selected
+//                          positions as a bitmap over the sequence, and a flag
+//                          on every slot whose position an earlier slot of the
+//                          row already holds.
+//   attn_bwd_dq_kernel     per (token, head group), over the index list:
+//                          S^T and dP^T again, P from lse, dS, and
+//                          dq^T += K^T dS^T with K^T read by the LDS transpose
+//                          load.  In scatter mode it also sums each slot's
+//                          dK / dV over the group's heads and adds them to the
+//                          cache rows with float atomics: every slot (latent
+//                          layout) or only the flagged repeats.
+//   attn_bwd_kv_kernel     key-major, per (sequence, 128 key positions,
+//                          chunk of the sequence's tokens): each wave keeps
+//                          32 keys' K and V operands in registers and their
+//                          dK, dV in accumulators, and walks the chunk's
+//                          tokens that selected any of the block's keys
+//                          (their Q, do, Q^T, do^T staged in an LDS ring by
+//                          direct loads).  One float atomic per (chunk, key,
+//                          element) merges the chunks: about 1/16 of the
+//                          per-slot scatter at the prefill shapes.
 #include "launch.h"
 #include "sa_device.h"
 
 namespace sa {
 
-constexpr int kBwdThreads = 256;
-constexpr int kBwdTK = 32;              // keys per tile
+constexpr float kBLog2e = 1.4426950408889634f;
+constexpr int kBwdTK = 64;              // slots per LDS tile of the query-major kernel
+constexpr int kBwdChunk = 1024;         // slots whose rows one pass resolves up front
+constexpr int kKvKeys = 128;            // key positions per key-major workgroup
+constexpr int kKvTokens = 256;          // tokens per key-major chunk
+constexpr int kPrepMaxH = 256;
 
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_b;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_b;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2_b;
 
-template <int D, int H>
-__global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(
-    Batch bt, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
-    int64_t rs, const int32_t *__restrict__ idx, int K, const uint16_t *__restrict__ gate, int per_channel,
-    float scale, const uint16_t *__restrict__ y, const float *__restrict__ lse, const uint16_t *__restrict__ dy,
-    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dvv, float *__restrict__ dgate)
+// ------------------------------------------------------------------ prep
+// One workgroup per token.  D_h and the per-head gate gradient by one wave per
+// head; do, Q^T and do^T 32 columns at a time through an LDS tile, so the
+// transposed rows are written whole.
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
+    int H, int DQK, int DV, const uint16_t *__restrict__ q, const uint16_t *__restrict__ gate, int per_channel,
+    const uint16_t *__restrict__ y, const uint16_t *__restrict__ dy, uint16_t *__restrict__ dO,
+    uint16_t *__restrict__ QT, uint16_t *__restrict__ dOT, float *__restrict__ Dh, float *__restrict__ dgate)
 {
-    constexpr int HP = H < 32 ? 32 : H;     // heads padded to the MFMA k-step of the head contractions
-    constexpr int DP = D + 8;               // padded rows (bank spread)
-    constexpr int HPP = HP + 8;
-    constexpr int TKP = kBwdTK + 8;
-    __shared__ __align__(16) __bf16 Qs[H][DP];
-    __shared__ __align__(16) __bf16 QT[D][HPP];
-    __shared__ __align__(16) __bf16 dOs[H][DP];
-    __shared__ __align__(16) __bf16 dOT[D][HPP];
-    __shared__ __align__(16) __bf16 Ks[kBwdTK][DP];
-    __shared__ __align__(16) __bf16 KT[D][TKP];
-    __shared__ __align__(16) __bf16 Vs[kBwdTK][DP];
-    __shared__ __align__(16) __bf16 PT[kBwdTK][HPP];
-    __shared__ __align__(16) __bf16 dS[H][TKP];
-    __shared__ __align__(16) __bf16 dST[kBwdTK][HPP];
-    __shared__ float lse_s[H], Dh[H];
-    __shared__ int64_t rows[kBwdTK];
-
-    const int tok = blockIdx.x;
-    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-    const int col = lane & 15, grp = lane >> 4;
-    const int b = seq_of_token(bt, tok);
-    const int64_t row0 = phys_row(bt, b, 0);
-    const int32_t *irow = idx + (int64_t)tok * K;
-
-    // ---- per token: Q, dO = dy * g (both layouts), D_h = dy . y, the gate gradient
-    for (int e = tid; e < H * D; e += kBwdThreads) {
-        const int h = e / D, d = e % D;
-        const __bf16 qv = __builtin_bit_cast(__bf16, q[((int64_t)tok * H + h) * D + d]);
-        Qs[h][d] = qv;
-        QT[d][h] = qv;
-    }
-    for (int e = tid; e < (HP - H) * D; e += kBwdThreads)
-        QT[e % D][H + e / D] = (__bf16)0.0f;
-    for (int h = wv; h < H; h += kBwdThreads / 64) {
+    __shared__ uint16_t tile[kPrepMaxH][34];
+    const int tok = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    for (int h = wv; h < H; h += 4) {
         float dsum = 0.0f, gsum = 0.0f;
-        for (int c = lane; c < D; c += 64) {
-            const int64_t o = ((int64_t)tok * H + h) * D + c;
+        for (int c = lane; c < DV; c += 64) {
+            const int64_t o = ((int64_t)tok * H + h) * DV + c;
             const float G = bf16_bits_to_f32(per_channel ? gate[o] : gate[(int64_t)tok * H + h]);
             const float g = 1.0f / (1.0f + __expf(-G));
             const float dyc = bf16_bits_to_f32(dy[o]), yc = bf16_bits_to_f32(y[o]);
-            const __bf16 dov = (__bf16)(dyc * g);
-            dOs[h][c] = dov;
-            dOT[c][h] = dov;
             dsum += dyc * yc;
             const float dg = dyc * yc * (1.0f - g);
             if (per_channel)
@@ -95,154 +88,732 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_kernel(
         if (!per_channel)
             gsum = wave_sum(gsum);
         if (lane == 0) {
-            Dh[h] = dsum;
-            lse_s[h] = lse[(int64_t)tok * H + h];
+            Dh[(int64_t)tok * H + h] = dsum;
             if (!per_channel)
                 dgate[(int64_t)tok * H + h] = gsum;
         }
     }
-    for (int e = tid; e < (HP - H) * D; e += kBwdThreads)
-        dOT[e % D][H + e / D] = (__bf16)0.0f;
-    for (int e = tid; e < kBwdTK * (HP - H); e += kBwdThreads) {
-        PT[e / (HP - H)][H + e % (HP - H)] = (__bf16)0.0f;
-        dST[e / (HP - H)][H + e % (HP - H)] = (__bf16)0.0f;
+    const int cmax = DQK > DV ? DQK : DV;
+    for (int c0 = 0; c0 < cmax; c0 += 32) {
+        if (c0 < DQK) {
+            for (int e = tid; e < H * 32; e += 256) {
+                const int h = e >> 5, x = e & 31;
+                tile[h][x] = c0 + x < DQK ? q[((int64_t)tok * H + h) * DQK + c0 + x] : (uint16_t)0;
+            }
+            __syncthreads();
+            for (int e = tid; e < H * 32; e += 256) {
+                const int x = e / H, h = e - x * H;
+                if (c0 + x < DQK)
+                    QT[((int64_t)tok * DQK + c0 + x) * H + h] = tile[h][x];
+            }
+            __syncthreads();
+        }
+        if (c0 < DV) {
+            for (int e = tid; e < H * 32; e += 256) {
+                const int h = e >> 5, x = e & 31, c = c0 + x;
+                uint16_t v = 0;
+                if (c < DV) {
+                    const int64_t o = ((int64_t)tok * H + h) * DV + c;
+                    const float G = bf16_bits_to_f32(per_channel ? gate[o] : gate[(int64_t)tok * H + h]);
+                    const float g = 1.0f / (1.0f + __expf(-G));
+                    v = f32_to_bf16_bits(bf16_bits_to_f32(dy[o]) * g);
+                    dO[o] = v;
+                }
+                tile[h][x] = v;
+            }
+            __syncthreads();
+            for (int e = tid; e < H * 32; e += 256) {
+                const int x = e / H, h = e - x * H;
+                if (c0 + x < DV)
+                    dOT[((int64_t)tok * DV + c0 + x) * H + h] = tile[h][x];
+            }
+            __syncthreads();
+        }
     }
+}
 
-    // dq tiles owned by this wave: (head tile, dim tile) pairs t = wv + 4u
-    constexpr int NQT = (H / 16) * (D / 16);
-    constexpr int QPW = (NQT + 3) / 4;
-    f32x4 dqa[QPW];
+// ------------------------------------------------------------------ mask
+// One workgroup per token: clear the token's bitmap row, then set one bit per
+// valid slot.  The slot whose atomic finds its bit already set repeats a
+// position and is flagged (its contribution goes through the scatter).
+__global__ __launch_bounds__(256) void attn_bwd_mask_kernel(const int32_t *__restrict__ idx, int K, int W,
+                                                           int max_ctx, uint32_t *__restrict__ bits,
+                                                           uint8_t *__restrict__ flags)
+{
+    const int tok = blockIdx.x;
+    uint32_t *row = bits + (int64_t)tok * W;
+    for (int w = threadIdx.x; w < W; w += 256)
+        row[w] = 0u;
+    __threadfence();
+    __syncthreads();
+    for (int j = threadIdx.x; j < K; j += 256) {
+        const int s = idx[(int64_t)tok * K + j];
+        uint8_t rep = 0;
+        if (s >= 0 && s < max_ctx) {
+            const uint32_t bit = 1u << (s & 31);
+            rep = (atomicOr(&row[s >> 5], bit) & bit) ? 1 : 0;
+        }
+        flags[(int64_t)tok * K + j] = rep;
+    }
+}
+
+// ------------------------------------------------------------------ dq
+// One workgroup per (token, 16*NW heads), a wave per 16 heads, 64-slot tiles
+// gathered by direct loads into two LDS buffers (the layout of the forward's
+// kernel: 8-row blocks of 8 sixteen-byte chunks, chunks XOR-swizzled by row).
+// Per 32-slot half tile on 16x16x32 bf16 MFMA: S^T = K Q^T and dP^T = V do^T
+// (a lane owns one head's column, keys 4g..4g+3 and 16+4g..16+4g+3 in its
+// registers), P = exp(scale S - lse), dS = P (dP - D), and dq^T += K^T dS^T
+// with the K^T operand read by ds_read_b64_tr_b16 from the row-major tile, in
+// the key order the registers hold.
+__device__ __forceinline__ int bswz(int r) { return r & 7; }
+
+template <int DQK, int DV, bool MLA, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
+    Batch bt, const uint16_t *__restrict__ q, int Hq, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, int64_t rs, const int32_t *__restrict__ idx, int K, float scale,
+    const float *__restrict__ lse, const uint16_t *__restrict__ dO, const float *__restrict__ Dh,
+    float *__restrict__ dq, int mode, const uint8_t *__restrict__ flags, const uint16_t *__restrict__ QT,
+    const uint16_t *__restrict__ dOT, float *__restrict__ dk, float *__restrict__ dv)
+{
+    constexpr int NT = NW * 64;
+    constexpr int NKQ = DQK / 32;           // k-steps over d_qk
+    constexpr int NKV = DV / 32;            // k-steps over d_v
+    constexpr int NMQ = DQK / 16;           // 16-dim tiles of dq
+    constexpr int KCH = DQK / 8, VCH = DV / 8;
+    constexpr int KCB = KCH / 8, VCB = VCH / 8;
+    constexpr int VROWB = MLA ? KCB : VCB;
+    constexpr int KCHUNKS = kBwdTK * KCH, VCHUNKS = MLA ? 0 : kBwdTK * VCH;
+    constexpr int HW = 16 * NW;             // heads of the workgroup
+    constexpr int HWP = HW < 32 ? 32 : HW;  // padded to the k-step of the head contraction
+    constexpr int XS = HWP + 8;             // row of the scatter operands (bank spread)
+    static_assert(DQK % 64 == 0 && DV % 32 == 0 && KCH % 8 == 0 && VCH % 8 == 0, "dims");
+    static_assert(kBwdTK % (8 * NW) == 0, "whole 8-row groups per wave");
+    __shared__ __align__(16) uint8_t lk0[KCHUNKS * 16];
+    __shared__ __align__(16) uint8_t lk1[KCHUNKS * 16];
+    __shared__ __align__(16) uint8_t lv0[(MLA ? 16 : VCHUNKS * 16)];
+    __shared__ __align__(16) uint8_t lv1[(MLA ? 16 : VCHUNKS * 16)];
+    __shared__ int32_t prow[kBwdChunk];
+    __shared__ __align__(16) __bf16 xds[32][XS];     // scatter: scale*dS^T [key][head]
+    __shared__ __align__(16) __bf16 xp[32][XS];      // scatter: P^T [key][head]
+    __shared__ int32_t xrow[32];
+
+    const int tok = blockIdx.x, hg = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int g = lane >> 4, n = lane & 15;
+    const int hl = wv * 16 + n;             // head within the workgroup
+    const int h = hg * HW + hl;
+    const int b = seq_of_token(bt, tok);
+    const int32_t *irow = idx + (int64_t)tok * K;
+    const float sl2 = scale * kBLog2e;
+    const float L = lse[(int64_t)tok * Hq + h];
+    const bool live = L != -INFINITY;       // a head with no valid key has no gradient
+    const float L2 = live ? L * kBLog2e : 0.0f;
+    const float Dv = Dh[(int64_t)tok * Hq + h];
+
+    bf16x8 qop[NKQ], dop[NKV];
+    {
+        const uint16_t *qp = q + ((int64_t)tok * Hq + h) * DQK + 8 * g;
 #pragma unroll
-    for (int u = 0; u < QPW; ++u)
-        dqa[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < NKQ; ++ks)
+            qop[ks] = *(const bf16x8 *)(qp + 32 * ks);
+        const uint16_t *dp = dO + ((int64_t)tok * Hq + h) * DV + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < NKV; ++ks)
+            dop[ks] = *(const bf16x8 *)(dp + 32 * ks);
+    }
+    f32x4 dqa[NMQ];
+#pragma unroll
+    for (int mt = 0; mt < NMQ; ++mt)
+        dqa[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (mode != 0) {
+        for (int e = tid; e < 32 * XS; e += NT) {
+            (&xds[0][0])[e] = (__bf16)0.0f;
+            (&xp[0][0])[e] = (__bf16)0.0f;
+        }
+    }
+    const int row0 = (int)phys_row(bt, b, 0);
+    lds_u8 *const LK0 = (lds_u8 *)lk0, *const LK1 = (lds_u8 *)lk1;
+    lds_u8 *const LV0 = (lds_u8 *)lv0, *const LV1 = (lds_u8 *)lv1;
+    constexpr int RG = kBwdTK / 8;
 
-    const int ntiles = (K + kBwdTK - 1) / kBwdTK;
-    for (int t = 0; t < ntiles; ++t) {
-        __syncthreads();                    // the previous tile's LDS is free
-        // ---- gather the tile's K and V rows (invalid keys read row 0 and are masked)
-        if (tid < kBwdTK) {
-            const int j = t * kBwdTK + tid;
-            const int s = j < K ? irow[j] : -1;
-            rows[tid] = s >= 0 ? phys_row(bt, b, s) : -1;
+    for (int c0 = 0; c0 < K; c0 += kBwdChunk) {
+        const int nslots = min(kBwdChunk, K - c0);
+        __syncthreads();                    // the previous chunk's rows and tiles are done with
+        for (int j = tid; j < nslots; j += NT) {
+            const int s = irow[c0 + j];
+            prow[j] = s >= 0 ? (int)phys_row(bt, b, s) : -1 - row0;
         }
         __syncthreads();
-        for (int e = tid; e < kBwdTK * (D / 8); e += kBwdThreads) {
-            const int r = e / (D / 8), c8 = e % (D / 8);
-            const int64_t pr = rows[r] >= 0 ? rows[r] : row0;
-            const bf16x8 kv = *(const bf16x8 *)(kc + pr * rs + 8 * c8);
-            const bf16x8 vv = *(const bf16x8 *)(vc + pr * rs + 8 * c8);
-            *(lds_bf16x8_t *)&Ks[r][8 * c8] = kv;
-            *(lds_bf16x8_t *)&Vs[r][8 * c8] = vv;
+        const int ntiles = (nslots + kBwdTK - 1) / kBwdTK;
+        auto issue = [&](int t, lds_u8 *dk_, lds_u8 *dv_, int ln) {
 #pragma unroll
-            for (int x = 0; x < 8; ++x)
-                KT[8 * c8 + x][r] = kv[x];
-        }
-        __syncthreads();
-
-        // ---- S = Q K^T and dP = dO V^T per (head tile, key tile); P, dS to LDS
-        constexpr int NST = (H / 16) * 2;
-        for (int st = wv; st < NST; st += 4) {
-            const int m0 = 16 * (st >> 1), n0 = 16 * (st & 1);
-            f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f}, dp = f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int rg = wv; rg < RG; rg += NW) {
+                const int r = 8 * rg + (ln >> 3);
+                const int slot = t * kBwdTK + r;
+                int pr = prow[slot < nslots ? slot : 0];
+                pr = pr >= 0 ? pr : -1 - pr;
+                const int cpos = (ln & 7) ^ bswz(r);
+                const uint16_t *ksrc = kc + (int64_t)pr * rs + cpos * 8;
 #pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks) {
-                const int d0 = 32 * ks + 8 * grp;
-                s = mma16_bf16(*(const lds_bf16x8_t *)&Qs[m0 + col][d0], *(const lds_bf16x8_t *)&Ks[n0 + col][d0], s);
-                dp = mma16_bf16(*(const lds_bf16x8_t *)&dOs[m0 + col][d0], *(const lds_bf16x8_t *)&Vs[n0 + col][d0],
-                                dp);
+                for (int cb = 0; cb < KCB; ++cb)
+                    __builtin_amdgcn_global_load_lds(ksrc + cb * 64, (lds_void *)(dk_ + (rg * KCB + cb) * 1024), 16,
+                                                     0, 0);
+                if (!MLA) {
+                    const uint16_t *vsrc = vc + (int64_t)pr * rs + cpos * 8;
+#pragma unroll
+                    for (int cb = 0; cb < VCB; ++cb)
+                        __builtin_amdgcn_global_load_lds(vsrc + cb * 64, (lds_void *)(dv_ + (rg * VCB + cb) * 1024),
+                                                         16, 0, 0);
+                }
             }
-            // lane: key n0 + col, heads m0 + 4 grp + i
-            const int key = n0 + col;
-            const bool valid = rows[key] >= 0;
-            float pv[4], dsv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = m0 + 4 * grp + i;
-                const float L = lse_s[h];
-                const float p = (valid && L != -INFINITY) ? __expf(scale * s[i] - L) : 0.0f;
-                pv[i] = p;
-                dsv[i] = p * (dp[i] - Dh[h]) * scale;
-                dS[h][key] = (__bf16)dsv[i];
+        };
+        if (ntiles > 0)
+            issue(0, LK0, LV0, lane);
+        for (int t = 0; t < ntiles; ++t) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            __syncthreads();
+            const bool odd = t & 1;
+            const int ln = opaque(lane);
+            const int myslot = t * kBwdTK + ln;
+            const bool myvalid = myslot < nslots && prow[myslot < nslots ? myslot : 0] >= 0;
+            const uint64_t vmask = __ballot(myvalid);
+            // scatter this tile: every valid slot (mode 1) or the flagged repeats (mode 2);
+            // every wave forms the same mask
+            bool sc_me = false;
+            if (mode == 1)
+                sc_me = myvalid;
+            else if (mode == 2 && myvalid)
+                sc_me = flags[(int64_t)tok * K + c0 + myslot] != 0;
+            const uint64_t scmask = __ballot(sc_me);
+            const bool scatter = scmask != 0;
+            lds_u8 *tk = odd ? LK1 : LK0;
+            lds_u8 *tv = MLA ? tk : (odd ? LV1 : LV0);
+            if (t + 1 < ntiles) {
+                if (odd)
+                    issue(t + 1, LK0, LV0, ln);
+                else
+                    issue(t + 1, LK1, LV1, ln);
             }
+#pragma unroll 1
+            for (int kh = 0; kh < 2; ++kh) {
+                const int rb = 32 * kh;
+                const int lk = opaque(lane);
+                const int g_ = lk >> 4, n_ = lk & 15;
+                // ---- S^T = K Q^T and dP^T = V do^T for keys rb..rb+15 (s0, p0) and rb+16..rb+31
+                f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
+                {
+                    const int r0 = rb + n_, r1 = rb + 16 + n_;
+                    lds_u8 *k0 = tk + (r0 >> 3) * KCB * 1024 + (r0 & 7) * 128;
+                    lds_u8 *k1 = tk + (r1 >> 3) * KCB * 1024 + (r1 & 7) * 128;
+                    lds_u8 *v0 = tv + (r0 >> 3) * VROWB * 1024 + (r0 & 7) * 128;
+                    lds_u8 *v1 = tv + (r1 >> 3) * VROWB * 1024 + (r1 & 7) * 128;
+                    auto lda = [&](lds_u8 *row, int r, int ks) {
+                        return *(lds_bf16x8_b *)(row + 1024 * (ks >> 1) + 16 * ((4 * (ks & 1) + g_) ^ bswz(r)));
+                    };
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                PT[key][m0 + 4 * grp + i] = (__bf16)pv[i];
-                dST[key][m0 + 4 * grp + i] = (__bf16)dsv[i];
-            }
-        }
-        __syncthreads();
-
-        // ---- dq += dS K  (k-step: the tile's 32 keys)
+                    for (int ks = 0; ks < NKQ; ++ks) {
+                        s0 = mma16_bf16(lda(k0, r0, ks), qop[ks], s0);
+                        s1 = mma16_bf16(lda(k1, r1, ks), qop[ks], s1);
+                    }
 #pragma unroll
-        for (int u = 0; u < QPW; ++u) {
-            const int qt = wv + 4 * u;
-            if (qt < NQT) {
-                const int m0 = 16 * (qt / (D / 16)), n0 = 16 * (qt % (D / 16));
-                dqa[u] = mma16_bf16(*(const lds_bf16x8_t *)&dS[m0 + col][8 * grp],
-                                    *(const lds_bf16x8_t *)&KT[n0 + col][8 * grp], dqa[u]);
-            }
-        }
-        // ---- dK = dS^T Q and dV = P^T dO per (key tile, dim tile), added to the rows
-        constexpr int NKT = 2 * (D / 16);
-        for (int kt = wv; kt < NKT; kt += 4) {
-            const int m0 = 16 * (kt / (D / 16)), n0 = 16 * (kt % (D / 16));
-            f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int ks = 0; ks < NKV; ++ks) {
+                        d0 = mma16_bf16(lda(v0, r0, ks), dop[ks], d0);
+                        d1 = mma16_bf16(lda(v1, r1, ks), dop[ks], d1);
+                    }
+                }
+                // ---- P and dS for keys rb+4g+i (first four) and rb+16+4g+i
+                float pv[8], dsv[8];
 #pragma unroll
-            for (int ks = 0; ks < HP / 32; ++ks) {
-                const int h0 = 32 * ks + 8 * grp;
-                ak = mma16_bf16(*(const lds_bf16x8_t *)&dST[m0 + col][h0], *(const lds_bf16x8_t *)&QT[n0 + col][h0],
-                                ak);
-                av = mma16_bf16(*(const lds_bf16x8_t *)&PT[m0 + col][h0], *(const lds_bf16x8_t *)&dOT[n0 + col][h0],
-                                av);
-            }
-            // lane: dim n0 + col, keys m0 + 4 grp + i
+                for (int i = 0; i < 4; ++i) {
+                    const bool va = live && ((vmask >> (rb + 4 * g_ + i)) & 1);
+                    const bool vb = live && ((vmask >> (rb + 16 + 4 * g_ + i)) & 1);
+                    pv[i] = va ? __builtin_amdgcn_exp2f(fmaf(s0[i], sl2, -L2)) : 0.0f;
+                    pv[4 + i] = vb ? __builtin_amdgcn_exp2f(fmaf(s1[i], sl2, -L2)) : 0.0f;
+                    dsv[i] = pv[i] * (d0[i] - Dv);
+                    dsv[4 + i] = pv[4 + i] * (d1[i] - Dv);
+                }
+                bf16x8 dsop;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int64_t pr = rows[m0 + 4 * grp + i];
-                if (pr >= 0) {
-                    unsafeAtomicAdd(dk + pr * rs + n0 + col, ak[i]);
-                    unsafeAtomicAdd(dvv + pr * rs + n0 + col, av[i]);
+                for (int i = 0; i < 8; ++i)
+                    dsop[i] = (__bf16)dsv[i];
+                // ---- dq^T += K^T dS^T; the transpose load gives lane (dim i, group g)
+                // the dims of keys rb+4g..+3 (first load) and rb+16+4g..+3 (second)
+                {
+                    const int jj = lk & 15;
+                    const int ra_ = rb + 4 * g_ + (jj >> 2), rc_ = ra_ + 16;
+                    const int cc = jj & 3, hh = cc >> 1;
+                    const int fa = bswz(ra_), fc = bswz(rc_);
+                    lds_u8 *ka = tk + (ra_ >> 3) * KCB * 1024 + (ra_ & 7) * 128 + (cc & 1) * 8;
+                    lds_u8 *kb = tk + (rc_ >> 3) * KCB * 1024 + (rc_ & 7) * 128 + (cc & 1) * 8;
+                    auto ldk = [&](lds_u8 *v, int f, int mt) {
+                        return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                            (lds_bf16x4_b *)(v + 1024 * (mt >> 2) + 16 * ((2 * (mt & 3) + hh) ^ f)));
+                    };
+#pragma unroll
+                    for (int mt = 0; mt < NMQ; ++mt) {
+                        const bf16x4 la = ldk(ka, fa, mt), lc = ldk(kb, fc, mt);
+                        const bf16x8 kop = {la[0], la[1], la[2], la[3], lc[0], lc[1], lc[2], lc[3]};
+                        dqa[mt] = mma16_bf16(kop, dsop, dqa[mt]);
+                    }
+                }
+                // ---- scatter: sum each slot's dK, dV over the workgroup's heads
+                if (scatter) {
+                    // this half tile's rows and operands: P^T and scale*dS^T, zero where not scattered
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const int kl = (i < 4 ? 4 * g_ + i : 16 + 4 * g_ + (i - 4));
+                        const bool on = (scmask >> (rb + kl)) & 1;
+                        xp[kl][hl] = (__bf16)(on ? pv[i] : 0.0f);
+                        xds[kl][hl] = (__bf16)(on ? scale * dsv[i] : 0.0f);
+                    }
+                    if (tid < 32) {
+                        const int slot = t * kBwdTK + rb + tid;
+                        xrow[tid] = ((scmask >> (rb + tid)) & 1) ? prow[slot] : -1;
+                    }
+                    __syncthreads();
+                    constexpr int NDQ = DQK / 16;
+                    constexpr int HK = HWP / 32;
+                    const uint16_t *qtr = QT + (int64_t)tok * DQK * Hq + hg * HW + 8 * g_;
+                    const uint16_t *dotr = dOT + (int64_t)tok * DV * Hq + hg * HW + 8 * g_;
+                    for (int dt = wv; dt < NDQ; dt += NW) {
+                        const int d = 16 * dt + n_;
+                        bf16x8 bq[HK], bo[HK];
+#pragma unroll
+                        for (int kk = 0; kk < HK; ++kk) {
+                            const bool hv = 32 * kk + 8 * g_ < HW;
+                            bq[kk] = hv ? *(const bf16x8 *)(qtr + (int64_t)d * Hq + 32 * kk) : bf16x8{};
+                            bo[kk] = (hv && d < DV) ? *(const bf16x8 *)(dotr + (int64_t)d * Hq + 32 * kk) : bf16x8{};
+                        }
+#pragma unroll
+                        for (int mt = 0; mt < 2; ++mt) {
+                            f32x4 ak = f32x4{0.f, 0.f, 0.f, 0.f}, av = ak;
+#pragma unroll
+                            for (int kk = 0; kk < HK; ++kk) {
+                                const bf16x8 a1 = *(const lds_bf16x8_b *)&xds[16 * mt + n_][32 * kk + 8 * g_];
+                                ak = mma16_bf16(a1, bq[kk], ak);
+                                if (16 * dt < DV) {
+                                    const bf16x8 a2 = *(const lds_bf16x8_b *)&xp[16 * mt + n_][32 * kk + 8 * g_];
+                                    av = mma16_bf16(a2, bo[kk], av);
+                                }
+                            }
+                            // lane: dim d, keys 16mt + 4g + i
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int pr = xrow[16 * mt + 4 * g_ + i];
+                                if (pr >= 0) {
+                                    if (MLA) {
+                                        unsafeAtomicAdd(dk + (int64_t)pr * rs + d, ak[i] + av[i]);
+                                    } else {
+                                        unsafeAtomicAdd(dk + (int64_t)pr * rs + d, ak[i]);
+                                        if (16 * dt < DV)
+                                            unsafeAtomicAdd(dv + (int64_t)pr * rs + d, av[i]);
+                                    }
+                                }
+                            }
+                        }
+                    }
+                    __syncthreads();
                 }
             }
         }
     }
-    // ---- dq out: lane holds dim n0 + col, heads m0 + 4 grp + i
+    // ---- dq out: lane holds head h, dims 16mt + 4g + i
+    float *dqp = dq + ((int64_t)tok * Hq + h) * DQK + 4 * g;
 #pragma unroll
-    for (int u = 0; u < QPW; ++u) {
-        const int qt = wv + 4 * u;
-        if (qt < NQT) {
-            const int m0 = 16 * (qt / (D / 16)), n0 = 16 * (qt % (D / 16));
+    for (int mt = 0; mt < NMQ; ++mt)
+        *(f32x4 *)(dqp + 16 * mt) = dqa[mt] * scale;
+}
+
+// ------------------------------------------------------------------ dK, dV (key-major)
+// Workgroup = (sequence b, key positions p0 .. p0+127, tokens t0 .. t0+255 of
+// b); wave w owns keys p0+32w .. +31.  On 32x32x16 bf16 MFMA per token i:
+//   S = Q_i K_w^T and dP = do_i V_w^T (heads x keys: a lane owns one key's
+//   column, its registers the heads 8(r>>2) + 4(lane>>5) + (r&3));
+//   P, dS from lse_i and D_i where the token selected the key;
+//   dV_w += P^T do_i and dK_w += (scale dS)^T Q_i, the head contraction taking
+//   the registers in that order, with the matching head pairs read from the
+//   staged do_i^T and Q_i^T rows.
+// Staged per token (direct loads, 1 KB each, spread over the waves): Q_i and
+// do_i row-major ([h][d], 16-byte chunks XOR-swizzled by row), Q_i^T and
+// do_i^T ([d][h], likewise), lse_i and D_i.
+template <int D, int H>
+struct KvShape {
+    static constexpr int MT = H >= 32 ? H / 32 : 1;     // 32-head tiles of S
+    static constexpr int QB = H * D * 2;                 // bytes of one staged operand
+    static constexpr int OPB = 4 * QB;                   // the four operands
+    static constexpr int SB = OPB + 512;                 // + lse and D (256 bytes each)
+    static constexpr int R = 3 * SB <= 112 * 1024 ? 3 : 2;
+    static constexpr int NPW = OPB / 1024 / 4 + 1;       // direct loads per wave per token
+};
+
+template <int D, int H, bool SHARED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_kv_kernel(
+    Batch bt, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
+    int64_t rs, float scale, const float *__restrict__ lse, const uint16_t *__restrict__ dO,
+    const uint16_t *__restrict__ QT, const uint16_t *__restrict__ dOT, const float *__restrict__ Dh,
+    const uint32_t *__restrict__ bits, int W, int nkb, int ntc, float *__restrict__ dk, float *__restrict__ dv)
+{
+    typedef KvShape<D, H> S_;
+    constexpr int MT = S_::MT, QB = S_::QB, SB = S_::SB, R = S_::R, NPW = S_::NPW;
+    constexpr int KS = D / 16;              // k-steps over d
+    constexpr int NTD = D / 32;             // 32-dim tiles of dK, dV
+    constexpr int HKS = H / 16;             // k-steps over heads
+    constexpr int RC = 2 * D / 16;          // chunks per Q / do row
+    constexpr int RCT = 2 * H / 16;         // chunks per Q^T / do^T row
+    // chunk swizzles: row r's logical chunk c sits at c ^ ((r >> LR) & (chunks - 1)), LR
+    // = log2 of the rows per 256-byte bank period, so the 32 rows an operand read
+    // touches cover 16 distinct 16-byte bank groups
+    constexpr int LRQ = D == 128 ? 0 : 1;
+    constexpr int LRT = H == 16 ? 3 : (H == 32 ? 2 : 1);
+    static_assert(H % 16 == 0 && D % 32 == 0 && (QB % 1024) == 0 && (4 * QB / 1024) % 4 == 0, "shape");
+    static_assert(RC <= 16 && RCT >= 2, "row chunks");
+    __shared__ __align__(16) uint8_t stage[R * SB];
+    __shared__ int32_t ltok[kKvTokens];
+    __shared__ uint32_t lwd[kKvTokens][4];
+    __shared__ int32_t lrow[kKvKeys];
+    __shared__ int32_t lcount[4];
+
+    const int item = blockIdx.x;
+    const int b = item / (nkb * ntc);
+    const int kb = (item / ntc) % nkb, tc = item % ntc;
+    const int ctx = bt.ctx_len[b];
+    const int p0 = kb * kKvKeys;
+    const int q0 = bt.q_start[b], nq = bt.q_start[b + 1] - q0;
+    const int t0 = tc * kKvTokens;
+    if (p0 >= ctx || t0 >= nq)
+        return;
+    const int t1 = min(nq, t0 + kKvTokens);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 31, hf = lane >> 5;
+
+    // ---- the chunk's tokens that selected any of the block's keys, in order
+    {
+        const int t = t0 + tid;
+        uint32_t w4[4] = {0u, 0u, 0u, 0u};
+        if (t < t1) {
+            const uint32_t *bw = bits + (int64_t)(q0 + t) * W + (p0 >> 5);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dq[((int64_t)tok * H + m0 + 4 * grp + i) * D + n0 + col] = dqa[u][i];
+            for (int w = 0; w < 4; ++w)
+                w4[w] = (p0 >> 5) + w < W ? bw[w] : 0u;
+        }
+        const bool act = (w4[0] | w4[1] | w4[2] | w4[3]) != 0u;
+        const uint64_t bal = __ballot(act);
+        if (lane == 0)
+            lcount[tid >> 6] = __popcll(bal);
+        if (tid < kKvKeys) {
+            const int p = p0 + tid;
+            lrow[tid] = p < ctx ? (int)phys_row(bt, b, p) : -1;
+        }
+        __syncthreads();
+        int base = 0;
+        for (int w = 0; w < (tid >> 6); ++w)
+            base += lcount[w];
+        if (act) {
+            const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+            ltok[pos] = q0 + t;
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                lwd[pos][w] = w4[w];
+        }
+        __syncthreads();
+    }
+    const int nact = lcount[0] + lcount[1] + lcount[2] + lcount[3];
+    if (nact == 0)
+        return;
+
+    // ---- this wave's keys: K and V operands (B of S and dP: key = lane & 31, dims 16kk + 8hf ..)
+    const int myrow = lrow[32 * wv + col];
+    const int64_t pr = myrow >= 0 ? myrow : 0;
+    bf16x8 kop[KS], vop[SHARED ? 1 : KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) {
+        kop[kk] = myrow >= 0 ? *(const bf16x8 *)(kc + pr * rs + 16 * kk + 8 * hf) : bf16x8{};
+        if (!SHARED)
+            vop[kk] = myrow >= 0 ? *(const bf16x8 *)(vc + pr * rs + 16 * kk + 8 * hf) : bf16x8{};
+    }
+    f32x16 ak[NTD], av[NTD];
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt) {
+        ak[nt] = f32x16{};
+        av[nt] = f32x16{};
+    }
+    // the compiler does not count the asm loads: the operand loads above land first
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+
+    // ---- staging: token m's block k (1 KB) of the four operands goes to the
+    // ring slot m % R; wave w issues blocks w, w+4, ... and one 256-byte load
+    // (wave 0: lse, wave 1: D, waves 2-3: lse again, unused)
+    auto issue = [&](int m, int ln) {
+        const int tk = ltok[m < nact ? m : nact - 1];
+        lds_u8 *dst = (lds_u8 *)stage + (m % R) * SB;
+        constexpr int NB = 4 * QB / 1024;
+#pragma unroll
+        for (int j = 0; j < NB / 4; ++j) {
+            const int kb_ = wv + 4 * j;
+            const int op = kb_ / (QB / 1024);                   // 0 Q, 1 do, 2 Q^T, 3 do^T
+            const int off = (kb_ % (QB / 1024)) * 1024 + 16 * ln;   // byte offset of this lane's chunk position
+            const uint8_t *src;
+            int roff;
+            if (op < 2) {
+                const int r = off / (2 * D), p = (off % (2 * D)) / 16;
+                const int c = p ^ ((r >> LRQ) & (RC - 1));
+                roff = r * 2 * D + 16 * c;
+                src = op == 0 ? (const uint8_t *)(q + (int64_t)tk * H * D) : (const uint8_t *)(dO + (int64_t)tk * H * D);
+            } else {
+                const int r = off / (2 * H), p = (off % (2 * H)) / 16;
+                const int c = p ^ ((r >> LRT) & (RCT - 1));
+                roff = r * 2 * H + 16 * c;
+                src = op == 2 ? (const uint8_t *)(QT + (int64_t)tk * D * H) : (const uint8_t *)(dOT + (int64_t)tk * D * H);
+            }
+            dma_b128(src + roff, dst + kb_ * 1024);
+        }
+        const int hh = ln < H ? ln : 0;
+        const float *src2 = (wv == 1 ? Dh : lse) + (int64_t)tk * H + hh;
+        dma_b32(src2, dst + 4 * QB + (wv == 1 ? 256 : 0));
+    };
+#pragma unroll
+    for (int m = 0; m < R - 1; ++m)
+        issue(m, lane);
+    const float sl2 = scale * kBLog2e;
+    for (int m = 0; m < nact; ++m) {
+        // token m's loads were followed by those of tokens m+1 .. m+R-2
+        if (R == 3)
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPW) : "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        const int ln = opaque(lane);
+        issue(m + R - 1, ln);
+        const uint32_t word = lwd[m][wv];
+        if (word == 0u)
+            continue;
+        const lds_u8 *st = (const lds_u8 *)stage + (m % R) * SB;
+        const lds_u8 *sQ = st, *sO = st + QB, *sQT = st + 2 * QB, *sOT = st + 3 * QB;
+        const float *sL = (const float *)(st + 4 * QB), *sD = (const float *)(st + 4 * QB + 256);
+        // ---- S and dP (heads x keys), MT tiles of 32 heads
+        f32x16 s[MT], dp[MT];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+            s[mt] = f32x16{};
+            dp[mt] = f32x16{};
+            const int hr = 32 * mt + col;                   // A row: head
+            const bool hv = hr < H;
+            const lds_u8 *qrow = sQ + (hv ? hr : 0) * 2 * D;
+            const lds_u8 *orow = sO + (hv ? hr : 0) * 2 * D;
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const int c = (2 * kk + hf) ^ ((hr >> LRQ) & (RC - 1));
+                bf16x8 aq = *(const lds_bf16x8_b *)(qrow + 16 * c);
+                bf16x8 ao = *(const lds_bf16x8_b *)(orow + 16 * c);
+                if (!hv) {
+                    aq = bf16x8{};
+                    ao = bf16x8{};
+                }
+                s[mt] = mma32_bf16(aq, kop[kk], s[mt]);
+                dp[mt] = mma32_bf16(ao, SHARED ? kop[kk] : vop[kk], dp[mt]);
+            }
+        }
+        // ---- P and scale*dS, packed as A operands of the head contractions: k-step
+        // ks covers heads 16ks .. 16ks+15 in the register order of tile ks/2
+        const bool sel = ((word >> col) & 1u) != 0u;
+        bf16x8 pa[HKS > 0 ? HKS : 1], da[HKS > 0 ? HKS : 1];
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int hh = 32 * mt + mfma32_row(i, lane);
+                float p = 0.0f, ds = 0.0f;
+                if (sel && hh < H) {
+                    p = __builtin_amdgcn_exp2f(fmaf(s[mt][i], sl2, -sL[hh] * kBLog2e));
+                    ds = scale * p * (dp[mt][i] - sD[hh]);
+                }
+                const int ks = 2 * mt + (i >> 3);
+                if (ks < HKS) {
+                    pa[ks][i & 7] = (__bf16)p;
+                    da[ks][i & 7] = (__bf16)ds;
+                }
+            }
+        // ---- dV += P^T do and dK += (scale dS)^T Q: B lane (dim d, half hf) holds the
+        // heads 16ks + 4hf .. +3 and 16ks + 8 + 4hf .. +3 of row d of do^T / Q^T
+#pragma unroll
+        for (int nt = 0; nt < NTD; ++nt) {
+            const int d = 32 * nt + col;
+            const lds_u8 *qtr = sQT + d * 2 * H, *otr = sOT + d * 2 * H;
+            const int sw = (d >> LRT) & (RCT - 1);
+#pragma unroll
+            for (int ks = 0; ks < HKS; ++ks) {
+                const int ca = (2 * ks) ^ sw, cb = (2 * ks + 1) ^ sw;
+                const u32x2 qa = *(const lds_u32x2_b *)(qtr + 16 * ca + 8 * hf);
+                const u32x2 qb = *(const lds_u32x2_b *)(qtr + 16 * cb + 8 * hf);
+                const u32x2 oa = *(const lds_u32x2_b *)(otr + 16 * ca + 8 * hf);
+                const u32x2 ob = *(const lds_u32x2_b *)(otr + 16 * cb + 8 * hf);
+                const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{qa.x, qa.y, qb.x, qb.y});
+                const bf16x8 bo = __builtin_bit_cast(bf16x8, u32x4{oa.x, oa.y, ob.x, ob.y});
+                av[nt] = mma32_bf16(pa[ks], bo, av[nt]);
+                ak[nt] = mma32_bf16(da[ks], bq, ak[nt]);
+            }
+        }
+    }
+    // the ring's last loads land before the workgroup's LDS is released
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // ---- merge into the gradient rows: lane holds dim 32nt + col, keys mfma32_row(i)
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt) {
+        const int d = 32 * nt + col;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int key = 32 * wv + mfma32_row(i, lane);
+            const int r = lrow[key];
+            if (r >= 0) {
+                if (SHARED) {
+                    unsafeAtomicAdd(dk + (int64_t)r * rs + d, ak[nt][i] + av[nt][i]);
+                } else {
+                    unsafeAtomicAdd(dk + (int64_t)r * rs + d, ak[nt][i]);
+                    unsafeAtomicAdd(dv + (int64_t)r * rs + d, av[nt][i]);
+                }
+            }
         }
     }
 }
 
-int attn_bwd_supported(int dtype, int Hq, int d_qk, int d_v)
+// ------------------------------------------------------------------ host side
+static bool kv_shape(int Hq, int d_qk, int d_v)
 {
-    return dtype == 1 && d_qk == d_v && (d_qk == 64 || d_qk == 128) && (Hq == 16 || Hq == 32 || Hq == 64);
+    return d_qk == d_v && (d_qk == 64 || d_qk == 128) && (Hq == 16 || Hq == 32 || Hq == 64);
 }
 
-hipError_t launch_attn_bwd(const Batch &bt, int Hq, int D, const void *q, const void *kc, const void *vc,
-                           int64_t rs, const int32_t *idx, int K, const void *gate, int per_channel, float scale,
-                           const void *y, const float *lse, const void *dy, float *dq, float *dk, float *dv,
-                           float *dgate, hipStream_t st)
+int attn_bwd_supported(int dtype, int Hq, int d_qk, int d_v)
 {
-#define SA_BWD(DD, HH)                                                                                          \
-    hipLaunchKernelGGL((attn_bwd_kernel<DD, HH>), dim3(bt.total_q), dim3(kBwdThreads), 0, st, bt,              \
-                       (const uint16_t *)q, (const uint16_t *)kc, (const uint16_t *)vc, rs, idx, K,            \
-                       (const uint16_t *)gate, per_channel, scale, (const uint16_t *)y, lse, (const uint16_t *)dy, \
-                       dq, dk, dv, dgate)
-    if (D == 64 && Hq == 16) SA_BWD(64, 16);
-    else if (D == 64 && Hq == 32) SA_BWD(64, 32);
-    else if (D == 64 && Hq == 64) SA_BWD(64, 64);
-    else if (D == 128 && Hq == 16) SA_BWD(128, 16);
-    else if (D == 128 && Hq == 32) SA_BWD(128, 32);
-    else if (D == 128 && Hq == 64) SA_BWD(128, 64);
-    else
-        return hipErrorInvalidValue;
-#undef SA_BWD
+    if (dtype != 1 || Hq < 16 || Hq % 16 || Hq > kPrepMaxH)
+        return 0;
+    return (d_qk == d_v && (d_qk == 64 || d_qk == 128)) || (d_qk == 576 && d_v == 512);
+}
+
+int attn_bwd_needs_shared(int d_qk, int d_v)
+{
+    return d_qk == 576 && d_v == 512;
+}
+
+struct BwdLayout {
+    size_t dO, QT, dOT, Dh, bits, flags, total;
+    int W;
+    bool km;
+};
+
+static size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+static BwdLayout bwd_layout(int T, int max_ctx, int Hq, int d_qk, int d_v, int K)
+{
+    BwdLayout L{};
+    L.km = kv_shape(Hq, d_qk, d_v);
+    L.W = (max_ctx + 31) / 32;
+    size_t o = 0;
+    L.dO = o;
+    o += up256((size_t)T * Hq * d_v * 2);
+    L.QT = o;
+    o += up256((size_t)T * Hq * d_qk * 2);
+    L.dOT = o;
+    o += up256((size_t)T * Hq * d_v * 2);
+    L.Dh = o;
+    o += up256((size_t)T * Hq * 4);
+    if (L.km) {
+        L.bits = o;
+        o += up256((size_t)T * L.W * 4);
+        L.flags = o;
+        o += up256((size_t)T * K);
+    }
+    L.total = o;
+    return L;
+}
+
+size_t attn_bwd_ws_bytes(int T, int max_ctx, int Hq, int d_qk, int d_v, int K)
+{
+    return T > 0 ? bwd_layout(T, max_ctx, Hq, d_qk, d_v, K).total : 0;
+}
+
+static int bwd_waves(int Hq, int d_qk)
+{
+    const int cap = d_qk == 576 ? 4 : 8;
+    for (int nw = cap; nw > 1; nw >>= 1)
+        if (Hq % (16 * nw) == 0)
+            return nw;
+    return 1;
+}
+
+hipError_t launch_attn_bwd(const Batch &bt, int Hq, int d_qk, int d_v, const void *q, const void *kc,
+                           const void *vc, int64_t rs, const int32_t *idx, int K, const void *gate, int per_channel,
+                           float scale, const void *y, const float *lse, const void *dy, float *dq, float *dk,
+                           float *dv, float *dgate, void *ws, hipStream_t st)
+{
+    const int T = bt.total_q;
+    const BwdLayout L = bwd_layout(T, bt.max_ctx, Hq, d_qk, d_v, K);
+    uint8_t *w = (uint8_t *)ws;
+    uint16_t *dO = (uint16_t *)(w + L.dO), *QT = (uint16_t *)(w + L.QT), *dOT = (uint16_t *)(w + L.dOT);
+    float *Dh = (float *)(w + L.Dh);
+    uint32_t *bits = L.km ? (uint32_t *)(w + L.bits) : nullptr;
+    uint8_t *flags = L.km ? (uint8_t *)(w + L.flags) : nullptr;
+    const bool shared = kc == vc;
+
+    hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(T), dim3(256), 0, st, Hq, d_qk, d_v, (const uint16_t *)q,
+                       (const uint16_t *)gate, per_channel, (const uint16_t *)y, (const uint16_t *)dy, dO, QT, dOT,
+                       Dh, dgate);
+    if (L.km)
+        hipLaunchKernelGGL(attn_bwd_mask_kernel, dim3(T), dim3(256), 0, st, idx, K, L.W, bt.max_ctx, bits, flags);
+    const int nw = bwd_waves(Hq, d_qk);
+    const int mode = L.km ? 2 : 1;
+    const dim3 grid(T, Hq / (16 * nw));
+#define SA_DQ(DQ, DV_, MLA_, NW_)                                                                                 \
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<DQ, DV_, MLA_, NW_>), grid, dim3(NW_ * 64), 0, st, bt,                \
+                       (const uint16_t *)q, Hq, (const uint16_t *)kc, (const uint16_t *)vc, rs, idx, K, scale, lse, \
+                       dO, Dh, dq, mode, flags, QT, dOT, dk, dv)
+#define SA_DQ_NW(DQ, DV_, MLA_)                    \
+    switch (nw) {                                  \
+    case 8: SA_DQ(DQ, DV_, MLA_, 8); break;        \
+    case 4: SA_DQ(DQ, DV_, MLA_, 4); break;        \
+    case 2: SA_DQ(DQ, DV_, MLA_, 2); break;        \
+    default: SA_DQ(DQ, DV_, MLA_, 1); break;       \
+    }
+    if (d_qk == 576) {
+        switch (nw) {
+        case 4: SA_DQ(576, 512, true, 4); break;
+        case 2: SA_DQ(576, 512, true, 2); break;
+        default: SA_DQ(576, 512, true, 1); break;
+        }
+    } else if (d_qk == 128 && shared) {
+        SA_DQ_NW(128, 128, true)
+    } else if (d_qk == 128) {
+        SA_DQ_NW(128, 128, false)
+    } else if (shared) {
+        SA_DQ_NW(64, 64, true)
+    } else {
+        SA_DQ_NW(64, 64, false)
+    }
+#undef SA_DQ_NW
+#undef SA_DQ
+    if (L.km) {
+        const int nkb = (bt.max_ctx + kKvKeys - 1) / kKvKeys;
+        const int ntc = (bt.max_q + kKvTokens - 1) / kKvTokens;
+        const int64_t items = (int64_t)bt.num_seqs * nkb * ntc;
+        if (items > 0x7fffffff)
+            return hipErrorInvalidValue;
+#define SA_KV(DD, HH, SH)                                                                                         \
+    hipLaunchKernelGGL((attn_bwd_kv_kernel<DD, HH, SH>), dim3((unsigned)items), dim3(256), 0, st, bt,            \
+                       (const uint16_t *)q, (const uint16_t *)kc, (const uint16_t *)vc, rs, scale, lse, dO, QT, dOT, \
+                       Dh, bits, L.W, nkb, ntc, dk, dv)
+#define SA_KV_H(DD, SH)                                    \
+    if (Hq == 16) SA_KV(DD, 16, SH);                       \
+    else if (Hq == 32) SA_KV(DD, 32, SH);                  \
+    else SA_KV(DD, 64, SH);
+        if (d_qk == 128) {
+            if (shared) { SA_KV_H(128, true) } else { SA_KV_H(128, false) }
+        } else {
+            if (shared) { SA_KV_H(64, true) } else { SA_KV_H(64, false) }
+        }
+#undef SA_KV_H
+#undef SA_KV
+    }
     return hipGetLastError();
 }
 

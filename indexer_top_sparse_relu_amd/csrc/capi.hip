@@ -347,12 +347,21 @@ sa_status sparse_block_expand(const sa_batch *batch, const int32_t *block_idx, i
     return launched(sa::launch_block_expand(bt, block_idx, kb, indices, (hipStream_t)stream));
 }
 
+size_t sparse_gated_attn_bwd_workspace_size(const sa_batch *batch, int32_t n_q_heads, int32_t d_qk, int32_t d_v,
+                                            int32_t k)
+{
+    sa::Batch bt;
+    if (make_batch(batch, &bt) != SA_OK || n_q_heads < 1 || d_qk < 1 || d_v < 1 || k < 1)
+        return 0;
+    return sa::attn_bwd_ws_bytes(bt.total_q, bt.max_ctx, n_q_heads, d_qk, d_v, k);
+}
+
 sa_status sparse_gated_attn_bwd(const sa_batch *batch, sa_dtype dtype, const void *q, int32_t n_q_heads,
                                 int32_t d_qk, const void *k_cache, const void *v_cache, int32_t d_v,
                                 int64_t kv_row_stride, const int32_t *indices, int32_t k, const void *gate_logits,
                                 int32_t gate_per_channel, float softmax_scale, const void *out, const float *lse,
                                 const void *d_out, float *d_q, float *d_k_cache, float *d_v_cache, float *d_gate,
-                                sa_stream_t stream)
+                                void *workspace, size_t workspace_bytes, sa_stream_t stream)
 {
     sa::Batch bt;
     sa_status st = make_batch(batch, &bt);
@@ -367,15 +376,23 @@ sa_status sparse_gated_attn_bwd(const sa_batch *batch, sa_dtype dtype, const voi
         return SA_EINVAL;
     if (!(softmax_scale == softmax_scale) || softmax_scale > 3.0e38f || softmax_scale < -3.0e38f)
         return SA_EINVAL;
-    if ((kv_row_stride * 2) % 16 || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache))
+    if ((kv_row_stride * 2) % 16 || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(d_out) ||
+        !aligned16(out) || !aligned16(d_q))
         return SA_EINVAL;
     if ((k_cache == v_cache) != (d_k_cache == d_v_cache))
         return SA_EINVAL;
     if (!sa::attn_bwd_supported((int)dtype, n_q_heads, d_qk, d_v))
         return SA_EUNSUPPORTED;
-    return launched(sa::launch_attn_bwd(bt, n_q_heads, d_qk, q, k_cache, v_cache, kv_row_stride, indices, k,
+    if (sa::attn_bwd_needs_shared(d_qk, d_v) && k_cache != v_cache)
+        return SA_EUNSUPPORTED;
+    const size_t need = sa::attn_bwd_ws_bytes(bt.total_q, bt.max_ctx, n_q_heads, d_qk, d_v, k);
+    if (workspace_bytes < need || (need && !workspace))
+        return SA_EWORKSPACE;
+    if (workspace && ((uintptr_t)workspace & 255))
+        return SA_EINVAL;
+    return launched(sa::launch_attn_bwd(bt, n_q_heads, d_qk, d_v, q, k_cache, v_cache, kv_row_stride, indices, k,
                                         gate_logits, gate_per_channel ? 1 : 0, softmax_scale, out, lse, d_out, d_q,
-                                        d_k_cache, d_v_cache, d_gate, (hipStream_t)stream));
+                                        d_k_cache, d_v_cache, d_gate, workspace, (hipStream_t)stream));
 }
 
 sa_status sparse_window_indices(const sa_batch *batch, int32_t window, int32_t *indices, sa_stream_t stream)

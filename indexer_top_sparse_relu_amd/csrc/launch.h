@@ -51,10 +51,12 @@ hipError_t launch_block_expand(const Batch &bt, const int32_t *blk, int kb, int3
 
 // backward over fixed indices
 int attn_bwd_supported(int dtype, int Hq, int d_qk, int d_v);
-hipError_t launch_attn_bwd(const Batch &bt, int Hq, int D, const void *q, const void *kc, const void *vc,
-                           int64_t rs, const int32_t *idx, int K, const void *gate, int per_channel, float scale,
-                           const void *y, const float *lse, const void *dy, float *dq, float *dk, float *dv,
-                           float *dgate, hipStream_t st);
+int attn_bwd_needs_shared(int d_qk, int d_v);
+size_t attn_bwd_ws_bytes(int T, int max_ctx, int Hq, int d_qk, int d_v, int K);
+hipError_t launch_attn_bwd(const Batch &bt, int Hq, int d_qk, int d_v, const void *q, const void *kc,
+                           const void *vc, int64_t rs, const int32_t *idx, int K, const void *gate, int per_channel,
+                           float scale, const void *y, const float *lse, const void *dy, float *dq, float *dk,
+                           float *dv, float *dgate, void *ws, hipStream_t st);
 
 // branch fusion with a local branch
 hipError_t launch_window_indices(const Batch &bt, int w, int32_t *indices, hipStream_t st);

@@ -211,6 +211,22 @@ def epilogue_mix_floor(inp, fb, a, b_abs, rows=None):
     return O.branch_fuse(inp, np.zeros_like(fb), fb, rows) + fmix
 
 
+def sub_inputs(inp, b, first, n):
+    """Inputs holding only tokens first .. first+n-1 (global indices, all of sequence b) at their own
+    positions: the sub-batch's context ends at the last of them."""
+    q0, q1 = int(inp.q_start[b]), int(inp.q_start[b + 1])
+    assert q0 <= first and first + n <= q1
+    pos0 = int(inp.ctx_len[b]) - (q1 - q0) + (first - q0)
+    rows = np.arange(first, first + n)
+    return O.Inputs(q_start=np.array([0, n], np.int32), ctx_len=np.array([pos0 + n], np.int32),
+                    page_table=inp.page_table[b:b + 1], page_size=inp.page_size, idx_dtype=inp.idx_dtype,
+                    attn_dtype=inp.attn_dtype, q_idx=inp.q_idx[rows], q_scale=None if inp.q_scale is None
+                    else inp.q_scale[rows], w=inp.w[rows], k_idx=inp.k_idx, k_scale=inp.k_scale, q=inp.q[rows],
+                    k_cache=inp.k_cache, v_cache=inp.v_cache, gate=inp.gate[rows], H_I=inp.H_I, d_I=inp.d_I,
+                    Hq=inp.Hq, d_qk=inp.d_qk, d_v=inp.d_v, row_stride=inp.row_stride,
+                    gate_per_channel=inp.gate_per_channel)
+
+
 # --------------------------------------------------------- host marshalling
 
 def to_np(t: torch.Tensor) -> np.ndarray:

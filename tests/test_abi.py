@@ -145,7 +145,8 @@ def test_empty_batch_is_a_no_op(B):
     assert L.sparse_block_topk(e, None, 0, 16, None, None, 0, None) == B.SA_OK
     assert L.sparse_block_expand(e, None, 16, None, None) == B.SA_OK
     assert L.sparse_gated_attn_bwd(e, 1, None, 16, 128, None, None, 128, 128, None, 64, None, 1, f, None, None,
-                                   None, None, None, None, None, None) == B.SA_OK
+                                   None, None, None, None, None, None, 0, None) == B.SA_OK
+    assert L.sparse_gated_attn_bwd_workspace_size(e, 16, 128, 128, 64) == 0
     assert L.sparse_window_indices(e, 64, None, None) == B.SA_OK
     assert L.sparse_cache_append(e, 1, None, 128, None, 128, None, None, 128, 1, None, 128, 2, None, None,
                                  None) == B.SA_OK
@@ -200,3 +201,28 @@ def test_fused_mix_entry_point_checks_the_other_branch(B):
     assert call(ctypes.c_void_p(0x30008)) == B.SA_EINVAL
     assert call(ctypes.c_void_p(0x30000), gate=None) == B.SA_EINVAL
     assert call(ctypes.c_void_p(0x30000), H=24) == B.SA_EUNSUPPORTED
+
+
+def test_backward_checks_shapes_layout_and_workspace(B):
+    """sparse_gated_attn_bwd: supported shapes, the latent layout's shared cache, and its workspace
+    (size, 256-byte alignment) are checked on the host before anything is launched."""
+    L = B.lib()
+    f = ctypes.c_float(1.0 / 12)
+    bt = batch(B)
+    OTHER = 0x40000
+
+    def call(H=32, dqk=128, dv=128, vc=FAKE, dk=FAKE, dvc=FAKE, ws=FAKE, wsb=1 << 40):
+        return L.sparse_gated_attn_bwd(ctypes.byref(bt), 1, FAKE, H, dqk, FAKE, vc, dv, dqk, FAKE, 64, FAKE, 1, f,
+                                       FAKE, FAKE, FAKE, FAKE, dk, dvc, FAKE, ws, wsb, None)
+
+    need = L.sparse_gated_attn_bwd_workspace_size(ctypes.byref(bt), 32, 128, 128, 64)
+    assert need > 0
+    assert call(H=24) == B.SA_EUNSUPPORTED                     # heads not a multiple of 16
+    assert call(H=272) == B.SA_EUNSUPPORTED                    # above 256 heads
+    assert call(dqk=96, dv=96) == B.SA_EUNSUPPORTED
+    assert call(dqk=576, dv=512, vc=OTHER, dvc=OTHER) == B.SA_EUNSUPPORTED   # latent rows need one cache
+    assert call(vc=OTHER) == B.SA_EINVAL                       # separate caches, one gradient array
+    assert call(wsb=need - 1) == B.SA_EWORKSPACE
+    assert call(ws=None, wsb=need) == B.SA_EWORKSPACE
+    assert call(ws=FAKE + 16, wsb=need) == B.SA_EINVAL         # not 256-byte aligned
+    assert L.sparse_gated_attn_bwd_workspace_size(ctypes.byref(bt), 32, 128, 128, 64) == need
