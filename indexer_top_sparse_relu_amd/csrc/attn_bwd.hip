@@ -133,27 +133,42 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
 }
 
 // ------------------------------------------------------------------ mask
-// One workgroup per token: clear the token's bitmap row, then set one bit per
-// valid slot.  The slot whose atomic finds its bit already set repeats a
-// position and is flagged (its contribution goes through the scatter).
+// One workgroup per token: a cleared bitmap row gets one bit per valid slot.
+// The slot whose atomic finds its bit already set repeats a position and is
+// flagged (its contribution goes through the per-slot merge).  Rows of up to
+// kMaskLdsWords words are built in LDS and written out whole; longer ones with
+// global atomics.
+constexpr int kMaskLdsWords = 8192;
+
 __global__ __launch_bounds__(256) void attn_bwd_mask_kernel(const int32_t *__restrict__ idx, int K, int W,
                                                            int max_ctx, uint32_t *__restrict__ bits,
                                                            uint8_t *__restrict__ flags)
 {
+    __shared__ uint32_t lb[kMaskLdsWords];
     const int tok = blockIdx.x;
     uint32_t *row = bits + (int64_t)tok * W;
-    for (int w = threadIdx.x; w < W; w += 256)
-        row[w] = 0u;
-    __threadfence();
-    __syncthreads();
+    const bool in_lds = W <= kMaskLdsWords;
+    for (int w = threadIdx.x; w < W; w += 256) {
+        if (in_lds)
+            lb[w] = 0u;
+        else
+            row[w] = 0u;
+    }
+    __syncthreads();            // (the barrier waits for the cleared words: only this workgroup touches the row)
     for (int j = threadIdx.x; j < K; j += 256) {
         const int s = idx[(int64_t)tok * K + j];
         uint8_t rep = 0;
         if (s >= 0 && s < max_ctx) {
             const uint32_t bit = 1u << (s & 31);
-            rep = (atomicOr(&row[s >> 5], bit) & bit) ? 1 : 0;
+            const uint32_t old = in_lds ? atomicOr(&lb[s >> 5], bit) : atomicOr(&row[s >> 5], bit);
+            rep = (old & bit) ? 1 : 0;
         }
         flags[(int64_t)tok * K + j] = rep;
+    }
+    if (in_lds) {
+        __syncthreads();
+        for (int w = threadIdx.x; w < W; w += 256)
+            row[w] = lb[w];
     }
 }
 
@@ -427,56 +442,75 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
 
 // ------------------------------------------------------------------ dK, dV (key-major)
 // Workgroup = (sequence b, key positions p0 .. p0+127, tokens t0 .. t0+255 of
-// b); wave w owns keys p0+32w .. +31.  On 32x32x16 bf16 MFMA per token i:
-//   S = Q_i K_w^T and dP = do_i V_w^T (heads x keys: a lane owns one key's
-//   column, its registers the heads 8(r>>2) + 4(lane>>5) + (r&3));
-//   P, dS from lse_i and D_i where the token selected the key;
-//   dV_w += P^T do_i and dK_w += (scale dS)^T Q_i, the head contraction taking
-//   the registers in that order, with the matching head pairs read from the
-//   staged do_i^T and Q_i^T rows.
-// Staged per token (direct loads, 1 KB each, spread over the waves): Q_i and
-// do_i row-major ([h][d], 16-byte chunks XOR-swizzled by row), Q_i^T and
-// do_i^T ([d][h], likewise), lse_i and D_i.
+// b); wave w owns keys p0+32w .. +31, their K and V operands in registers and
+// their dK, dV in accumulators.  On 32x32x16 bf16 MFMA per token i that
+// selected any of the block's keys:
+//   S = Q_i K^T and dP = do_i V^T (heads x keys: a lane owns one key's column,
+//   its registers the heads 8(r>>2) + 4(lane>>5) + (r&3));
+//   P and scale*dS where the token selected the key;
+//   dV += P^T do_i and dK += (scale dS)^T Q_i.  The head contraction takes the
+//   registers in that order: lane (dim d, half) needs heads 16ks + 4half .. +3
+//   and 16ks + 8 + 4half .. +3 of column d, which two LDS transpose loads read
+//   straight from the row-major Q_i / do_i (no transposed copy is staged).
+// Staged per token in an LDS ring by direct loads (1 KB each, spread over the
+// waves): Q_i and do_i, rows of 16-byte chunks XOR-swizzled by row, and
+// lse_i, D_i.
+// dK / dV accumulation held in AGPRs.  Written as asm so that the loop-carried
+// accumulators stay in the AGPR half of the register file: left to the compiler
+// they live in VGPRs between tokens and are copied over before every MFMA.  The
+// compiler does not insert wait states around asm, so each MFMA is preceded by
+// enough for operands a VALU instruction (or an accumulator write) has just
+// produced; the dependent MFMAs of one accumulator chain back to back (same
+// opcode), and the caller pads the final reads of the accumulators.
+__device__ __forceinline__ void mma32_acc_agpr(f32x16 &acc, const bf16x8 &a, const bf16x8 &b)
+{
+    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
 template <int D, int H>
 struct KvShape {
     static constexpr int MT = H >= 32 ? H / 32 : 1;     // 32-head tiles of S
-    static constexpr int QB = H * D * 2;                 // bytes of one staged operand
-    static constexpr int OPB = 4 * QB;                   // the four operands
-    static constexpr int SB = OPB + 512;                 // + lse and D (256 bytes each)
-    static constexpr int R = 3 * SB <= 112 * 1024 ? 3 : 2;
-    static constexpr int NPW = OPB / 1024 / 4 + 1;       // direct loads per wave per token
+    static constexpr int QB = H * D * 2;                 // bytes of Q_i (and of do_i)
+    static constexpr int SB = 2 * QB + 512;              // + lse and D (256 bytes each)
+    static constexpr int R = 4 * SB <= 100 * 1024 ? 4 : (3 * SB <= 100 * 1024 ? 3 : 2);
+    static constexpr int NPW = 2 * QB / 1024 / 4 + 1;   // direct loads per wave per token
 };
 
 template <int D, int H, bool SHARED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_kv_kernel(
     Batch bt, const uint16_t *__restrict__ q, const uint16_t *__restrict__ kc, const uint16_t *__restrict__ vc,
     int64_t rs, float scale, const float *__restrict__ lse, const uint16_t *__restrict__ dO,
-    const uint16_t *__restrict__ QT, const uint16_t *__restrict__ dOT, const float *__restrict__ Dh,
-    const uint32_t *__restrict__ bits, int W, int nkb, int ntc, float *__restrict__ dk, float *__restrict__ dv)
+    const float *__restrict__ Dh, const uint32_t *__restrict__ bits, int W, int nkb, int ntc,
+    float *__restrict__ dk, float *__restrict__ dv)
 {
     typedef KvShape<D, H> S_;
     constexpr int MT = S_::MT, QB = S_::QB, SB = S_::SB, R = S_::R, NPW = S_::NPW;
     constexpr int KS = D / 16;              // k-steps over d
     constexpr int NTD = D / 32;             // 32-dim tiles of dK, dV
     constexpr int HKS = H / 16;             // k-steps over heads
-    constexpr int RC = 2 * D / 16;          // chunks per Q / do row
-    constexpr int RCT = 2 * H / 16;         // chunks per Q^T / do^T row
-    // chunk swizzles: row r's logical chunk c sits at c ^ ((r >> LR) & (chunks - 1)), LR
-    // = log2 of the rows per 256-byte bank period, so the 32 rows an operand read
-    // touches cover 16 distinct 16-byte bank groups
+    constexpr int RC = 2 * D / 16;          // 16-byte chunks per row of Q_i, do_i
+    // row r's logical chunk c sits at c ^ ((r >> LRQ) & (RC - 1)), LRQ = log2 of the rows
+    // per 256-byte bank period: the 32 rows an operand read touches spread over the banks
     constexpr int LRQ = D == 128 ? 0 : 1;
-    constexpr int LRT = H == 16 ? 3 : (H == 32 ? 2 : 1);
-    static_assert(H % 16 == 0 && D % 32 == 0 && (QB % 1024) == 0 && (4 * QB / 1024) % 4 == 0, "shape");
-    static_assert(RC <= 16 && RCT >= 2, "row chunks");
+    constexpr int NB = 2 * QB / 1024;       // 1 KB loads per token
+    static_assert(H % 16 == 0 && D % 32 == 0 && QB % 1024 == 0 && NB % 4 == 0 && RC <= 16, "shape");
+    static_assert(kKvKeys == 32 * 4 && kKvKeys <= 256 && kKvTokens <= 256, "one wave per 32 keys, a thread per token");
     __shared__ __align__(16) uint8_t stage[R * SB];
     __shared__ int32_t ltok[kKvTokens];
-    __shared__ uint32_t lwd[kKvTokens][4];
+    __shared__ uint32_t lwd[kKvTokens][kKvKeys / 32];
     __shared__ int32_t lrow[kKvKeys];
     __shared__ int32_t lcount[4];
 
-    const int item = blockIdx.x;
-    const int b = item / (nkb * ntc);
-    const int kb = (item / ntc) % nkb, tc = item % ntc;
+    // Workgroup i runs on XCD i % 8.  A group is one (sequence, token chunk); its nkb
+    // key blocks go to one XCD back to back, so the workgroups that XCD runs at
+    // once stream the same tokens and share them through its L2.  Groups are dealt
+    // to the XCDs in a snake order (0..7, 7..0, ...) to even out their work.
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int kg = j / nkb, kb = j - kg * nkb;
+    const int grp = 8 * kg + ((kg & 1) ? 7 - xcd : xcd);
+    if (grp >= bt.num_seqs * ntc)
+        return;
+    const int b = grp / ntc, tc = grp - b * ntc;
     const int ctx = bt.ctx_len[b];
     const int p0 = kb * kKvKeys;
     const int q0 = bt.q_start[b], nq = bt.q_start[b + 1] - q0;
@@ -490,15 +524,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     // ---- the chunk's tokens that selected any of the block's keys, in order
     {
+        constexpr int NWD = kKvKeys / 32;
         const int t = t0 + tid;
-        uint32_t w4[4] = {0u, 0u, 0u, 0u};
-        if (t < t1) {
-            const uint32_t *bw = bits + (int64_t)(q0 + t) * W + (p0 >> 5);
+        uint32_t wd[NWD];
+        bool act = false;
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                w4[w] = (p0 >> 5) + w < W ? bw[w] : 0u;
+        for (int w = 0; w < NWD; ++w) {
+            wd[w] = 0u;
+            if (tid < kKvTokens && t < t1 && (p0 >> 5) + w < W)
+                wd[w] = bits[(int64_t)(q0 + t) * W + (p0 >> 5) + w];
+            act |= wd[w] != 0u;
         }
-        const bool act = (w4[0] | w4[1] | w4[2] | w4[3]) != 0u;
         const uint64_t bal = __ballot(act);
         if (lane == 0)
             lcount[tid >> 6] = __popcll(bal);
@@ -514,8 +550,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
             ltok[pos] = q0 + t;
 #pragma unroll
-            for (int w = 0; w < 4; ++w)
-                lwd[pos][w] = w4[w];
+            for (int w = 0; w < NWD; ++w)
+                lwd[pos][w] = wd[w];
         }
         __syncthreads();
     }
@@ -524,14 +560,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         return;
 
     // ---- this wave's keys: K and V operands (B of S and dP: key = lane & 31, dims 16kk + 8hf ..)
-    const int myrow = lrow[32 * wv + col];
-    const int64_t pr = myrow >= 0 ? myrow : 0;
     bf16x8 kop[KS], vop[SHARED ? 1 : KS];
+    {
+        const int r = lrow[32 * wv + col];
+        const int64_t pr = r >= 0 ? r : 0;
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-        kop[kk] = myrow >= 0 ? *(const bf16x8 *)(kc + pr * rs + 16 * kk + 8 * hf) : bf16x8{};
-        if (!SHARED)
-            vop[kk] = myrow >= 0 ? *(const bf16x8 *)(vc + pr * rs + 16 * kk + 8 * hf) : bf16x8{};
+        for (int kk = 0; kk < KS; ++kk) {
+            kop[kk] = r >= 0 ? *(const bf16x8 *)(kc + pr * rs + 16 * kk + 8 * hf) : bf16x8{};
+            if (!SHARED)
+                vop[kk] = r >= 0 ? *(const bf16x8 *)(vc + pr * rs + 16 * kk + 8 * hf) : bf16x8{};
+        }
     }
     f32x16 ak[NTD], av[NTD];
 #pragma unroll
@@ -542,62 +580,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // the compiler does not count the asm loads: the operand loads above land first
     __builtin_amdgcn_s_waitcnt(0x0F70);
 
-    // ---- staging: token m's block k (1 KB) of the four operands goes to the
-    // ring slot m % R; wave w issues blocks w, w+4, ... and one 256-byte load
-    // (wave 0: lse, wave 1: D, waves 2-3: lse again, unused)
+    // ---- staging: token m's 1 KB blocks of Q_i and do_i go to ring slot m % R;
+    // wave w issues blocks w, w+4, ... and one 256-byte load (wave 1: D, the
+    // others lse; only wave 0's lse copy is read)
     auto issue = [&](int m, int ln) {
         const int tk = ltok[m < nact ? m : nact - 1];
         lds_u8 *dst = (lds_u8 *)stage + (m % R) * SB;
-        constexpr int NB = 4 * QB / 1024;
 #pragma unroll
-        for (int j = 0; j < NB / 4; ++j) {
-            const int kb_ = wv + 4 * j;
-            const int op = kb_ / (QB / 1024);                   // 0 Q, 1 do, 2 Q^T, 3 do^T
-            const int off = (kb_ % (QB / 1024)) * 1024 + 16 * ln;   // byte offset of this lane's chunk position
-            const uint8_t *src;
-            int roff;
-            if (op < 2) {
-                const int r = off / (2 * D), p = (off % (2 * D)) / 16;
-                const int c = p ^ ((r >> LRQ) & (RC - 1));
-                roff = r * 2 * D + 16 * c;
-                src = op == 0 ? (const uint8_t *)(q + (int64_t)tk * H * D) : (const uint8_t *)(dO + (int64_t)tk * H * D);
-            } else {
-                const int r = off / (2 * H), p = (off % (2 * H)) / 16;
-                const int c = p ^ ((r >> LRT) & (RCT - 1));
-                roff = r * 2 * H + 16 * c;
-                src = op == 2 ? (const uint8_t *)(QT + (int64_t)tk * D * H) : (const uint8_t *)(dOT + (int64_t)tk * D * H);
-            }
-            dma_b128(src + roff, dst + kb_ * 1024);
+        for (int jb = 0; jb < NB / 4; ++jb) {
+            const int kb_ = wv + 4 * jb;
+            const int op = kb_ / (QB / 1024);                        // 0 Q, 1 do
+            const int off = (kb_ % (QB / 1024)) * 1024 + 16 * ln;    // this lane's position in the operand
+            const int r = off / (2 * D), p = (off % (2 * D)) / 16;
+            const int c = p ^ ((r >> LRQ) & (RC - 1));
+            const uint16_t *src = (op == 0 ? q : dO) + (int64_t)tk * H * D + r * D + 8 * c;
+            dma_b128(src, dst + kb_ * 1024);
         }
         const int hh = ln < H ? ln : 0;
-        const float *src2 = (wv == 1 ? Dh : lse) + (int64_t)tk * H + hh;
-        dma_b32(src2, dst + 4 * QB + (wv == 1 ? 256 : 0));
+        dma_b32((wv == 1 ? Dh : lse) + (int64_t)tk * H + hh, dst + 2 * QB + (wv == 1 ? 256 : 0));
     };
 #pragma unroll
     for (int m = 0; m < R - 1; ++m)
         issue(m, lane);
     const float sl2 = scale * kBLog2e;
+    const int G = lane >> 4, i16 = lane & 15;
     for (int m = 0; m < nact; ++m) {
         // token m's loads were followed by those of tokens m+1 .. m+R-2
-        if (R == 3)
-            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NPW) : "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((R - 2) * NPW) : "memory");
         __syncthreads();
         const int ln = opaque(lane);
         issue(m + R - 1, ln);
-        const uint32_t word = lwd[m][wv];
-        if (word == 0u)
+        const uint32_t wd = lwd[m][wv];
+        if (wd == 0u)
             continue;
         const lds_u8 *st = (const lds_u8 *)stage + (m % R) * SB;
-        const lds_u8 *sQ = st, *sO = st + QB, *sQT = st + 2 * QB, *sOT = st + 3 * QB;
-        const float *sL = (const float *)(st + 4 * QB), *sD = (const float *)(st + 4 * QB + 256);
-        // ---- S and dP (heads x keys), MT tiles of 32 heads
-        f32x16 s[MT], dp[MT];
+        const lds_u8 *sQ = st, *sO = st + QB;
+        const float *sL = (const float *)(st + 2 * QB), *sD = (const float *)(st + 2 * QB + 256);
+        // ---- S and dP (heads x keys), then P and scale*dS packed as A operands of the
+        // head contractions: k-step ks covers heads 16ks .. 16ks+15 in the register order
+        // of head tile ks/2
+        const bool sel = ((wd >> col) & 1u) != 0u;
+        bf16x8 pa[HKS], da[HKS];
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
-            s[mt] = f32x16{};
-            dp[mt] = f32x16{};
+            // this lane's heads 32mt + 8j + 4hf + (0..3): lse and D four at a time
+            f32x4 lv[4], dv4[4];
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                lv[jj] = *(const __attribute__((address_space(3))) f32x4 *)(sL + 32 * mt + 8 * jj + 4 * hf);
+                dv4[jj] = *(const __attribute__((address_space(3))) f32x4 *)(sD + 32 * mt + 8 * jj + 4 * hf);
+            }
+            f32x16 s = f32x16{}, dp = f32x16{};
             const int hr = 32 * mt + col;                   // A row: head
             const bool hv = hr < H;
             const lds_u8 *qrow = sQ + (hv ? hr : 0) * 2 * D;
@@ -611,61 +644,59 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     aq = bf16x8{};
                     ao = bf16x8{};
                 }
-                s[mt] = mma32_bf16(aq, kop[kk], s[mt]);
-                dp[mt] = mma32_bf16(ao, SHARED ? kop[kk] : vop[kk], dp[mt]);
+                s = mma32_bf16(aq, kop[kk], s);
+                dp = mma32_bf16(ao, SHARED ? kop[kk] : vop[kk], dp);
             }
-        }
-        // ---- P and scale*dS, packed as A operands of the head contractions: k-step
-        // ks covers heads 16ks .. 16ks+15 in the register order of tile ks/2
-        const bool sel = ((word >> col) & 1u) != 0u;
-        bf16x8 pa[HKS > 0 ? HKS : 1], da[HKS > 0 ? HKS : 1];
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int hh = 32 * mt + mfma32_row(i, lane);
-                float p = 0.0f, ds = 0.0f;
-                if (sel && hh < H) {
-                    p = __builtin_amdgcn_exp2f(fmaf(s[mt][i], sl2, -sL[hh] * kBLog2e));
-                    ds = scale * p * (dp[mt][i] - sD[hh]);
-                }
+                const bool on = sel && (H >= 32 || hh < H);
+                const float e = __builtin_amdgcn_exp2f(fmaf(s[i], sl2, -lv[i >> 2][i & 3] * kBLog2e));
+                const float p = on ? e : 0.0f;
+                const float ds = (scale * p) * (dp[i] - dv4[i >> 2][i & 3]);
                 const int ks = 2 * mt + (i >> 3);
                 if (ks < HKS) {
                     pa[ks][i & 7] = (__bf16)p;
                     da[ks][i & 7] = (__bf16)ds;
                 }
             }
-        // ---- dV += P^T do and dK += (scale dS)^T Q: B lane (dim d, half hf) holds the
-        // heads 16ks + 4hf .. +3 and 16ks + 8 + 4hf .. +3 of row d of do^T / Q^T
+        }
+        // ---- dV += P^T do and dK += (scale dS)^T Q.  Transpose loads: the 16 lanes of
+        // group G supply rows (heads) base + (i16 >> 2), dims blk + 4(i16 & 3) .. +3,
+        // and each receives dim blk + i16 of the four heads
+        const int hb = 4 * (G >> 1) + (i16 >> 2);
 #pragma unroll
         for (int nt = 0; nt < NTD; ++nt) {
-            const int d = 32 * nt + col;
-            const lds_u8 *qtr = sQT + d * 2 * H, *otr = sOT + d * 2 * H;
-            const int sw = (d >> LRT) & (RCT - 1);
+            const int d0 = 32 * nt + 16 * (G & 1) + 4 * (i16 & 3);
+            const int cd = d0 >> 3, cb = 2 * (d0 & 7);
 #pragma unroll
             for (int ks = 0; ks < HKS; ++ks) {
-                const int ca = (2 * ks) ^ sw, cb = (2 * ks + 1) ^ sw;
-                const u32x2 qa = *(const lds_u32x2_b *)(qtr + 16 * ca + 8 * hf);
-                const u32x2 qb = *(const lds_u32x2_b *)(qtr + 16 * cb + 8 * hf);
-                const u32x2 oa = *(const lds_u32x2_b *)(otr + 16 * ca + 8 * hf);
-                const u32x2 ob = *(const lds_u32x2_b *)(otr + 16 * cb + 8 * hf);
-                const bf16x8 bq = __builtin_bit_cast(bf16x8, u32x4{qa.x, qa.y, qb.x, qb.y});
-                const bf16x8 bo = __builtin_bit_cast(bf16x8, u32x4{oa.x, oa.y, ob.x, ob.y});
-                av[nt] = mma32_bf16(pa[ks], bo, av[nt]);
-                ak[nt] = mma32_bf16(da[ks], bq, ak[nt]);
+                const int ra = 16 * ks + hb, rb2 = ra + 8;
+                const lds_u8 *qa = sQ + ra * 2 * D + 16 * (cd ^ ((ra >> LRQ) & (RC - 1))) + cb;
+                const lds_u8 *qb = sQ + rb2 * 2 * D + 16 * (cd ^ ((rb2 >> LRQ) & (RC - 1))) + cb;
+                const lds_u8 *oa = sO + ra * 2 * D + 16 * (cd ^ ((ra >> LRQ) & (RC - 1))) + cb;
+                const lds_u8 *ob = sO + rb2 * 2 * D + 16 * (cd ^ ((rb2 >> LRQ) & (RC - 1))) + cb;
+                const bf16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b *)qa);
+                const bf16x4 q2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b *)qb);
+                const bf16x4 o1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b *)oa);
+                const bf16x4 o2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b *)ob);
+                const bf16x8 bq = {q1[0], q1[1], q1[2], q1[3], q2[0], q2[1], q2[2], q2[3]};
+                const bf16x8 bo = {o1[0], o1[1], o1[2], o1[3], o2[0], o2[1], o2[2], o2[3]};
+                mma32_acc_agpr(av[nt], pa[ks], bo);
+                mma32_acc_agpr(ak[nt], da[ks], bq);
             }
         }
     }
-    // the ring's last loads land before the workgroup's LDS is released
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // the ring's last loads land before the workgroup's LDS is released, and the
+    // last MFMAs finish before their accumulators are read
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
     // ---- merge into the gradient rows: lane holds dim 32nt + col, keys mfma32_row(i)
 #pragma unroll
     for (int nt = 0; nt < NTD; ++nt) {
         const int d = 32 * nt + col;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int key = 32 * wv + mfma32_row(i, lane);
-            const int r = lrow[key];
+            const int r = lrow[32 * wv + mfma32_row(i, lane)];
             if (r >= 0) {
                 if (SHARED) {
                     unsafeAtomicAdd(dk + (int64_t)r * rs + d, ak[nt][i] + av[nt][i]);
@@ -795,13 +826,13 @@ hipError_t launch_attn_bwd(const Batch &bt, int Hq, int d_qk, int d_v, const voi
     if (L.km) {
         const int nkb = (bt.max_ctx + kKvKeys - 1) / kKvKeys;
         const int ntc = (bt.max_q + kKvTokens - 1) / kKvTokens;
-        const int64_t items = (int64_t)bt.num_seqs * nkb * ntc;
+        const int64_t items = 8LL * (((int64_t)bt.num_seqs * ntc + 7) / 8) * nkb;
         if (items > 0x7fffffff)
             return hipErrorInvalidValue;
 #define SA_KV(DD, HH, SH)                                                                                         \
     hipLaunchKernelGGL((attn_bwd_kv_kernel<DD, HH, SH>), dim3((unsigned)items), dim3(256), 0, st, bt,            \
-                       (const uint16_t *)q, (const uint16_t *)kc, (const uint16_t *)vc, rs, scale, lse, dO, QT, dOT, \
-                       Dh, bits, L.W, nkb, ntc, dk, dv)
+                       (const uint16_t *)q, (const uint16_t *)kc, (const uint16_t *)vc, rs, scale, lse, dO, Dh,   \
+                       bits, L.W, nkb, ntc, dk, dv)
 #define SA_KV_H(DD, SH)                                    \
     if (Hq == 16) SA_KV(DD, 16, SH);                       \
     else if (Hq == 32) SA_KV(DD, 32, SH);                  \
