@@ -310,10 +310,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
                 else
                     issue(t + 1, LK1, LV1, ln);
             }
-#pragma unroll 1
+#pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
                 const int rb = 32 * kh;
-                const int lk = opaque(lane);
+                const int lk = lane;
                 const int g_ = lk >> 4, n_ = lk & 15;
                 // ---- S^T = K Q^T and dP^T = V do^T for keys rb..rb+15 (s0, p0) and rb+16..rb+31
                 f32x4 s0 = f32x4{0.f, 0.f, 0.f, 0.f}, s1 = s0, d0 = s0, d1 = s0;
