@@ -1391,9 +1391,12 @@ AttnPlan attn_plan(int total_q, int Hq, int d_v, int k)
     const int64_t wgs = (int64_t)total_q * groups;
     int ns = 1;
     if (wgs < 512) {
+        // at most 8 splits: each split writes a partial of d_v + 4 floats per head,
+        // which the combine reads back (16 decode tokens x 128 latent heads: 0.061
+        // ms with 8 splits, 0.072 with 16, 0.079 with 4)
         ns = (int)((512 + wgs - 1) / wgs);
         ns = min(ns, max(1, k / 128));
-        ns = min(ns, 16);
+        ns = min(ns, 8);
     }
     ns = max(ns, (k + kMaxSplit - 1) / kMaxSplit);     // a workgroup resolves at most kMaxSplit slots
     if (ns > 1) {

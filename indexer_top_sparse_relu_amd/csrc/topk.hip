@@ -826,12 +826,255 @@ __global__ __launch_bounds__(kTkThreads) void topk_merge_kernel(int K, int n_can
     select_topk<true>(cval + o, cidx + o, len, 0, K, oidx + w, oval ? oval + w : nullptr, tk_smem(K));
 }
 
+// ---------------------------------------------------------------- few long rows
+// A row of up to millions of slots, with too few rows to fill the GPU: a
+// threshold from a large sample of the row, a compaction of each chunk to the
+// slots at or above it, and the exact selection among those in one workgroup
+// per row.  As in the single-pass selection the threshold is the sample key
+// whose rank is the K-th key's expected rank in the sample plus about four
+// standard deviations, so that the kept slots very likely number between K
+// and kCap; the result never depends on the sample: a row whose kept count
+// falls outside [K, kCap] (or a chunk that keeps more than kThrCap slots) is
+// selected from its scores by the single-workgroup path instead.
+constexpr int kThrRuns = 512;           // sample: runs of 64 consecutive slots
+constexpr int kThrSample = kThrRuns * 64;
+constexpr int kThrCap = 1024;           // kept (key, position) pairs a chunk may write
+constexpr int kThrWaveCap = kThrCap / kTkWaves;
+
+// The sample's keys, streamed twice from memory (L2 the second time): the
+// window of keys at or below the rlow-th largest, to 1/NB^2 of the keys' range.
+__global__ __launch_bounds__(kTkThreads) void topk_thr_kernel(Batch bt, const float *__restrict__ scores,
+                                                              int64_t ld, int K, uint32_t *__restrict__ thr,
+                                                              int len_shift)
+{
+    const int row = blockIdx.x;
+    const int n = row_length(bt, row, len_shift);
+    const TkSmem sm = tk_smem_fast();
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const float rexp = (float)K * (float)kThrSample / (float)max(n, 1);
+    const int rlow = (int)(rexp + 4.0f * sqrtf(rexp) + 4.0f) + 1;
+    if (n < 4 * kThrSample || n >= (1 << 30) || rlow >= kThrSample) {
+        if (tid == 0)
+            thr[row] = 0u;              // not thresholded: the finish selects from the scores
+        return;
+    }
+    const float *vals = scores + (int64_t)row * ld;
+    // every run value of this lane loaded at once, kept as keys in registers
+    constexpr int RPW = kThrRuns / kTkWaves;
+    uint32_t kv[RPW];
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        const int r = wv + kTkWaves * i;
+        kv[i] = fkey(vals[(int64_t)r * (n - 64) / (kThrRuns - 1) + lane]);
+    }
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+    for (int i = 0; i < RPW; ++i) {
+        mn = min(mn, kv[i]);
+        mx = max(mx, kv[i]);
+    }
+    block_minmax(mn, mx, sm.misc);
+    uint32_t lo = mn, span = mx - mn, need = (uint32_t)rlow;
+    constexpr int LB = __builtin_ctz(kBins);
+#pragma unroll 1
+    for (int lv = 0; lv < 2; ++lv) {
+        const int sh = max(0, bitlen(span) - LB);
+        for (int b = tid; b < kBins; b += kTkThreads)
+            sm.hist[b] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < RPW; ++i)
+            if (kv[i] >= lo && kv[i] - lo <= span)
+                atomicAdd(&sm.hist[(kv[i] - lo) >> sh], 1u);
+        __syncthreads();
+        int b;
+        uint32_t gt;
+        find_bin<kBins>(sm, need, b, gt);
+        need -= gt;
+        lo += (uint32_t)b << sh;
+        if (sh == 0)
+            break;
+        span = (1u << sh) - 1u;
+    }
+    if (tid == 0)
+        thr[row] = max(lo, 1u);
+}
+
+// One workgroup per (chunk, row): the chunk's slots with key >= thr, in slot
+// order, as (key, position) pairs; count -1 when the row is not thresholded or
+// the chunk keeps more than kThrCap.  Wave w scans its own contiguous share in
+// steps of 256 slots with every load of the share in flight, compacts by lane
+// prefix counts from ballots into its LDS region, and the regions leave in wave
+// order.
+__global__ __launch_bounds__(kTkThreads) void topk_thr_chunk_kernel(Batch bt, const float *__restrict__ scores,
+                                                                    int64_t ld, int chunk, int n_chunks,
+                                                                    const uint32_t *__restrict__ thr,
+                                                                    int32_t *__restrict__ counts,
+                                                                    u32x2 *__restrict__ pairs, int len_shift)
+{
+    const int c = blockIdx.x, row = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = row_length(bt, row, len_shift);
+    const int j0 = c * chunk;
+    const int len = max(0, min(chunk, n - j0));
+    const uint32_t t = thr[row];
+    int32_t *cnt = counts + (int64_t)row * n_chunks + c;
+    if (t == 0u) {
+        if (tid == 0)
+            *cnt = -1;
+        return;
+    }
+    __shared__ u32x2 rgn[kTkWaves][kThrWaveCap];
+    __shared__ uint32_t wcnt[kTkWaves];
+    const float *vals = scores + (int64_t)row * ld + j0;
+    // wave shares of whole 256-slot steps; a slot past the chunk is masked, and
+    // its load clamped to the chunk's last slot
+    constexpr int STEP = 256, MAXS = 8;     // at most 8 steps per wave: chunks up to 16384 slots
+    const int share = (len + kTkWaves * STEP - 1) / (kTkWaves * STEP) * STEP;
+    const int s0 = wv * share;
+    float v[MAXS][4];
+    const bool v4 = (ld & 3) == 0;          // rows 16-byte aligned and readable to a multiple of 4 slots
+#pragma unroll
+    for (int st = 0; st < MAXS; ++st) {
+        const int j = s0 + st * STEP + 4 * lane;
+        const bool in = st * STEP < share && j < len;
+        if (v4) {
+            const float4 f = in ? *(const float4 *)(vals + j) : float4{0.f, 0.f, 0.f, 0.f};
+            v[st][0] = f.x;
+            v[st][1] = f.y;
+            v[st][2] = f.z;
+            v[st][3] = f.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                v[st][q] = (in && j + q < len) ? vals[j + q] : 0.0f;
+        }
+    }
+    uint32_t wc = 0;
+#pragma unroll
+    for (int st = 0; st < MAXS; ++st) {
+        if (st * STEP >= share)
+            break;
+        const int j = s0 + st * STEP + 4 * lane;
+        uint32_t kk[4], m = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            kk[q] = fkey(v[st][q]);
+            if (j + q < len && kk[q] >= t)
+                m |= 1u << q;
+        }
+        const int cq = __popc(m);
+        const uint64_t b0 = __ballot(cq & 1), b1 = __ballot(cq & 2), b2 = __ballot(cq & 4);
+        if ((b0 | b1 | b2) == 0)
+            continue;
+        auto below = [](uint64_t b) {
+            return __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u));
+        };
+        uint32_t p = wc + below(b0) + 2u * below(b1) + 4u * below(b2);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if ((m >> q) & 1u) {
+                if (p < (uint32_t)kThrWaveCap)
+                    rgn[wv][p] = u32x2{kk[q], (uint32_t)(j0 + j + q)};
+                ++p;
+            }
+        wc += (uint32_t)(__popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2));
+    }
+    if (lane == 0)
+        wcnt[wv] = wc;
+    __syncthreads();
+    uint32_t base = 0, total = 0;
+    bool ovf = false;
+#pragma unroll
+    for (int w = 0; w < kTkWaves; ++w) {
+        const uint32_t x = wcnt[w];
+        base += w < wv ? x : 0u;
+        total += x;
+        ovf |= x > (uint32_t)kThrWaveCap;
+    }
+    u32x2 *out = pairs + ((int64_t)row * n_chunks + c) * kThrCap;
+    if (!ovf)
+        for (uint32_t i = lane; i < wc; i += 64)
+            out[base + i] = rgn[wv][i];
+    if (tid == 0)
+        *cnt = ovf ? -1 : (int32_t)total;
+}
+
+// One workgroup per row: the chunks' kept pairs, concatenated in chunk order
+// (slot order), hold the row's top K when their count is in [K, kCap]; else the
+// row is selected from its scores.
+__global__ __launch_bounds__(kTkThreads) void topk_thr_finish_kernel(Batch bt, const float *__restrict__ scores,
+                                                                     int64_t ld, int K, int n_chunks,
+                                                                     const uint32_t *__restrict__ thr,
+                                                                     const int32_t *__restrict__ counts,
+                                                                     const u32x2 *__restrict__ pairs,
+                                                                     int32_t *__restrict__ out, int len_shift)
+{
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int n = row_length(bt, row, len_shift);
+    const TkSmem sm = tk_smem(K);
+    int32_t *o = out + (int64_t)row * K;
+    const float *vals = scores + (int64_t)row * ld;
+    const int32_t *cr = counts + (int64_t)row * n_chunks;
+    // chunk counts (a thread per chunk): total, validity and each chunk's offset
+    __shared__ uint32_t coff[kTkThreads + 1];
+    const int32_t x = tid < n_chunks ? cr[tid] : 0;
+    const uint32_t bad = __syncthreads_or(x < 0);
+    uint32_t tot;
+    const uint32_t ex = block_scan(x > 0 ? (uint32_t)x : 0u, sm.misc, tot);
+    if (bad || tot < (uint32_t)K || tot > (uint32_t)kCap) {
+        if (!select_topk_fast<kBins, 3>(vals, n, (ld & 3) == 0, 0, K, o, nullptr, sm))
+            select_topk<false>(vals, nullptr, n, 0, K, o, nullptr, sm);
+        return;
+    }
+    if (tid < n_chunks)
+        coff[tid] = ex;
+    if (tid == 0)
+        coff[n_chunks] = tot;
+    __syncthreads();
+    // kept pair i sits in the last chunk whose offset is <= i
+    uint32_t kmx = 0u;
+    for (uint32_t i = tid; i < tot; i += kTkThreads) {
+        int lo_ = 0, hi_ = n_chunks - 1;
+        while (lo_ < hi_) {
+            const int mid = (lo_ + hi_ + 1) >> 1;
+            if (coff[mid] <= i)
+                lo_ = mid;
+            else
+                hi_ = mid - 1;
+        }
+        const u32x2 pr = pairs[((int64_t)row * n_chunks + lo_) * kThrCap + (i - coff[lo_])];
+        sm.ckey[i] = pr.x;
+        sm.cidx[i] = (int32_t)pr.y;
+        kmx = max(kmx, pr.x);
+    }
+    uint32_t kmn = 0xFFFFFFFFu;
+    block_minmax(kmn, kmx, sm.misc);
+    finish_select<kBins>(thr[row], kmx, tot, 0u, (uint32_t)K, false, K, o, nullptr, sm, true);
+}
+
 TopkPlan topk_plan(int total_q, int max_ctx, int k)
 {
-    TopkPlan p{0, 0, 1, 1, 0};
-    // Few rows cannot fill 256 CUs: cut long rows into chunks (>= 4 * k each).
-    // Rows of up to 64K positions are still faster whole, one workgroup each
-    // (64 rows of 8K-32K: 0.024 ms against 0.043 chunked and merged).
+    TopkPlan p{0, 0, 1, 1, 0, 0};
+    // Few rows cannot fill 256 CUs: cut long rows into chunks.  Rows of up to
+    // 64K positions are still faster whole, one workgroup each (64 rows of
+    // 8K-32K: 0.024 ms against 0.043 chunked and merged).  With k <= kCap / 2
+    // the chunks are compacted against a per-row sampled threshold (about 512
+    // workgroups of up to 16384 slots); otherwise each chunk's top k is
+    // selected (chunks >= 4 k) and the lists merged.
+    if (total_q < 256 && max_ctx > 65536 && 2 * k <= kCap && max_ctx <= kTkThreads * 16384) {
+        int chunk = (int)(((int64_t)max_ctx * total_q + 511) / 512);
+        chunk = min(16384, max(4096, (chunk + 1023) / 1024 * 1024));
+        p.chunked = 1;
+        p.thr = 1;
+        p.chunk = chunk;
+        p.n_chunks = (max_ctx + chunk - 1) / chunk;
+        p.group = p.n_chunks;
+        const size_t a = ((size_t)total_q * 4 + 255) / 256 * 256;
+        const size_t b = ((size_t)total_q * p.n_chunks * 4 + 255) / 256 * 256;
+        p.ws_bytes = a + b + (size_t)total_q * p.n_chunks * kThrCap * 8;
+        return p;
+    }
     if (total_q < 256 && max_ctx > 65536) {
         const int want_chunks = (512 + total_q - 1) / total_q;
         int chunk = (max_ctx + want_chunks - 1) / want_chunks;
@@ -876,6 +1119,24 @@ hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *score
             hipFuncSetAttribute((const void *)topk_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)smem) != hipSuccess)
             return hipErrorInvalidValue;
+    }
+    if (plan.thr) {
+        if (bt.total_q > 65535)
+            return hipErrorInvalidValue;
+        if (smem > 65536 && hipFuncSetAttribute((const void *)topk_thr_finish_kernel,
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) != hipSuccess)
+            return hipErrorInvalidValue;
+        uint32_t *thr = (uint32_t *)ws;
+        int32_t *counts = (int32_t *)((char *)ws + ((size_t)bt.total_q * 4 + 255) / 256 * 256);
+        u32x2 *pairs = (u32x2 *)((char *)counts + ((size_t)bt.total_q * plan.n_chunks * 4 + 255) / 256 * 256);
+        hipLaunchKernelGGL(topk_thr_kernel, dim3(bt.total_q), dim3(kTkThreads), kTkSmemFast, st, bt, scores, ld, k,
+                           thr, len_shift);
+        hipLaunchKernelGGL(topk_thr_chunk_kernel, dim3(plan.n_chunks, bt.total_q), dim3(kTkThreads), 0, st, bt,
+                           scores, ld, plan.chunk, plan.n_chunks, (const uint32_t *)thr, counts, pairs, len_shift);
+        hipLaunchKernelGGL(topk_thr_finish_kernel, dim3(bt.total_q), dim3(kTkThreads), smem, st, bt, scores, ld, k,
+                           plan.n_chunks, (const uint32_t *)thr, (const int32_t *)counts, (const u32x2 *)pairs,
+                           indices, len_shift);
+        return hipGetLastError();
     }
     if (!plan.chunked) {
         hipLaunchKernelGGL(topk_rows_fast_kernel, dim3(bt.total_q), dim3(kTkThreads), kTkSmemFast, st, bt, scores,

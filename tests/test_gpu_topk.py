@@ -3,10 +3,12 @@
 The rows kernel and the chunked kernels try a single pass whose threshold comes
 from a sample of 64 (128 on rows of 32K slots or more) runs of 64 consecutive
 slots; when the kept count misses [K, capacity] they fall back to the general
-selection.  These rows drive both
-branches: plain random rows, constant rows and coarse alphabets (massive
-ties), ramps, rows whose large values sit exactly on (or exactly off) the
-sampled runs, and signed zeros.
+selection.  Few long rows (k <= 2048) take a per-row threshold from 512 runs
+instead, compact every chunk against it and finish per row, falling back to
+the single-workgroup selection of the row.  These rows drive every branch:
+plain random rows, constant rows and coarse alphabets (massive ties), ramps,
+rows whose large values sit exactly on (or exactly off) the sampled runs of
+either sample, and signed zeros.
 """
 import numpy as np
 import pytest
@@ -31,9 +33,9 @@ def sample_runs(n):
     return 128 if n >= 32768 else 64
 
 
-def sampled_mask(n):
-    """Slots the single-pass sample reads: run r starts at r*(n-64)//(runs-1)."""
-    runs = sample_runs(n)
+def sampled_mask(n, runs=None):
+    """Slots a sample reads: run r starts at r*(n-64)//(runs-1) (the single pass's runs by default)."""
+    runs = runs or sample_runs(n)
     m = np.zeros(n, bool)
     for r in range(runs):
         j = (r * (n - 64)) // (runs - 1)
@@ -59,6 +61,12 @@ def pattern_row(kind, n, rng):
         v = rng.uniform(10.0, 11.0, n).astype(np.float32)
         m = sampled_mask(n)
         v[m] = rng.uniform(0.0, 1.0, int(m.sum())).astype(np.float32)
+        return v
+    if kind in ("on_sample512", "off_sample512"):
+        hi, lo = (10.0, 0.0) if kind == "on_sample512" else (0.0, 10.0)
+        v = rng.uniform(lo, lo + 1.0, n).astype(np.float32)
+        m = sampled_mask(n, 512)
+        v[m] = rng.uniform(hi, hi + 1.0, int(m.sum())).astype(np.float32)
         return v
     if kind == "signed_zero":
         v = rng.standard_normal(n).astype(np.float32)
@@ -113,10 +121,21 @@ def test_topk_rows_kernel_crafted_rows():
 
 
 def test_topk_chunked_crafted_rows():
-    """Few long rows (chunked selection, then merge), every pattern."""
+    """Few long rows (sampled threshold, chunk compaction, per-row finish), every pattern."""
     lengths = [300000, 150001, 70000, 40960, 262144, 100000, 65537, 200000]
     P.say("[topk-chunked] 8 rows up to 300K, K=2048")
     wsb = run_rows(lengths, KINDS, 2048, seed=9)
+    assert wsb > 0
+
+
+@pytest.mark.parametrize("K", [64, 4096])
+def test_topk_chunked_long_rows_k(K):
+    """Rows past 131072 slots (sampled from 512 runs), including rows made to fool that sample;
+    k = 4096 takes the per-chunk selection and merge instead."""
+    lengths = [1000003, 524288, 131072, 140000, 400000, 1000]
+    kinds = ["normal", "on_sample512", "off_sample512", "rounded", "alphabet", "normal"]
+    P.say(f"[topk-long] 6 rows up to 1M, K={K}")
+    wsb = run_rows(lengths, kinds, K, seed=12 + K)
     assert wsb > 0
 
 
