@@ -23,6 +23,7 @@ struct TopkPlan {
     int group;        // chunk lists per first-level merge (n_chunks: one merge level)
     size_t ws_bytes;  // workspace the plan needs
     int thr;          // chunked by a per-row sampled threshold (compaction, then one finish per row)
+    int reg;          // slots per thread when every row is held in registers (16), else 0
 };
 TopkPlan topk_plan(int total_q, int max_ctx, int k);
 // len_shift 0: row i holds the pos_i + 1 position scores; len_shift > 0: the

@@ -777,6 +777,116 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_fast_kernel(Batch bt, co
         o[0] = kTkPending;
 }
 
+// Rows of up to 512 * PER slots, one workgroup each, in one launch: the row is
+// loaded once into registers (thread t holds the 4-slot groups t, t + 512, ...,
+// so every load is coalesced), the K-th largest key is found by three LDS
+// histogram levels over its bits (12, 12 and 8), and the winners are written in
+// slot order: one block scan per round of groups counts, before each thread,
+// the keys above the K-th and the keys equal to it (ties go to the lowest
+// positions).
+template <int PER>
+__global__ __launch_bounds__(kTkThreads) void topk_rows_reg_kernel(Batch bt, const float *__restrict__ scores,
+                                                                   int64_t ld, int K, int32_t *__restrict__ out,
+                                                                   int len_shift)
+{
+    static_assert(PER % 4 == 0, "4-slot groups");
+    constexpr int G = PER / 4;                  // groups per thread
+    __shared__ uint32_t hist[kBins];
+    __shared__ uint32_t misc[64];
+    TkSmem sm;
+    sm.hist = hist;
+    sm.misc = misc;
+    const int row = blockIdx.x, tid = threadIdx.x;
+    const int n = row_length(bt, row, len_shift);
+    const float *vals = scores + (int64_t)row * ld;
+    int32_t *o = out + (int64_t)row * K;
+    if (n <= K) {
+        // every slot is selected: position j goes to output j, the rest is -1
+        for (int j = tid; j < K; j += kTkThreads)
+            o[j] = j < n ? j : -1;
+        return;
+    }
+    const bool v4 = (ld & 3) == 0 && (((uintptr_t)vals) & 15u) == 0;
+    uint32_t key[G][4];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        const int j = 4 * (tid + kTkThreads * u);
+        float f[4];
+        if (v4 && j + 3 < n) {
+            const float4 x = *(const float4 *)(vals + j);
+            f[0] = x.x;
+            f[1] = x.y;
+            f[2] = x.z;
+            f[3] = x.w;
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                f[q] = j + q < n ? vals[j + q] : 0.0f;
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            key[u][q] = j + q < n ? fkey(f[q]) : 0u;      // 0: below every finite score's key
+    }
+    // ---- the K-th largest key, 12 + 12 + 8 bits
+    uint32_t prefix = 0u, need = (uint32_t)K;
+    const int shifts[3] = {20, 8, 0};
+    const uint32_t masks[3] = {0xFFFu, 0xFFFu, 0xFFu};
+#pragma unroll
+    for (int lv = 0; lv < 3; ++lv) {
+        const int sh = shifts[lv];
+        for (int b = tid; b < kBins; b += kTkThreads)
+            hist[b] = 0u;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < G; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int j = 4 * (tid + kTkThreads * u) + q;
+                const uint32_t k = key[u][q];
+                // keys whose bits above this level match the prefix found so far
+                if (j < n && (lv == 0 || (k >> (sh + (lv == 1 ? 12 : 8))) == prefix))
+                    atomicAdd(&hist[(k >> sh) & masks[lv]], 1u);
+            }
+        __syncthreads();
+        int b;
+        uint32_t gt;
+        find_bin<kBins>(sm, need, b, gt);
+        need -= gt;
+        prefix = (prefix << (lv == 0 ? 12 : (lv == 1 ? 12 : 8))) | (uint32_t)b;
+    }
+    const uint32_t kth = prefix;                // the K-th largest key
+    const uint32_t ties = need;                 // keys equal to it that are taken (lowest positions)
+    // ---- winners in slot order
+    uint32_t above_done = 0, ties_done = 0;     // before this round, over the whole block
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+        const int j = 4 * (tid + kTkThreads * u);
+        uint32_t a = 0, e = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = j + q < n;
+            a += ok && key[u][q] > kth;
+            e += ok && key[u][q] == kth;
+        }
+        uint32_t tot;
+        const uint32_t ex = block_scan(a | (e << 16), misc, tot);
+        uint32_t ab = above_done + (ex & 0xFFFFu), tb = ties_done + (ex >> 16);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (j + q >= n)
+                continue;
+            const uint32_t k = key[u][q];
+            if (k > kth || (k == kth && tb < ties)) {
+                o[ab + min(tb, ties)] = j + q;
+            }
+            ab += k > kth;
+            tb += k == kth;
+        }
+        above_done += tot & 0xFFFFu;
+        ties_done += tot >> 16;
+    }
+}
+
 __global__ __launch_bounds__(kTkThreads) void topk_rows_kernel(Batch bt, const float *__restrict__ scores,
                                                                int64_t ld, int K, int32_t *__restrict__ out,
                                                                int len_shift)
@@ -1055,7 +1165,15 @@ __global__ __launch_bounds__(kTkThreads) void topk_thr_finish_kernel(Batch bt, c
 
 TopkPlan topk_plan(int total_q, int max_ctx, int k)
 {
-    TopkPlan p{0, 0, 1, 1, 0, 0};
+    TopkPlan p{0, 0, 1, 1, 0, 0, 0};
+    // rows of up to 8192 slots: one launch, each row held in registers (8192
+    // rows of up to 8192: 0.103 ms against 0.201 for the single pass and the
+    // general path; 64 rows of 8K-32K at 64 slots per thread took 0.037 ms
+    // against 0.029: too few workgroups)
+    if (max_ctx <= 512 * 16) {
+        p.reg = 16;
+        return p;
+    }
     // Few rows cannot fill 256 CUs: cut long rows into chunks.  Rows of up to
     // 64K positions are still faster whole, one workgroup each (64 rows of
     // 8K-32K: 0.024 ms against 0.043 chunked and merged).  With k <= kCap / 2
@@ -1119,6 +1237,11 @@ hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *score
             hipFuncSetAttribute((const void *)topk_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)smem) != hipSuccess)
             return hipErrorInvalidValue;
+    }
+    if (plan.reg) {
+        hipLaunchKernelGGL((topk_rows_reg_kernel<16>), dim3(bt.total_q), dim3(kTkThreads), 0, st, bt, scores, ld, k,
+                           indices, len_shift);
+        return hipGetLastError();
     }
     if (plan.thr) {
         if (bt.total_q > 65535)

@@ -128,6 +128,19 @@ def test_topk_chunked_crafted_rows():
     assert wsb > 0
 
 
+@pytest.mark.parametrize("K", [1, 2048, 4096])
+def test_topk_register_rows_crafted(K):
+    """Rows of up to 8192 slots, one workgroup each with the row in registers (16 slots per
+    thread): every pattern, rows shorter than K included; and 64 rows of up to 32768 (the single
+    pass and the general path)."""
+    rng = np.random.default_rng(20 + K)
+    for hi, nrows in ((8192, 300), (32768, 64)):
+        lengths = rng.integers(1, hi + 1, nrows).tolist()
+        lengths[0], lengths[1] = hi, max(1, K - 1)
+        P.say(f"[topk-reg] {nrows} rows up to {hi}, K={K}")
+        assert run_rows(lengths, KINDS, K, seed=30 + K + hi) == 0
+
+
 @pytest.mark.parametrize("K", [64, 4096])
 def test_topk_chunked_long_rows_k(K):
     """Rows past 131072 slots (sampled from 512 runs), including rows made to fool that sample;
