@@ -855,7 +855,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int NI = TK / RPI;            // load instructions per tile and cache
     constexpr int NT = SHARED ? 1 : 2;      // LDS tiles per wave (K, V)
     static_assert(D % 64 == 0 && NKQ % 4 == 0 && 64 % (D / 8) == 0, "dims");
-    constexpr int MAXT = kMaxSplit / TK + 2;   // tiles of a list, plus the two loaded past its end
+    constexpr int MAXT = kMaxSplit / TK + 3;   // tiles of a list, the two loaded past its end, and one more
+                                               // whose offsets are read (not used) after the last step
     __shared__ __align__(16) uint8_t ltile[NW * NT * TB];
     __shared__ uint64_t loff[NW * MAXT * TK];  // byte offset of each slot's cache row
     __shared__ uint32_t lmask[NW * MAXT];     // valid slots of each tile, one bit per key
@@ -904,7 +905,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // bounds, their keys are masked)
         const uint64_t rsb = (uint64_t)rs * 2;
         const int64_t row0 = phys_row(bt, b, 0);
-        constexpr int PS = kMaxSplit / 64 + 1;
+        constexpr int PS = kMaxSplit / 64 + 2;
         int sv[PS];
 #pragma unroll
         for (int u = 0; u < PS; ++u) {
@@ -951,12 +952,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int lrow = lane / (D / 8), lch = lane % (D / 8);
     const uint8_t *const kbase = (const uint8_t *)kc + 16 * lch;
     const uint8_t *const vbase = (const uint8_t *)vc + 16 * lch;
-    auto load_stage = [&](int t) {
-        Stage st;
+    // the byte offsets of this lane's rows of tile t, read from LDS one tile
+    // before its loads are issued, so that the issue waits on no LDS read
+    struct Offs {
+        uint64_t o[NI];
+    };
+    auto read_offs = [&](int t) {
+        Offs r;
         const uint64_t *o = off + t * TK + lrow;
 #pragma unroll
+        for (int i = 0; i < NI; ++i)
+            r.o[i] = o[RPI * i];
+        return r;
+    };
+    auto load_stage = [&](const Offs &of) {
+        Stage st;
+#pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const uint64_t ob = o[RPI * i];
+            const uint64_t ob = of.o[i];
             st.k[i] = *(const i32x4 *)(kbase + ob);
             if constexpr (!SHARED)
                 st.v[i] = *(const i32x4 *)(vbase + ob);
@@ -1012,12 +1025,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bf16x8 *qop = qo.v;
         // two stages in registers: tile t is written to LDS while t+1 is in flight,
         // then the stage is reloaded with tile t+2
-        Stage s0 = load_stage(0), s1 = load_stage(1);
+        Stage s0 = load_stage(read_offs(0)), s1 = load_stage(read_offs(1));
+        Offs on = read_offs(2);
         auto step = [&](int t, Stage &st, auto first_c, auto partial_c) {
             constexpr bool FIRST = decltype(first_c)::value, PARTIAL = decltype(partial_c)::value;
             put_stage(st);
             asm volatile("" ::: "memory");      // the tile's writes precede its reads
-            st = load_stage(t + 2);
+            st = load_stage(on);                // tile t + 2
+            on = read_offs(t + 3);
             // ---- S^T = K Q^T: A = K row cl, chunk 2ks + hl
             // (written as asm so that the accumulator stays in VGPRs, where the
             // softmax reads it; the AGPRs hold O.  The last MFMA is followed by the
@@ -1065,15 +1080,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     m_ref = mx;
             }
             if (mode != 1) {
-                const float base = m_ref == -INFINITY ? 0.0f : m_ref;
-                bf16x8 pop[2];
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const float pi = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -base));
-                    l_run += pi;
-                    pop[i >> 3][i & 7] = (__bf16)pi;
-                }
-                // ---- O^T += V^T P^T (transpose loads; the latent kernel's V^T mapping)
+                // ---- O^T += V^T P^T (transpose loads; the latent kernel's V^T mapping).
+                // The first V^T operands are read before the softmax terms, whose
+                // VALU work covers their LDS latency.
                 auto ldv = [&](int dt, int j, int sec) {
                     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
                         (lds_bf16x4 *)(vb[dt & 1][sec] + (2 * j + sec) * KCB * 1024 + (dt >> 1) * 1024));
@@ -1088,6 +1097,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
                 for (int d = 0; d < PD; ++d)
                     va[d] = ldv8(vstep(d));
+                const float base = m_ref == -INFINITY ? 0.0f : m_ref;
+                bf16x8 pop[2];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float pi = __builtin_amdgcn_exp2f(fmaf(s[i], scale_log2, -base));
+                    l_run += pi;
+                    pop[i >> 3][i & 7] = (__bf16)pi;
+                }
 #pragma unroll
                 for (int u = 0; u < 2 * NDT; ++u) {
                     oa[u % NDT] = mma32_bf16(va[u % PD], pop[u / NDT], oa[u % NDT]);
