@@ -489,9 +489,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int NTD = D / 32;             // 32-dim tiles of dK, dV
     constexpr int HKS = H / 16;             // k-steps over heads
     constexpr int RC = 2 * D / 16;          // 16-byte chunks per row of Q_i, do_i
-    // row r's logical chunk c sits at c ^ ((r >> LRQ) & (RC - 1)), LRQ = log2 of the rows
-    // per 256-byte bank period: the 32 rows an operand read touches spread over the banks
-    constexpr int LRQ = D == 128 ? 0 : 1;
+    // Row r's logical chunk c sits at c ^ swz(r).  Two reads must hit distinct banks
+    // (64 four-byte banks, 256 bytes per bank period, rows of 2D bytes):
+    //   - a 128-bit operand read: 16 lanes, 16 consecutive rows (mod 16), one chunk;
+    //   - a 64-bit transpose read: 32 lanes, rows 4m .. 4m+3 x chunks 4n .. 4n+3, each
+    //     half a chunk.
+    // d = 128 (one row per bank period): swz swaps the two 2-bit halves of r mod 16, so
+    // that the 4 rows of a transpose read differ in position bits 2-3 and its 4 chunks in
+    // bits 0-1.  d = 64 (two rows per period, told apart by r & 1): swz takes bit 1 of r
+    // to position bit 2 and bits 2-3 of r to position bits 0-1.  (Plain c ^ (r mod 16)
+    // put the 16 row-chunk pairs of a transpose read on 4 positions: 4-way conflicts.)
+    static_assert(D == 64 || D == 128, "swizzle for 64 or 128 dims");
+    auto swz = [](int r) {
+        return D == 128 ? ((r & 3) << 2) | ((r >> 2) & 3) : (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+    };
     constexpr int NB = 2 * QB / 1024;       // 1 KB loads per token
     static_assert(H % 16 == 0 && D % 32 == 0 && QB % 1024 == 0 && NB % 4 == 0 && RC <= 16, "shape");
     static_assert(kKvKeys == 32 * 4 && kKvKeys <= 256 && kKvTokens <= 256, "one wave per 32 keys, a thread per token");
@@ -592,7 +603,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int op = kb_ / (QB / 1024);                        // 0 Q, 1 do
             const int off = (kb_ % (QB / 1024)) * 1024 + 16 * ln;    // this lane's position in the operand
             const int r = off / (2 * D), p = (off % (2 * D)) / 16;
-            const int c = p ^ ((r >> LRQ) & (RC - 1));
+            const int c = p ^ swz(r);
             const uint16_t *src = (op == 0 ? q : dO) + (int64_t)tk * H * D + r * D + 8 * c;
             dma_b128(src, dst + kb_ * 1024);
         }
@@ -637,7 +648,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const lds_u8 *orow = sO + (hv ? hr : 0) * 2 * D;
 #pragma unroll
             for (int kk = 0; kk < KS; ++kk) {
-                const int c = (2 * kk + hf) ^ ((hr >> LRQ) & (RC - 1));
+                const int c = (2 * kk + hf) ^ swz(hr);
                 bf16x8 aq = *(const lds_bf16x8_b *)(qrow + 16 * c);
                 bf16x8 ao = *(const lds_bf16x8_b *)(orow + 16 * c);
                 if (!hv) {
@@ -672,10 +683,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
             for (int ks = 0; ks < HKS; ++ks) {
                 const int ra = 16 * ks + hb, rb2 = ra + 8;
-                const lds_u8 *qa = sQ + ra * 2 * D + 16 * (cd ^ ((ra >> LRQ) & (RC - 1))) + cb;
-                const lds_u8 *qb = sQ + rb2 * 2 * D + 16 * (cd ^ ((rb2 >> LRQ) & (RC - 1))) + cb;
-                const lds_u8 *oa = sO + ra * 2 * D + 16 * (cd ^ ((ra >> LRQ) & (RC - 1))) + cb;
-                const lds_u8 *ob = sO + rb2 * 2 * D + 16 * (cd ^ ((rb2 >> LRQ) & (RC - 1))) + cb;
+                const lds_u8 *qa = sQ + ra * 2 * D + 16 * (cd ^ swz(ra)) + cb;
+                const lds_u8 *qb = sQ + rb2 * 2 * D + 16 * (cd ^ swz(rb2)) + cb;
+                const lds_u8 *oa = sO + ra * 2 * D + 16 * (cd ^ swz(ra)) + cb;
+                const lds_u8 *ob = sO + rb2 * 2 * D + 16 * (cd ^ swz(rb2)) + cb;
                 const bf16x4 q1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b *)qa);
                 const bf16x4 q2 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b *)qb);
                 const bf16x4 o1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_b *)oa);
