@@ -896,7 +896,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     };
     const QOp q0 = load_q();
     // leading tiles with every key valid, and the tiles up to the last valid key
-    // (lists from sparse_topk hold their valid positions first, then -1)
+    // (lists from sparse_topk hold their valid positions first, then -1, so all
+    // but the last of their tiles are full; any other list takes the masked step
+    // from its first tile with a missing key on)
     int nfull = 0, ntiles = 0;
     {
         // every slot's index, then every page-table entry (two round trips); each
@@ -1017,12 +1019,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // One pass over the index list.  mode 0: reference from the first valid
     // keys, accumulate; mode 1: exact maximum only (m_true); mode 2: reference
     // m_ref as given, accumulate.
-    // The reference is taken from tile 0 (a list's first valid keys) and the
-    // leading full tiles need no key mask, so the steady-state tile step carries
-    // neither: `first` and `partial` are compile-time flags.  (With no valid key
-    // in tile 0 the reference stays -inf; any overflow then takes the rerun.)
+    // The reference is taken from the first tile with a valid key (tile 0 for a
+    // list from sparse_topk) and the leading full tiles need no key mask, so the
+    // steady-state tile step carries neither: `first` and `partial` are
+    // compile-time flags, and later tiles test the wave-uniform have_ref only
+    // until some tile has set the reference.
     auto run = [&](f32x16 (&oa)[NDT], const int mode, const QOp &qo) {
         const bf16x8 *qop = qo.v;
+        bool have_ref = false;      // mode 0: the reference has been set from some valid key
         // two stages in registers: tile t is written to LDS while t+1 is in flight,
         // then the stage is reloaded with tile t+2
         Stage s0 = load_stage(read_offs(0)), s1 = load_stage(read_offs(1));
@@ -1062,22 +1066,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 }
             }
             // logits in log2 units; keys outside the list get -inf (a term of 0)
+            const uint32_t vmask = PARTIAL ? __builtin_amdgcn_readfirstlane(msk[t]) : 0xFFFFFFFFu;
             if constexpr (PARTIAL) {
-                const uint32_t vmask = __builtin_amdgcn_readfirstlane(msk[t]);
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     s[i] = ((vmask >> (8 * (i >> 2) + 4 * hl + (i & 3))) & 1) ? s[i] : -INFINITY;
             }
-            if (mode == 1 || (mode == 0 && FIRST)) {
+            if (mode == 1 || (mode == 0 && (FIRST || !have_ref))) {
                 float mx = -INFINITY;
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
                     mx = fmaxf(mx, s[i] * scale_log2);
                 mx = max_halves(mx);
-                if (mode == 1)
+                if (mode == 1) {
                     m_true = fmaxf(m_true, mx);
-                else
+                } else {
                     m_ref = mx;
+                    have_ref = vmask != 0u;
+                }
             }
             if (mode != 1) {
                 // ---- O^T += V^T P^T (transpose loads; the latent kernel's V^T mapping).
@@ -1119,11 +1125,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         if (ntiles == 0)
             return;
         // tile 0 (stage s0), then the full tiles in pairs (s1, s0), then the tail
-        if (nfull == 0) {
+        if (nfull == 0)
             step(0, s0, T_{}, T_{});
-            return;
-        }
-        step(0, s0, T_{}, F_{});
+        else
+            step(0, s0, T_{}, F_{});
         int t = 1;
         for (; t + 1 < nfull; t += 2) {
             step(t, s1, F_{}, F_{});

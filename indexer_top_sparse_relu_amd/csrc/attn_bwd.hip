@@ -252,15 +252,35 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
     lds_u8 *const LV0 = (lds_u8 *)lv0, *const LV1 = (lds_u8 *)lv1;
     constexpr int RG = kBwdTK / 8;
 
+    static_assert(kBwdChunk / kBwdTK <= 32, "a bit per tile of a pass");
+    __shared__ uint32_t lfm;
     for (int c0 = 0; c0 < K; c0 += kBwdChunk) {
         const int nslots = min(kBwdChunk, K - c0);
+        const int ntiles = (nslots + kBwdTK - 1) / kBwdTK;
         __syncthreads();                    // the previous chunk's rows and tiles are done with
+        // the tiles this pass visits (bit t: tile t): all of them, or in mode 3 only
+        // those holding a flagged repeat
+        uint32_t fm = ntiles >= 32 ? 0xFFFFFFFFu : (1u << ntiles) - 1u;
+        if (mode == 3) {
+            uint32_t m = 0u;
+            for (int j = tid; j < nslots; j += NT)
+                if (flags[(int64_t)tok * K + c0 + j])
+                    m |= 1u << (j / kBwdTK);
+            if (tid == 0)
+                lfm = 0u;
+            __syncthreads();
+            if (m)
+                atomicOr(&lfm, m);
+            __syncthreads();
+            fm = lfm;
+            if (fm == 0u)
+                continue;
+        }
         for (int j = tid; j < nslots; j += NT) {
             const int s = irow[c0 + j];
             prow[j] = s >= 0 ? (int)phys_row(bt, b, s) : -1 - row0;
         }
         __syncthreads();
-        const int ntiles = (nslots + kBwdTK - 1) / kBwdTK;
         auto issue = [&](int t, lds_u8 *dk_, lds_u8 *dv_, int ln) {
 #pragma unroll
             for (int rg = wv; rg < RG; rg += NW) {
@@ -283,32 +303,39 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
                 }
             }
         };
-        if (ntiles > 0)
-            issue(0, LK0, LV0, lane);
-        for (int t = 0; t < ntiles; ++t) {
+        const int nvisit = __popc(fm);
+        int tcur = fm ? __builtin_ctz(fm) : 0;
+        uint32_t rest = fm & (fm - 1u);
+        if (nvisit > 0)
+            issue(tcur, LK0, LV0, lane);
+        for (int it = 0; it < nvisit; ++it) {
+            const int t = tcur;
+            const int tnext = rest ? __builtin_ctz(rest) : -1;
+            tcur = tnext;
+            rest &= rest - 1u;
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
-            const bool odd = t & 1;
+            const bool odd = it & 1;
             const int ln = opaque(lane);
             const int myslot = t * kBwdTK + ln;
             const bool myvalid = myslot < nslots && prow[myslot < nslots ? myslot : 0] >= 0;
             const uint64_t vmask = __ballot(myvalid);
-            // scatter this tile: every valid slot (mode 1) or the flagged repeats (mode 2);
-            // every wave forms the same mask
+            // scatter this tile: every valid slot (mode 1) or the flagged repeats (modes 2
+            // and 3); every wave forms the same mask
             bool sc_me = false;
             if (mode == 1)
                 sc_me = myvalid;
-            else if (mode == 2 && myvalid)
+            else if (mode >= 2 && myvalid)
                 sc_me = flags[(int64_t)tok * K + c0 + myslot] != 0;
             const uint64_t scmask = __ballot(sc_me);
             const bool scatter = scmask != 0;
             lds_u8 *tk = odd ? LK1 : LK0;
             lds_u8 *tv = MLA ? tk : (odd ? LV1 : LV0);
-            if (t + 1 < ntiles) {
+            if (tnext >= 0) {
                 if (odd)
-                    issue(t + 1, LK0, LV0, ln);
+                    issue(tnext, LK0, LV0, ln);
                 else
-                    issue(t + 1, LK1, LV1, ln);
+                    issue(tnext, LK1, LV1, ln);
             }
 #pragma unroll
             for (int kh = 0; kh < 2; ++kh) {
@@ -433,11 +460,298 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
             }
         }
     }
+    if (mode == 3)
+        return;                             // d_q comes from attn_bwd_dq32_kernel
     // ---- dq out: lane holds head h, dims 16mt + 4g + i
     float *dqp = dq + ((int64_t)tok * Hq + h) * DQK + 4 * g;
 #pragma unroll
     for (int mt = 0; mt < NMQ; ++mt)
         *(f32x4 *)(dqp + 16 * mt) = dqa[mt] * scale;
+}
+
+// ------------------------------------------------------------------ dq, 32 heads per wave
+// d_qk = d_v = 128, a multiple of 32 query heads, lists of at most kDq32MaxK slots:
+// one wave per (token, 32 heads), the four waves of a workgroup independent
+// (consecutive tokens, no workgroup barrier), on 32x32x16 bf16 MFMA.  The gather
+// is the forward MQA kernel's: each load instruction covers four whole rows, into
+// VGPRs two tiles ahead (row offsets read one tile before that), then into the
+// wave's LDS tiles, blocks of 8 rows x 8 sixteen-byte chunks at position
+// (c & 7) ^ g(r).  Per 32-key tile:
+//   - S^T = K Q^T and dP^T = V do^T, two interleaved chains of 8 MFMAs (asm, so
+//     that their accumulators stay in VGPRs while dq^T holds AGPRs); a lane holds
+//     one head's column, keys 8(i >> 2) + 4hq + (i & 3) in register i;
+//   - P = 2^(S scale log2 e - lse log2 e), zero for slots outside the list, and
+//     dS = P (dP - D);
+//   - dq^T += K^T dS^T (8 MFMAs): K^T by transpose loads of the row-major K tile,
+//     dS^T the lane's own registers, in the key order the loads deliver.
+// d_q = scale dq^T leaves as whole 16-byte runs.  The flagged repeats' dK, dV are
+// merged by attn_bwd_dq_kernel in its repeats-only mode.
+constexpr int kDq32MaxK = 2048;
+
+__device__ __forceinline__ int dq32_g(int r) { return (((r >> 1) & 1) << 2) | (((r >> 3) & 1) << 1) | ((r >> 2) & 1); }
+
+template <bool SHARED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attn_bwd_dq32_kernel(
+    Batch bt, const uint16_t *__restrict__ q, int Hq, const uint16_t *__restrict__ kc,
+    const uint16_t *__restrict__ vc, int64_t rs, const int32_t *__restrict__ idx, int K, float scale,
+    const float *__restrict__ lse, const uint16_t *__restrict__ dO, const float *__restrict__ Dh,
+    float *__restrict__ dq, int n_units)
+{
+    constexpr int D = 128;
+    constexpr int NW = 4;
+    constexpr int NKQ = D / 16;             // k-steps of the S^T and dP^T chains
+    constexpr int NDT = D / 32;             // 32-dim tiles of dq^T
+    constexpr int KCB = D / 64;             // 8-chunk blocks per row
+    constexpr int TK = 32;                  // keys per tile
+    constexpr int TB = TK * D * 2;          // bytes of one K (or V) tile in LDS
+    constexpr int RPI = 64 / (D / 8);       // rows per load instruction
+    constexpr int NI = TK / RPI;            // load instructions per tile and cache
+    constexpr int NT = SHARED ? 1 : 2;      // LDS tiles per wave (K, V)
+    constexpr int MAXT = kDq32MaxK / TK + 3;   // a list's tiles, two loaded past its end, one more read
+    static_assert(RPI == 4, "four rows per load instruction");
+    __shared__ __align__(16) uint8_t ltile[NW * NT * TB];
+    __shared__ uint64_t loff[NW * MAXT * TK];  // byte offset of each slot's cache row
+    __shared__ uint32_t lmask[NW * MAXT];     // valid slots of each tile, one bit per key
+
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int unit = blockIdx.x * NW + wv;
+    if (unit >= n_units)
+        return;
+    const int HG = Hq >> 5;
+    const int hg = unit % HG, tok = unit / HG;
+    const int col = lane & 31, hq = lane >> 5;
+    const int h = hg * 32 + col;
+    const int b = seq_of_token(bt, tok);
+    const int32_t *irow = idx + (int64_t)tok * K;
+    lds_u8 *const tk = (lds_u8 *)ltile + wv * NT * TB;
+    lds_u8 *const tv = SHARED ? tk : tk + TB;
+    uint64_t *const off = loff + wv * MAXT * TK;
+    uint32_t *const msk = lmask + wv * MAXT;
+
+    // this lane's head: lse (a head with no valid key has lse = -inf and no gradient:
+    // its terms are 2^-inf = 0) and D = dy . y
+    const float L = lse[(int64_t)tok * Hq + h];
+    const float L2 = L != -INFINITY ? L * kBLog2e : INFINITY;
+    const float Dv = Dh[(int64_t)tok * Hq + h];
+    const float sl2 = scale * kBLog2e;
+    // B operands Q^T and do^T: head h, dims 16ks + 8hq .. +7
+    bf16x8 qop[NKQ], dop[NKQ];
+    {
+        const uint16_t *qp = q + ((int64_t)tok * Hq + h) * D + 8 * hq;
+        const uint16_t *dp = dO + ((int64_t)tok * Hq + h) * D + 8 * hq;
+#pragma unroll
+        for (int ks = 0; ks < NKQ; ++ks) {
+            qop[ks] = *(const bf16x8 *)(qp + 16 * ks);
+            dop[ks] = *(const bf16x8 *)(dp + 16 * ks);
+        }
+    }
+    // every slot's index, then every page-table entry (two round trips); slots past
+    // the list or holding -1 keep position 0's row (in bounds, masked)
+    int ntiles = 0;
+    {
+        const uint64_t rsb = (uint64_t)rs * 2;
+        const int64_t row0 = phys_row(bt, b, 0);
+        constexpr int PS = kDq32MaxK / 64 + 2;
+        int sv[PS];
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            const int j = lane + 64 * u;
+            sv[u] = j < K ? irow[j] : -1;
+        }
+        int pg[PS];
+#pragma unroll
+        for (int u = 0; u < PS; ++u)
+            pg[u] = bt.page_table[(int64_t)b * bt.max_pages + ((sv[u] >= 0 ? sv[u] : 0) >> bt.page_shift)];
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            const int j = lane + 64 * u;
+            const int64_t pr = sv[u] >= 0 ? ((int64_t)pg[u] << bt.page_shift) + (sv[u] & ((1 << bt.page_shift) - 1))
+                                          : row0;
+            if (j < MAXT * TK)
+                off[j] = (uint64_t)pr * rsb;
+            const uint64_t vb = __ballot(sv[u] >= 0);
+            const uint32_t lo = (uint32_t)vb, hi = (uint32_t)(vb >> 32);
+            if (lo)
+                ntiles = 2 * u + 1;
+            if (hi)
+                ntiles = 2 * u + 2;
+            if (lane == 0 && 2 * u < MAXT) {
+                msk[2 * u] = lo;
+                if (2 * u + 1 < MAXT)
+                    msk[2 * u + 1] = hi;
+            }
+        }
+    }
+
+    // ---- the gather: instruction i, lane l -> tile row RPI*i + l / (D/8), chunk l % (D/8)
+    struct Stage {
+        i32x4 k[NI];
+        i32x4 v[SHARED ? 1 : NI];
+    };
+    struct Offs {
+        uint64_t o[NI];
+    };
+    const int lrow = lane / (D / 8), lch = lane % (D / 8);
+    const uint8_t *const kbase = (const uint8_t *)kc + 16 * lch;
+    const uint8_t *const vbase = (const uint8_t *)vc + 16 * lch;
+    auto read_offs = [&](int t) {
+        Offs r;
+        const uint64_t *o = off + t * TK + lrow;
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            r.o[i] = o[RPI * i];
+        return r;
+    };
+    auto load_stage = [&](const Offs &of) {
+        Stage st;
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            st.k[i] = *(const i32x4 *)(kbase + of.o[i]);
+            if constexpr (!SHARED)
+                st.v[i] = *(const i32x4 *)(vbase + of.o[i]);
+        }
+        return st;
+    };
+    // LDS position of chunk c of tile row r = RPI*i + lrow: block (i >> 1) * KCB + c / 8,
+    // row 4(i & 1) + lrow of the block, position (c & 7) ^ g(r), g(r) = 4(lrow >> 1) + (i & 3)
+    lds_u8 *wbase[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+        wbase[c] = tk + (lch >> 3) * 1024 + lrow * 128 + 16 * (((lch & 7) ^ (4 * (lrow >> 1))) ^ c);
+    auto put_stage = [&](const Stage &st) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int cst = (i >> 1) * KCB * 1024 + (i & 1) * 512;
+            *(__attribute__((address_space(3))) i32x4 *)(wbase[i & 3] + cst) = st.k[i];
+            if constexpr (!SHARED)
+                *(__attribute__((address_space(3))) i32x4 *)(wbase[i & 3] + (tv - tk) + cst) = st.v[i];
+        }
+    };
+    // A operands of the chains: row cl, chunk 2ks + hl of the K (or V) tile
+    const int cl = lane & 31, hl = lane >> 5;
+    lds_u8 *kb[4];
+    {
+        lds_u8 *krow = tk + (cl >> 3) * KCB * 1024 + (cl & 7) * 128;
+        const int gh = hl ^ dq32_g(cl);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            kb[m] = krow + 16 * ((2 * m) ^ gh);
+    }
+    // K^T transpose-load bases (group G = lane / 16, i = lane % 16 reads row
+    // 16j + 8sec + 4hl + (i >> 2), dims 32dt + 16(G & 1) + 4(i & 3) .. +3)
+    lds_u8 *ktb[2][2];
+    {
+        const int G = lane >> 4, i16 = lane & 15;
+        lds_u8 *trow = tk + (4 * hl + (i16 >> 2)) * 128 + 8 * (i16 & 1) + 16 * (((i16 & 3) >> 1) ^ hl);
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int sc = 0; sc < 2; ++sc)
+                ktb[a][sc] = trow + 64 * (a ^ ((i16 >> 3) & 1)) + 32 * ((G & 1) ^ sc);
+    }
+    typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_q;
+
+    f32x16 dqa[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        dqa[dt] = f32x16{};
+    Stage s0 = load_stage(read_offs(0)), s1 = load_stage(read_offs(1));
+    Offs on = read_offs(2);
+    auto step = [&](int t, Stage &st) {
+        put_stage(st);
+        asm volatile("" ::: "memory");      // the tile's writes precede its reads
+        st = load_stage(on);                // tile t + 2
+        on = read_offs(t + 3);
+        // ---- S^T = K Q^T and dP^T = V do^T, interleaved.  The compiler inserts no wait
+        // states around asm, and with the register file full it copies operands back
+        // from AGPRs (VALU writes) right before an MFMA: each MFMA is preceded by the
+        // wait states such a write needs, and the last one followed by those a VALU
+        // read of its result needs.
+        f32x16 sa, pa;
+        {
+            constexpr int QD = 3;
+            auto lda = [&](int ks) { return *(lds_bf16x8_q *)(kb[ks & 3] + 1024 * (ks >> 2)); };
+            auto ldv = [&](int ks) { return *(lds_bf16x8_q *)(kb[ks & 3] + (tv - tk) + 1024 * (ks >> 2)); };
+            bf16x8 ka[QD], va[QD];
+#pragma unroll
+            for (int d = 0; d < QD; ++d) {
+                ka[d] = lda(d);
+                if constexpr (!SHARED)
+                    va[d] = ldv(d);
+            }
+#pragma unroll
+            for (int ks = 0; ks < NKQ; ++ks) {
+                const bf16x8 &kv = ka[ks % QD];
+                const bf16x8 &vv = SHARED ? ka[ks % QD] : va[ks % QD];
+                if (ks == 0) {
+                    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(sa) : "v"(kv), "v"(qop[ks]));
+                    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(pa) : "v"(vv), "v"(dop[ks]));
+                } else if (ks + 1 < NKQ) {
+                    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sa) : "v"(kv), "v"(qop[ks]));
+                    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(pa) : "v"(vv), "v"(dop[ks]));
+                } else {
+                    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(sa) : "v"(kv), "v"(qop[ks]));
+                    asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0\n\t"
+                                 "s_nop 7\n\ts_nop 7\n\ts_nop 3"
+                                 : "+v"(pa) : "v"(vv), "v"(dop[ks]));
+                }
+                if (ks + QD < NKQ) {
+                    ka[ks % QD] = lda(ks + QD);
+                    if constexpr (!SHARED)
+                        va[ks % QD] = ldv(ks + QD);
+                }
+            }
+        }
+        // ---- the first K^T operands, read before the dS terms whose VALU work
+        // covers their LDS latency
+        auto ldt = [&](int dt, int j, int sec) {
+            return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (lds_bf16x4_b *)(ktb[dt & 1][sec] + (2 * j + sec) * KCB * 1024 + (dt >> 1) * 1024));
+        };
+        auto tstep = [](int u) { return 2 * (u % NDT) + u / NDT; };
+        auto ldt8 = [&](int stp) {
+            const bf16x4 lo = ldt(stp >> 1, stp & 1, 0), hi = ldt(stp >> 1, stp & 1, 1);
+            return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        constexpr int PD = 4;
+        bf16x8 kt[PD];
+#pragma unroll
+        for (int d = 0; d < PD; ++d)
+            kt[d] = ldt8(tstep(d));
+        // ---- P and dS for keys 8(i >> 2) + 4hq + (i & 3)
+        const uint32_t vmask = __builtin_amdgcn_readfirstlane(msk[t]);
+        bf16x8 dso[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const bool on_ = (vmask >> (8 * (i >> 2) + 4 * hq + (i & 3))) & 1u;
+            const float p = on_ ? __builtin_amdgcn_exp2f(fmaf(sa[i], sl2, -L2)) : 0.0f;
+            dso[i >> 3][i & 7] = (__bf16)(p * (pa[i] - Dv));
+        }
+        // ---- dq^T += K^T dS^T: step u covers dim tile u % NDT and k-half u / NDT
+#pragma unroll
+        for (int u = 0; u < 2 * NDT; ++u) {
+            dqa[u % NDT] = mma32_bf16(kt[u % PD], dso[u / NDT], dqa[u % NDT]);
+            if (u + PD < 2 * NDT)
+                kt[u % PD] = ldt8(tstep(u + PD));
+        }
+        asm volatile("" ::: "memory");      // the tile's reads precede the next tile's writes
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+        step(t, s0);
+        step(t + 1, s1);
+    }
+    if (t < ntiles)
+        step(t, s0);
+    // ---- d_q: lane holds head h, dims 32dt + 8g + 4hq + {0..3} of tile dt
+    float *dqp = dq + ((int64_t)tok * Hq + h) * D + 4 * hq;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+            *(f32x4 *)(dqp + 32 * dt + 8 * g) =
+                f32x4{dqa[dt][4 * g], dqa[dt][4 * g + 1], dqa[dt][4 * g + 2], dqa[dt][4 * g + 3]} * scale;
 }
 
 // ------------------------------------------------------------------ dK, dV (key-major)
@@ -803,8 +1117,25 @@ hipError_t launch_attn_bwd(const Batch &bt, int Hq, int d_qk, int d_v, const voi
                        Dh, dgate);
     if (L.km)
         hipLaunchKernelGGL(attn_bwd_mask_kernel, dim3(T), dim3(256), 0, st, idx, K, L.W, bt.max_ctx, bits, flags);
+    // d_q on one wave per 32 heads where the shape allows; the query-major kernel then
+    // only merges the flagged repeats' dK, dV (mode 3)
+    const bool dq32 = L.km && d_qk == 128 && d_v == 128 && Hq % 32 == 0 && K <= kDq32MaxK;
+    if (dq32) {
+        const int64_t units = (int64_t)T * (Hq / 32);
+        if (units > 0x7fffffffLL)
+            return hipErrorInvalidValue;
+        const dim3 g32((unsigned)((units + 3) / 4));
+        if (shared)
+            hipLaunchKernelGGL((attn_bwd_dq32_kernel<true>), g32, dim3(256), 0, st, bt, (const uint16_t *)q, Hq,
+                               (const uint16_t *)kc, (const uint16_t *)vc, rs, idx, K, scale, lse, dO, Dh, dq,
+                               (int)units);
+        else
+            hipLaunchKernelGGL((attn_bwd_dq32_kernel<false>), g32, dim3(256), 0, st, bt, (const uint16_t *)q, Hq,
+                               (const uint16_t *)kc, (const uint16_t *)vc, rs, idx, K, scale, lse, dO, Dh, dq,
+                               (int)units);
+    }
     const int nw = bwd_waves(Hq, d_qk);
-    const int mode = L.km ? 2 : 1;
+    const int mode = L.km ? (dq32 ? 3 : 2) : 1;
     const dim3 grid(T, Hq / (16 * nw));
 #define SA_DQ(DQ, DV_, MLA_, NW_)                                                                                 \
     hipLaunchKernelGGL((attn_bwd_dq_kernel<DQ, DV_, MLA_, NW_>), grid, dim3(NW_ * 64), 0, st, bt,                \

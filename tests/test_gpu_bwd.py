@@ -174,6 +174,26 @@ def test_bwd_index_list_longer_than_one_pass():
     check_bwd(spec, "bwd-long-list")
 
 
+def test_bwd_index_list_beyond_the_one_wave_dq_kernel():
+    """32 heads x 128 with K = 2500: longer than the lists the one-wave-per-32-heads d_q kernel takes
+    (2048), so d_q and the flagged repeats go through the query-major kernel in several passes."""
+    spec = W.prefill_bf16(T=24).replace(q_lens=(24,), ctx_lens=(4000,), K=2500, paged_random=True, seed=74)
+    check_bwd(spec, "bwd-long-list")
+
+
+def test_bwd_rows_without_valid_slots_and_holes():
+    """Rows whose list is all -1 (no key: lse = -inf, no gradient) and rows with -1 holes in the middle
+    of the list (masked slots inside full tiles), on the one-wave-per-32-heads d_q kernel."""
+    def mutate(idx):
+        v = idx.clone()
+        v[0:3, :] = -1
+        v[3:9, 1::3] = -1
+        idx.copy_(v)
+
+    spec = W.prefill_bf16(T=72).replace(q_lens=(72,), ctx_lens=(900,), K=192, paged_random=True, seed=75)
+    check_bwd(spec, "bwd-holes", mutate=mutate)
+
+
 def test_bwd_repeated_positions():
     """Positions repeated inside a row: slot 1 repeats slot 0 on every row, slots 2 and 3 repeat slot 5
     on even rows.  The forward attends over every slot, so the backward counts each repeat once more:

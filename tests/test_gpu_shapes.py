@@ -98,6 +98,47 @@ def test_attention_shape(dt, dqk, dv, mla, hq, mode):
     P.say(f"[attn {dt} {dqk}/{dv} h{hq} {mode}] ok: worst {w:.2f} of the bound")
 
 
+# one instance of each attention kernel: MQA rows (one wave per 32 heads), the general
+# kernel, the latent kernel, fp32
+HOLE_SHAPES = [("bf16", 128, 128, False, 32), ("bf16", 128, 128, True, 64), ("bf16", 128, 128, False, 16),
+               ("bf16", 576, 512, True, 128), ("f32", 64, 64, False, 4)]
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("dt,dqk,dv,mla,hq", HOLE_SHAPES,
+                         ids=[f"{a}-{b}x{c}-{'shared' if d else 'sep'}-h{e}" for a, b, c, d, e in HOLE_SHAPES])
+def test_attention_index_holes(dt, dqk, dv, mla, hq, mode):
+    """Padding (-1) anywhere in a list, not only at its end: rows with no valid entry (out = 0,
+    lse = -inf), rows with a hole every third slot from slot 1 (the first tile already has a
+    missing key), and rows whose first 40 slots are padding."""
+    spec = _base(mode, seed=300 + hq + dqk).replace(attn_dtype=dt, d_qk=dqk, d_v=dv, mla=mla, Hq=hq,
+                                                  gate_per_channel=(hq % 2 == 0), name=f"holes-{dt}-{dqk}")
+    P.say(f"[holes {dt} {dqk}/{dv} {'shared' if mla else 'separate'} h{hq} {mode}] T={spec.T}")
+    wl = W.generate(spec, DEV)
+    pl = B.Pipeline(wl)
+    pl.out.fill_(float("nan"))
+    pl.indexer()
+    pl.topk()
+    v = pl.indices.clone()
+    T = v.shape[0]
+    a, b = min(2, T), min(8, T)
+    v[0:a, :] = -1
+    v[a:b, 1::3] = -1
+    v[b:min(b + 4, T), :40] = -1
+    pl.indices.copy_(v)
+    pl.attn()
+    torch.cuda.synchronize()
+    inp = O.Inputs.from_workload(wl)
+    idx = pl.indices.cpu().numpy()
+    ref, ref_lse = O.sparse_attn(inp, idx, None, spec.softmax_scale, with_lse=True)
+    w = P.check_attn(pl.out.float().cpu().numpy(), ref, P.RTOL[dt], P.attn_floor(inp, idx, None, spec.softmax_scale))
+    lse = pl.lse.cpu().numpy()
+    dead = ~np.isfinite(ref_lse)
+    assert np.all(lse[dead] == -np.inf), "lse of heads with no valid entry"
+    assert P.close(lse[~dead], ref_lse[~dead], P.RTOL[dt]).all(), "lse"
+    P.say(f"[holes {dt} {dqk}/{dv} h{hq} {mode}] ok: worst {w:.2f} of the bound")
+
+
 @pytest.mark.parametrize("mode", ["prefill", "decode"])
 @pytest.mark.parametrize("dt,dqk,dv,mla,hq", ATTN_SHAPES,
                          ids=[f"{a}-{b}x{c}-{'shared' if d else 'sep'}-h{e}" for a, b, c, d, e in ATTN_SHAPES])
