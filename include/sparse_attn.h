@@ -162,7 +162,10 @@ sa_status sparse_topk(const sa_batch *batch, const float *scores, int64_t ld_sco
  *   k_cache      [num_pages, page_size, kv_row_stride]: K row = first d_qk elements
  *   v_cache      [num_pages, page_size, kv_row_stride]: V row = first d_v elements;
  *                may equal k_cache (latent layout, d_v <= d_qk)
- *   indices      [T, k] int32 positions (as produced by sparse_topk)
+ *   indices      [T, k] int32 positions (as produced by sparse_topk); padding
+ *                (< 0) may sit anywhere in a row.  Valid entries must lie in
+ *                [0, ctx_len[b]) of the token's sequence: they are not checked,
+ *                and one past the sequence's pages reads outside its page table.
  *   gate_logits  [T, n_q_heads, d_v] if gate_per_channel else [T, n_q_heads], in dtype
  *   out          [T, n_q_heads, d_v] in dtype (bf16 rounded to nearest even)
  *   lse          [T, n_q_heads] fp32, or NULL
