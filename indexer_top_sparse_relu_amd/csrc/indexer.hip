@@ -405,6 +405,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             scores + (int64_t)(tok0 + wt0) * ld, 0, (int)(TPW * ld * 4), 0x00020000);
 
         constexpr int MH = MT / 2, TH = TPW / 2;
+        // Per half gh of the M-tiles, loop-invariant: the lane's score limit (it writes
+        // position s when s < lim, i.e. s <= pos(token) and s < kb1; 0 when it writes
+        // nothing), its token row's byte offset in the buffer, and half its token's scale.
+        int lim[2];
+        uint32_t rowoff[2];
+        float qh[2];
+#pragma unroll
+        for (int gh = 0; gh < 2; ++gh) {
+            const int tw = TH == 1 ? 0 : half;
+            const int tl = wv * TPW + gh * TH + tw;
+            const bool writes = (TH > 1 || half == gh) && tl < ntok;
+            lim[gh] = writes ? min(kb1, pos0 + tl + 1) : 0;
+            rowoff[gh] = writes ? (uint32_t)((int64_t)(tl - wt0) * ld * 4) : 0u;
+            qh[gh] = 0.5f * ((TH > 1 && half) ? qs[gh * TH + TH - 1] : qs[gh * TH]);
+        }
         auto epi = [&](const f32x16 (&c)[MH], int gh, int s, float ks_s, float L) {
             float acc[TH];
 #pragma unroll
@@ -423,13 +438,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             for (int t = 0; t < TH; ++t)
                 acc[t] = sum_halves(acc[t]);
             // writer of token gh*TH + t is the half t%2 (TH == 2) or half gh (TH == 1)
-            const int tw = TH == 1 ? 0 : half;
             const float a = (TH > 1 && half) ? acc[TH - 1] : acc[0];
-            const float qv = (TH > 1 && half) ? qs[gh * TH + TH - 1] : qs[gh * TH];
-            const int tl = wv * TPW + gh * TH + tw;
-            const bool ok = (TH > 1 || half == gh) && tl < ntok && s <= pos0 + tl && s < kb1;
-            const uint32_t off = ok ? (uint32_t)(((int64_t)(tl - wt0) * ld + s) * 4) : 0x80000000u;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(0.5f * (a + L) * qv * ks_s), srs, off, 0, 0);
+            const uint32_t off = s < lim[gh] ? rowoff[gh] + 4u * (uint32_t)s : 0x80000000u;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((a + L) * qh[gh] * ks_s), srs, off, 0, 0);
         };
         f32x16 c0[MH], c1[MH];
         int s_prev = 0;
