@@ -64,6 +64,35 @@ def test_indexer_shape(dt, h, d, mode):
     P.say(f"[indexer {dt} {h}x{d} {mode}] ok: worst score rel {w1:.2e}, recall {rec:.4f}")
 
 
+# page sizes other than 64 on each indexer path: the fp8 linear-term tile kernel, the
+# bf16 and fp32 tile kernels, and the decode kernels
+PAGE_CASES = [(dt, h, d, ps) for dt, h, d in (("fp8", 64, 128), ("bf16", 16, 64), ("f32", 4, 32)) for ps in (16, 256)]
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("dt,h,d,ps", PAGE_CASES, ids=[f"{a}-h{b}-d{c}-p{e}" for a, b, c, e in PAGE_CASES])
+def test_indexer_page_size(dt, h, d, ps, mode):
+    spec = _base(mode, seed=400 + h + ps).replace(idx_dtype=dt, H_I=h, d_I=d, page_size=ps,
+                                                  name=f"indexer-{dt}-{h}x{d}-p{ps}")
+    P.say(f"[indexer page {ps} {dt} {h}x{d} {mode}] T={spec.T} max_ctx={spec.max_ctx}")
+    wl = W.generate(spec, DEV)
+    pl = B.Pipeline(wl)
+    pl.scores.fill_(float("nan"))
+    pl.indexer()
+    pl.topk()
+    torch.cuda.synchronize()
+    inp = O.Inputs.from_workload(wl)
+    n = P.token_geometry(spec)[2]
+    sc = pl.scores.cpu().numpy()
+    w1 = P.check_scores(sc, O.indexer(inp, ld=pl.ld), n, P.RTOL[dt])
+    for r in range(spec.T):
+        assert np.all(np.isnan(sc[r, n[r]:])), f"row {r} written past n"
+    idx = pl.indices.cpu().numpy()
+    P.check_idx_invariants(idx, n, spec.K)
+    P.check_topk_exact(idx, sc, n, spec.K)
+    P.say(f"[indexer page {ps} {dt} {h}x{d} {mode}] ok: worst score rel {w1:.2e}")
+
+
 # (dtype, d_qk, d_v, shared K/V row, query heads): every kernel instance the library
 # dispatches to -- fp32 per head; bf16 MQA rows of 128 with 1, 2, 4 or 8 waves of 16
 # heads, separate or shared; the 576/512 latent row on the general kernel (heads not a
@@ -137,6 +166,30 @@ def test_attention_index_holes(dt, dqk, dv, mla, hq, mode):
     assert np.all(lse[dead] == -np.inf), "lse of heads with no valid entry"
     assert P.close(lse[~dead], ref_lse[~dead], P.RTOL[dt]).all(), "lse"
     P.say(f"[holes {dt} {dqk}/{dv} h{hq} {mode}] ok: worst {w:.2f} of the bound")
+
+
+ATTN_PAGE_CASES = [(*shape, ps) for shape in HOLE_SHAPES for ps in (16, 256)]
+
+
+@pytest.mark.parametrize("mode", ["prefill", "decode"])
+@pytest.mark.parametrize("dt,dqk,dv,mla,hq,ps", ATTN_PAGE_CASES,
+                         ids=[f"{a}-{b}x{c}-{'shared' if d else 'sep'}-h{e}-p{f}" for a, b, c, d, e, f in ATTN_PAGE_CASES])
+def test_attention_page_size(dt, dqk, dv, mla, hq, ps, mode):
+    """Page sizes other than 64 on each attention kernel (the gather resolves every slot
+    through the page table)."""
+    spec = _base(mode, seed=500 + hq + ps).replace(attn_dtype=dt, d_qk=dqk, d_v=dv, mla=mla, Hq=hq, page_size=ps,
+                                                  gate_per_channel=(hq % 2 == 0), name=f"page-{dt}-{dqk}")
+    P.say(f"[attn page {ps} {dt} {dqk}/{dv} h{hq} {mode}] T={spec.T}")
+    wl = W.generate(spec, DEV)
+    pl = B.Pipeline(wl)
+    pl.out.fill_(float("nan"))
+    pl.run()
+    torch.cuda.synchronize()
+    inp = O.Inputs.from_workload(wl)
+    idx = pl.indices.cpu().numpy()
+    ref = O.sparse_attn(inp, idx, None, spec.softmax_scale)
+    w = P.check_attn(pl.out.float().cpu().numpy(), ref, P.RTOL[dt], P.attn_floor(inp, idx, None, spec.softmax_scale))
+    P.say(f"[attn page {ps} {dt} {dqk}/{dv} h{hq} {mode}] ok: worst {w:.2f} of the bound")
 
 
 @pytest.mark.parametrize("mode", ["prefill", "decode"])
