@@ -364,7 +364,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         // The lane's key positions of tile tt (NB rows of the key tile, NS key
         // scales) and their physical pages.  The pages are read from LDS one
         // tile ahead of the loads, inside the previous tile's MFMA work, so the
-        // issue itself waits on nothing.
+        // issue itself waits on nothing.  A row-block load covers one 8-row group
+        // (8-aligned, so inside one page: pages hold a power of two >= 16 rows): its
+        // page is wave-uniform and kept in a scalar register, and the address is a
+        // scalar page base plus a 32-bit lane offset.  Positions past the chunk are
+        // clamped to its last key, which lies in the group's own page or, for a
+        // group wholly past it, in the page all of its rows are clamped to.
         struct Pg { int p[NB + NS]; };
         auto krow_of = [&](int m, int ln) { return (kIdxWaves * m + wv) * 8 + (ln >> 3); };
         auto kpos = [&](int tt, int ln, int which) {
@@ -374,21 +379,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         };
         auto pages = [&](int tt, int ln) {
             Pg g;
+            const int t0 = kb0 + tt * LT;
 #pragma unroll
-            for (int w = 0; w < NB + NS; ++w)
-                g.p[w] = lpt[(kpos(tt, ln, w) >> pshift) - pg0];
+            for (int w = 0; w < NB + NS; ++w) {
+                if (w < NB)
+                    g.p[w] = __builtin_amdgcn_readfirstlane(
+                        lpt[(min(t0 + 8 * (kIdxWaves * w + wv), kb1 - 1) >> pshift) - pg0]);
+                else
+                    g.p[w] = lpt[(kpos(tt, ln, w) >> pshift) - pg0];
+            }
             return g;
         };
         // load w of tile tt: row block w (w < NB) or key-scale load w - NB
         auto issue_part = [&](int tt, int ln, const Pg &pg, int w) {
             const int st = tt % KST;
-            const int64_t pr = ((int64_t)pg.p[w] << pshift) + (kpos(tt, ln, w) & pmask);
+            const uint32_t inpage = (uint32_t)(kpos(tt, ln, w) & pmask);
             if (w < NB) {
                 const int r = krow_of(w, ln);
-                dma_b128(k_idx + pr * 128 + ((ln & 7) ^ ((r >> 1) & 7)) * 16,
-                         stage(st) + (kIdxWaves * w + wv) * 1024);
+                const uint8_t *sb = k_idx + ((uint64_t)(uint32_t)pg.p[w] << (pshift + 7));
+                dma_b128_sv(sb, (inpage << 7) + (uint32_t)(((ln & 7) ^ ((r >> 1) & 7)) * 16),
+                            stage(st) + (kIdxWaves * w + wv) * 1024);
             } else {
-                dma_b32(k_scale + pr, (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * LT + 64 * (w - NB)));
+                dma_b32(k_scale + (((int64_t)pg.p[w] << pshift) + inpage),
+                        (const lds_u8 *)(LKS + (st * kIdxWaves + wv) * LT + 64 * (w - NB)));
             }
         };
         auto issue = [&](int tt, int ln, const Pg &pg) {

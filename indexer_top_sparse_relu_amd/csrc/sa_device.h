@@ -189,6 +189,17 @@ __device__ __forceinline__ void dma_b32(const void *src, const lds_u8 *lds)
                  : "=&s"(saved) : "v"(src), "s"(base) : "memory");
 }
 
+// The same with a wave-uniform base in scalar registers and a 32-bit per-lane
+// byte offset (the saddr form): the address costs the lanes one 32-bit value.
+__device__ __forceinline__ void dma_b128_sv(const void *sbase, uint32_t voff, const lds_u8 *lds)
+{
+    const uint32_t base = (uint32_t)(uintptr_t)lds;
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+                 "global_load_lds_dwordx4 %1, %2\n\ts_nop 0\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved) : "v"(voff), "s"(sbase), "s"(base) : "memory");
+}
+
 // ------------------------------------------------------------ wave helpers
 template <typename T>
 __device__ __forceinline__ T shfl_xor(T v, int m)
