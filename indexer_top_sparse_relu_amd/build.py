@@ -16,12 +16,16 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["capi.hip", "indexer.hip", "topk.hip", "attn.hip", "append.hip", "blocks.hip", "fusion.hip", "attn_bwd.hip"]
+SOURCES = ["capi.hip", "indexer.hip", "topk.hip", "attn.hip", "append.hip", "blocks.hip", "fusion.hip", "attn_bwd.hip",
+           "attn_bwd_kv.hip"]
 # per-source code generation options: the indexer keeps MFMA accumulators in
 # arch VGPRs, where its VALU epilogue reads them without v_accvgpr_read copies,
 # and assumes finite values (scores are defined for finite inputs), so max(x, 0)
-# needs no NaN-quieting instruction in front of it
-SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"]}
+# needs no NaN-quieting instruction in front of it; the key-major backward keeps
+# its S and dP accumulators in VGPRs, so that its dK, dV accumulators have the
+# AGPRs to themselves
+SOURCE_FLAGS = {"indexer.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+                "attn_bwd_kv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

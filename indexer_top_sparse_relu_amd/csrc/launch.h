@@ -55,6 +55,10 @@ hipError_t launch_block_expand(const Batch &bt, const int32_t *blk, int kb, int3
 int attn_bwd_supported(int dtype, int Hq, int d_qk, int d_v);
 int attn_bwd_needs_shared(int d_qk, int d_v);
 size_t attn_bwd_ws_bytes(int T, int max_ctx, int Hq, int d_qk, int d_v, int K);
+// key-major dK, dV (d = 64 or 128; 16, 32 or 64 heads), from the backward's workspace
+hipError_t launch_attn_bwd_kv(const Batch &bt, int Hq, int d, bool shared, const void *q, const void *kc,
+                              const void *vc, int64_t rs, float scale, const float *lse, const uint16_t *dO,
+                              const float *Dh, const uint32_t *bits, int W, float *dk, float *dv, hipStream_t st);
 hipError_t launch_attn_bwd(const Batch &bt, int Hq, int d_qk, int d_v, const void *q, const void *kc,
                            const void *vc, int64_t rs, const int32_t *idx, int K, const void *gate, int per_channel,
                            float scale, const void *y, const float *lse, const void *dy, float *dq, float *dk,
