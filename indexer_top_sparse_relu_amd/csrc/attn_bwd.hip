@@ -135,12 +135,13 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
 // The slot whose atomic finds its bit already set repeats a position and is
 // flagged (its contribution goes through the per-slot merge).  Rows of up to
 // kMaskLdsWords words are built in LDS and written out whole; longer ones with
-// global atomics.
+// global atomics.  trep[tok] tells whether the row flagged any slot, so that the
+// pass merging the repeats skips the other rows at once.
 constexpr int kMaskLdsWords = 8192;
 
 __global__ __launch_bounds__(256) void attn_bwd_mask_kernel(const int32_t *__restrict__ idx, int K, int W,
                                                            int max_ctx, uint32_t *__restrict__ bits,
-                                                           uint8_t *__restrict__ flags)
+                                                           uint8_t *__restrict__ flags, uint8_t *__restrict__ trep)
 {
     __shared__ uint32_t lb[kMaskLdsWords];
     const int tok = blockIdx.x;
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(256) void attn_bwd_mask_kernel(const int32_t *__res
             row[w] = 0u;
     }
     __syncthreads();            // (the barrier waits for the cleared words: only this workgroup touches the row)
+    bool mine = false;
     for (int j = threadIdx.x; j < K; j += 256) {
         const int s = idx[(int64_t)tok * K + j];
         uint8_t rep = 0;
@@ -161,10 +163,13 @@ __global__ __launch_bounds__(256) void attn_bwd_mask_kernel(const int32_t *__res
             const uint32_t old = in_lds ? atomicOr(&lb[s >> 5], bit) : atomicOr(&row[s >> 5], bit);
             rep = (old & bit) ? 1 : 0;
         }
+        mine = mine || rep;
         flags[(int64_t)tok * K + j] = rep;
     }
+    const int any = __syncthreads_or(mine);     // also the barrier before an LDS row is written out
+    if (threadIdx.x == 0)
+        trep[tok] = any ? 1 : 0;
     if (in_lds) {
-        __syncthreads();
         for (int w = threadIdx.x; w < W; w += 256)
             row[w] = lb[w];
     }
@@ -186,8 +191,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
     Batch bt, const uint16_t *__restrict__ q, int Hq, const uint16_t *__restrict__ kc,
     const uint16_t *__restrict__ vc, int64_t rs, const int32_t *__restrict__ idx, int K, float scale,
     const float *__restrict__ lse, const uint16_t *__restrict__ dO, const float *__restrict__ Dh,
-    float *__restrict__ dq, int mode, const uint8_t *__restrict__ flags, const uint16_t *__restrict__ QT,
-    const uint16_t *__restrict__ dOT, float *__restrict__ dk, float *__restrict__ dv)
+    float *__restrict__ dq, int mode, const uint8_t *__restrict__ flags, const uint8_t *__restrict__ trep,
+    const uint16_t *__restrict__ QT, const uint16_t *__restrict__ dOT, float *__restrict__ dk, float *__restrict__ dv)
 {
     constexpr int NT = NW * 64;
     constexpr int NKQ = DQK / 32;           // k-steps over d_qk
@@ -212,6 +217,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(
     __shared__ int32_t xrow[32];
 
     const int tok = blockIdx.x, hg = blockIdx.y;
+    if (mode == 3 && trep[tok] == 0)
+        return;                             // repeats only, and this row has none
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int g = lane >> 4, n = lane & 15;
     const int hl = wv * 16 + n;             // head within the workgroup
@@ -771,7 +778,7 @@ int attn_bwd_needs_shared(int d_qk, int d_v)
 }
 
 struct BwdLayout {
-    size_t dO, QT, dOT, Dh, bits, flags, total;
+    size_t dO, QT, dOT, Dh, bits, flags, trep, total;
     int W;
     bool km;
 };
@@ -797,6 +804,8 @@ static BwdLayout bwd_layout(int T, int max_ctx, int Hq, int d_qk, int d_v, int K
         o += up256((size_t)T * L.W * 4);
         L.flags = o;
         o += up256((size_t)T * K);
+        L.trep = o;
+        o += up256((size_t)T);
     }
     L.total = o;
     return L;
@@ -828,13 +837,15 @@ hipError_t launch_attn_bwd(const Batch &bt, int Hq, int d_qk, int d_v, const voi
     float *Dh = (float *)(w + L.Dh);
     uint32_t *bits = L.km ? (uint32_t *)(w + L.bits) : nullptr;
     uint8_t *flags = L.km ? (uint8_t *)(w + L.flags) : nullptr;
+    uint8_t *trep = L.km ? (uint8_t *)(w + L.trep) : nullptr;
     const bool shared = kc == vc;
 
     hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(T), dim3(256), 0, st, Hq, d_qk, d_v, (const uint16_t *)q,
                        (const uint16_t *)gate, per_channel, (const uint16_t *)y, (const uint16_t *)dy, dO, QT, dOT,
                        Dh, dgate);
     if (L.km)
-        hipLaunchKernelGGL(attn_bwd_mask_kernel, dim3(T), dim3(256), 0, st, idx, K, L.W, bt.max_ctx, bits, flags);
+        hipLaunchKernelGGL(attn_bwd_mask_kernel, dim3(T), dim3(256), 0, st, idx, K, L.W, bt.max_ctx, bits, flags,
+                           trep);
     // d_q on one wave per 32 heads where the shape allows; the query-major kernel then
     // only merges the flagged repeats' dK, dV (mode 3)
     const bool dq32 = L.km && d_qk == 128 && d_v == 128 && Hq % 32 == 0 && K <= kDq32MaxK;
@@ -858,7 +869,7 @@ hipError_t launch_attn_bwd(const Batch &bt, int Hq, int d_qk, int d_v, const voi
 #define SA_DQ(DQ, DV_, MLA_, NW_)                                                                                 \
     hipLaunchKernelGGL((attn_bwd_dq_kernel<DQ, DV_, MLA_, NW_>), grid, dim3(NW_ * 64), 0, st, bt,                \
                        (const uint16_t *)q, Hq, (const uint16_t *)kc, (const uint16_t *)vc, rs, idx, K, scale, lse, \
-                       dO, Dh, dq, mode, flags, QT, dOT, dk, dv)
+                       dO, Dh, dq, mode, flags, trep, QT, dOT, dk, dv)
 #define SA_DQ_NW(DQ, DV_, MLA_)                    \
     switch (nw) {                                  \
     case 8: SA_DQ(DQ, DV_, MLA_, 8); break;        \
