@@ -58,39 +58,65 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_b;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2_b;
 
 // ------------------------------------------------------------------ prep
-// One workgroup per token.  D_h and the per-head gate gradient by one wave per
-// head; do, Q^T and do^T 32 columns at a time through an LDS tile, so the
-// transposed rows are written whole.
+// One workgroup per token.  Each thread takes runs of 8 channels of one head
+// (16-byte loads and stores): do = bf16(dy g), the gate gradient, and D_h =
+// dy . y, summed over the DV / 8 runs of a head (a power of two <= 64, on
+// consecutive lanes) by a fixed xor-shuffle tree, so the sums do not depend on
+// timing.  Q^T and do^T (read by the per-slot merge) go out through an LDS tile
+// 32 columns at a time, for every row when trep is NULL, else only for rows
+// whose index list repeats a position.
 __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
     int H, int DQK, int DV, const uint16_t *__restrict__ q, const uint16_t *__restrict__ gate, int per_channel,
     const uint16_t *__restrict__ y, const uint16_t *__restrict__ dy, uint16_t *__restrict__ dO,
-    uint16_t *__restrict__ QT, uint16_t *__restrict__ dOT, float *__restrict__ Dh, float *__restrict__ dgate)
+    uint16_t *__restrict__ QT, uint16_t *__restrict__ dOT, float *__restrict__ Dh, float *__restrict__ dgate,
+    const uint8_t *__restrict__ trep)
 {
     __shared__ uint16_t tile[kPrepMaxH][34];
-    const int tok = blockIdx.x, tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-    for (int h = wv; h < H; h += 4) {
-        float dsum = 0.0f, gsum = 0.0f;
-        for (int c = lane; c < DV; c += 64) {
-            const int64_t o = ((int64_t)tok * H + h) * DV + c;
-            const float G = bf16_bits_to_f32(per_channel ? gate[o] : gate[(int64_t)tok * H + h]);
-            const float g = 1.0f / (1.0f + __expf(-G));
-            const float dyc = bf16_bits_to_f32(dy[o]), yc = bf16_bits_to_f32(y[o]);
-            dsum += dyc * yc;
-            const float dg = dyc * yc * (1.0f - g);
-            if (per_channel)
-                dgate[o] = dg;
-            else
-                gsum += dg;
+    const int tok = blockIdx.x, tid = threadIdx.x;
+    const int rph = DV >> 3;                // runs per head
+    for (int r = tid; r < H * rph; r += 256) {
+        const int h = r / rph, c0 = (r - h * rph) * 8;
+        const int64_t o = ((int64_t)tok * H + h) * DV + c0;
+        const u32x4 dyv = *(const u32x4 *)(dy + o), yv = *(const u32x4 *)(y + o);
+        u32x4 gv;
+        if (per_channel) {
+            gv = *(const u32x4 *)(gate + o);
+        } else {
+            const uint32_t g1 = gate[(int64_t)tok * H + h];
+            gv = u32x4{g1 | (g1 << 16), g1 | (g1 << 16), g1 | (g1 << 16), g1 | (g1 << 16)};
         }
-        dsum = wave_sum(dsum);
-        if (!per_channel)
-            gsum = wave_sum(gsum);
-        if (lane == 0) {
-            Dh[(int64_t)tok * H + h] = dsum;
+        float ds = 0.0f, gs = 0.0f, dg[8];
+        uint32_t ov[4];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int sh = 16 * (k & 1);
+            const float dyc = bf16_bits_to_f32((uint16_t)(dyv[k >> 1] >> sh));
+            const float yc = bf16_bits_to_f32((uint16_t)(yv[k >> 1] >> sh));
+            const float g = 1.0f / (1.0f + __expf(-bf16_bits_to_f32((uint16_t)(gv[k >> 1] >> sh))));
+            ds += dyc * yc;
+            dg[k] = dyc * yc * (1.0f - g);
+            gs += dg[k];
+            const uint32_t b = f32_to_bf16_bits(dyc * g);
+            ov[k >> 1] = (k & 1) ? (ov[k >> 1] | (b << 16)) : b;
+        }
+        *(u32x4 *)(dO + o) = u32x4{ov[0], ov[1], ov[2], ov[3]};
+        if (per_channel) {
+            *(f32x4 *)(dgate + o) = f32x4{dg[0], dg[1], dg[2], dg[3]};
+            *(f32x4 *)(dgate + o + 4) = f32x4{dg[4], dg[5], dg[6], dg[7]};
+        }
+        // the head's runs are rph consecutive lanes, rph-aligned (64 % rph == 0)
+        for (int m = rph >> 1; m >= 1; m >>= 1) {
+            ds += __shfl_xor(ds, m, 64);
+            gs += __shfl_xor(gs, m, 64);
+        }
+        if (c0 == 0) {
+            Dh[(int64_t)tok * H + h] = ds;
             if (!per_channel)
-                dgate[(int64_t)tok * H + h] = gsum;
+                dgate[(int64_t)tok * H + h] = gs;
         }
     }
+    if (trep != nullptr && trep[tok] == 0)
+        return;
     const int cmax = DQK > DV ? DQK : DV;
     for (int c0 = 0; c0 < cmax; c0 += 32) {
         if (c0 < DQK) {
@@ -115,7 +141,6 @@ __global__ __launch_bounds__(256) void attn_bwd_prep_kernel(
                     const float G = bf16_bits_to_f32(per_channel ? gate[o] : gate[(int64_t)tok * H + h]);
                     const float g = 1.0f / (1.0f + __expf(-G));
                     v = f32_to_bf16_bits(bf16_bits_to_f32(dy[o]) * g);
-                    dO[o] = v;
                 }
                 tile[h][x] = v;
             }
@@ -840,15 +865,16 @@ hipError_t launch_attn_bwd(const Batch &bt, int Hq, int d_qk, int d_v, const voi
     uint8_t *trep = L.km ? (uint8_t *)(w + L.trep) : nullptr;
     const bool shared = kc == vc;
 
-    hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(T), dim3(256), 0, st, Hq, d_qk, d_v, (const uint16_t *)q,
-                       (const uint16_t *)gate, per_channel, (const uint16_t *)y, (const uint16_t *)dy, dO, QT, dOT,
-                       Dh, dgate);
+    // d_q on one wave per 32 heads where the shape allows; the query-major kernel then
+    // only merges the flagged repeats' dK, dV (mode 3), and needs Q^T, do^T only for
+    // the rows with repeats
+    const bool dq32 = L.km && d_qk == 128 && d_v == 128 && Hq % 32 == 0 && K <= kDq32MaxK;
     if (L.km)
         hipLaunchKernelGGL(attn_bwd_mask_kernel, dim3(T), dim3(256), 0, st, idx, K, L.W, bt.max_ctx, bits, flags,
                            trep);
-    // d_q on one wave per 32 heads where the shape allows; the query-major kernel then
-    // only merges the flagged repeats' dK, dV (mode 3)
-    const bool dq32 = L.km && d_qk == 128 && d_v == 128 && Hq % 32 == 0 && K <= kDq32MaxK;
+    hipLaunchKernelGGL(attn_bwd_prep_kernel, dim3(T), dim3(256), 0, st, Hq, d_qk, d_v, (const uint16_t *)q,
+                       (const uint16_t *)gate, per_channel, (const uint16_t *)y, (const uint16_t *)dy, dO, QT, dOT,
+                       Dh, dgate, dq32 ? (const uint8_t *)trep : nullptr);
     if (dq32) {
         const int64_t units = (int64_t)T * (Hq / 32);
         if (units > 0x7fffffffLL)
