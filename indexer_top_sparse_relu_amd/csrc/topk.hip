@@ -777,6 +777,22 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_fast_kernel(Batch bt, co
         o[0] = kTkPending;
 }
 
+// Fewer than 256 rows (the GPU is not filled either way): the single pass and,
+// for a row it cannot finish, the general path in the same workgroup, which then
+// holds the general path's LDS: one launch instead of two.
+__global__ __launch_bounds__(kTkThreads) void topk_rows_one_kernel(Batch bt, const float *__restrict__ scores,
+                                                                   int64_t ld, int K, int32_t *__restrict__ out,
+                                                                   int len_shift)
+{
+    const int row = blockIdx.x;
+    const int n = row_length(bt, row, len_shift);
+    const TkSmem sm = tk_smem(K);
+    const float *vals = scores + (int64_t)row * ld;
+    int32_t *o = out + (int64_t)row * K;
+    if (!select_topk_fast<kBins, 3>(vals, n, (ld & 3) == 0, 0, K, o, nullptr, sm))
+        select_topk<false>(vals, nullptr, n, 0, K, o, nullptr, sm);
+}
+
 // Rows of up to 512 * PER slots, one workgroup each, in one launch: the row is
 // loaded once into registers (thread t holds the 4-slot groups t, t + 512, ...,
 // so every load is coalesced), the K-th largest key is found by three LDS
@@ -1232,6 +1248,8 @@ hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *score
         // above the default dynamic-LDS limit: raise it for the kernels this plan launches
         if (hipFuncSetAttribute((const void *)topk_rows_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)smem) != hipSuccess ||
+            hipFuncSetAttribute((const void *)topk_rows_one_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)smem) != hipSuccess ||
             hipFuncSetAttribute((const void *)topk_chunk_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)smem) != hipSuccess ||
             hipFuncSetAttribute((const void *)topk_merge_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1258,6 +1276,11 @@ hipError_t launch_topk(const Batch &bt, const TopkPlan &plan, const float *score
                            scores, ld, plan.chunk, plan.n_chunks, (const uint32_t *)thr, counts, pairs, len_shift);
         hipLaunchKernelGGL(topk_thr_finish_kernel, dim3(bt.total_q), dim3(kTkThreads), smem, st, bt, scores, ld, k,
                            plan.n_chunks, (const uint32_t *)thr, (const int32_t *)counts, (const u32x2 *)pairs,
+                           indices, len_shift);
+        return hipGetLastError();
+    }
+    if (!plan.chunked && bt.total_q < 256) {
+        hipLaunchKernelGGL(topk_rows_one_kernel, dim3(bt.total_q), dim3(kTkThreads), smem, st, bt, scores, ld, k,
                            indices, len_shift);
         return hipGetLastError();
     }

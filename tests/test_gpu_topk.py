@@ -120,6 +120,15 @@ def test_topk_rows_kernel_crafted_rows():
     assert wsb == 0                       # 256 rows: no chunking
 
 
+def test_topk_few_rows_crafted():
+    """Fewer than 256 rows of 9K-40K (one launch: the single pass, and the general path in the same
+    workgroup for the rows it cannot finish), every pattern."""
+    rng = np.random.default_rng(17)
+    lengths = rng.integers(9000, 40000, 96).tolist()
+    P.say("[topk-few] 96 rows, K=2048")
+    assert run_rows(lengths, KINDS, 2048, seed=18) == 0
+
+
 def test_topk_chunked_crafted_rows():
     """Few long rows (sampled threshold, chunk compaction, per-row finish), every pattern."""
     lengths = [300000, 150001, 70000, 40960, 262144, 100000, 65537, 200000]
