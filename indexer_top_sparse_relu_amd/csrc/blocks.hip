@@ -135,17 +135,25 @@ __global__ __launch_bounds__(kBlkThreads) void qbar_kernel(const uint8_t *__rest
         qbar[i * d_qk + d] = sums[d];
 }
 
-// Block scores on fp32 MFMA (32x32x2): a workgroup takes 32 consecutive
-// tokens of one sequence and 128 blocks (32 per wave).  Over each 32-dim
-// chunk of d_qk, lane half hf supplies dims 16hf .. 16hf+15 of its token row
-// (A) and block row (B) to 16 MFMAs, so both operands are contiguous 64-byte
-// loads; the next chunk's loads are issued before this chunk's MFMAs.  Tokens
-// past the tile and blocks past the sequence read row 0 and are not stored.
+// Block scores on fp32 MFMA (32x32x2): a workgroup takes 32 consecutive tokens
+// of one sequence and 128 blocks (32 per wave).  Each 32-dim chunk of the token
+// rows (A) and the block rows (B) goes into LDS by direct loads of whole
+// 128-byte row pieces (8 rows per load instruction), double-buffered; lane (row
+// l % 32, half h) then reads dims 16h .. 16h+15 of its rows with four 16-byte
+// LDS reads.  Chunk c of row r sits at slot c ^ ((r >> 1) & 7), so the 16 lanes
+// of a read phase hit distinct banks.  Tokens past the tile and blocks past the
+// sequence read row 0 and are not stored.  (Loaded straight into the MFMA
+// layout, every load instruction touched 32 rows: the address unit's cost.)
+constexpr int kBsRows = kBlkTok + kBlkCols;     // LDS rows of 128 bytes per chunk
+constexpr int kBsLoads = kBsRows / 8 / 4;       // direct loads per wave per chunk
+static_assert(kBsRows % 32 == 0, "whole load instructions per wave");
+
 __global__ __launch_bounds__(kBlkThreads) void block_scores_kernel(Batch bt, const float *__restrict__ qbar, int d_qk,
                                                                    const float *__restrict__ k_blocks,
                                                                    float *__restrict__ scores, int64_t ld,
                                                                    int n_tiles_max)
 {
+    __shared__ __align__(16) uint8_t lbuf[2][kBsRows * 128];
     int tile = blockIdx.x;
     if (tile >= n_tiles_max)
         return;
@@ -164,36 +172,59 @@ __global__ __launch_bounds__(kBlkThreads) void block_scores_kernel(Batch bt, con
     const int ntok = min(kBlkTok, nq - tile * kBlkTok);
     const int pos0 = bt.ctx_len[b] - nq + tile * kBlkTok;        // position of token tok0
     const int nb_max = ((pos0 + ntok - 1) >> bt.page_shift) + 1;  // candidate blocks of the tile's last token
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int j0 = blockIdx.y * kBlkCols + wv * 32;
-    if (j0 >= nb_max)
-        return;
+    const int jg0 = blockIdx.y * kBlkCols;
+    if (jg0 >= nb_max)
+        return;                             // the whole workgroup
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 31, hf = lane >> 5;
-    const int tr = col < ntok ? col : 0;
-    const int jb = j0 + col < nb_max ? j0 + col : 0;
-    const float *arow = qbar + (int64_t)(tok0 + tr) * d_qk + 16 * hf;
-    const float *brow = k_blocks + (int64_t)bt.page_table[(int64_t)b * bt.max_pages + jb] * d_qk + 16 * hf;
-    const int nch = d_qk / 32;
-    f32x4 a[2][4], bb[2][4];
-    auto load = [&](int c, int buf) {
+    // load i of this wave covers LDS rows 8u .. 8u+7, u = wv + 4i: lane l brings the
+    // 16 bytes of physical slot l & 7 of row 8u + (l >> 3), i.e. its logical chunk
+    // (l & 7) ^ ((row >> 1) & 7); rows 0..31 are the tile's tokens, rows 32.. its blocks
+    const float *src[kBsLoads];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            a[buf][u] = *(const f32x4 *)(arow + 32 * c + 4 * u);
-            bb[buf][u] = *(const f32x4 *)(brow + 32 * c + 4 * u);
+    for (int i = 0; i < kBsLoads; ++i) {
+        const int row = 8 * (wv + 4 * i) + (lane >> 3);
+        const int lc = (lane & 7) ^ ((row >> 1) & 7);
+        const float *rp;
+        if (row < kBlkTok) {
+            rp = qbar + (int64_t)(tok0 + (row < ntok ? row : 0)) * d_qk;
+        } else {
+            const int j = jg0 + row - kBlkTok;
+            rp = k_blocks + (int64_t)bt.page_table[(int64_t)b * bt.max_pages + (j < nb_max ? j : 0)] * d_qk;
         }
+        src[i] = rp + 4 * lc;
+    }
+    auto issue = [&](int c, int buf) {
+#pragma unroll
+        for (int i = 0; i < kBsLoads; ++i)
+            dma_b128(src[i] + 32 * c, (const lds_u8 *)&lbuf[buf][(wv + 4 * i) * 1024]);
     };
+    const int ra = col, rb = kBlkTok + wv * 32 + col;
+    auto ld4 = [&](int buf, int row, int q) {
+        const int slot = (4 * hf + q) ^ ((row >> 1) & 7);
+        return *(const __attribute__((address_space(3))) f32x4 *)&lbuf[buf][row * 128 + 16 * slot];
+    };
+    const int nch = d_qk / 32;
     f32x16 acc = f32x16{};
-    load(0, 0);
+    issue(0, 0);
     for (int c = 0; c < nch; ++c) {
         const int cur = c & 1;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");    // this wave's loads of chunk c
+        __syncthreads();                    // every wave's loads of chunk c; buffer cur ^ 1 is free
         if (c + 1 < nch)
-            load(c + 1, cur ^ 1);
+            issue(c + 1, cur ^ 1);
+        f32x4 a[4], bb[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            a[q] = ld4(cur, ra, q);
+            bb[q] = ld4(cur, rb, q);
+        }
 #pragma unroll
         for (int m = 0; m < 16; ++m)
-            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[cur][m >> 2][m & 3], bb[cur][m >> 2][m & 3], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[m >> 2][m & 3], bb[m >> 2][m & 3], acc, 0, 0, 0);
     }
-    // output: lane holds block column j0 + col, token rows 8*(i/4) + 4*hf + i%4
-    const int j = j0 + col;
+    // output: lane holds block column jg0 + 32wv + col, token rows 8*(i/4) + 4*hf + i%4
+    const int j = jg0 + wv * 32 + col;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         const int r = 8 * (i >> 2) + 4 * hf + (i & 3);

@@ -101,3 +101,9 @@ def test_block_selection_ragged_prefill_fp32():
     spec = W.tiny_prefill_fp32().replace(q_lens=(40, 70), ctx_lens=(300, 70), page_size=16, paged_random=True,
                                          seed=42)
     check_blocks(spec, kb=4, tag="blocks-f32")
+
+
+def test_block_selection_long_context():
+    """More than 128 candidate blocks per token: the scoring spans several column groups of workgroups."""
+    spec = W.chunked_prefill_mla(cached=20000, T=70).replace(seed=43)
+    check_blocks(spec, kb=8, tag="blocks-long", attn_rows=P.sample_tokens(70, 8, seed=10))
