@@ -377,14 +377,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             const int r = which < NB ? krow_of(which, ln) : 64 * (which - NB) + ln;
             return min(t0 + r, kb1 - 1);
         };
+        // The row blocks' pages come from one LDS read (lane w reads block w's) and
+        // reach scalar registers by lane reads, so the wave waits on a single LDS
+        // round trip for them.
         auto pages = [&](int tt, int ln) {
             Pg g;
             const int t0 = kb0 + tt * LT;
+            const int wl = min(ln, NB - 1);
+            const int pw = lpt[(min(t0 + 8 * (kIdxWaves * wl + wv), kb1 - 1) >> pshift) - pg0];
 #pragma unroll
             for (int w = 0; w < NB + NS; ++w) {
                 if (w < NB)
-                    g.p[w] = __builtin_amdgcn_readfirstlane(
-                        lpt[(min(t0 + 8 * (kIdxWaves * w + wv), kb1 - 1) >> pshift) - pg0]);
+                    g.p[w] = __builtin_amdgcn_readlane(pw, w);
                 else
                     g.p[w] = lpt[(kpos(tt, ln, w) >> pshift) - pg0];
             }
