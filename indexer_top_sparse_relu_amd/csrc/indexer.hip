@@ -428,6 +428,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
         int lim[2];
         uint32_t rowoff[2];
         float qh[2];
+        // With one token per half (two per wave) the limit is wave-uniform: each
+        // token gets a buffer resource of exactly its lim scores, so the range
+        // check drops positions past it and the other half's lanes carry an
+        // offset past the end; a store then needs one address operation.
+        __amdgpu_buffer_rsrc_t srt[2];
 #pragma unroll
         for (int gh = 0; gh < 2; ++gh) {
             const int tw = TH == 1 ? 0 : half;
@@ -436,6 +441,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
             lim[gh] = writes ? min(kb1, pos0 + tl + 1) : 0;
             rowoff[gh] = writes ? (uint32_t)((int64_t)(tl - wt0) * ld * 4) : 0u;
             qh[gh] = 0.5f * ((TH > 1 && half) ? qs[gh * TH + TH - 1] : qs[gh * TH]);
+            if constexpr (TH == 1) {
+                const int tu = wv * TPW + gh;                       // wave-uniform
+                const int lu = tu < ntok ? min(kb1, pos0 + tu + 1) : 0;
+                srt[gh] = __builtin_amdgcn_make_buffer_rsrc(scores + (int64_t)(tok0 + min(tu, ntok - 1)) * ld, 0,
+                                                            4 * lu, 0x00020000);
+                rowoff[gh] = half == gh ? 0u : 0x80000000u;
+            }
         }
         auto epi = [&](const f32x16 (&c)[MH], int gh, int s, float ks_s, float L) {
             float acc[TH];
@@ -456,8 +468,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                 acc[t] = sum_halves(acc[t]);
             // writer of token gh*TH + t is the half t%2 (TH == 2) or half gh (TH == 1)
             const float a = (TH > 1 && half) ? acc[TH - 1] : acc[0];
-            const uint32_t off = s < lim[gh] ? rowoff[gh] + 4u * (uint32_t)s : 0x80000000u;
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((a + L) * qh[gh] * ks_s), srs, off, 0, 0);
+            if constexpr (TH == 1) {
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((a + L) * qh[gh] * ks_s), srt[gh],
+                                                      rowoff[gh] + 4u * (uint32_t)s, 0, 0);
+            } else {
+                const uint32_t off = s < lim[gh] ? rowoff[gh] + 4u * (uint32_t)s : 0x80000000u;
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint((a + L) * qh[gh] * ks_s), srs, off, 0, 0);
+            }
         };
         f32x16 c0[MH], c1[MH];
         int s_prev = 0;
