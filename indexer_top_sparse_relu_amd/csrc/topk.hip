@@ -873,7 +873,7 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_reg_kernel(Batch bt, con
     const uint32_t kth = prefix;                // the K-th largest key
     const uint32_t ties = need;                 // keys equal to it that are taken (lowest positions)
     // ---- winners in slot order
-    uint32_t above_done = 0, ties_done = 0;     // before this round, over the whole block
+    uint32_t above_done = 0, ties_done = 0;     // before this group of slots, over the whole block
 #pragma unroll
     for (int u = 0; u < G; ++u) {
         const int j = 4 * (tid + kTkThreads * u);
