@@ -284,8 +284,8 @@ sa_status sparse_block_expand(const sa_batch *batch, const int32_t *block_idx, i
  * (576, 512) with v_cache == k_cache (latent layout); n_q_heads a multiple of
  * 16 up to 256; 1 <= k <= 65536.
  * sparse_gated_attn_bwd_workspace_size: bytes of device workspace (do, Q^T
- * and do^T copies, D, and for the first group of shapes a position bitmap and
- * a byte per slot); 0 for an empty batch.  The workspace is 256-byte aligned
+ * and do^T copies, D, and for the first group of shapes a position bitmap, a
+ * byte per slot and a byte per token); 0 for an empty batch.  The workspace is 256-byte aligned
  * (SA_EINVAL otherwise); fewer bytes than reported: SA_EWORKSPACE.
  */
 size_t sparse_gated_attn_bwd_workspace_size(const sa_batch *batch, int32_t n_q_heads, int32_t d_qk, int32_t d_v,
