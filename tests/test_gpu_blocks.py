@@ -107,3 +107,10 @@ def test_block_selection_long_context():
     """More than 128 candidate blocks per token: the scoring spans several column groups of workgroups."""
     spec = W.chunked_prefill_mla(cached=20000, T=70).replace(seed=43)
     check_blocks(spec, kb=8, tag="blocks-long", attn_rows=P.sample_tokens(70, 8, seed=10))
+
+
+def test_block_selection_large_pages_two_sequences():
+    """256-position blocks over a random page permutation, two ragged bf16 sequences with separate K/V caches."""
+    spec = W.prefill_bf16(T=100).replace(q_lens=(37, 63), ctx_lens=(1500, 700), page_size=256, paged_random=True,
+                                         seed=44)
+    check_blocks(spec, kb=3, tag="blocks-p256")
