@@ -223,7 +223,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int tl = wv * TPW + t;
-        qs[t] = ldexpf(((FP8 && tl < ntok) ? q_scale[tok0 + tl] : 1.0f) * IdxEpi<DT>::UNSCALE, -wsh[t]);
+        qs[t] = ldexpf(((FP8 && tl < ntok) ? q_scale[tok0 + tl] : 1.0f) * (LIN ? 1.0f : IdxEpi<DT>::UNSCALE), -wsh[t]);
     }
 
     // Physical page of every page the chunk touches, staged once in LDS, so a
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                     const int row = TPW == 2 ? 8 * tt + t : 8 * (2 * (tt >> 1) + (t >> 2)) + 4 * (tt & 1) + (t & 3);
                     *(uint16_t *)(myterm + row * LTS + 2 * lane) = (uint16_t)pk;
                     if (lane == 0)
-                        myscl[row] = e + 122;                  // with B's 2^-5: 2^(e - 10)
+                        myscl[row] = e + 127;                  // 2^e (B unscaled)
                 }
             }
         }
@@ -553,7 +553,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
 #pragma unroll
                     for (int w2 = 0; w2 < 2; ++w2)
                         pq[w2] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(at, load_bq(nt, w2), f32x4{}, 0,
-                                                                                  0, 0, sal, 0, 122);
+                                                                                  0, 0, sal, 0, 127);
                     const float sp = (pq[0][0] + pq[0][1]) + (pq[0][2] + pq[0][3]);
                     const float sq = (pq[1][0] + pq[1][1]) + (pq[1][2] + pq[1][3]);
                     const auto x = __builtin_amdgcn_permlane16_swap(__float_as_uint(sp), __float_as_uint(sq), false, false);
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
                         cl = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            *(const i32x8 *)(arow + ks * X::KS), bop[ks], cl, 0, 0, 0, sal, 0, 122);
+                            *(const i32x8 *)(arow + ks * X::KS), bop[ks], cl, 0, 0, 0, sal, 0, 127);
 #pragma unroll
                     for (int i = 0; i < 8; ++i) {
                         La += cl[i];
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                     c0[m] = f32x16{};
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        c0[m] = X::mma(a[m][ks], bop[ks], c0[m]);
+                        c0[m] = mma32_fp8_plain(a[m][ks], bop[ks], c0[m]);
                 }
                 if (it > 0 || nt > 0)
                     epi(c1, 1, s_prev, ks_prev, L_prev);
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
                     c1[m] = f32x16{};
 #pragma unroll
                     for (int ks = 0; ks < NKS; ++ks)
-                        c1[m] = X::mma(a[MH + m][ks], bop[ks], c1[m]);
+                        c1[m] = mma32_fp8_plain(a[MH + m][ks], bop[ks], c1[m]);
                 }
                 if (nt + 1 < LT / 32)
                     cur = load_b(nt + 1);

@@ -103,6 +103,12 @@ __device__ __forceinline__ f32x16 mma32_fp8(i32x8 a, i32x8 b, f32x16 c)
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// The plain (unscaled) instruction: zero scale operands select it.
+__device__ __forceinline__ f32x16 mma32_fp8_plain(i32x8 a, i32x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
 // Same, with both block scales 2^-5 (E8M0 122): the product comes out scaled by
 // 2^-10, which keeps any fp8 dot of length <= 128 (|dot| <= 128 * 448^2) inside
 // the fp16 range for a packed-fp16 epilogue.

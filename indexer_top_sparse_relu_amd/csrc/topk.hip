@@ -766,7 +766,8 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_fast_kernel(Batch bt, co
                                                                     int64_t ld, int K, int32_t *__restrict__ out,
                                                                     int len_shift)
 {
-    const int row = blockIdx.x;
+    // last rows first: the scores a preceding indexer wrote last may still be in the cache
+    const int row = gridDim.x - 1 - blockIdx.x;
     const int n = row_length(bt, row, len_shift);
     const TkSmem sm = tk_smem_fast();
     const float *vals = scores + (int64_t)row * ld;
