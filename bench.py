@@ -101,6 +101,43 @@ def stats_ms(vals):
     return {"mean": sum(vals) / len(vals), "median": statistics.median(vals), "min": min(vals), "max": max(vals)}
 
 
+def graph_step(pl, steps, flush_bytes):
+    """The step (indexer, Top-K, attention) captured once in a HIP graph and replayed, as a serving
+    loop would run it: the graph submits the launches together, so the gaps between kernels shrink.
+    Between replays the outputs get a canary and the cache flush runs (eager work); every replay
+    must reproduce the eager step's indices and output bit for bit."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    ref_idx, ref_out = pl.indices.clone(), pl.out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream()
+        pl.indexer(s)
+        pl.topk(s)
+        pl.attn(s, with_lse=False)
+    flush = torch.empty(flush_bytes // 4, device="cuda") if flush_bytes else None
+    clean = torch.zeros(flush_bytes // 4, device="cuda") if flush_bytes else None
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    same = True
+    for i in range(steps):
+        pl.indices.fill_(-7)
+        if flush is not None:
+            flush.fill_(float(i))
+            clean.amax()
+        ev[i][0].record(stream)
+        g.replay()
+        ev[i][1].record(stream)
+        same = same and torch.equal(pl.indices, ref_idx) and torch.equal(pl.out.view(torch.int16),
+                                                                         ref_out.view(torch.int16))
+    torch.cuda.synchronize()
+    del g, flush, clean
+    st = stats_ms([e[0].elapsed_time(e[1]) for e in ev])
+    assert same, "a graph replay differs from the eager step"
+    return {"ms_per_step": st["median"], "ms_per_step_stats": st,
+            "query_tokens_per_s": pl.wl.spec.T / (st["median"] * 1e-3), "replays_match_eager": same}
+
+
 def machine_info():
     """GPU, ROCm and host facts for the record."""
     import glob
@@ -532,29 +569,49 @@ def main(argv=None):
         pl.run(stream)
     torch.cuda.synchronize()
 
-    # between timed steps a 512 MiB buffer is written on the same stream, outside the event
-    # pairs, so that no step finds its inputs in L2 or the 256 MB MALL left by the previous one
-    flush = torch.empty(FLUSH_BYTES // 4, device="cuda") if not args.no_flush else None
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        if flush is not None:
-            flush.fill_(float(i))
-        e = ev[i]
-        e[0].record(stream)
-        pl.indexer(stream)
-        e[1].record(stream)
-        pl.topk(stream)
-        e[2].record(stream)
-        pl.attn(stream, with_lse=False)
-        e[3].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    del flush
-    per = {"indexer": [e[0].elapsed_time(e[1]) for e in ev], "topk": [e[1].elapsed_time(e[2]) for e in ev],
-           "attn": [e[2].elapsed_time(e[3]) for e in ev], "step": [e[0].elapsed_time(e[3]) for e in ev]}
-    st_ms = {k: stats_ms(v) for k, v in per.items()}
+    # Between timed steps, on the same stream and outside the event pairs, a 512 MiB buffer is
+    # written and then another 512 MiB buffer read, so that no step finds its inputs in L2 or the
+    # 256 MB MALL. The read replaces the written (dirty) lines with clean ones: after a write alone,
+    # the next step's reads would first have to write up to 256 MB of those lines back to HBM, a
+    # cost of the flush, not of the step. The write-only protocol is timed as well and reported.
+    def timed_steps(modes):
+        """args.steps timed steps per flush mode, the modes alternating step by step (so that
+        neither gets the warmer clock); per mode, per stage statistics and the wall time."""
+        wbuf = torch.empty(FLUSH_BYTES // 4, device="cuda") if modes != ["none"] else None
+        rbuf = torch.zeros(FLUSH_BYTES // 4, device="cuda") if "write+read" in modes else None
+        ev = {m: [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+              for m in modes}
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            for m in modes:
+                if m != "none":
+                    wbuf.fill_(float(i))
+                if m == "write+read":
+                    rbuf.amax()
+                e = ev[m][i]
+                e[0].record(stream)
+                pl.indexer(stream)
+                e[1].record(stream)
+                pl.topk(stream)
+                e[2].record(stream)
+                pl.attn(stream, with_lse=False)
+                e[3].record(stream)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / len(modes)
+        del wbuf, rbuf
+        res = {}
+        for m in modes:
+            per = {"indexer": [e[0].elapsed_time(e[1]) for e in ev[m]],
+                   "topk": [e[1].elapsed_time(e[2]) for e in ev[m]],
+                   "attn": [e[2].elapsed_time(e[3]) for e in ev[m]],
+                   "step": [e[0].elapsed_time(e[3]) for e in ev[m]]}
+            res[m] = {k: stats_ms(v) for k, v in per.items()}
+        return res, wall
+
+    res, wall = timed_steps(["none"] if args.no_flush else ["write+read", "write"])
+    st_ms = res["none"] if args.no_flush else res["write+read"]
+    st_write = None if args.no_flush else res["write"]
     stage_ms = {k: st_ms[k]["mean"] for k in ("indexer", "topk", "attn")}
     step_ms = st_ms["step"]["median"]
     wall_ms = wall * 1e3 / args.steps
@@ -616,8 +673,9 @@ def main(argv=None):
         "ms_per_step_stats": st_ms["step"],
         "wall_ms_per_step": wall_ms,
         "timing": ("HIP events on the kernels' stream around each stage; value and ms_per_step from the median "
-                   "step" + ("" if args.no_flush else f"; a {FLUSH_BYTES >> 20} MiB buffer written between steps, "
-                                                       "outside the events, evicts L2 and the MALL")
+                   "step" + ("" if args.no_flush else f"; between steps, outside the events, a {FLUSH_BYTES >> 20} "
+                                                       f"MiB buffer is written and another {FLUSH_BYTES >> 20} MiB "
+                                                       "read, which evicts L2 and the MALL and leaves them clean")
                    + "; roofline achieved from the dominant stage's mean duration"),
         "higher_is_better": True,
         "scaling": "weak",
@@ -631,6 +689,13 @@ def main(argv=None):
         "roofline": roof,
         "stages": rl,
     }
+    if st_write is not None:
+        # the same steps after a write-only flush: the step then also pays for writing the flush's
+        # dirty lines back to HBM
+        line["write_only_flush"] = {"ms_per_step": st_write["step"]["median"],
+                                    "query_tokens_per_s": tokens / (st_write["step"]["median"] * 1e-3),
+                                    "stage_ms_mean": {k: st_write[k]["mean"] for k in ("indexer", "topk", "attn")}}
+    line["graph_step"] = graph_step(pl, args.steps, 0 if args.no_flush else FLUSH_BYTES)
     line["machine"] = machine_info()
     if not args.step_only:
         line["measured_ceilings"] = measured_ceilings(stream)
