@@ -863,8 +863,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int unit = blockIdx.x * NW + wv;
-    if (unit >= n_units)
+    // units in reverse: in causal prefill the last tokens have the longest lists,
+    // so they start first and the short lists of the first tokens fill the tail
+    const int unit = n_units - 1 - (blockIdx.x * NW + wv);
+    if (unit < 0)
         return;
     const int HG = Hq >> 5;
     const int sp = unit % n_split;

@@ -813,7 +813,9 @@ __global__ __launch_bounds__(kTkThreads) void topk_rows_reg_kernel(Batch bt, con
     TkSmem sm;
     sm.hist = hist;
     sm.misc = misc;
-    const int row = blockIdx.x, tid = threadIdx.x;
+    // last rows first: in causal prefill they are the longest (the short rows fill
+    // the tail), and the scores a preceding indexer wrote last may still be cached
+    const int row = gridDim.x - 1 - blockIdx.x, tid = threadIdx.x;
     const int n = row_length(bt, row, len_shift);
     const float *vals = scores + (int64_t)row * ld;
     int32_t *o = out + (int64_t)row * K;
