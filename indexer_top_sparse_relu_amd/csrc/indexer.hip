@@ -84,7 +84,8 @@ template <int DT, int H, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void indexer_tile_kernel(
     Batch bt, const uint8_t *__restrict__ q_idx, const float *__restrict__ q_scale,
     const float *__restrict__ w, const uint8_t *__restrict__ k_idx, const float *__restrict__ k_scale,
-    float *__restrict__ scores, int64_t ld, int key_chunk, int n_chunks, int n_tiles_max, int rotate)
+    float *__restrict__ scores, int64_t ld, int key_chunk, int n_chunks, int n_tiles_max, int rotate,
+    int last_open)
 {
     typedef IdxT<DT> X;
     constexpr int MT = IdxShape<H>::MT, TPW = IdxShape<H>::TPW;
@@ -146,7 +147,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void i
     const int ntok = min(TQ, nq - tile * TQ);
     const int pos0 = bt.ctx_len[b] - nq + tile * TQ;      // position of token tok0
     const int kb0 = chunk * key_chunk;
-    const int kb1 = min(kb0 + key_chunk, pos0 + ntok);    // last token sees pos0+ntok-1
+    // last token sees pos0+ntok-1; an open last chunk runs to it
+    const int kb1 = (last_open && chunk == n_chunks - 1) ? pos0 + ntok : min(kb0 + key_chunk, pos0 + ntok);
     if (kb0 >= kb1)
         return;
 
@@ -1160,9 +1162,25 @@ static hipError_t launch_indexer_t(const Batch &bt, const void *q_idx, const flo
         // rotate the chunk -> XCD map when every chunk's keys fit in one L2 together
         const int64_t key_bytes = (int64_t)n_chunks * key_chunk * D * IdxT<DT>::ELEM;
         const int rotate = n_chunks % 8 == 0 && key_bytes <= (2 << 20);
+        // Without rotation chunk c runs on XCD c % 8, and equal chunks of max_ctx keys
+        // give the last one less causal work (its tokens stop at their own positions):
+        // at 4096 new tokens on 131072 cached ones it has 88% of the others' pairs, and
+        // its XCD idles for the rest.  Chunks sized on the mean causal limit of the
+        // longest query run, with the last chunk open to each token's limit, even that
+        // out, as long as the longer last chunk's pages fit the staged page table.
+        int last_open = 0;
+        if (!rotate && n_chunks % 8 == 0 && n_chunks > 1) {
+            int kc = (bt.max_ctx - bt.max_q / 2 + n_chunks - 1) / n_chunks;
+            kc = (kc + kIdxTileKeys - 1) / kIdxTileKeys * kIdxTileKeys;
+            const int last_len = bt.max_ctx - (n_chunks - 1) * kc;
+            if (kc < key_chunk && (last_len >> bt.page_shift) + 2 <= kIdxMaxChunk / 16 + 2) {
+                key_chunk = kc;
+                last_open = 1;
+            }
+        }
         hipLaunchKernelGGL((indexer_tile_kernel<DT, H, D>), dim3((unsigned)grid), dim3(256), 0, st, bt,
                            (const uint8_t *)q_idx, q_scale, w, (const uint8_t *)k_idx, k_scale, scores, ld,
-                           key_chunk, n_chunks, n_tiles_max, rotate);
+                           key_chunk, n_chunks, n_tiles_max, rotate, last_open);
     } else {
         // enough workgroups to cover the GPU even for a handful of sequences
         int key_chunk = kIdxTokChunk;
