@@ -198,6 +198,33 @@ def test_chunked_prefill_mla_full_size_sampled():
     P.say(f"[mla-prefill-full] ok: attention on {len(arows)} rows, worst {w2:.2f} of the bound")
 
 
+@pytest.mark.parametrize("page_size", [64, 16])
+def test_chunked_prefill_two_sequences_balanced_chunks(page_size):
+    """Prefill key chunks sized on the mean causal limit, the last one open to each token's
+    limit (long contexts: no rotation), in a batch whose longest query run and longest
+    context belong to different sequences: scores, Top-K exactness and the selection rule
+    on sampled rows of both."""
+    spec = W.chunked_prefill_mla(cached=0, T=0).replace(q_lens=(48, 400), ctx_lens=(40000, 22000),
+                                                        page_size=page_size, seed=90 + page_size)
+    P.say(f"[mla-prefill-2seq-p{page_size}] T={spec.T} ctx={spec.ctx_lens}")
+    wl = W.generate(spec, DEV)
+    pl = run(wl, stages=("indexer", "topk"))
+    seq, pos, n = P.token_geometry(spec)
+    idx = pl.indices.cpu().numpy()
+    P.check_idx_invariants(idx, n, spec.K)
+    rows = np.asarray(sorted(set(P.sample_tokens(48, 12, seed=1, edge=3)) |
+                             {48 + r for r in P.sample_tokens(400, 20, seed=2, edge=4)}))
+    sc = pl.scores[torch.as_tensor(rows, device=DEV)].cpu().numpy()
+    for i, r in enumerate(rows):
+        assert np.all(np.isnan(sc[i, n[r]:])), f"row {r} written past n"
+    P.check_topk_exact(idx[rows], sc, n[rows], spec.K)
+    inp = O.Inputs.from_workload(wl)
+    ref = O.indexer(inp, rows=rows, ld=pl.ld)
+    w1 = P.check_scores(sc, ref, n[rows], P.RTOL["fp8"])
+    rec = P.check_selection(idx[rows], ref, n[rows], spec.K)
+    P.say(f"[mla-prefill-2seq-p{page_size}] ok on {len(rows)} rows: worst rel {w1:.2e}, recall {rec:.4f}")
+
+
 def test_long_decode_mla_reduced_with_ties():
     spec = W.long_decode_mla(lo=5000, hi=40000)
     full_check(spec, "long-decode-reduced")
