@@ -174,22 +174,38 @@ def machine_info():
         if clocks:
             break
     info["clocks"] = clocks or None
-    cpu = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            for line in f:
-                if line.startswith("model name"):
-                    cpu = line.split(":", 1)[1].strip()
-                    break
-    except OSError:
-        pass
-    info["cpu"] = cpu or platform.processor()
+    info.update(machine_info_cpu())
     info["host_cpus"] = os.cpu_count()
     try:
         info["host_cpus_usable"] = len(os.sched_getaffinity(0))
     except AttributeError:
         info["host_cpus_usable"] = None
     return info
+
+
+def machine_info_cpu():
+    """The host CPU: its model name and identification fields."""
+    import platform
+
+    cpu, ids = None, {}
+    try:
+        # the first processor's entry: a virtualised host may give only the brand as its
+        # model name, so the family, model number and stepping (the generation) go with it
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if not line.strip():
+                    break
+                key, _, val = line.partition(":")
+                key, val = key.strip(), val.strip()
+                if key == "model name":
+                    cpu = val
+                elif key in ("vendor_id", "cpu family", "model", "stepping", "cpu MHz"):
+                    ids[key.replace(" ", "_")] = val
+                elif key == "flags":
+                    ids["avx512f"] = "avx512f" in val.split()
+    except OSError:
+        pass
+    return {"cpu": cpu or platform.processor(), "cpu_id": ids or None}
 
 
 def measured_ceilings(stream):
@@ -281,7 +297,8 @@ def cpu_baseline(wl, gpu_indices, sample_tokens: int):
     return {"value": S / dt, "unit": "query_tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"last {S} of {s.T} query tokens (positions {s.ctx_lens[-1] - S}..{s.ctx_lens[-1] - 1}), "
                       f"full indexer + Top-K + gated attention in fp64, {dt:.1f} s",
-            "recall_at_K": float(np.mean(rec)), "recall_min": float(np.min(rec)), "recall_rows": S}
+            "recall_at_K": float(np.mean(rec)), "recall_min": float(np.min(rec)), "recall_rows": S,
+            "cpu": {k: machine_info_cpu()[k] for k in ("cpu", "cpu_id")}}
 
 
 def before_path(wl, steps: int, stream):
