@@ -56,8 +56,10 @@ template <> struct IdxT<2> {
     static __device__ __forceinline__ Op load(const uint8_t *p) { return *(const i32x8 *)p; }
     static __device__ __forceinline__ f32x16 mma(Op a, Op b, f32x16 c) { return mma32_fp8_s10(a, b, c); }
 };
-// fp8 MFMAs return dots scaled by 2^-10 (UNSCALE gives it back per score);
-// with at least 8 heads the fp8 epilogue runs on packed fp16 pairs.
+// fp8 MFMAs of the packed-fp16 epilogue return dots scaled by 2^-10 (UNSCALE
+// gives it back per score); with at least 8 heads the fp8 epilogue runs on
+// packed fp16 pairs.  The linear-term path (fp32 epilogue) takes the products
+// unscaled.
 template <int DT> struct IdxEpi {
     static constexpr bool F16 = DT == 2;
     static constexpr float UNSCALE = DT == 2 ? 1024.0f : 1.0f;
